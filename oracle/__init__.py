@@ -1,0 +1,143 @@
+"""fp64 sequential oracle of the selective state-space scan (ctypes wrapper over ssm_oracle.c).
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg
+of ``bench.py`` may import this package. The GPU library never loads it, and it imports nothing
+from the GPU package: the two share no code.
+
+Every array goes in and comes out as float64 (bf16 and fp32 inputs widen to float64 exactly).
+Layouts follow the C header: x, delta, z, y are [b, d, L]; A is [d, N]; B, C are [b, L, N];
+D is [d]; states are [b, d, N].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "ssm_oracle.c")
+LIB_PATH = os.path.join(_HERE, "libssm_oracle.so")
+
+_DP = ctypes.POINTER(ctypes.c_double)
+
+
+def compile_library(src: str, out: str) -> str:
+    """gcc build of an oracle source file into a shared library (always recompiles)."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+           "-Wall", "-Wextra", "-I", _HERE, "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build() -> str:
+    """Compile the oracle library in place. Returns its path."""
+    return compile_library(SOURCE, LIB_PATH)
+
+
+def _f64(a, shape=None):
+    if a is None:
+        return None
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if shape is not None and arr.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {arr.shape}")
+    return arr
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_DP)
+
+
+class Oracle:
+    """The oracle's entry points bound to one compiled library."""
+
+    def __init__(self, lib_path: str = LIB_PATH):
+        if lib_path == LIB_PATH and not os.path.exists(LIB_PATH):
+            build()
+        lib = ctypes.CDLL(lib_path)
+        L = ctypes.c_long
+        lib.oracle_scan_fwd.argtypes = [_DP] * 10 + [L, L, L, L]
+        lib.oracle_scan_fwd.restype = ctypes.c_int
+        lib.oracle_scan_step.argtypes = [_DP] * 9 + [L, L, L]
+        lib.oracle_scan_step.restype = ctypes.c_int
+        lib.oracle_zoh.argtypes = [ctypes.c_double, ctypes.c_double, _DP, _DP]
+        lib.oracle_zoh.restype = None
+        self.lib = lib
+        self.path = lib_path
+
+    def zoh(self, delta: float, a: float):
+        """(Ā, bcoef) for one diagonal entry, with B̄ = bcoef · B."""
+        ab = ctypes.c_double()
+        bc = ctypes.c_double()
+        self.lib.oracle_zoh(float(delta), float(a), ctypes.byref(ab), ctypes.byref(bc))
+        return ab.value, bc.value
+
+    def scan_fwd(self, x, delta, A, B, C, D=None, z=None, h0=None):
+        """Prefill: returns (y [b, d, L], h_final [b, d, N]), both float64."""
+        x = _f64(x)
+        if x.ndim != 3:
+            raise ValueError("x must be [b, d, L]")
+        b, d, L = x.shape
+        A = _f64(A)
+        if A.ndim != 2:
+            raise ValueError("A must be [d, N]")
+        N = A.shape[1]
+        delta = _f64(delta, (b, d, L))
+        A = _f64(A, (d, N))
+        B = _f64(B, (b, L, N))
+        C = _f64(C, (b, L, N))
+        D = _f64(D, (d,))
+        z = _f64(z, (b, d, L))
+        h0 = _f64(h0, (b, d, N))
+        y = np.empty((b, d, L), dtype=np.float64)
+        h = np.empty((b, d, N), dtype=np.float64)
+        rc = self.lib.oracle_scan_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                      _ptr(z), _ptr(h0), _ptr(y), _ptr(h), b, d, L, N)
+        if rc != 0:
+            raise ValueError("oracle_scan_fwd rejected its arguments")
+        return y, h
+
+    def scan_step(self, state, x, delta, A, B, C, D=None, z=None):
+        """Decode step: returns (y [b, d], new_state [b, d, N]); `state` itself is not modified."""
+        st = np.array(_f64(state), dtype=np.float64, copy=True)
+        if st.ndim != 3:
+            raise ValueError("state must be [b, d, N]")
+        b, d, N = st.shape
+        x = _f64(x, (b, d))
+        delta = _f64(delta, (b, d))
+        A = _f64(A, (d, N))
+        B = _f64(B, (b, N))
+        C = _f64(C, (b, N))
+        D = _f64(D, (d,))
+        z = _f64(z, (b, d))
+        y = np.empty((b, d), dtype=np.float64)
+        rc = self.lib.oracle_scan_step(_ptr(st), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                       _ptr(D), _ptr(z), _ptr(y), b, d, N)
+        if rc != 0:
+            raise ValueError("oracle_scan_step rejected its arguments")
+        return y, st
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def zoh(delta, a):
+    return default().zoh(delta, a)
+
+
+def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None):
+    return default().scan_fwd(x, delta, A, B, C, D, z, h0)
+
+
+def scan_step(state, x, delta, A, B, C, D=None, z=None):
+    return default().scan_step(state, x, delta, A, B, C, D, z)

@@ -1,0 +1,62 @@
+/*
+ * ssm_oracle.h — fp64 sequential reference of the selective state-space scan.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link, load or call this
+ * library: only the test suite, the smoke check and the CPU-baseline leg of the benchmark use it.
+ * It shares no code, header, table or constant with the GPU library.
+ *
+ * Sources (page title, then section / equation):
+ *   [SSM-intro]  "State Space Models（SSM）とMamba" (hatohato.jp ai_intro):
+ *                §2.1 continuous-time SSM, §2.2 ZOH discretisation and the discrete update,
+ *                §4.2 selective SSM (per-token Δ, B, C).
+ *   [kasblo]     "Mambaとは？Transformer以外の系列モデル" (kasblo.com):
+ *                section "状態空間モデルを一つの式から理解する" (ẋ = Ah + Bx, y = Ch + Dx; ZOH for
+ *                Ā and B̄; the recurrent form h_t = Ā h_{t−1} + B̄ x_t, y_t = C h_t + D x_t),
+ *                section "Mambaの核心は入力依存のDelta、B、C" (Δ_t, B_t, C_t per token; A not),
+ *                section "Mamba blockのarchitecture" (main-branch output times SiLU of the gate).
+ *   [sharin]     "Mamba / SSMと拡散LM" (sharin-2a1.pages.dev), section ① (the scan updates the state
+ *                first and then reads it out at the same step).
+ *
+ * Readings where the pages leave a step open (each one is listed in the design notes):
+ *   - A is diagonal, stored per channel as A[d][n]; B_t and C_t are shared by all channels of a batch
+ *     row, stored as B[b][t][n], C[b][t][n].
+ *   - ZOH for a diagonal entry a: Ā = exp(Δ·a), B̄ = (exp(Δ·a) − 1)/a · B; at a = 0 the continuous
+ *     limit Ā = 1, B̄ = Δ·B is used.
+ *   - The readout uses the updated state h_t, plus the skip term D·x_t (D may be absent = 0).
+ *   - The optional gate multiplies the SSM output by silu(z) = z / (1 + exp(−z)).
+ *   - Prefill starts from the zero state unless an initial state is given.
+ *
+ * Layout (all row-major, all values fp64):
+ *   x, delta, z, y : [b][d][L]
+ *   A              : [d][N]
+ *   B, C           : [b][L][N]
+ *   D              : [d]
+ *   h0, h          : [b][d][N]
+ */
+#ifndef SSM_ORACLE_H
+#define SSM_ORACLE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Sequential prefill scan over every (b, d) row. D, z, h0 and h may be NULL.
+ * Returns 0 on success, -1 on a NULL required pointer or a negative size. */
+int oracle_scan_fwd(const double *x, const double *delta, const double *A, const double *B,
+                    const double *C, const double *D, const double *z, const double *h0,
+                    double *y, double *h, long b, long d, long L, long N);
+
+/* One recurrent step per (b, d): state[b][d][N] is read as h_{t−1} and overwritten with h_t.
+ * x, delta, z, y are [b][d]; B, C are [b][N]. D and z may be NULL. Returns 0 or -1. */
+int oracle_scan_step(double *state, const double *x, const double *delta, const double *A,
+                     const double *B, const double *C, const double *D, const double *z,
+                     double *y, long b, long d, long N);
+
+/* ZOH coefficients of one diagonal entry: *abar = exp(delta·a), *bcoef = (exp(delta·a) − 1)/a
+ * (delta at a = 0), so that B̄ = bcoef · B. */
+void oracle_zoh(double delta, double a, double *abar, double *bcoef);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,297 @@
+"""Pins of the fp64 oracle: checks against what the pages print and what mathematics fixes.
+
+Each pin takes an oracle instance (so the mutation test can run them on deliberately broken
+builds) and raises AssertionError when the oracle disagrees. None of them re-types the oracle's
+own formulas: ZOH is re-derived through the matrix exponential of the augmented system (Van Loan),
+the LTI case through the convolution kernel K̄, the selective case through a brute-force unroll of
+the time-varying products, and associativity through random tree-ordered affine compositions.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import scipy.linalg
+from scipy.special import expit
+
+from conftest import read_golden
+
+
+# ---------------------------------------------------------------------------------------------
+# Independent constructions
+# ---------------------------------------------------------------------------------------------
+def zoh_vanloan(a_diag, b_vec, delta):
+    """Exact ZOH of h' = diag(a) h + b x with x held over [0, Δ]:
+    expm([[ΔA, Δb], [0, 0]]) = [[Ā, B̄], [0, 1]] (Van Loan's block exponential)."""
+    a_diag = np.asarray(a_diag, dtype=np.float64)
+    N = a_diag.shape[0]
+    M = np.zeros((N + 1, N + 1))
+    M[:N, :N] = np.diag(a_diag) * delta
+    M[:N, N] = np.asarray(b_vec, dtype=np.float64) * delta
+    E = scipy.linalg.expm(M)
+    return E[:N, :N], E[:N, N]
+
+
+def silu_lib(v):
+    return v * expit(v)
+
+
+def _close(got, want, rtol=1e-11, atol=1e-12, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, f"{what}: shape {got.shape} vs {want.shape}"
+    err = np.abs(got - want)
+    bound = atol + rtol * np.abs(want)
+    bad = ~(err <= bound)
+    assert not bad.any(), f"{what}: max err {err.max():.3e} at {np.unravel_index(err.argmax(), err.shape)}"
+
+
+def _golden_pairs(name):
+    out = {}
+    for row in read_golden(name):
+        if len(row) == 2:
+            out[row[0]] = float(row[1])
+    return out
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------------------------
+# Pins
+# ---------------------------------------------------------------------------------------------
+def pin_scalar_worked_example(orc):
+    """kasblo page, scalar example: Ā, B̄ and the four printed impulse weights."""
+    g = _golden_pairs("kasblo_scalar_example.txt")
+    half = 0.5 * 10.0 ** (-g["printed_decimals"])
+    abar, bcoef = orc.zoh(g["delta"], g["A"])
+    bbar = bcoef * g["B"]
+    assert abs(abar - g["abar"]) <= half, abar
+    assert abs(bbar - g["bbar"]) <= half, bbar
+    # the page's closed forms: Ā = e^{-1/2}, B̄ = 1 - e^{-1/2}
+    _close(abar, math.exp(-0.5), what="abar closed form")
+    _close(bbar, 1.0 - math.exp(-0.5), what="bbar closed form")
+    L = 8
+    x = np.zeros((1, 1, L)); x[0, 0, 0] = 1.0
+    y, _ = orc.scan_fwd(x, np.full((1, 1, L), g["delta"]), [[g["A"]]], np.full((1, L, 1), g["B"]),
+                        np.full((1, L, 1), g["C"]), D=[g["D"]])
+    for k in range(4):
+        assert abs(y[0, 0, k] - g[f"weight_lag{k}"]) <= half, (k, y[0, 0, k])
+    # unrolled closed form: y_k = B̄ Ā^k for an impulse (C = 1)
+    _close(y[0, 0], (1.0 - math.exp(-0.5)) * np.exp(-0.5 * np.arange(L)), what="impulse response")
+
+
+def pin_delta_gate(orc):
+    """kasblo page, Δ as a gate: printed retention for Δ = 0.1 and Δ = 2 at A = -1."""
+    rows = read_golden("kasblo_delta_gate.txt")
+    hdr = {r[0]: float(r[1]) for r in rows if len(r) == 2}
+    half = 0.5 * 10.0 ** (-hdr["printed_decimals"])
+    cases = [(float(r[1]), float(r[3])) for r in rows if len(r) == 4 and r[0] == "delta"]
+    assert len(cases) == 2
+    for dlt, printed in cases:
+        abar, _ = orc.zoh(dlt, hdr["A"])
+        assert abs(abar - printed) <= half, (dlt, abar)
+        _close(abar, math.exp(-dlt), what="retention closed form")
+
+
+def pin_decay_impulse(orc):
+    """sharin page §①: an impulse under decay 0.8 has all but vanished 50 steps later (0.8^50)."""
+    g = _golden_pairs("sharin_scan_properties.txt")
+    r, steps = g["decay"], int(g["steps"])
+    A = math.log(r)
+    B = A / (r - 1.0)  # makes B̄ = (r - 1)/A · B = 1
+    L = steps + 1
+    x = np.zeros((1, 1, L)); x[0, 0, 0] = 1.0
+    y, h = orc.scan_fwd(x, np.ones((1, 1, L)), [[A]], np.full((1, L, 1), B), np.ones((1, L, 1)),
+                        D=[0.0])
+    _close(y[0, 0], r ** np.arange(L), rtol=1e-12, what="0.8^t")
+    assert y[0, 0, steps] / y[0, 0, 0] < 1e-4
+    _close(h[0, 0, 0], r ** steps, rtol=1e-12, what="state after 50 steps")
+
+
+def pin_cumulative_sum(orc):
+    """sharin page §①: discrete a = 1 accumulates; here the continuous limit A = 0."""
+    L = 128
+    rng = _rng(11)
+    x = rng.integers(-8, 9, size=(1, 1, L)).astype(np.float64)
+    y, h = orc.scan_fwd(x, np.ones((1, 1, L)), [[0.0]], np.ones((1, L, 1)), np.ones((1, L, 1)),
+                        D=[0.0])
+    assert np.array_equal(y[0, 0], np.cumsum(x[0, 0])), "A = 0 must give the exact running sum"
+    assert h[0, 0, 0] == np.sum(x)
+
+
+def pin_lti_convolution(orc):
+    """Time-invariant Δ, B, C: the scan equals y = x * K̄ + D x with K̄_k = C Ā^k B̄
+    ("State Space Models（SSM）とMamba" §2.3; kasblo page, recurrence vs convolution section)."""
+    rng = _rng(3)
+    b, d, N, L = 2, 2, 4, 16
+    A = -rng.uniform(0.2, 2.0, size=(d, N)); A[1, 2] = 0.0
+    dl = rng.uniform(0.05, 0.8, size=(b, d))
+    Bv = rng.normal(size=(b, N)); Cv = rng.normal(size=(b, N)); D = rng.normal(size=d)
+    x = rng.normal(size=(b, d, L))
+    delta = np.repeat(dl[:, :, None], L, axis=2)
+    B = np.repeat(Bv[:, None, :], L, axis=1); C = np.repeat(Cv[:, None, :], L, axis=1)
+    y, _ = orc.scan_fwd(x, delta, A, B, C, D=D)
+    want = np.empty_like(y)
+    for ib in range(b):
+        for idd in range(d):
+            Ab, Bb = zoh_vanloan(A[idd], Bv[ib], dl[ib, idd])
+            K = np.array([Cv[ib] @ np.linalg.matrix_power(Ab, k) @ Bb for k in range(L)])
+            want[ib, idd] = np.convolve(x[ib, idd], K)[:L] + D[idd] * x[ib, idd]
+    _close(y, want, what="LTI convolution")
+
+
+def pin_selective_unroll(orc):
+    """Time-varying Δ_t, B_t, C_t: brute-force unroll y_t = Σ_{s<=t} C_t (Π_{r=s+1..t} Ā_r) B̄_s x_s + D x_t."""
+    rng = _rng(5)
+    b, d, N, L = 2, 3, 5, 12
+    A = -rng.uniform(0.1, 3.0, size=(d, N)); A[2, 0] = 0.0
+    delta = rng.uniform(0.01, 1.5, size=(b, d, L))
+    B = rng.normal(size=(b, L, N)); C = rng.normal(size=(b, L, N)); D = rng.normal(size=d)
+    x = rng.normal(size=(b, d, L))
+    y, h = orc.scan_fwd(x, delta, A, B, C, D=D)
+    want_y = np.empty_like(y)
+    want_h = np.empty_like(h)
+    for ib in range(b):
+        for idd in range(d):
+            Abars, Bbars = zip(*[zoh_vanloan(A[idd], B[ib, t], delta[ib, idd, t]) for t in range(L)])
+            for t in range(L + 1):
+                hs = np.zeros(N)
+                for s in range(min(t + 1, L)):
+                    P = np.eye(N)
+                    for r in range(s + 1, min(t + 1, L)):
+                        P = Abars[r] @ P
+                    hs = hs + P @ Bbars[s] * x[ib, idd, s]
+                if t < L:
+                    want_y[ib, idd, t] = C[ib, t] @ hs + D[idd] * x[ib, idd, t]
+                else:
+                    want_h[ib, idd] = hs
+    _close(y, want_y, what="selective unroll y")
+    _close(h, want_h, what="selective unroll final state")
+
+
+def pin_closed_gate(orc):
+    """sharin page §②: a closed gate (B_t = 0) lets the state only decay, by Π Ā_t = exp(A Σ Δ_t)."""
+    rng = _rng(7)
+    b, d, N, t0, t1 = 1, 2, 3, 9, 20
+    A = -rng.uniform(0.1, 1.0, size=(d, N))
+    delta = rng.uniform(0.05, 0.5, size=(b, d, t1))
+    B = rng.normal(size=(b, t1, N)); B[:, t0:, :] = 0.0
+    C = rng.normal(size=(b, t1, N)); x = rng.normal(size=(b, d, t1))
+    _, h_at = orc.scan_fwd(x[:, :, :t0], delta[:, :, :t0], A, B[:, :t0], C[:, :t0])
+    _, h_end = orc.scan_fwd(x, delta, A, B, C)
+    decay = np.exp(A[None, :, :] * delta[:, :, t0:].sum(axis=2)[:, :, None])
+    _close(h_end, decay * h_at, what="closed-gate decay")
+
+
+def pin_delta_limits(orc):
+    """Δ -> 0 keeps the state (Ā = 1, B̄ = 0); Δ -> ∞ with A < 0 writes the input (h -> -B x / A)."""
+    rng = _rng(9)
+    b, d, N = 2, 3, 4
+    A = -rng.uniform(0.5, 2.0, size=(d, N))
+    st = rng.normal(size=(b, d, N)); x = rng.normal(size=(b, d))
+    B = rng.normal(size=(b, N)); C = rng.normal(size=(b, N)); D = rng.normal(size=d)
+    y, st2 = orc.scan_step(st, x, np.zeros((b, d)), A, B, C, D=D)
+    assert np.array_equal(st2, st), "Δ = 0 must leave the state untouched"
+    _close(y, np.einsum("bn,bdn->bd", C, st) + D[None, :] * x, what="Δ = 0 readout")
+    _, st3 = orc.scan_step(st, x, np.full((b, d), 200.0), A, B, C)
+    _close(st3, -B[:, None, :] * x[:, :, None] / A[None, :, :], rtol=1e-12, what="Δ -> ∞ state")
+
+
+def pin_affine_associativity(orc):
+    """kasblo page, selective-scan section: (A2,b2)∘(A1,b1) = (A2A1, A2b1 + b2) is associative, so any
+    tree order of the per-step maps gives the sequential state; chaining calls through h0 is one
+    such order (segments carried across calls)."""
+    rng = _rng(13)
+    b, d, N, L = 1, 2, 3, 33
+    A = -rng.uniform(0.05, 1.5, size=(d, N))
+    delta = rng.uniform(0.01, 0.9, size=(b, d, L))
+    B = rng.normal(size=(b, L, N)); C = rng.normal(size=(b, L, N)); x = rng.normal(size=(b, d, L))
+    D = rng.normal(size=d); z = rng.normal(size=(b, d, L))
+    y, h = orc.scan_fwd(x, delta, A, B, C, D=D, z=z)
+    for idd in range(d):
+        maps = []
+        for t in range(L):
+            Ab, Bb = zoh_vanloan(A[idd], B[0, t], delta[0, idd, t])
+            maps.append((np.diag(Ab).copy(), Bb * x[0, idd, t]))
+        for trial in range(4):
+            items = list(maps)
+            while len(items) > 1:  # random adjacent merges = a random parenthesisation
+                i = int(rng.integers(0, len(items) - 1))
+                (a1, b1), (a2, b2) = items[i], items[i + 1]
+                items[i:i + 2] = [(a2 * a1, a2 * b1 + b2)]
+            _close(items[0][1], h[0, idd], what=f"tree order {trial}")
+    cuts = [0, 5, 6, 20, L]
+    hc = None
+    ys = []
+    for s, e in zip(cuts[:-1], cuts[1:]):
+        yy, hc = orc.scan_fwd(x[:, :, s:e], delta[:, :, s:e], A, B[:, s:e], C[:, s:e], D=D,
+                              z=z[:, :, s:e], h0=hc)
+        ys.append(yy)
+    _close(np.concatenate(ys, axis=2), y, what="chained segments y")
+    _close(hc, h, what="chained segments state")
+
+
+def pin_prefill_equals_decode(orc):
+    """Training/prefill and recurrent decode compute the same map (kasblo page, prefill vs decode)."""
+    rng = _rng(17)
+    b, d, N, L = 2, 3, 4, 10
+    A = -rng.uniform(0.1, 2.0, size=(d, N))
+    delta = rng.uniform(0.01, 1.0, size=(b, d, L))
+    B = rng.normal(size=(b, L, N)); C = rng.normal(size=(b, L, N)); x = rng.normal(size=(b, d, L))
+    D = rng.normal(size=d); z = rng.normal(size=(b, d, L))
+    y, h = orc.scan_fwd(x, delta, A, B, C, D=D, z=z)
+    st = np.zeros((b, d, N))
+    for t in range(L):
+        yt, st = orc.scan_step(st, x[:, :, t], delta[:, :, t], A, B[:, t], C[:, t], D=D, z=z[:, :, t])
+        _close(yt, y[:, :, t], what=f"decode step {t}")
+    _close(st, h, what="decode final state")
+
+
+def pin_skip_and_gate(orc):
+    """C = 0 leaves only the skip D·x, times silu(z) from the gate; z = 0 closes the output exactly."""
+    rng = _rng(19)
+    b, d, N, L = 2, 3, 4, 9
+    A = -rng.uniform(0.1, 2.0, size=(d, N))
+    delta = rng.uniform(0.01, 1.0, size=(b, d, L))
+    B = rng.normal(size=(b, L, N)); x = rng.normal(size=(b, d, L)); D = rng.normal(size=d)
+    z = 3.0 * rng.normal(size=(b, d, L))
+    y, _ = orc.scan_fwd(x, delta, A, B, np.zeros((b, L, N)), D=D, z=z)
+    _close(y, D[None, :, None] * x * silu_lib(z), what="skip times silu gate")
+    C = rng.normal(size=(b, L, N))
+    y0, _ = orc.scan_fwd(x, delta, A, B, C, D=D, z=np.zeros((b, d, L)))
+    assert np.all(y0 == 0.0)
+    ynog, _ = orc.scan_fwd(x, delta, A, B, C, D=D)
+    yg, _ = orc.scan_fwd(x, delta, A, B, C, D=D, z=z)
+    _close(yg, ynog * silu_lib(z), what="gate multiplies the SSM output")
+
+
+def pin_linearity(orc):
+    """With the gate off the map x -> y is linear (the recurrence is linear in x)."""
+    rng = _rng(23)
+    b, d, N, L = 1, 2, 3, 15
+    A = -rng.uniform(0.1, 2.0, size=(d, N))
+    delta = rng.uniform(0.01, 1.0, size=(b, d, L))
+    B = rng.normal(size=(b, L, N)); C = rng.normal(size=(b, L, N)); D = rng.normal(size=d)
+    x1 = rng.normal(size=(b, d, L)); x2 = rng.normal(size=(b, d, L))
+    y1, _ = orc.scan_fwd(x1, delta, A, B, C, D=D)
+    y2, _ = orc.scan_fwd(x2, delta, A, B, C, D=D)
+    y12, _ = orc.scan_fwd(2.0 * x1 - 0.5 * x2, delta, A, B, C, D=D)
+    _close(y12, 2.0 * y1 - 0.5 * y2, rtol=1e-10, atol=1e-12, what="linearity in x")
+
+
+ALL_PINS = [
+    pin_scalar_worked_example,
+    pin_delta_gate,
+    pin_decay_impulse,
+    pin_cumulative_sum,
+    pin_lti_convolution,
+    pin_selective_unroll,
+    pin_closed_gate,
+    pin_delta_limits,
+    pin_affine_associativity,
+    pin_prefill_equals_decode,
+    pin_skip_and_gate,
+    pin_linearity,
+]

@@ -1,0 +1,60 @@
+"""Plausible mistakes planted in a copy of the oracle source must each fail at least one pin.
+
+The mutants are compiled from text substitutions on the CPU only; the real oracle is untouched.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from pins import ALL_PINS
+
+MUTANTS = {
+    "drop_skip_D": ("double yt = acc + dskip * xt;", "double yt = acc;"),
+    "exp_sign": ("*abar = exp(u);", "*abar = exp(-u);"),
+    "euler_bbar": ("expm1(u) / a", "u / a"),
+    "a0_limit_zero": (": delta;", ": 0.0;"),
+    "no_decay": ("h[n] = abar * h[n] +", "h[n] = h[n] +"),
+    "readout_before_update": (
+        "            h[n] = abar * h[n] + bcoef * Bt[t * N + n] * xt;\n"
+        "            /* y_t = C h_t with the just-updated state (both pages update first, then read). */\n"
+        "            acc += Ct[t * N + n] * h[n];",
+        "            acc += Ct[t * N + n] * h[n];\n"
+        "            h[n] = abar * h[n] + bcoef * Bt[t * N + n] * xt;"),
+    "B_transposed": ("bcoef * Bt[t * N + n]", "bcoef * Bt[n * L + t]"),
+    "C_transposed": ("acc += Ct[t * N + n]", "acc += Ct[n * L + t]"),
+    "sigmoid_gate": ("return v / (1.0 + exp(-v));", "return 1.0 / (1.0 + exp(-v));"),
+    "A_channel0": ("delta + row * (size_t)L, A + (size_t)id * (size_t)N,", "delta + row * (size_t)L, A,"),
+    "step_A_channel0": ("scan_row(x + row, delta + row, A + (size_t)id * (size_t)N,",
+                        "scan_row(x + row, delta + row, A,"),
+    "step_B_batch0": ("B + (size_t)ib * (size_t)N,\n                     C + (size_t)ib * (size_t)N,",
+                      "B,\n                     C + (size_t)ib * (size_t)N,"),
+    "B_batch0": ("B + (size_t)ib * (size_t)L * (size_t)N, C", "B, C"),
+    "ignore_h0": ("hrow[n] = h0 ? h0[row * (size_t)N + (size_t)n] : 0.0;", "hrow[n] = 0.0;"),
+    "gate_on_skip_only": ("if (z) yt *= silu(z[t]);", "if (z) yt = acc + dskip * xt * silu(z[t]);"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SOURCE, encoding="utf-8") as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, source, name):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    src = tmp_path / "mutant.c"
+    src.write_text(source.replace(old, new), encoding="utf-8")
+    lib = oracle.compile_library(str(src), str(tmp_path / "libmutant.so"))
+    orc = oracle.Oracle(lib)
+    failed = []
+    with np.errstate(all="ignore"):
+        for pin in ALL_PINS:
+            try:
+                pin(orc)
+            except (AssertionError, ValueError, FloatingPointError):
+                failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
