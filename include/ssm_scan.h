@@ -1,0 +1,156 @@
+/*
+ * ssm_scan.h — C ABI of the MI355X (gfx950) selective state-space scan library, libssmscan.so.
+ *
+ * The operation (sources: page "State Space Models（SSM）とMamba" §2.1–§2.2 and §4.2; page
+ * "Mambaとは？Transformer以外の系列モデル", sections 状態空間モデルを一つの式から理解する,
+ * Mambaの核心は入力依存のDelta、B、C, Selective Scanは選択機構そのものではない, Mamba blockの
+ * architecture and training、prefill、decodeでは計算の姿が違う):
+ *
+ *   for every batch row b and channel d, with a diagonal continuous-time A[d][·] and per-token
+ *   step Δ_t, input matrices B_t and C_t (shared by all channels of the batch row):
+ *     Ā_t[n] = exp(Δ_t · A[d][n])                        zero-order hold
+ *     B̄_t[n] = (exp(Δ_t · A[d][n]) − 1) / A[d][n] · B_t[n]   (Δ_t · B_t[n] at A = 0, the limit)
+ *     h_t[n] = Ā_t[n] · h_{t−1}[n] + B̄_t[n] · x_t         the recurrence (h_{−1} = 0 in prefill)
+ *     y_t    = Σ_n C_t[n] · h_t[n] + D[d] · x_t            readout with the updated state + skip
+ *     y_t    ← y_t · z_t · σ(z_t)                           optional SiLU gate
+ *
+ * Prefill (ssm_scan_fwd) evaluates the whole sequence; decode (ssm_scan_step) advances a stored
+ * state by one token. Both compute in fp32 with an fp32 state.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers to tensors are DEVICE pointers owned by the caller; the library never frees them.
+ *     All tensors are dense, row-major, with no padding:
+ *       x, delta, z, y : [b][d][L]        (decode: [b][d])
+ *       A              : [d][N]  fp32
+ *       B, C           : [b][L][N]        (decode: [b][N])
+ *       D              : [d]     fp32
+ *       states         : [b][d][N] fp32
+ *     `dtype` is the storage type of x, delta, z, B, C and y (SSM_F32 = float, SSM_BF16 = bf16 bit
+ *     patterns, rounded to nearest-even on output). A, D and states are always fp32.
+ *   - delta is used as given (a positive step; no softplus or bias is applied here).
+ *   - Arguments are validated on the host before any launch; a failed check returns a non-zero
+ *     status and launches nothing. Work is enqueued on `stream` (0 = the null stream) and the call
+ *     returns without synchronising. Asynchronous device faults surface at the caller's next
+ *     synchronisation of that stream.
+ *   - Calls are reentrant: the library keeps no per-call global state. Calls on different streams
+ *     may run concurrently. Prefill calls whose sequence is split into several time segments
+ *     take stream-ordered scratch memory (hipMallocAsync / hipFreeAsync on `stream`).
+ *   - NaN and Inf inputs propagate; nothing is clamped.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+#define SSM_MAX_N 64
+
+/* Exported symbols (the library is built with hidden visibility by default). */
+#if defined(__GNUC__)
+#define SSM_API __attribute__((visibility("default")))
+#else
+#define SSM_API
+#endif
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_NULL = 1,        /* a required pointer is NULL                                   */
+    SSM_ERR_SHAPE = 2,       /* a size is out of range (b, d, N < 1; L < 0; overflow)         */
+    SSM_ERR_UNSUPPORTED = 3, /* N > SSM_MAX_N, unknown dtype, or an option value not accepted */
+    SSM_ERR_HIP = 4,         /* a HIP runtime call or a launch failed                          */
+    SSM_ERR_ALIAS = 5        /* an output overlaps an input or another output                 */
+} ssm_status_t;
+
+/*
+ * Prefill: the selective scan over a whole sequence (the parallel "prefill" mode), h_{−1} = 0.
+ *   x, delta   [b][d][L] dtype      required
+ *   A          [d][N] fp32          required; any finite value, A = 0 takes the ZOH limit
+ *   B, C       [b][L][N] dtype      required
+ *   D          [d] fp32             optional (NULL = no skip term)
+ *   z          [b][d][L] dtype      optional (NULL = no gate)
+ *   y          [b][d][L] dtype      required output; must not overlap any input
+ *   final_state[b][d][N] fp32       optional output h_{L−1} (NULL = not written)
+ *   b, d, N >= 1; L >= 0; N <= SSM_MAX_N. With L = 0 the call writes zeros to final_state and
+ *   touches nothing else, so x, delta, A, B, C, y may then be NULL.
+ *   Errors: SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_UNSUPPORTED, SSM_ERR_ALIAS (nothing launched);
+ *   SSM_ERR_HIP when scratch allocation or a launch fails (work already enqueued may have run).
+ */
+SSM_API ssm_status_t ssm_scan_fwd(const void *x, const void *delta, const float *A, const void *B,
+                          const void *C, const float *D, const void *z, void *y,
+                          float *final_state, int64_t b, int64_t d, int64_t L, int64_t N,
+                          ssm_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Decode: one recurrent step per (b, d) on a state kept in HBM (the recurrent "decode" mode).
+ *   state      [b][d][N] fp32       required, in/out: read as h_{t−1}, overwritten with h_t
+ *   x, delta   [b][d] dtype         required
+ *   A          [d][N] fp32          required
+ *   B, C       [b][N] dtype         required
+ *   D          [d] fp32             optional
+ *   z          [b][d] dtype         optional
+ *   y          [b][d] dtype         required output
+ *   b, d, N >= 1; N <= SSM_MAX_N. The state is read and written in place (it may not overlap any
+ *   other argument). Errors as for ssm_scan_fwd.
+ */
+SSM_API ssm_status_t ssm_scan_step(float *state, const void *x, const void *delta, const float *A,
+                           const void *B, const void *C, const float *D, const void *z, void *y,
+                           int64_t b, int64_t d, int64_t N, ssm_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Options of ssm_scan_fwd_ex. Zero-initialise, then set what you need; zero means "choose".
+ *   seg_len          time-segment length (multiple of 32) carried across by the chunk-carry pass;
+ *                    0 = chosen from the shape, >= L = one segment
+ *   states_per_wave  4, 8 or 16 states per wavefront (a workgroup holds ceil(N / this) waves,
+ *                    at most 4); 0 = chosen from the shape
+ *   initial_state    [b][d][N] fp32 device pointer, h_{−1} (NULL = zeros); lets a caller
+ *                    continue a sequence that an earlier call ended (pass its final_state)
+ *   ev_begin, ev_end hipEvent_t values (may be NULL); when set, recorded on `stream` right before
+ *                    and right after the output-pass kernel, for timing that kernel alone
+ */
+typedef struct {
+    int32_t seg_len;
+    int32_t states_per_wave;
+    const float *initial_state;
+    void *ev_begin;
+    void *ev_end;
+    int64_t reserved[4];
+} ssm_fwd_opts_t;
+
+/* ssm_scan_fwd with explicit options (opts may be NULL = all defaults). */
+SSM_API ssm_status_t ssm_scan_fwd_ex(const void *x, const void *delta, const float *A, const void *B,
+                             const void *C, const float *D, const void *z, void *y,
+                             float *final_state, int64_t b, int64_t d, int64_t L, int64_t N,
+                             ssm_dtype_t dtype, hipStream_t stream, const ssm_fwd_opts_t *opts);
+
+/* The launch plan ssm_scan_fwd_ex would use for this shape and these options (host only, no
+ * device work), planned for a 256-CU device (MI355X). Writes the resolved seg_len and states_per_wave, plus the number of segments and
+ * workgroups per pass, and the scratch bytes. Returns SSM_OK or the validation error. */
+typedef struct {
+    int32_t seg_len;
+    int32_t states_per_wave;
+    int32_t n_segments;
+    int32_t waves_per_group;
+    int64_t groups_output_pass;
+    int64_t groups_aggregate_pass;
+    int64_t scratch_bytes;
+} ssm_fwd_plan_t;
+
+SSM_API ssm_status_t ssm_scan_fwd_plan(int64_t b, int64_t d, int64_t L, int64_t N, ssm_dtype_t dtype,
+                               const ssm_fwd_opts_t *opts, ssm_fwd_plan_t *plan);
+
+/* Human-readable name of a status code (static string, never NULL). */
+SSM_API const char *ssm_status_string(ssm_status_t s);
+
+/* SSM_ABI_VERSION of the loaded library. */
+SSM_API int ssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_SCAN_H */

@@ -1,0 +1,202 @@
+"""Thin Python binding of libssmscan.so: torch tensors in, raw device pointers to the C ABI out.
+
+Argument marshalling only: every step of the scan runs in the library's HIP kernels. torch
+provides device memory and the current stream. There is no fallback: if the library is missing
+or the tensors are not on a ROCm GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libssmscan.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+SSM_OK = 0
+STATUS_NAMES = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_UNSUPPORTED",
+                4: "SSM_ERR_HIP", 5: "SSM_ERR_ALIAS"}
+
+
+class SsmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class FwdOpts(ctypes.Structure):
+    """ssm_fwd_opts_t."""
+    _fields_ = [("seg_len", ctypes.c_int32), ("states_per_wave", ctypes.c_int32),
+                ("initial_state", ctypes.c_void_p), ("ev_begin", ctypes.c_void_p),
+                ("ev_end", ctypes.c_void_p), ("reserved", ctypes.c_int64 * 4)]
+
+
+class FwdPlan(ctypes.Structure):
+    """ssm_fwd_plan_t."""
+    _fields_ = [("seg_len", ctypes.c_int32), ("states_per_wave", ctypes.c_int32),
+                ("n_segments", ctypes.c_int32), ("waves_per_group", ctypes.c_int32),
+                ("groups_output_pass", ctypes.c_int64), ("groups_aggregate_pass", ctypes.c_int64),
+                ("scratch_bytes", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library with argument types declared (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950) first")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    fwd = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
+    L.ssm_scan_fwd.argtypes = fwd
+    L.ssm_scan_fwd.restype = i32
+    L.ssm_scan_fwd_ex.argtypes = fwd + [ctypes.POINTER(FwdOpts)]
+    L.ssm_scan_fwd_ex.restype = i32
+    L.ssm_scan_fwd_plan.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(FwdOpts), ctypes.POINTER(FwdPlan)]
+    L.ssm_scan_fwd_plan.restype = i32
+    L.ssm_scan_step.argtypes = [vp] * 9 + [i64, i64, i64, i32, vp]
+    L.ssm_scan_step.restype = i32
+    L.ssm_status_string.argtypes = [i32]
+    L.ssm_status_string.restype = ctypes.c_char_p
+    L.ssm_abi_version.argtypes = []
+    L.ssm_abi_version.restype = i32
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().ssm_status_string(int(status)).decode()
+
+
+def _raise(status: int, what: str):
+    if status != SSM_OK:
+        raise SsmError(status, f"{what}: {status_string(status)}")
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return SSM_F32
+    if t == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"unsupported storage dtype {t}; use float32 or bfloat16")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(name, t, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, *, y=None, final_state=None, return_final_state=True,
+                 seg_len=0, states_per_wave=0, initial_state=None, events=None):
+    """Prefill scan. x, delta, z: [b, d, L]; A: [d, N] fp32; B, C: [b, L, N]; D: [d] fp32.
+    x, delta, z, B, C share one storage dtype (float32 or bfloat16); y gets it too.
+    Returns (y, final_state) (final_state is None when return_final_state is False and none is given).
+    events: optional (begin, end) torch.cuda.Event pair recorded around the output-pass kernel."""
+    if x.dim() != 3:
+        raise ValueError("x must be [b, d, L]")
+    b, d, L = x.shape
+    if A.dim() != 2:
+        raise ValueError("A must be [d, N]")
+    N = A.shape[1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a ROCm GPU")
+    st = x.dtype
+    code = _dtype_code(st)
+    _check("delta", delta, (b, d, L), st, dev)
+    _check("A", A, (d, N), torch.float32, dev)
+    _check("B", B, (b, L, N), st, dev)
+    _check("C", C, (b, L, N), st, dev)
+    _check("D", D, (d,), torch.float32, dev)
+    _check("z", z, (b, d, L), st, dev)
+    _check("x", x, (b, d, L), st, dev)
+    _check("initial_state", initial_state, (b, d, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty((b, d, L), dtype=st, device=dev)
+    _check("y", y, (b, d, L), st, dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((b, d, N), dtype=torch.float32, device=dev)
+    _check("final_state", final_state, (b, d, N), torch.float32, dev)
+    args = [_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), _ptr(final_state),
+            b, d, L, N, code, _stream(dev)]
+    if seg_len or states_per_wave or initial_state is not None or events is not None:
+        o = FwdOpts()
+        o.seg_len = int(seg_len)
+        o.states_per_wave = int(states_per_wave)
+        o.initial_state = None if initial_state is None else initial_state.data_ptr()
+        if events is not None:
+            o.ev_begin = events[0].cuda_event
+            o.ev_end = events[1].cuda_event
+        status = lib().ssm_scan_fwd_ex(*args, ctypes.byref(o))
+    else:
+        status = lib().ssm_scan_fwd(*args)
+    _raise(status, "ssm_scan_fwd")
+    return y, final_state
+
+
+def ssm_scan_step(state, x, delta, A, B, C, D=None, z=None, *, y=None):
+    """Decode step: state [b, d, N] fp32 (updated in place); x, delta, z [b, d]; B, C [b, N];
+    A [d, N] fp32; D [d] fp32. Returns y [b, d]."""
+    if state.dim() != 3:
+        raise ValueError("state must be [b, d, N]")
+    b, d, N = state.shape
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a ROCm GPU")
+    st = x.dtype
+    code = _dtype_code(st)
+    _check("state", state, (b, d, N), torch.float32, dev)
+    _check("x", x, (b, d), st, dev)
+    _check("delta", delta, (b, d), st, dev)
+    _check("A", A, (d, N), torch.float32, dev)
+    _check("B", B, (b, N), st, dev)
+    _check("C", C, (b, N), st, dev)
+    _check("D", D, (d,), torch.float32, dev)
+    _check("z", z, (b, d), st, dev)
+    if y is None:
+        y = torch.empty((b, d), dtype=st, device=dev)
+    _check("y", y, (b, d), st, dev)
+    status = lib().ssm_scan_step(_ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                 _ptr(y), b, d, N, code, _stream(dev))
+    _raise(status, "ssm_scan_step")
+    return y
+
+
+def ssm_scan_fwd_plan(b, d, L, N, dtype=torch.float32, seg_len=0, states_per_wave=0) -> dict:
+    """The launch plan ssm_scan_fwd would use (host only)."""
+    o = FwdOpts()
+    o.seg_len = int(seg_len)
+    o.states_per_wave = int(states_per_wave)
+    p = FwdPlan()
+    status = lib().ssm_scan_fwd_plan(b, d, L, N, _dtype_code(dtype), ctypes.byref(o), ctypes.byref(p))
+    _raise(status, "ssm_scan_fwd_plan")
+    return {k: getattr(p, k) for k, _ in FwdPlan._fields_}

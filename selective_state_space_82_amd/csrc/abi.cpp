@@ -1,0 +1,265 @@
+// abi.cpp — the C ABI of libssmscan.so: argument validation, launch planning, scratch, dispatch.
+// See include/ssm_scan.h for the contract of every entry point.
+#include "ssm_scan.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "launch.h"
+
+namespace {
+
+using ssm::FwdLaunch;
+using ssm::StepLaunch;
+
+bool valid_dtype(ssm_dtype_t t) { return t == SSM_F32 || t == SSM_BF16; }
+
+// a * b without overflow past 2^62 (sizes are far below that in practice)
+bool mul_ok(int64_t a, int64_t b, int64_t *out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > (INT64_C(1) << 62) / a) return false;
+    *out = a * b;
+    return true;
+}
+
+struct Span {
+    const void *p;
+    int64_t bytes;
+};
+
+bool overlaps(const Span &u, const Span &v) {
+    if (!u.p || !v.p || u.bytes <= 0 || v.bytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(u.p), a1 = a0 + (uintptr_t)u.bytes;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(v.p), b1 = b0 + (uintptr_t)v.bytes;
+    return a0 < b1 && b0 < a1;
+}
+
+// Compute units of the current device, cached per device id.
+int cu_count() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// Keep freed stream-ordered scratch in the device's default pool instead of returning it to the
+// driver at every synchronisation, so repeated calls do not pay for re-mapping it. Once per device.
+void keep_pool_memory() {
+    static std::mutex mu;
+    static bool done[64] = {false};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done[dev]) return;
+    done[dev] = true;
+    hipMemPool_t pool = nullptr;
+    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess && pool) {
+        uint64_t threshold = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+    }
+}
+
+struct Plan {
+    int npl, waves, n_seg;
+    int64_t seg_len, groups_out, groups_agg, scratch_bytes;
+};
+
+// Launch plan. Each workgroup holds 64 channels of one batch row for one time segment; a
+// sequence is cut into segments only when the channel blocks alone cannot fill the device, since
+// every extra segment costs an aggregate rescan of its inputs.
+ssm_status_t make_plan(int64_t b, int64_t d, int64_t L, int64_t N, const ssm_fwd_opts_t *o, int cus, Plan *pl) {
+    int npl = o ? o->states_per_wave : 0;
+    if (npl == 0) npl = N <= 16 ? 4 : (N <= 32 ? 8 : 16);
+    if (npl != 4 && npl != 8 && npl != 16) return SSM_ERR_UNSUPPORTED;
+    int waves = (int)((N + npl - 1) / npl);
+    if (waves > 4) return SSM_ERR_UNSUPPORTED;
+    if (waves == 3) waves = 4;
+    const int64_t n_db = (d + ssm::kGroupRows - 1) / ssm::kGroupRows;
+    const int64_t ncb = b * n_db;
+    int64_t seg_len = o ? o->seg_len : 0;
+    if (seg_len < 0 || (seg_len % ssm::kTile) != 0) return SSM_ERR_UNSUPPORTED;
+    const int64_t Lr = ((L + ssm::kTile - 1) / ssm::kTile) * ssm::kTile;
+    if (seg_len == 0) {
+        // aim for about 8 wavefronts per compute unit, never segments shorter than 256 steps
+        const int64_t want_groups = (int64_t)cus * (8 / waves);
+        int64_t S = (want_groups + ncb - 1) / ncb;
+        const int64_t max_seg = Lr / 256 > 0 ? Lr / 256 : 1;
+        if (S > max_seg) S = max_seg;
+        if (S > 64) S = 64;
+        if (S < 1) S = 1;
+        seg_len = ((Lr / S + ssm::kTile - 1) / ssm::kTile) * ssm::kTile;
+    }
+    if (seg_len > Lr || seg_len == 0) seg_len = Lr > 0 ? Lr : ssm::kTile;
+    int64_t n_seg = L > 0 ? (L + seg_len - 1) / seg_len : 1;
+    if (n_seg > 4096) return SSM_ERR_UNSUPPORTED;
+    int64_t scratch = 0;
+    if (n_seg > 1) {
+        int64_t per = 0;
+        if (!mul_ok((n_seg - 1) * b, d * N, &per)) return SSM_ERR_SHAPE;
+        scratch = 3 * per * (int64_t)sizeof(float);
+    }
+    pl->npl = npl;
+    pl->waves = waves;
+    pl->n_seg = (int)n_seg;
+    pl->seg_len = seg_len;
+    pl->groups_out = n_seg * ncb;
+    pl->groups_agg = (n_seg - 1) * ncb;
+    pl->scratch_bytes = scratch;
+    if (pl->groups_out > 0x7fffffffLL) return SSM_ERR_SHAPE;
+    return SSM_OK;
+}
+
+ssm_status_t check_fwd_sizes(int64_t b, int64_t d, int64_t L, int64_t N, ssm_dtype_t dtype) {
+    if (!valid_dtype(dtype)) return SSM_ERR_UNSUPPORTED;
+    if (b < 1 || d < 1 || N < 1 || L < 0) return SSM_ERR_SHAPE;
+    if (N > SSM_MAX_N) return SSM_ERR_UNSUPPORTED;
+    int64_t t = 0;
+    if (!mul_ok(b, d, &t) || !mul_ok(t, L > 0 ? L : 1, &t) || !mul_ok(t, N, &t)) return SSM_ERR_SHAPE;
+    return SSM_OK;
+}
+
+// Option values that need no device information.
+ssm_status_t check_opts(int64_t N, const ssm_fwd_opts_t *o) {
+    if (!o) return SSM_OK;
+    const int npl = o->states_per_wave;
+    if (npl != 0 && npl != 4 && npl != 8 && npl != 16) return SSM_ERR_UNSUPPORTED;
+    if (npl != 0 && (N + npl - 1) / npl > 4) return SSM_ERR_UNSUPPORTED;
+    if (o->seg_len < 0 || (o->seg_len % ssm::kTile) != 0) return SSM_ERR_UNSUPPORTED;
+    return SSM_OK;
+}
+
+ssm_status_t fwd_impl(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                      const float *D, const void *z, void *y, float *final_state, int64_t b, int64_t d,
+                      int64_t L, int64_t N, ssm_dtype_t dtype, hipStream_t stream, const ssm_fwd_opts_t *o) {
+    ssm_status_t st = check_fwd_sizes(b, d, L, N, dtype);
+    if (st != SSM_OK) return st;
+    // With L = 0 nothing but final_state is touched, so the (empty) sequence tensors may be NULL.
+    if (L > 0 && (!x || !delta || !A || !B || !C || !y)) return SSM_ERR_NULL;
+    st = check_opts(N, o);
+    if (st != SSM_OK) return st;
+    const int64_t es = dtype == SSM_BF16 ? 2 : 4;
+    const int64_t bdl = b * d * L, bln = b * L * N, bdn = b * d * N;
+    const Span sy{y, bdl * es}, sf{final_state, bdn * 4};
+    const Span ins[] = {{x, bdl * es}, {delta, bdl * es}, {z, bdl * es}, {B, bln * es}, {C, bln * es},
+                        {A, d * N * 4}, {D, d * 4}, {o ? o->initial_state : nullptr, bdn * 4}};
+    for (const Span &s : ins)
+        if (overlaps(sy, s) || overlaps(sf, s)) return SSM_ERR_ALIAS;
+    if (overlaps(sy, sf)) return SSM_ERR_ALIAS;
+
+    if (L == 0) {
+        if (final_state && ssm::launch_fill_zero(final_state, bdn, stream) != hipSuccess) return SSM_ERR_HIP;
+        return SSM_OK;
+    }
+    Plan pl{};
+    st = make_plan(b, d, L, N, o, cu_count(), &pl);
+    if (st != SSM_OK) return st;
+    FwdLaunch p{};
+    p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.y = y;
+    p.final_state = final_state;
+    p.init_state = o ? o->initial_state : nullptr;
+    p.b = b; p.d = d; p.L = L; p.N = N;
+    p.bf16 = dtype == SSM_BF16;
+    p.states_per_wave = pl.npl;
+    p.waves = pl.waves;
+    p.seg_len = pl.seg_len;
+    p.n_seg = pl.n_seg;
+    p.ev_begin = o ? static_cast<hipEvent_t>(o->ev_begin) : nullptr;
+    p.ev_end = o ? static_cast<hipEvent_t>(o->ev_end) : nullptr;
+    void *scratch = nullptr;
+    if (pl.scratch_bytes > 0) {
+        keep_pool_memory();
+        if (hipMallocAsync(&scratch, (size_t)pl.scratch_bytes, stream) != hipSuccess) return SSM_ERR_HIP;
+        p.scratch = static_cast<float *>(scratch);
+    }
+    const hipError_t e = ssm::launch_scan_fwd(p, stream);
+    if (scratch) {
+        if (hipFreeAsync(scratch, stream) != hipSuccess) return SSM_ERR_HIP;
+    }
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ssm_status_string(ssm_status_t s) {
+    switch (s) {
+        case SSM_OK: return "SSM_OK";
+        case SSM_ERR_NULL: return "SSM_ERR_NULL: a required pointer is NULL";
+        case SSM_ERR_SHAPE: return "SSM_ERR_SHAPE: a size is out of range";
+        case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: N, dtype or an option value is not supported";
+        case SSM_ERR_HIP: return "SSM_ERR_HIP: a HIP runtime call or kernel launch failed";
+        case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS: an output overlaps an input or another output";
+    }
+    return "unknown ssm_status_t";
+}
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+ssm_status_t ssm_scan_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                          const float *D, const void *z, void *y, float *final_state, int64_t b, int64_t d,
+                          int64_t L, int64_t N, ssm_dtype_t dtype, hipStream_t stream) {
+    return fwd_impl(x, delta, A, B, C, D, z, y, final_state, b, d, L, N, dtype, stream, nullptr);
+}
+
+ssm_status_t ssm_scan_fwd_ex(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                             const float *D, const void *z, void *y, float *final_state, int64_t b, int64_t d,
+                             int64_t L, int64_t N, ssm_dtype_t dtype, hipStream_t stream,
+                             const ssm_fwd_opts_t *opts) {
+    return fwd_impl(x, delta, A, B, C, D, z, y, final_state, b, d, L, N, dtype, stream, opts);
+}
+
+ssm_status_t ssm_scan_fwd_plan(int64_t b, int64_t d, int64_t L, int64_t N, ssm_dtype_t dtype,
+                               const ssm_fwd_opts_t *opts, ssm_fwd_plan_t *plan) {
+    if (!plan) return SSM_ERR_NULL;
+    ssm_status_t st = check_fwd_sizes(b, d, L, N, dtype);
+    if (st != SSM_OK) return st;
+    st = check_opts(N, opts);
+    if (st != SSM_OK) return st;
+    Plan pl{};
+    st = make_plan(b, d, L, N, opts, 256, &pl);
+    if (st != SSM_OK) return st;
+    plan->seg_len = (int32_t)pl.seg_len;
+    plan->states_per_wave = pl.npl;
+    plan->n_segments = pl.n_seg;
+    plan->waves_per_group = pl.waves;
+    plan->groups_output_pass = pl.groups_out;
+    plan->groups_aggregate_pass = pl.groups_agg;
+    plan->scratch_bytes = pl.scratch_bytes;
+    return SSM_OK;
+}
+
+ssm_status_t ssm_scan_step(float *state, const void *x, const void *delta, const float *A, const void *B,
+                           const void *C, const float *D, const void *z, void *y, int64_t b, int64_t d,
+                           int64_t N, ssm_dtype_t dtype, hipStream_t stream) {
+    if (!state || !x || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
+    if (!valid_dtype(dtype)) return SSM_ERR_UNSUPPORTED;
+    if (b < 1 || d < 1 || N < 1) return SSM_ERR_SHAPE;
+    if (N > SSM_MAX_N) return SSM_ERR_UNSUPPORTED;
+    int64_t bd = 0, bdn = 0, tmp = 0;
+    if (!mul_ok(b, d, &bd) || !mul_ok(bd, N, &bdn) || !mul_ok(bd, 16, &tmp)) return SSM_ERR_SHAPE;
+    const int64_t es = dtype == SSM_BF16 ? 2 : 4;
+    const Span sy{y, bd * es}, ss{state, bdn * 4};
+    const Span ins[] = {{x, bd * es}, {delta, bd * es}, {z, bd * es}, {B, b * N * es}, {C, b * N * es},
+                        {A, d * N * 4}, {D, d * 4}};
+    for (const Span &s : ins)
+        if (overlaps(sy, s) || overlaps(ss, s)) return SSM_ERR_ALIAS;
+    if (overlaps(sy, ss)) return SSM_ERR_ALIAS;
+    StepLaunch p{};
+    p.state = state; p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.y = y;
+    p.b = b; p.d = d; p.N = N;
+    p.bf16 = dtype == SSM_BF16;
+    return ssm::launch_scan_step(p, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// launch.h — private host-side interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// Everything the prefill launchers need; validated by the ABI layer beforehand.
+struct FwdLaunch {
+    const void *x, *delta;
+    const float *A;
+    const void *B, *C;
+    const float *D;
+    const void *z;
+    void *y;
+    float *final_state;
+    const float *init_state;  // h_{-1} of segment 0, or nullptr (zeros)
+    int64_t b, d, L, N;
+    bool bf16;
+    int states_per_wave;      // 4, 8 or 16
+    int waves;                // 1, 2 or 4 waves per workgroup (states_per_wave * waves >= N)
+    int64_t seg_len;          // multiple of 32
+    int n_seg;                // ceil(L / seg_len) >= 1
+    float *scratch;           // 3 * (n_seg - 1) * b * d * N floats when n_seg > 1
+    hipEvent_t ev_begin, ev_end;
+};
+
+struct StepLaunch {
+    float *state;
+    const void *x, *delta;
+    const float *A;
+    const void *B, *C;
+    const float *D;
+    const void *z;
+    void *y;
+    int64_t b, d, N;
+    bool bf16;
+};
+
+hipError_t launch_scan_fwd(const FwdLaunch &p, hipStream_t stream);
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t stream);
+hipError_t launch_scan_step(const StepLaunch &p, hipStream_t stream);
+
+constexpr int kTile = 32;       // timesteps per LDS tile
+constexpr int kGroupRows = 64;  // channels per workgroup: one per lane of a wavefront
+
+}  // namespace ssm

@@ -1,0 +1,239 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on the same seeded inputs.
+
+Bar: max |y - y_ref| / (1 + |y_ref|) <= 1e-4 for fp32 storage and <= 2e-2 for bf16 storage with an
+fp32 state; final states to the same bounds. Every result must be finite.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TAU, assert_close, from_torch, oracle_prefill_rows, sample_rows, upload
+from selective_state_space_82_amd import api
+from selective_state_space_82_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm GPU visible")
+    api.lib()  # raises if the library is missing
+
+
+def run_fwd(inp, **kw):
+    t = upload(inp)
+    y, h = api.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], **kw)
+    torch.cuda.synchronize()
+    return from_torch(y), from_torch(h)
+
+
+def check_rows(inp, y, h, rows, what, h0=None):
+    yr, hr = oracle_prefill_rows(inp, rows, h0=h0)
+    idx = tuple(np.array(rows).T)
+    tau = TAU[inp["dtype"]]
+    e1 = assert_close(y[idx], yr, tau, f"{what} y")
+    e2 = assert_close(h[idx], hr, tau, f"{what} final state")
+    print(f"[{what}] rows={len(rows)} max rel err y={e1:.2e} h={e2:.2e}", flush=True)
+
+
+def all_rows(b, d):
+    return [(ib, c) for ib in range(b) for c in range(d)]
+
+
+# ------------------------------------------------------------------------------------------
+# The five Mamba-shaped workloads at full size, in the launch configuration the benchmark uses
+# ------------------------------------------------------------------------------------------
+def test_tiny_workload_full():
+    inp = I.prefill_inputs("tiny_f32_b1_d8_L128_N4")
+    y, h = run_fwd(inp)
+    check_rows(inp, y, h, all_rows(1, 8), "tiny_f32_b1_d8_L128_N4")
+
+
+def test_mamba130m_workload_full():
+    w = I.WORKLOADS["mamba130m_f32_b4_d1536_L2048_N16"]
+    inp = I.prefill_inputs(w)
+    y, h = run_fwd(inp)
+    check_rows(inp, y, h, all_rows(w.b, w.d), w.name)
+
+
+def test_mamba1p4b_workload_sampled():
+    w = I.WORKLOADS["mamba1p4b_bf16_b8_d4096_L4096_N16"]
+    inp = I.prefill_inputs(w)
+    y, h = run_fwd(inp)
+    check_rows(inp, y, h, sample_rows(w.b, w.d, 96), w.name)
+
+
+def test_longctx_workload_sampled():
+    w = I.WORKLOADS["longctx_bf16_b1_d2048_L131072_N16"]
+    inp = I.prefill_inputs(w)
+    plan = api.ssm_scan_fwd_plan(w.b, w.d, w.L, w.N, torch.bfloat16)
+    assert plan["n_segments"] > 1, "the long-context workload is meant to exercise the chunk carry"
+    y, h = run_fwd(inp)
+    check_rows(inp, y, h, sample_rows(w.b, w.d, 40), w.name)
+
+
+def test_decode_workload_64_steps():
+    """64 successive steps on the 512 x 4096 x 16 state; a grid of sampled (b, d) pairs is followed
+    by the oracle at every step."""
+    w = I.WORKLOADS["decode_bf16_b512_d4096_N16_x64"]
+    dev = torch.device("cuda:0")
+    st0 = I.decode_initial_state(w)
+    state = torch.from_numpy(st0).to(dev)
+    rng = np.random.default_rng(1)
+    sb = np.unique(np.concatenate([[0, w.b - 1], rng.integers(0, w.b, size=46)]))
+    sd = np.unique(np.concatenate([[0, w.d - 1], rng.integers(0, w.d, size=62)]))
+    ref = st0[np.ix_(sb, sd)].astype(np.float64)  # [len(sb), len(sd), N]
+    tau = TAU[w.dtype]
+    wd = lambda a: I.widen(a, w.dtype)
+    worst = 0.0
+    for step in range(w.steps):
+        s = I.decode_step_inputs(w, step)
+        t = upload(s)
+        y = api.ssm_scan_step(state, t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"])
+        yr, ref = oracle.scan_step(ref, wd(s["x"])[np.ix_(sb, sd)], wd(s["delta"])[np.ix_(sb, sd)], s["A"][sd],
+                                   wd(s["B"])[sb], wd(s["C"])[sb], s["D"][sd], wd(s["z"])[np.ix_(sb, sd)])
+        worst = max(worst, assert_close(from_torch(y)[np.ix_(sb, sd)], yr, tau, f"decode step {step} y"))
+    torch.cuda.synchronize()
+    e = assert_close(from_torch(state)[np.ix_(sb, sd)], ref, tau, "decode final state")
+    print(f"[decode 64 steps] samples={len(sb) * len(sd)} max rel err y={worst:.2e} state={e:.2e}", flush=True)
+
+
+# ------------------------------------------------------------------------------------------
+# Small shapes: ragged tiles, partial channel blocks, odd N, every plan variant, A = 0
+# ------------------------------------------------------------------------------------------
+SMALL = [
+    # b, d, L, N, dtype, gate, D, extra options
+    (1, 1, 1, 1, "f32", False, True, {}),
+    (1, 3, 5, 3, "f32", True, True, {}),
+    (2, 65, 33, 16, "f32", True, True, {}),
+    (2, 65, 33, 16, "bf16", True, True, {}),
+    (1, 130, 100, 5, "f32", True, False, {}),
+    (3, 64, 257, 16, "f32", True, True, {"seg_len": 64}),
+    (3, 64, 257, 16, "bf16", True, True, {"seg_len": 96}),
+    (2, 70, 300, 16, "f32", True, True, {"seg_len": 32}),
+    (1, 64, 512, 16, "f32", True, True, {"states_per_wave": 8}),
+    (1, 64, 512, 16, "f32", True, True, {"states_per_wave": 16}),
+    (1, 64, 512, 16, "bf16", True, True, {"states_per_wave": 16, "seg_len": 128}),
+    (2, 33, 200, 33, "f32", True, True, {}),
+    (1, 40, 150, 64, "f32", True, True, {}),
+    (1, 40, 150, 64, "bf16", False, True, {"seg_len": 64}),
+    (2, 128, 1000, 16, "bf16", True, True, {}),
+    (1, 64, 4096, 4, "f32", True, True, {}),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"b{c[0]}_d{c[1]}_L{c[2]}_N{c[3]}_{c[4]}_g{int(c[5])}_{c[7]}")
+def test_small_shapes(case):
+    b, d, L, N, dt, gate, with_D, opts = case
+    inp = I.random_prefill(b, d, L, N, dtype=dt, gate=gate, with_D=with_D, seed=L + N)
+    y, h = run_fwd(inp, **opts)
+    check_rows(inp, y, h, all_rows(b, d), f"small b{b} d{d} L{L} N{N} {dt} {opts}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_zero_and_tiny_A_take_the_limit(dt):
+    """A = 0 entries (ZOH limit Δ·B) and |A| < 2^-10 entries mixed with ordinary ones."""
+    inp = I.random_prefill(2, 96, 300, 16, dtype=dt, seed=5, a_zero_frac=0.25)
+    inp["A"][3, :4] = np.float32(1e-7)
+    inp["A"][50, 7] = np.float32(-3e-5)
+    y, h = run_fwd(inp, seg_len=128)
+    check_rows(inp, y, h, all_rows(2, 96), f"zero/tiny A {dt}")
+
+
+def test_running_sum_is_exact_on_gpu():
+    """A = 0, Δ = B = C = 1, D = 0: y is the exact running sum of small integers."""
+    L = 256
+    rng = np.random.default_rng(2)
+    inp = {"x": rng.integers(-8, 9, size=(1, 64, L)).astype(np.float32),
+           "delta": np.ones((1, 64, L), np.float32), "z": None, "A": np.zeros((64, 4), np.float32),
+           "B": np.ones((1, L, 4), np.float32), "C": np.ones((1, L, 4), np.float32) * 0.25,
+           "D": np.zeros(64, np.float32), "dtype": "f32"}
+    y, h = run_fwd(inp, seg_len=64)
+    assert np.array_equal(y, np.cumsum(inp["x"].astype(np.float64), axis=2))
+
+
+def test_L_zero_writes_zero_state():
+    t = upload(I.random_prefill(2, 3, 0, 4, dtype="f32"))
+    fs = torch.full((2, 3, 4), 7.0, device="cuda")
+    y, h = api.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], final_state=fs)
+    torch.cuda.synchronize()
+    assert y.numel() == 0 and torch.all(h == 0)
+
+
+# ------------------------------------------------------------------------------------------
+# Invariants
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_segment_length_invariance(dt):
+    inp = I.random_prefill(2, 64, 640, 16, dtype=dt, seed=9, delta_mu=-4.0)
+    outs = [run_fwd(inp, seg_len=s) for s in (32, 96, 224, 640)]
+    tau = TAU[dt]
+    for y, h in outs[1:]:
+        assert_close(y, outs[0][0], tau, "y across segment lengths")
+        assert_close(h, outs[0][1], tau, "state across segment lengths")
+
+
+def test_bitwise_deterministic():
+    inp = I.random_prefill(2, 128, 700, 16, dtype="bf16", seed=4)
+    a = run_fwd(inp)
+    b = run_fwd(inp)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_initial_state_chaining_equals_one_call():
+    inp = I.random_prefill(2, 80, 400, 16, dtype="f32", seed=8)
+    t = upload(inp)
+    y_all, h_all = api.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"])
+    cut = 160
+    sl = lambda k, a, b_: t[k][:, :, a:b_].contiguous()
+    slB = lambda k, a, b_: t[k][:, a:b_].contiguous()
+    y1, h1 = api.ssm_scan_fwd(sl("x", 0, cut), sl("delta", 0, cut), t["A"], slB("B", 0, cut), slB("C", 0, cut),
+                              t["D"], sl("z", 0, cut))
+    y2, h2 = api.ssm_scan_fwd(sl("x", cut, 400), sl("delta", cut, 400), t["A"], slB("B", cut, 400),
+                              slB("C", cut, 400), t["D"], sl("z", cut, 400), initial_state=h1)
+    torch.cuda.synchronize()
+    assert_close(from_torch(torch.cat([y1, y2], dim=2)), from_torch(y_all), 1e-5, "chained y")
+    assert_close(from_torch(h2), from_torch(h_all), 1e-5, "chained state")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_prefill_equals_repeated_decode(dt):
+    """L decode steps from the zero state give the prefill outputs and final state."""
+    b, d, L, N = 2, 96, 40, 16
+    inp = I.random_prefill(b, d, L, N, dtype=dt, seed=12)
+    t = upload(inp)
+    y_pf, h_pf = api.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"])
+    state = torch.zeros((b, d, N), dtype=torch.float32, device="cuda")
+    ys = []
+    for s in range(L):
+        ys.append(api.ssm_scan_step(state, t["x"][:, :, s].contiguous(), t["delta"][:, :, s].contiguous(), t["A"],
+                                    t["B"][:, s].contiguous(), t["C"][:, s].contiguous(), t["D"],
+                                    t["z"][:, :, s].contiguous()))
+    torch.cuda.synchronize()
+    y_dec = from_torch(torch.stack(ys, dim=2))
+    tau = TAU[dt]
+    assert_close(y_dec, from_torch(y_pf), tau, "decode vs prefill y")
+    assert_close(from_torch(state), from_torch(h_pf), 1e-4, "decode vs prefill state")
+    yr, hr = oracle_prefill_rows(inp, all_rows(b, d))
+    assert_close(y_dec.reshape(b * d, L), yr, tau, "decode vs oracle")
+
+
+@pytest.mark.parametrize("N", [1, 3, 4, 7, 16, 33, 64])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_decode_small(N, dt):
+    b, d = 3, 37
+    rng = np.random.default_rng(N)
+    st0 = (rng.standard_normal((b, d, N)) * 0.3).astype(np.float32)
+    inp = I.random_prefill(b, d, 1, N, dtype=dt, seed=N)
+    inp["A"][0, 0] = 0.0
+    t = upload(inp)
+    state = torch.from_numpy(st0).cuda()
+    y = api.ssm_scan_step(state, t["x"][:, :, 0].contiguous(), t["delta"][:, :, 0].contiguous(), t["A"],
+                          t["B"][:, 0].contiguous(), t["C"][:, 0].contiguous(), t["D"], t["z"][:, :, 0].contiguous())
+    torch.cuda.synchronize()
+    yr, hr = oracle_prefill_rows(inp, all_rows(b, d), h0=st0.astype(np.float64))
+    tau = TAU[dt]
+    assert_close(from_torch(y).reshape(-1), yr[:, 0], tau, "decode y")
+    assert_close(from_torch(state).reshape(b * d, N), hr, tau, "decode state")
