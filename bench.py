@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Throughput of the selective scan on one MI355X.
+
+A step is one ssm_scan_fwd call over one batch of the Mamba-130M-like layer workload
+(b=4, d=1536, L=2048, N=16, fp32 storage, gate on, final state returned): ZOH discretisation,
+recurrence, readout, gate/skip epilogue, and the chunk carry when the plan splits time. Inputs are
+synthetic (seeded draws with the workload's distributions) and resident in HBM before timing.
+Several copies of the inputs and outputs rotate so the 256 MB last-level cache cannot hold them.
+
+Printed: one JSON line. `value` is GB/s of algorithmic traffic (inputs read once, outputs written
+once) over the whole timed call; `roofline` describes the output-pass kernel, timed with HIP
+events on the launch stream; `cpu_baseline` times the fp64 oracle on the host; `extra` carries
+the decode-step rate and the other prefill workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0                        # MI355X HBM3E, published
+VALU_PEAK_TSLOT = 256 * 4 * 16 * 2.4e9 / 1e12  # 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz = 39.32 T lane-slots/s
+MALL_BYTES = 256 << 20
+HEADLINE = "mamba130m_f32_b4_d1536_L2048_N16"
+METRIC = "selective-scan GB/s & % of HBM peak; (b·d·L)/s at N=16; decode steps/s"
+
+
+def valu_slots_per_element(N, gate):
+    """Issue slots the method needs per (b, d, t) on CDNA4: per state one exp (2 slots, half rate)
+    and six fp32 VALU operations (Δ·A; s + B·x; Ā − 1; the update FMA; C/A; the readout FMA); per
+    element the skip FMA and, with the gate, silu and the product (mul, exp, add, rcp, mul, mul)."""
+    return 8 * N + (1 + (8 if gate else 0))
+
+
+def algorithmic_bytes(b, d, L, N, esize, gate, with_D=True, with_state=True):
+    rows = b * d * L * esize
+    return (rows * (3 if gate else 2) + rows            # x, delta, (z) read; y written
+            + 2 * b * L * N * esize                      # B, C
+            + d * N * 4 + (d * 4 if with_D else 0)       # A, D
+            + (b * d * N * 4 if with_state else 0))      # final state
+
+
+def to_dev(arr, dev):
+    import torch
+    if arr is None:
+        return None
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+
+
+def bench_prefill(name, steps, warmup, rotate=0, quiet=False):
+    import torch
+    from selective_state_space_82_amd import api
+    from selective_state_space_82_amd import inputs as I
+
+    w = I.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    t_gen = time.time()
+    inp = I.prefill_inputs(w)
+    gen_s = time.time() - t_gen
+    esize = 4 if w.dtype == "f32" else 2
+    nbytes = algorithmic_bytes(w.b, w.d, w.L, w.N, esize, w.gate)
+    if rotate <= 0:
+        rotate = int(min(8, max(1, -(-2 * MALL_BYTES // nbytes))))
+    sets = []
+    for _ in range(rotate):
+        s = {k: to_dev(inp[k], dev) for k in ("x", "delta", "z", "A", "B", "C", "D")}
+        s["y"] = torch.empty_like(s["x"])
+        s["h"] = torch.empty((w.b, w.d, w.N), dtype=torch.float32, device=dev)
+        sets.append(s)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:  # materialise the underlying HIP events before handing them to the library
+        e0.record(); e1.record()
+
+    def call(i, events=None):
+        s = sets[i % rotate]
+        api.ssm_scan_fwd(s["x"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], y=s["y"], final_state=s["h"],
+                         events=events)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(i, ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    plan = api.ssm_scan_fwd_plan(w.b, w.d, w.L, w.N, torch.float32 if w.dtype == "f32" else torch.bfloat16)
+    elems = w.b * w.d * w.L
+    slots = elems * valu_slots_per_element(w.N, w.gate)
+    res = {
+        "workload": name, "ms_per_call": ms, "GBps": nbytes / (ms * 1e-3) / 1e9,
+        "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "elements_per_s": elems / (ms * 1e-3),
+        "output_kernel_ms": kern_ms, "algorithmic_bytes": nbytes, "rotating_sets": rotate, "plan": plan,
+        "valu_slots_per_element": valu_slots_per_element(w.N, w.gate),
+        "kernel_valu_Tslot_s": slots / (kern_ms * 1e-3) / 1e12,
+        "kernel_GBps": nbytes / (kern_ms * 1e-3) / 1e9, "input_gen_s": gen_s,
+    }
+    if not quiet:
+        print(f"# {name}: {ms * 1e3:.1f} us/call, {res['GBps']:.0f} GB/s, output kernel {kern_ms * 1e3:.1f} us "
+              f"({res['kernel_valu_Tslot_s']:.2f} T VALU slot/s), plan {plan}", file=sys.stderr, flush=True)
+    del sets
+    torch.cuda.empty_cache()
+    return res, inp
+
+
+def bench_decode(name, rotate_states, quiet=False):
+    """The decode workload: `steps` successive single-token steps, each with fresh inputs, on one
+    state (rotate_states = 1, the literal workload) or cycling through several layer states."""
+    import torch
+    from selective_state_space_82_amd import api
+    from selective_state_space_82_amd import inputs as I
+
+    w = I.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    st0 = torch.from_numpy(I.decode_initial_state(w)).to(dev)
+    states = [st0.clone() for _ in range(rotate_states)]
+    stepin = []
+    for s in range(w.steps):
+        si = I.decode_step_inputs(w, s)
+        stepin.append({k: to_dev(si[k], dev) for k in ("x", "delta", "z", "A", "B", "C", "D")})
+    ys = [torch.empty((w.b, w.d), dtype=stepin[0]["x"].dtype, device=dev) for _ in range(2)]
+
+    def step(i):
+        t = stepin[i % w.steps]
+        api.ssm_scan_step(states[i % rotate_states], t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                          y=ys[i % 2])
+
+    for i in range(4):
+        step(i)
+    for j, s in enumerate(states):
+        s.copy_(st0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(w.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    esize = 2 if w.dtype == "bf16" else 4
+    per_step = (2 * w.b * w.d * w.N * 4 + 4 * w.b * w.d * esize + 2 * w.b * w.N * esize + w.d * w.N * 4 + w.d * 4)
+    per_step_s = gpu_ms * 1e-3 / w.steps
+    res = {"workload": name, "states_rotated": rotate_states, "steps": w.steps,
+           "steps_per_s": w.steps / (gpu_ms * 1e-3), "tokens_per_s": w.b * w.steps / (gpu_ms * 1e-3),
+           "us_per_step": per_step_s * 1e6, "GBps": per_step / per_step_s / 1e9,
+           "hbm_frac": per_step / per_step_s / 1e9 / HBM_PEAK_GBS, "bytes_per_step": per_step,
+           "wall_steps_per_s": w.steps / wall}
+    if not quiet:
+        print(f"# {name} (states rotated: {rotate_states}): {res['us_per_step']:.1f} us/step, "
+              f"{res['steps_per_s']:.0f} steps/s, {res['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+    return res
+
+
+def cpu_baseline(inp, name, threads):
+    """The fp64 oracle on the host over the whole workload (its rows split across threads)."""
+    import concurrent.futures as cf
+
+    import oracle
+    from selective_state_space_82_amd import inputs as I
+
+    w = I.WORKLOADS[name]
+    dt = inp["dtype"]
+    chunks = [(ib, c0, min(w.d, c0 + 128)) for ib in range(w.b) for c0 in range(0, w.d, 128)]
+
+    def one(job):
+        ib, c0, c1 = job
+        wd = lambda a: I.widen(a[ib:ib + 1, c0:c1], dt)
+        oracle.scan_fwd(wd(inp["x"]), wd(inp["delta"]), inp["A"][c0:c1], I.widen(inp["B"][ib:ib + 1], dt),
+                        I.widen(inp["C"][ib:ib + 1], dt), inp["D"][c0:c1],
+                        None if inp["z"] is None else wd(inp["z"]))
+
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one, chunks))
+    wall = time.perf_counter() - t0
+    esize = 4 if dt == "f32" else 2
+    nbytes = algorithmic_bytes(w.b, w.d, w.L, w.N, esize, w.gate)
+    return {"value": nbytes / wall / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole workload ({w.b * w.d} (b,d) rows x {w.L} steps x {w.N} states), "
+                      f"fp64 sequential rows on {threads} host threads, {wall:.2f} s wall",
+            "elements_per_s": w.b * w.d * w.L / wall}
+
+
+def copy_probe(nbytes):
+    """A plain device copy of known size (calibrates the HBM byte counters)."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--extra", default="decode,mamba1p4b_bf16_b8_d4096_L4096_N16",
+                    help="comma list: 'decode' and/or prefill workload names ('' for none, 'all' for every one)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=0, help="input/output sets to rotate (0 = enough to exceed the cache)")
+    ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the scan shards by batch row or "
+              "channel with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+
+    from selective_state_space_82_amd import inputs as I
+
+    head, inp = bench_prefill(args.workload, args.steps, args.warmup, args.rotate)
+    w = I.WORKLOADS[args.workload]
+    extra = []
+    names = [n for n in args.extra.split(",") if n]
+    if names == ["all"]:
+        names = ["decode"] + [n for n in I.PREFILL_WORKLOADS if n != args.workload]
+    for n in names:
+        if n == "decode":
+            for r in (1, 4):
+                extra.append(bench_decode(I.DECODE_WORKLOADS[0], r))
+        else:
+            r, _ = bench_prefill(n, max(3, args.steps // 4), 2)
+            extra.append(r)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = int(min(16, os.cpu_count() or 1))
+        cpu = cpu_baseline(inp, args.workload, threads)
+        print(f"# cpu baseline: {cpu['value']:.3f} GB/s on {threads} threads", file=sys.stderr, flush=True)
+
+    kern_s = head["output_kernel_ms"] * 1e-3
+    slots = w.b * w.d * w.L * head["valu_slots_per_element"]
+    traffic = None
+    prof = os.path.join(ROOT, "profiles", "traffic_counters.json")
+    if os.path.exists(prof):
+        try:
+            from selective_state_space_82_amd import build as B
+            with open(prof) as f:
+                tc = json.load(f)
+            if tc.get("kernel_source_sha256") == B.kernel_source_hash() and args.workload in tc.get("per_launch_bytes", {}):
+                traffic = tc["per_launch_bytes"][args.workload]
+        except Exception:  # a stale or unreadable counter file means no traffic figure
+            traffic = None
+    line = {
+        "metric": METRIC,
+        "value": round(head["GBps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_call"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Normal / softplus-Normal draws with the workload's distributions)",
+        "config": {"workload": args.workload, "b": w.b, "d": w.d, "L": w.L, "N": w.N, "gate": w.gate,
+                   "state": "f32", "plan": head["plan"], "rotating_sets": head["rotating_sets"]},
+        "hbm_frac": round(head["hbm_frac"], 4),
+        "elements_per_s": head["elements_per_s"],
+        "roofline": {"bound": "alu", "achieved": round(slots / kern_s / 1e12, 3), "peak": round(VALU_PEAK_TSLOT, 3),
+                     "unit": "Tslot/s", "frac": round(slots / kern_s / 1e12 / VALU_PEAK_TSLOT, 4),
+                     "traffic": traffic, "kernel": "scan_fwd_kernel (output pass)",
+                     "kernel_us": round(head["output_kernel_ms"] * 1e3, 2),
+                     "kernel_hbm_frac": round(head["kernel_GBps"] / HBM_PEAK_GBS, 4)},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -49,7 +49,7 @@ struct FwdArgs {
     int64_t seg_len;
     int64_t n_db;             // channel blocks per batch row
     int vec_rows;             // x/Δ/z rows allow 16-byte loads at every tile
-    int vec_bc;               // B/C rows allow vector loads of whole state groups
+    int vec_bc;               // B/C tile runs allow 16-byte loads
 };
 
 template <typename T> struct Chunk;                 // 16 bytes of one row
@@ -70,7 +70,22 @@ __device__ __forceinline__ void put_chunk<uint16_t>(float *dst, const uint4 &v) 
     *reinterpret_cast<float4 *>(dst + 4) = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
 }
 
-// Load one chunk (E consecutive timesteps of one row) with bounds; out-of-range elements are 0.
+// Widen one 16-byte chunk into `E` floats in registers.
+template <typename T>
+__device__ __forceinline__ void put_chunk_regs(float *dst, const uint4 &v);
+template <>
+__device__ __forceinline__ void put_chunk_regs<float>(float *dst, const uint4 &v) {
+    dst[0] = __uint_as_float(v.x); dst[1] = __uint_as_float(v.y);
+    dst[2] = __uint_as_float(v.z); dst[3] = __uint_as_float(v.w);
+}
+template <>
+__device__ __forceinline__ void put_chunk_regs<uint16_t>(float *dst, const uint4 &v) {
+    dst[0] = bf16_lo(v.x); dst[1] = bf16_hi(v.x); dst[2] = bf16_lo(v.y); dst[3] = bf16_hi(v.y);
+    dst[4] = bf16_lo(v.z); dst[5] = bf16_hi(v.z); dst[6] = bf16_lo(v.w); dst[7] = bf16_hi(v.w);
+}
+
+// Load one chunk (E consecutive elements of a row or run) with bounds; elements at or past
+// `t_end` are 0.
 template <typename T>
 __device__ __forceinline__ uint4 get_chunk(const T *__restrict__ row, int64_t t, int64_t t_end,
                                            bool row_ok, bool vec) {
@@ -85,111 +100,131 @@ __device__ __forceinline__ uint4 get_chunk(const T *__restrict__ row, int64_t t,
     return r;
 }
 
-// Read-only inputs addressed through the constant address space: a wave-uniform address turns
-// into a scalar load (s_load) whose value feeds the VALU as an SGPR operand.
-template <typename T> using cptr = const __attribute__((address_space(4))) T *;
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// LDS helpers -------------------------------------------------------------------------------
 
-// NPL values of B or C (one timestep, starting at state n0), wave-uniform.
-template <typename T, int NPL, bool VEC>
-__device__ __forceinline__ void load_group(cptr<T> p, int nvalid, float (&out)[NPL]) {
-    if constexpr (VEC) {
-        if constexpr (sizeof(T) == 4) {
-#pragma unroll
-            for (int j = 0; j < NPL; j += 4) {
-                const f32x4 v = *reinterpret_cast<cptr<f32x4>>(p + j);
-                out[j] = v.x; out[j + 1] = v.y; out[j + 2] = v.z; out[j + 3] = v.w;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < NPL; j += 4) {
-                const u32x2 v = *reinterpret_cast<cptr<u32x2>>(p + j);
-                out[j] = bf16_lo(v.x); out[j + 1] = bf16_hi(v.x);
-                out[j + 2] = bf16_lo(v.y); out[j + 3] = bf16_hi(v.y);
-            }
-        }
+// U consecutive floats from LDS (U = 1, 2 or 4).
+template <int U>
+__device__ __forceinline__ void lds_get(const float *p, float (&o)[U]) {
+    if constexpr (U == 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(p);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    } else if constexpr (U == 2) {
+        const float2 v = *reinterpret_cast<const float2 *>(p);
+        o[0] = v.x; o[1] = v.y;
     } else {
-#pragma unroll
-        for (int j = 0; j < NPL; ++j) out[j] = (j < nvalid) ? widen(p[j]) : 0.0f;
+        o[0] = *p;
     }
 }
 
-// Scan one LDS tile for this wavefront's NPL states. SAFE selects the unscaled path; AGG drops
-// the readout (aggregate pass); otherwise each timestep's readout partial goes to `part_row`.
-// Bt, Ct point at (batch row, first timestep of the tile, state n0); rows past `kmax` (the tail of
-// the sequence) re-read row kmax, whose values do not matter there because Δ = x = 0.
-template <typename T, int NPL, bool SAFE, bool AGG, bool VEC>
-__device__ __forceinline__ void scan_tile(const float *xrow, const float *drow, float *part_row,
-                                          cptr<T> Bt, cptr<T> Ct, int N, int kmax, int nvalid,
+template <int U>
+__device__ __forceinline__ void lds_put(float *p, const float (&v)[U]) {
+    if constexpr (U == 4) *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    else if constexpr (U == 2) *reinterpret_cast<float2 *>(p) = make_float2(v[0], v[1]);
+    else *p = v[0];
+}
+
+// Scan one LDS tile for this wavefront's NPL states.
+//   xrow, drow : this lane's x and Δ for the tile (LDS, fp32)
+//   Bn, Cn     : the tile's B and C planes [kTile][NPAD] (LDS, fp32), offset to state n0; the
+//                reads are wave-uniform, so every lane receives the same values
+//   prow       : this lane's readout partials for the tile (LDS), output pass only
+//   dskip      : D·x is added to this wave's partial (nonzero on wave 0 only)
+// SAFE selects the unscaled path; AGG drops the readout (aggregate pass).
+//
+// The tile is walked in sub-tiles of U = 8 / NPL timesteps (1 for NPL >= 8). Each step issues the LDS reads of the
+// NEXT sub-tile before computing the current one. LDS operations complete in order, so the wait
+// for the current sub-tile leaves the prefetch in flight.
+template <int NPL, int NPAD, bool SAFE, bool AGG>
+__device__ __forceinline__ void scan_tile(const float *xrow, const float *drow, const float *Bn,
+                                          const float *Cn, float *prow, float dskip,
                                           const float (&a2)[NPL], const float (&Av)[NPL],
                                           const float (&ia)[NPL], float (&s)[NPL], float &dsum) {
-#pragma unroll 2
-    for (int t4 = 0; t4 < kTile; t4 += 4) {
-        const float4 xv4 = *reinterpret_cast<const float4 *>(xrow + t4);
-        const float4 dv4 = *reinterpret_cast<const float4 *>(drow + t4);
-        const float xv[4] = {xv4.x, xv4.y, xv4.z, xv4.w};
-        const float dv[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
-        float yv[4];
+    constexpr int U = NPL >= 8 ? 1 : 8 / NPL;
+    constexpr int NSUB = kTile / U;  // even
+    struct Sub {
+        float x[U], d[U], B[U][NPL], C[U][NPL];
+    };
+    auto load_sub = [&](int u, Sub &o) {
+        lds_get<U>(xrow + u * U, o.x);
+        lds_get<U>(drow + u * U, o.d);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int kk = (t4 + k) < kmax ? (t4 + k) : kmax;
-            float Bv[NPL], Cv[NPL];
-            load_group<T, NPL, VEC>(Bt + kk * N, nvalid, Bv);
-            if constexpr (!AGG) load_group<T, NPL, VEC>(Ct + kk * N, nvalid, Cv);
-            const float xt = xv[k], dt = dv[k];
-            float acc = 0.0f;
+        for (int k = 0; k < U; ++k) {
+#pragma unroll
+            for (int j = 0; j < NPL; j += 4) {
+                const float4 b = *reinterpret_cast<const float4 *>(Bn + (u * U + k) * NPAD + j);
+                o.B[k][j] = b.x; o.B[k][j + 1] = b.y; o.B[k][j + 2] = b.z; o.B[k][j + 3] = b.w;
+                if constexpr (!AGG) {
+                    const float4 c = *reinterpret_cast<const float4 *>(Cn + (u * U + k) * NPAD + j);
+                    o.C[k][j] = c.x; o.C[k][j + 1] = c.y; o.C[k][j + 2] = c.z; o.C[k][j + 3] = c.w;
+                }
+            }
+        }
+    };
+    auto compute_sub = [&](int u, const Sub &c) {
+        float yv[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const float xt = c.x[k], dt = c.d[k];
+            float acc = dskip * xt;
 #pragma unroll
             for (int j = 0; j < NPL; ++j) {
                 const float abar = exp2_fast(dt * a2[j]);
                 if constexpr (!SAFE) {
-                    const float pre = __builtin_fmaf(Bv[j], xt, s[j]);      // s + B x
+                    const float pre = __builtin_fmaf(c.B[k][j], xt, s[j]);  // s + B x
                     s[j] = __builtin_fmaf(abar - 1.0f, pre, s[j]);          // s + (Ā − 1)(s + B x)
-                    if constexpr (!AGG) acc = __builtin_fmaf(Cv[j] * ia[j], s[j], acc);
+                    if constexpr (!AGG) acc = __builtin_fmaf(c.C[k][j] * ia[j], s[j], acc);
                 } else {
                     const float kc = zoh_input_coef(dt, Av[j], abar, ia[j]);
-                    s[j] = __builtin_fmaf(abar, s[j], kc * (Bv[j] * xt));   // Ā h + B̄ x
-                    if constexpr (!AGG) acc = __builtin_fmaf(Cv[j], s[j], acc);
+                    s[j] = __builtin_fmaf(abar, s[j], kc * (c.B[k][j] * xt));  // Ā h + B̄ x
+                    if constexpr (!AGG) acc = __builtin_fmaf(c.C[k][j], s[j], acc);
                 }
             }
             if constexpr (AGG) dsum += dt;
             yv[k] = acc;
         }
-        if constexpr (!AGG) *reinterpret_cast<float4 *>(part_row + t4) = make_float4(yv[0], yv[1], yv[2], yv[3]);
+        if constexpr (!AGG) lds_put<U>(prow + u * U, yv);
+    };
+    Sub s0, s1;
+    load_sub(0, s0);
+#pragma unroll 1
+    for (int u = 0; u < NSUB; u += 2) {
+        load_sub(u + 1, s1);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
+        compute_sub(u, s0);
+        load_sub(u + 2 < NSUB ? u + 2 : u + 1, s0);  // the last pass re-reads a sub-tile it has
+        __builtin_amdgcn_sched_barrier(0);
+        compute_sub(u + 1, s1);
     }
 }
 
-template <typename T, int NPL, bool AGG>
-__device__ __forceinline__ void scan_tile_any(bool safe, bool vec, const float *xrow, const float *drow,
-                                              float *part_row, cptr<T> Bt, cptr<T> Ct, int N, int kmax,
-                                              int nvalid, const float (&a2)[NPL], const float (&Av)[NPL],
-                                              const float (&ia)[NPL], float (&s)[NPL], float &dsum) {
-    if (!safe) {
-        if (vec) scan_tile<T, NPL, false, AGG, true>(xrow, drow, part_row, Bt, Ct, N, kmax, nvalid, a2, Av, ia, s, dsum);
-        else scan_tile<T, NPL, false, AGG, false>(xrow, drow, part_row, Bt, Ct, N, kmax, nvalid, a2, Av, ia, s, dsum);
-    } else {
-        if (vec) scan_tile<T, NPL, true, AGG, true>(xrow, drow, part_row, Bt, Ct, N, kmax, nvalid, a2, Av, ia, s, dsum);
-        else scan_tile<T, NPL, true, AGG, false>(xrow, drow, part_row, Bt, Ct, N, kmax, nvalid, a2, Av, ia, s, dsum);
-    }
-}
-
+// The kernel --------------------------------------------------------------------------------
+//
+// One workgroup: 64 channels (one per lane) of batch row bi, time segment `seg`, GW wavefronts
+// (wave w owns states [w*NPL, (w+1)*NPL)). Per tile of kTile timesteps:
+//   scan (LDS only) -> barrier -> store the prefetched next tile into LDS, epilogue of this tile,
+//   issue the global loads of the tile after next -> barrier.
+// The tile's x and Δ rows, and its B and C rows (one contiguous run of kTile*N elements each),
+// are fetched one tile ahead into registers with 16-byte loads and widened to fp32 on the way
+// into LDS, so the scan never touches global memory.
 template <typename T, int NPL, int GW, bool AGG>
 __global__ __launch_bounds__(kWave *GW) void scan_fwd_kernel(FwdArgs a) {
     constexpr int E = Chunk<T>::kElems;
+    constexpr int kThreads = kWave * GW;
     constexpr int kChunksPerRow = kTile / E;
-    constexpr int kCPT = kGroupRows * kChunksPerRow / (kWave * GW);  // chunks per thread
-    constexpr int kEPT = kGroupRows * kTile / (kWave * GW);          // epilogue elements per thread
-    constexpr int kPlanes = AGG ? 4 : 4 + GW;
-    __shared__ float smem[kPlanes * kRowsF + kGroupRows];
-    float *xs = smem;                      // [2][64][pitch] x, widened
-    float *dsh = smem + 2 * kRowsF;        // [2][64][pitch] Δ, widened
-    float *part = smem + 4 * kRowsF;       // [GW][64][pitch] readout partials (output pass)
-    float *Dsh = smem + kPlanes * kRowsF;  // [64] skip weights
+    constexpr int kCPT = kGroupRows * kChunksPerRow / kThreads;                 // x/Δ chunks per thread
+    constexpr int kEPT = kGroupRows * kTile / kThreads;                         // epilogue elements per thread
+    constexpr int NPAD = NPL * GW;                                              // states held in LDS per timestep
+    constexpr int kBCF = kTile * NPAD;                                          // floats per B or C plane
+    constexpr int kBCT = (kBCF / E + kThreads - 1) / kThreads;                  // B/C chunks per thread
+    __shared__ __attribute__((aligned(16))) float xs[kRowsF];
+    __shared__ __attribute__((aligned(16))) float dsh[kRowsF];
+    __shared__ __attribute__((aligned(16))) float Bs[kBCF];
+    __shared__ __attribute__((aligned(16))) float Cs[AGG ? 4 : kBCF];
+    __shared__ __attribute__((aligned(16))) float part[AGG ? 4 : GW * kRowsF];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    constexpr int kThreads = kWave * GW;
 
     const int64_t ncb = a.b * a.n_db;
     const int64_t blk = blockIdx.x;
@@ -201,28 +236,27 @@ __global__ __launch_bounds__(kWave *GW) void scan_fwd_kernel(FwdArgs a) {
     const int64_t t_end = (t_begin + a.seg_len < a.L) ? t_begin + a.seg_len : a.L;
     const int ntiles = (int)((t_end - t_begin + kTile - 1) / kTile);
     const int64_t bd = a.b * a.d;
+    const int N = (int)a.N;
 
     const T *__restrict__ xg = static_cast<const T *>(a.x);
     const T *__restrict__ dg = static_cast<const T *>(a.delta);
     const T *__restrict__ zg = static_cast<const T *>(a.z);
-    const int64_t bc_row = bi * a.L * a.N;
+    const T *__restrict__ Bg = static_cast<const T *>(a.B) + bi * a.L * a.N;
+    const T *__restrict__ Cg = static_cast<const T *>(a.C) + bi * a.L * a.N;
     T *__restrict__ yg = static_cast<T *>(a.y);
 
     // ---- per-lane channel constants for this wave's state group ----
     const int64_t ch = d0 + lane;
     const bool ch_ok = ch < a.d;
     const int n0 = wave * NPL;
-    const int nvalid = (int)((a.N - n0) < NPL ? (a.N - n0) : NPL);  // may be <= 0 for idle waves
-    const bool vec_bc = a.vec_bc && nvalid == NPL;
-    const cptr<T> Bc = (cptr<T>)(static_cast<const T *>(a.B)) + bc_row + n0;
-    const cptr<T> Cc = (cptr<T>)(static_cast<const T *>(a.C)) + bc_row + n0;
-    const int64_t row = bi * a.d + ch;  // (b, d) row index
+    const int nvalid = (N - n0) < NPL ? (N - n0) : NPL;  // <= 0 for a wave past the last state
+    const int64_t row = bi * a.d + ch;
     float Av[NPL], a2[NPL], ia[NPL], s[NPL];
     bool small_a = false;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
         const bool ok = ch_ok && j < nvalid;
-        const float av = ok ? a.A[ch * a.N + n0 + j] : -1.0f;  // idle states: harmless A = −1, B = C = 0
+        const float av = ok ? a.A[ch * a.N + n0 + j] : -1.0f;  // idle states: A = −1 with B = C = 0
         Av[j] = av;
         a2[j] = av * kLog2e;
         ia[j] = 1.0f / av;
@@ -244,12 +278,10 @@ __global__ __launch_bounds__(kWave *GW) void scan_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < NPL; ++j) s[j] *= Av[j];  // scaled state s = A·h
     }
-    if constexpr (!AGG) {
-        if (tid < kGroupRows) Dsh[tid] = (a.D && d0 + tid < a.d) ? a.D[d0 + tid] : 0.0f;
-    }
+    const float dskip = (!AGG && wave == 0 && ch_ok && a.D) ? a.D[ch] : 0.0f;
 
-    // ---- cooperative tile loads: chunk c -> row c / kChunksPerRow, part c % kChunksPerRow ----
-    uint4 px[kCPT], pd[kCPT];
+    // ---- tile prefetch (registers) and its store into LDS ----
+    uint4 px[kCPT], pd[kCPT], pb[kBCT], pc[kBCT];
     auto load_tile = [&](int64_t t0) {
 #pragma unroll
         for (int i = 0; i < kCPT; ++i) {
@@ -257,35 +289,66 @@ __global__ __launch_bounds__(kWave *GW) void scan_fwd_kernel(FwdArgs a) {
             const int r = c / kChunksPerRow;
             const int64_t tt = t0 + (c % kChunksPerRow) * E;
             const bool rok = d0 + r < a.d;
-            const int64_t off = (bi * a.d + d0 + r) * a.L;
-            px[i] = get_chunk<T>(xg + (rok ? off : 0), tt, t_end, rok, a.vec_rows);
-            pd[i] = get_chunk<T>(dg + (rok ? off : 0), tt, t_end, rok, a.vec_rows);
+            const int64_t off = rok ? (bi * a.d + d0 + r) * a.L : 0;
+            px[i] = get_chunk<T>(xg + off, tt, t_end, rok, a.vec_rows);
+            pd[i] = get_chunk<T>(dg + off, tt, t_end, rok, a.vec_rows);
+        }
+        // B and C rows t0 .. t0 + kTile − 1 form one run of kTile * N elements; rows at or past L
+        // are not read (their Δ is 0, so their values do not matter: zeros keep them finite).
+        const int64_t rows = (a.L - t0) < kTile ? (a.L - t0) : kTile;
+        const int64_t nel = rows * a.N;
+#pragma unroll
+        for (int i = 0; i < kBCT; ++i) {
+            const int c = tid + i * kThreads;
+            const int64_t e0 = (int64_t)c * E;
+            pb[i] = get_chunk<T>(Bg + t0 * a.N, e0, nel, e0 < (int64_t)kBCF, a.vec_bc);
+            if constexpr (!AGG) pc[i] = get_chunk<T>(Cg + t0 * a.N, e0, nel, e0 < (int64_t)kBCF, a.vec_bc);
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&]() {
 #pragma unroll
         for (int i = 0; i < kCPT; ++i) {
             const int c = tid + i * kThreads;
             const int r = c / kChunksPerRow;
             const int col = (c % kChunksPerRow) * E;
-            put_chunk<T>(xs + buf * kRowsF + r * kPitch + col, px[i]);
-            put_chunk<T>(dsh + buf * kRowsF + r * kPitch + col, pd[i]);
+            put_chunk<T>(xs + r * kPitch + col, px[i]);
+            put_chunk<T>(dsh + r * kPitch + col, pd[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < kBCT; ++i) {
+            const int c = tid + i * kThreads;
+            const int e0 = c * E;
+            if (e0 >= kTile * N) continue;
+            if (N == NPAD) {  // the run maps onto the [kTile][NPAD] plane one to one
+                put_chunk<T>(Bs + e0, pb[i]);
+                if constexpr (!AGG) put_chunk<T>(Cs + e0, pc[i]);
+            } else {          // scatter element by element; columns N .. NPAD−1 stay zero
+                float vb[E], vc[E];
+                put_chunk_regs<T>(vb, pb[i]);
+                if constexpr (!AGG) put_chunk_regs<T>(vc, pc[i]);
+#pragma unroll
+                for (int q = 0; q < E; ++q) {
+                    const int e = e0 + q;
+                    if (e < kTile * N) {
+                        const int t = e / N, n = e - t * N;
+                        Bs[t * NPAD + n] = vb[q];
+                        if constexpr (!AGG) Cs[t * NPAD + n] = vc[q];
+                    }
+                }
+            }
         }
     };
 
-    float dsum = 0.0f;
-    load_tile(t_begin);
-    store_tile(0);
-    __syncthreads();
+    if (N != NPAD) {  // padding columns of the B/C planes must read as zero
+        for (int i = tid; i < kBCF; i += kThreads) {
+            Bs[i] = 0.0f;
+            if constexpr (!AGG) Cs[i] = 0.0f;
+        }
+        __syncthreads();
+    }
 
-#pragma unroll 1
-    for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1;
-        const int64_t t0 = t_begin + (int64_t)it * kTile;
-        const bool has_next = it + 1 < ntiles;
-        if (has_next) load_tile(t0 + kTile);
-
-        float zv[kEPT];
+    float zv[kEPT];
+    auto load_z = [&](int64_t t0) {
         if constexpr (!AGG) {
 #pragma unroll
             for (int i = 0; i < kEPT; ++i) {
@@ -296,21 +359,28 @@ __global__ __launch_bounds__(kWave *GW) void scan_fwd_kernel(FwdArgs a) {
                 if (zg && d0 + r < a.d && tg < t_end) zv[i] = widen(zg[(bi * a.d + d0 + r) * a.L + tg]);
             }
         }
+    };
 
-        const float *xrow = xs + buf * kRowsF + lane * kPitch;
-        const float *drow = dsh + buf * kRowsF + lane * kPitch;
-        float *prow = part + wave * kRowsF + lane * kPitch;
-        if (nvalid > 0) {
-            const int kmax = (int)((a.L - t0) < kTile ? (a.L - t0) : kTile) - 1;
-            const int64_t toff = t0 * a.N;
-            scan_tile_any<T, NPL, AGG>(safe, vec_bc, xrow, drow, prow, Bc + toff, Cc + toff, (int)a.N, kmax,
-                                       nvalid, a2, Av, ia, s, dsum);
-        } else if constexpr (!AGG) {
-            for (int t4 = 0; t4 < kTile; t4 += 4) *reinterpret_cast<float4 *>(prow + t4) = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        if (has_next) store_tile(buf ^ 1);
+    float dsum = 0.0f;
+    load_tile(t_begin);
+    store_tile();
+    if (ntiles > 1) load_tile(t_begin + kTile);
+    load_z(t_begin);
+    __syncthreads();
+
+    const float *xrow = xs + lane * kPitch;
+    const float *drow = dsh + lane * kPitch;
+    float *prow = AGG ? part : part + wave * kRowsF + lane * kPitch;
+#pragma unroll 1
+    for (int it = 0; it < ntiles; ++it) {
+        const int64_t t0 = t_begin + (int64_t)it * kTile;
+        if (!safe)
+            scan_tile<NPL, NPAD, false, AGG>(xrow, drow, Bs + n0, Cs + n0, prow, dskip, a2, Av, ia, s, dsum);
+        else
+            scan_tile<NPL, NPAD, true, AGG>(xrow, drow, Bs + n0, Cs + n0, prow, dskip, a2, Av, ia, s, dsum);
         __syncthreads();
 
+        if (it + 1 < ntiles) store_tile();
         if constexpr (!AGG) {
             // Epilogue, time-major: consecutive lanes take consecutive timesteps of one row.
 #pragma unroll
@@ -323,13 +393,14 @@ __global__ __launch_bounds__(kWave *GW) void scan_fwd_kernel(FwdArgs a) {
                     float v = part[r * kPitch + col];
 #pragma unroll
                     for (int w = 1; w < GW; ++w) v += part[w * kRowsF + r * kPitch + col];
-                    v = __builtin_fmaf(Dsh[r], xs[buf * kRowsF + r * kPitch + col], v);
                     if (zg) v *= silu(zv[i]);
                     yg[(bi * a.d + d0 + r) * a.L + tg] = narrow<T>(v);
                 }
             }
-            __syncthreads();
         }
+        if (it + 2 < ntiles) load_tile(t0 + 2 * kTile);
+        if (it + 1 < ntiles) load_z(t0 + kTile);
+        __syncthreads();
     }
 
     // ---- segment results ----
@@ -416,9 +487,8 @@ hipError_t launch_scan_fwd(const FwdLaunch &p, hipStream_t stream) {
     const int64_t esize = p.bf16 ? 2 : 4;
     auto aligned16 = [](const void *q) { return q == nullptr || (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
     a.vec_rows = ((p.L * esize) % 16 == 0) && aligned16(p.x) && aligned16(p.delta) && aligned16(p.z);
-    const int64_t grp_bytes = 4 * esize;  // a vector B/C load covers 4 states
-    auto aligned_g = [&](const void *q) { return (reinterpret_cast<uintptr_t>(q) % grp_bytes) == 0; };
-    a.vec_bc = (p.N % 4 == 0) && aligned_g(p.B) && aligned_g(p.C);
+    // a tile's B/C run starts at element (bi*L + t0)*N with t0 a multiple of 32
+    a.vec_bc = ((p.L * p.N * esize) % 16 == 0) && aligned16(p.B) && aligned16(p.C);
     if (p.n_seg > 1) {
         const int64_t per = (int64_t)(p.n_seg - 1) * p.b * p.d * p.N;
         a.agg_P = p.scratch;
