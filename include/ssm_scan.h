@@ -104,10 +104,11 @@ SSM_API ssm_status_t ssm_scan_step(float *state, const void *x, const void *delt
 
 /*
  * Options of ssm_scan_fwd_ex. Zero-initialise, then set what you need; zero means "choose".
- *   seg_len          time-segment length (multiple of 32) carried across by the chunk-carry pass;
- *                    0 = chosen from the shape, >= L = one segment
- *   states_per_wave  4, 8 or 16 states per wavefront (a workgroup holds ceil(N / this) waves,
- *                    at most 4); 0 = chosen from the shape
+ *   seg_len            time-segment length (multiple of 32) carried across by the chunk-carry
+ *                      pass; 0 = chosen from the shape, >= L = one segment
+ *   lanes_per_channel  1, 2 or 4 lanes of a wavefront share one channel's N states (a wavefront
+ *                      then covers 64 / this channels; each lane holds at most 16 states);
+ *                      0 = chosen from the shape
  *   initial_state    [b][d][N] fp32 device pointer, h_{−1} (NULL = zeros); lets a caller
  *                    continue a sequence that an earlier call ended (pass its final_state)
  *   ev_begin, ev_end hipEvent_t values (may be NULL); when set, recorded on `stream` right before
@@ -115,7 +116,7 @@ SSM_API ssm_status_t ssm_scan_step(float *state, const void *x, const void *delt
  */
 typedef struct {
     int32_t seg_len;
-    int32_t states_per_wave;
+    int32_t lanes_per_channel;
     const float *initial_state;
     void *ev_begin;
     void *ev_end;
@@ -129,13 +130,15 @@ SSM_API ssm_status_t ssm_scan_fwd_ex(const void *x, const void *delta, const flo
                              ssm_dtype_t dtype, hipStream_t stream, const ssm_fwd_opts_t *opts);
 
 /* The launch plan ssm_scan_fwd_ex would use for this shape and these options (host only, no
- * device work), planned for a 256-CU device (MI355X). Writes the resolved seg_len and states_per_wave, plus the number of segments and
- * workgroups per pass, and the scratch bytes. Returns SSM_OK or the validation error. */
+ * device work), planned for a 256-CU device (MI355X): the resolved segment length, lanes per
+ * channel and states per lane, the number of segments, the one-wavefront workgroups of each
+ * segment and of each pass, and the scratch bytes. Returns SSM_OK or the validation error. */
 typedef struct {
     int32_t seg_len;
-    int32_t states_per_wave;
+    int32_t lanes_per_channel;
+    int32_t states_per_lane;
     int32_t n_segments;
-    int32_t waves_per_group;
+    int64_t waves_per_segment;
     int64_t groups_output_pass;
     int64_t groups_aggregate_pass;
     int64_t scratch_bytes;

@@ -28,15 +28,16 @@ class SsmError(RuntimeError):
 
 class FwdOpts(ctypes.Structure):
     """ssm_fwd_opts_t."""
-    _fields_ = [("seg_len", ctypes.c_int32), ("states_per_wave", ctypes.c_int32),
+    _fields_ = [("seg_len", ctypes.c_int32), ("lanes_per_channel", ctypes.c_int32),
                 ("initial_state", ctypes.c_void_p), ("ev_begin", ctypes.c_void_p),
                 ("ev_end", ctypes.c_void_p), ("reserved", ctypes.c_int64 * 4)]
 
 
 class FwdPlan(ctypes.Structure):
     """ssm_fwd_plan_t."""
-    _fields_ = [("seg_len", ctypes.c_int32), ("states_per_wave", ctypes.c_int32),
-                ("n_segments", ctypes.c_int32), ("waves_per_group", ctypes.c_int32),
+    _fields_ = [("seg_len", ctypes.c_int32), ("lanes_per_channel", ctypes.c_int32),
+                ("states_per_lane", ctypes.c_int32), ("n_segments", ctypes.c_int32),
+                ("waves_per_segment", ctypes.c_int64),
                 ("groups_output_pass", ctypes.c_int64), ("groups_aggregate_pass", ctypes.c_int64),
                 ("scratch_bytes", ctypes.c_int64)]
 
@@ -116,7 +117,7 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, *, y=None, final_state=None, return_final_state=True,
-                 seg_len=0, states_per_wave=0, initial_state=None, events=None):
+                 seg_len=0, lanes_per_channel=0, initial_state=None, events=None):
     """Prefill scan. x, delta, z: [b, d, L]; A: [d, N] fp32; B, C: [b, L, N]; D: [d] fp32.
     x, delta, z, B, C share one storage dtype (float32 or bfloat16); y gets it too.
     Returns (y, final_state) (final_state is None when return_final_state is False and none is given).
@@ -148,10 +149,10 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, *, y=None, final_state=None,
     _check("final_state", final_state, (b, d, N), torch.float32, dev)
     args = [_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), _ptr(final_state),
             b, d, L, N, code, _stream(dev)]
-    if seg_len or states_per_wave or initial_state is not None or events is not None:
+    if seg_len or lanes_per_channel or initial_state is not None or events is not None:
         o = FwdOpts()
         o.seg_len = int(seg_len)
-        o.states_per_wave = int(states_per_wave)
+        o.lanes_per_channel = int(lanes_per_channel)
         o.initial_state = None if initial_state is None else initial_state.data_ptr()
         if events is not None:
             o.ev_begin = events[0].cuda_event
@@ -191,11 +192,11 @@ def ssm_scan_step(state, x, delta, A, B, C, D=None, z=None, *, y=None):
     return y
 
 
-def ssm_scan_fwd_plan(b, d, L, N, dtype=torch.float32, seg_len=0, states_per_wave=0) -> dict:
+def ssm_scan_fwd_plan(b, d, L, N, dtype=torch.float32, seg_len=0, lanes_per_channel=0) -> dict:
     """The launch plan ssm_scan_fwd would use (host only)."""
     o = FwdOpts()
     o.seg_len = int(seg_len)
-    o.states_per_wave = int(states_per_wave)
+    o.lanes_per_channel = int(lanes_per_channel)
     p = FwdPlan()
     status = lib().ssm_scan_fwd_plan(b, d, L, N, _dtype_code(dtype), ctypes.byref(o), ctypes.byref(p))
     _raise(status, "ssm_scan_fwd_plan")

@@ -70,36 +70,44 @@ void keep_pool_memory() {
 }
 
 struct Plan {
-    int npl, waves, n_seg;
-    int64_t seg_len, groups_out, groups_agg, scratch_bytes;
+    int lanes, npl, n_seg;
+    int64_t seg_len, waves_per_seg, groups_out, groups_agg, scratch_bytes;
 };
 
-// Launch plan. Each workgroup holds 64 channels of one batch row for one time segment; a
-// sequence is cut into segments only when the channel blocks alone cannot fill the device, since
-// every extra segment costs an aggregate rescan of its inputs.
+// Smallest supported states-per-lane count holding ceil(N / lanes) states (0 = none).
+int states_per_lane(int64_t N, int lanes) {
+    const int64_t need = (N + lanes - 1) / lanes;
+    for (int npl : {4, 8, 16})
+        if (need <= npl) return npl;
+    return 0;
+}
+
+// Launch plan. A workgroup is one wavefront: 64 / G channels of one batch row (G lanes per
+// channel, each holding states_per_lane states) over one time segment. A sequence is cut into
+// segments only when the channel blocks alone cannot fill the device, since every segment after
+// the first costs an aggregate rescan of its inputs.
 ssm_status_t make_plan(int64_t b, int64_t d, int64_t L, int64_t N, const ssm_fwd_opts_t *o, int cus, Plan *pl) {
-    int npl = o ? o->states_per_wave : 0;
-    if (npl == 0) npl = N <= 16 ? 4 : (N <= 32 ? 8 : 16);
-    if (npl != 4 && npl != 8 && npl != 16) return SSM_ERR_UNSUPPORTED;
-    int waves = (int)((N + npl - 1) / npl);
-    if (waves > 4) return SSM_ERR_UNSUPPORTED;
-    if (waves == 3) waves = 4;
-    const int64_t n_db = (d + ssm::kGroupRows - 1) / ssm::kGroupRows;
-    const int64_t ncb = b * n_db;
+    int lanes = o ? o->lanes_per_channel : 0;
+    if (lanes == 0) lanes = 4;
+    if (lanes != 1 && lanes != 2 && lanes != 4) return SSM_ERR_UNSUPPORTED;
+    const int npl = states_per_lane(N, lanes);
+    if (npl == 0) return SSM_ERR_UNSUPPORTED;
+    const int64_t cw = 64 / lanes;
+    const int64_t ncb = b * ((d + cw - 1) / cw);  // wavefronts per time segment
     int64_t seg_len = o ? o->seg_len : 0;
-    if (seg_len < 0 || (seg_len % ssm::kTile) != 0) return SSM_ERR_UNSUPPORTED;
-    const int64_t Lr = ((L + ssm::kTile - 1) / ssm::kTile) * ssm::kTile;
+    if (seg_len < 0 || (seg_len % ssm::kSegQuantum) != 0) return SSM_ERR_UNSUPPORTED;
+    const int64_t Lr = ((L + ssm::kSegQuantum - 1) / ssm::kSegQuantum) * ssm::kSegQuantum;
     if (seg_len == 0) {
-        // aim for about 8 wavefronts per compute unit, never segments shorter than 256 steps
-        const int64_t want_groups = (int64_t)cus * (8 / waves);
-        int64_t S = (want_groups + ncb - 1) / ncb;
+        // about two wavefronts per SIMD (4 SIMDs per compute unit); segments of at least 256 steps
+        const int64_t want = (int64_t)cus * 4 * 2;
+        int64_t S = (want + ncb - 1) / ncb;
         const int64_t max_seg = Lr / 256 > 0 ? Lr / 256 : 1;
         if (S > max_seg) S = max_seg;
         if (S > 64) S = 64;
         if (S < 1) S = 1;
-        seg_len = ((Lr / S + ssm::kTile - 1) / ssm::kTile) * ssm::kTile;
+        seg_len = ((Lr / S + ssm::kSegQuantum - 1) / ssm::kSegQuantum) * ssm::kSegQuantum;
     }
-    if (seg_len > Lr || seg_len == 0) seg_len = Lr > 0 ? Lr : ssm::kTile;
+    if (seg_len > Lr || seg_len == 0) seg_len = Lr > 0 ? Lr : ssm::kSegQuantum;
     int64_t n_seg = L > 0 ? (L + seg_len - 1) / seg_len : 1;
     if (n_seg > 4096) return SSM_ERR_UNSUPPORTED;
     int64_t scratch = 0;
@@ -108,10 +116,11 @@ ssm_status_t make_plan(int64_t b, int64_t d, int64_t L, int64_t N, const ssm_fwd
         if (!mul_ok((n_seg - 1) * b, d * N, &per)) return SSM_ERR_SHAPE;
         scratch = 3 * per * (int64_t)sizeof(float);
     }
+    pl->lanes = lanes;
     pl->npl = npl;
-    pl->waves = waves;
     pl->n_seg = (int)n_seg;
     pl->seg_len = seg_len;
+    pl->waves_per_seg = ncb;
     pl->groups_out = n_seg * ncb;
     pl->groups_agg = (n_seg - 1) * ncb;
     pl->scratch_bytes = scratch;
@@ -131,10 +140,10 @@ ssm_status_t check_fwd_sizes(int64_t b, int64_t d, int64_t L, int64_t N, ssm_dty
 // Option values that need no device information.
 ssm_status_t check_opts(int64_t N, const ssm_fwd_opts_t *o) {
     if (!o) return SSM_OK;
-    const int npl = o->states_per_wave;
-    if (npl != 0 && npl != 4 && npl != 8 && npl != 16) return SSM_ERR_UNSUPPORTED;
-    if (npl != 0 && (N + npl - 1) / npl > 4) return SSM_ERR_UNSUPPORTED;
-    if (o->seg_len < 0 || (o->seg_len % ssm::kTile) != 0) return SSM_ERR_UNSUPPORTED;
+    const int lanes = o->lanes_per_channel;
+    if (lanes != 0 && lanes != 1 && lanes != 2 && lanes != 4) return SSM_ERR_UNSUPPORTED;
+    if (states_per_lane(N, lanes == 0 ? 4 : lanes) == 0) return SSM_ERR_UNSUPPORTED;
+    if (o->seg_len < 0 || (o->seg_len % ssm::kSegQuantum) != 0) return SSM_ERR_UNSUPPORTED;
     return SSM_OK;
 }
 
@@ -169,8 +178,8 @@ ssm_status_t fwd_impl(const void *x, const void *delta, const float *A, const vo
     p.init_state = o ? o->initial_state : nullptr;
     p.b = b; p.d = d; p.L = L; p.N = N;
     p.bf16 = dtype == SSM_BF16;
-    p.states_per_wave = pl.npl;
-    p.waves = pl.waves;
+    p.lanes_per_channel = pl.lanes;
+    p.states_per_lane = pl.npl;
     p.seg_len = pl.seg_len;
     p.n_seg = pl.n_seg;
     p.ev_begin = o ? static_cast<hipEvent_t>(o->ev_begin) : nullptr;
@@ -230,9 +239,10 @@ ssm_status_t ssm_scan_fwd_plan(int64_t b, int64_t d, int64_t L, int64_t N, ssm_d
     st = make_plan(b, d, L, N, opts, 256, &pl);
     if (st != SSM_OK) return st;
     plan->seg_len = (int32_t)pl.seg_len;
-    plan->states_per_wave = pl.npl;
+    plan->lanes_per_channel = pl.lanes;
+    plan->states_per_lane = pl.npl;
     plan->n_segments = pl.n_seg;
-    plan->waves_per_group = pl.waves;
+    plan->waves_per_segment = pl.waves_per_seg;
     plan->groups_output_pass = pl.groups_out;
     plan->groups_aggregate_pass = pl.groups_agg;
     plan->scratch_bytes = pl.scratch_bytes;

@@ -18,9 +18,9 @@ struct FwdLaunch {
     const float *init_state;  // h_{-1} of segment 0, or nullptr (zeros)
     int64_t b, d, L, N;
     bool bf16;
-    int states_per_wave;      // 4, 8 or 16
-    int waves;                // 1, 2 or 4 waves per workgroup (states_per_wave * waves >= N)
-    int64_t seg_len;          // multiple of 32
+    int lanes_per_channel;    // G = 1, 2 or 4 lanes share one channel (64 / G channels per wavefront)
+    int states_per_lane;      // 4, 8 or 16, with lanes_per_channel * states_per_lane >= N
+    int64_t seg_len;          // multiple of kSegQuantum
     int n_seg;                // ceil(L / seg_len) >= 1
     float *scratch;           // 3 * (n_seg - 1) * b * d * N floats when n_seg > 1
     hipEvent_t ev_begin, ev_end;
@@ -42,7 +42,6 @@ hipError_t launch_scan_fwd(const FwdLaunch &p, hipStream_t stream);
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t stream);
 hipError_t launch_scan_step(const StepLaunch &p, hipStream_t stream);
 
-constexpr int kTile = 32;       // timesteps per LDS tile
-constexpr int kGroupRows = 64;  // channels per workgroup: one per lane of a wavefront
+constexpr int kSegQuantum = 32; // time segments are multiples of this many steps
 
 }  // namespace ssm

@@ -6,32 +6,38 @@
 //   Ā = exp(Δ·A), B̄ = (Ā − 1)/A · B, h_t = Ā h_{t−1} + B̄ x_t, y_t = C_t·h_t + D x_t, y ← y·silu(z).
 //
 // Mapping onto CDNA4:
-//   * One lane owns one channel (b, d) and walks time in order, so the recurrence never leaves
-//     registers and needs no cross-lane traffic. A workgroup holds 64 channels of one batch row
-//     and 1, 2 or 4 wavefronts; each wavefront owns a contiguous group of `NPL` states of every
-//     channel, so B_t and C_t for that group are wave-uniform and come in through scalar loads.
-//   * x and Δ rows are read as coalesced 16-byte chunks (time is contiguous in memory), widened to
-//     fp32 once and staged in LDS, double-buffered; each lane then reads its own row.
+//   * Work unit = one wavefront, alone in its workgroup, with no barriers anywhere. A wavefront
+//     owns CW = 64 / G channels of one batch row for one time segment; each channel is owned by G
+//     adjacent lanes and lane g keeps the NPL states [g*NPL, (g+1)*NPL) of it in registers, walking
+//     time in order, so the recurrence never leaves registers.
 //   * Per (t, n) the fast path issues one exp and six fp32 VALU operations. With the scaled state
 //     s = A·h the ZOH input needs no division:  s_t = s_{t−1} + (Ā − 1)·(s_{t−1} + B x),
 //     and the readout is Σ_n (C_n / A_n)·s_n. Ā − 1 is exact in fp32 (Sterbenz) and damps the
-//     rounding of s + Bx. States of channels with |A| < 2^-10 use an unscaled path whose input
+//     rounding of s + Bx. Waves holding a channel with |A| < 2^-10 use an unscaled path whose input
 //     coefficient comes from the series of (e^v − 1)/v near v = 0 (the A = 0 limit is Δ·B).
-//   * The readout partials of the wavefronts meet in LDS; the epilogue (sum, + D·x, · silu(z),
-//     rounding) runs time-major so that y rows are written coalesced.
+//   * The readout over a channel's G lanes is an xor butterfly of DPP quad permutes (the same sum
+//     lands on every lane); lane g then finishes timestep t ≡ g (mod G): + D·x (folded into lane 0's
+//     partial), · silu(z), rounding, store. The epilogue thus costs each element once.
+//   * Each tile of kTile timesteps (x, Δ, z rows of the wave's channels; the B and C rows, one
+//     contiguous run) is fetched one tile ahead with 16-byte loads into registers, widened to fp32
+//     into the wave's private LDS, and read back as wave-uniform (B, C) or per-channel (x, Δ, z)
+//     LDS broadcasts, prefetched one sub-tile ahead. LDS operations of one wave complete in order,
+//     so nothing else is needed to order them.
 //   * Long sequences are cut into time segments (page "Mambaとは？…", section Selective Scanは
 //     選択機構そのものではない: affine maps (A, b) compose associatively). An aggregate pass gives
 //     each segment's (Π Ā, end state from zero); a carry pass chains them per (b, d, n); the output
 //     pass then rescans every segment from its true carry-in.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
 namespace ssm {
 namespace {
 
-constexpr int kPitch = kTile + 4;             // floats per LDS row: 16-byte pad, conflict-free b128
-constexpr int kRowsF = kGroupRows * kPitch;   // floats per [64][pitch] LDS plane
-constexpr float kSafeAbsA = 1.0f / 1024.0f;   // |A| below this takes the unscaled path
+constexpr int kTile = 32;                    // timesteps per tile
+constexpr int kPitch = kTile + 4;            // floats per LDS row of x, Δ, z (16-byte pad)
+constexpr float kSafeAbsA = 1.0f / 1024.0f;  // |A| below this takes the unscaled path
 
 struct FwdArgs {
     const void *x, *delta;
@@ -47,12 +53,12 @@ struct FwdArgs {
     float *agg_E;
     int64_t b, d, L, N;
     int64_t seg_len;
-    int64_t n_db;             // channel blocks per batch row
+    int64_t n_cw;             // channel blocks (of 64/G channels) per batch row
     int vec_rows;             // x/Δ/z rows allow 16-byte loads at every tile
     int vec_bc;               // B/C tile runs allow 16-byte loads
 };
 
-template <typename T> struct Chunk;                 // 16 bytes of one row
+template <typename T> struct Chunk;  // 16 bytes of a row or run
 template <> struct Chunk<float> { static constexpr int kElems = 4; };
 template <> struct Chunk<uint16_t> { static constexpr int kElems = 8; };
 
@@ -72,23 +78,23 @@ __device__ __forceinline__ void put_chunk<uint16_t>(float *dst, const uint4 &v) 
 
 // Widen one 16-byte chunk into `E` floats in registers.
 template <typename T>
-__device__ __forceinline__ void put_chunk_regs(float *dst, const uint4 &v);
+__device__ __forceinline__ void chunk_to_regs(float *dst, const uint4 &v);
 template <>
-__device__ __forceinline__ void put_chunk_regs<float>(float *dst, const uint4 &v) {
+__device__ __forceinline__ void chunk_to_regs<float>(float *dst, const uint4 &v) {
     dst[0] = __uint_as_float(v.x); dst[1] = __uint_as_float(v.y);
     dst[2] = __uint_as_float(v.z); dst[3] = __uint_as_float(v.w);
 }
 template <>
-__device__ __forceinline__ void put_chunk_regs<uint16_t>(float *dst, const uint4 &v) {
+__device__ __forceinline__ void chunk_to_regs<uint16_t>(float *dst, const uint4 &v) {
     dst[0] = bf16_lo(v.x); dst[1] = bf16_hi(v.x); dst[2] = bf16_lo(v.y); dst[3] = bf16_hi(v.y);
     dst[4] = bf16_lo(v.z); dst[5] = bf16_hi(v.z); dst[6] = bf16_lo(v.w); dst[7] = bf16_hi(v.w);
 }
 
-// Load one chunk (E consecutive elements of a row or run) with bounds; elements at or past
-// `t_end` are 0.
+// Load one chunk (E consecutive elements of a row or run starting at element t) with bounds;
+// elements at or past `t_end` read as 0.
 template <typename T>
-__device__ __forceinline__ uint4 get_chunk(const T *__restrict__ row, int64_t t, int64_t t_end,
-                                           bool row_ok, bool vec) {
+__device__ __forceinline__ uint4 get_chunk(const T *__restrict__ row, int64_t t, int64_t t_end, bool row_ok,
+                                           bool vec) {
     constexpr int E = Chunk<T>::kElems;
     uint4 r = make_uint4(0u, 0u, 0u, 0u);
     if (!row_ok) return r;
@@ -99,8 +105,6 @@ __device__ __forceinline__ uint4 get_chunk(const T *__restrict__ row, int64_t t,
     __builtin_memcpy(&r, tmp, sizeof(r));
     return r;
 }
-
-// LDS helpers -------------------------------------------------------------------------------
 
 // U consecutive floats from LDS (U = 1, 2 or 4).
 template <int U>
@@ -116,122 +120,72 @@ __device__ __forceinline__ void lds_get(const float *p, float (&o)[U]) {
     }
 }
 
-template <int U>
-__device__ __forceinline__ void lds_put(float *p, const float (&v)[U]) {
-    if constexpr (U == 4) *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
-    else if constexpr (U == 2) *reinterpret_cast<float2 *>(p) = make_float2(v[0], v[1]);
-    else *p = v[0];
+// Orders this wave's LDS accesses around a hand-off between its lanes (tile stores -> scan
+// reads, scan reads -> next tile stores). One wave's LDS operations already execute in order,
+// so this only fences the compiler; it emits no wait.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Scan one LDS tile for this wavefront's NPL states.
-//   xrow, drow : this lane's x and Δ for the tile (LDS, fp32)
-//   Bn, Cn     : the tile's B and C planes [kTile][NPAD] (LDS, fp32), offset to state n0; the
-//                reads are wave-uniform, so every lane receives the same values
-//   prow       : this lane's readout partials for the tile (LDS), output pass only
-//   dskip      : D·x is added to this wave's partial (nonzero on wave 0 only)
-// SAFE selects the unscaled path; AGG drops the readout (aggregate pass).
-//
-// The tile is walked in sub-tiles of U = 8 / NPL timesteps (1 for NPL >= 8). Each step issues the LDS reads of the
-// NEXT sub-tile before computing the current one. LDS operations complete in order, so the wait
-// for the current sub-tile leaves the prefetch in flight.
-template <int NPL, int NPAD, bool SAFE, bool AGG>
-__device__ __forceinline__ void scan_tile(const float *xrow, const float *drow, const float *Bn,
-                                          const float *Cn, float *prow, float dskip,
-                                          const float (&a2)[NPL], const float (&Av)[NPL],
-                                          const float (&ia)[NPL], float (&s)[NPL], float &dsum) {
-    constexpr int U = NPL >= 8 ? 1 : 8 / NPL;
-    constexpr int NSUB = kTile / U;  // even
-    struct Sub {
-        float x[U], d[U], B[U][NPL], C[U][NPL];
-    };
-    auto load_sub = [&](int u, Sub &o) {
-        lds_get<U>(xrow + u * U, o.x);
-        lds_get<U>(drow + u * U, o.d);
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-#pragma unroll
-            for (int j = 0; j < NPL; j += 4) {
-                const float4 b = *reinterpret_cast<const float4 *>(Bn + (u * U + k) * NPAD + j);
-                o.B[k][j] = b.x; o.B[k][j + 1] = b.y; o.B[k][j + 2] = b.z; o.B[k][j + 3] = b.w;
-                if constexpr (!AGG) {
-                    const float4 c = *reinterpret_cast<const float4 *>(Cn + (u * U + k) * NPAD + j);
-                    o.C[k][j] = c.x; o.C[k][j + 1] = c.y; o.C[k][j + 2] = c.z; o.C[k][j + 3] = c.w;
-                }
-            }
-        }
-    };
-    auto compute_sub = [&](int u, const Sub &c) {
-        float yv[U];
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const float xt = c.x[k], dt = c.d[k];
-            float acc = dskip * xt;
-#pragma unroll
-            for (int j = 0; j < NPL; ++j) {
-                const float abar = exp2_fast(dt * a2[j]);
-                if constexpr (!SAFE) {
-                    const float pre = __builtin_fmaf(c.B[k][j], xt, s[j]);  // s + B x
-                    s[j] = __builtin_fmaf(abar - 1.0f, pre, s[j]);          // s + (Ā − 1)(s + B x)
-                    if constexpr (!AGG) acc = __builtin_fmaf(c.C[k][j] * ia[j], s[j], acc);
-                } else {
-                    const float kc = zoh_input_coef(dt, Av[j], abar, ia[j]);
-                    s[j] = __builtin_fmaf(abar, s[j], kc * (c.B[k][j] * xt));  // Ā h + B̄ x
-                    if constexpr (!AGG) acc = __builtin_fmaf(c.C[k][j], s[j], acc);
-                }
-            }
-            if constexpr (AGG) dsum += dt;
-            yv[k] = acc;
-        }
-        if constexpr (!AGG) lds_put<U>(prow + u * U, yv);
-    };
-    Sub s0, s1;
-    load_sub(0, s0);
-#pragma unroll 1
-    for (int u = 0; u < NSUB; u += 2) {
-        load_sub(u + 1, s1);
-        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
-        compute_sub(u, s0);
-        load_sub(u + 2 < NSUB ? u + 2 : u + 1, s0);  // the last pass re-reads a sub-tile it has
-        __builtin_amdgcn_sched_barrier(0);
-        compute_sub(u + 1, s1);
-    }
+// Value of `v` held by lane (lane ^ 1) or (lane ^ 2) of the same quad: DPP quad permutes.
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kSwap1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int kSwap2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+
+// Sum over the G lanes of a channel. Floating-point addition is commutative, so every lane of
+// the group ends with bitwise the same value.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (G >= 2) v += quad_perm<kSwap1>(v);
+    if constexpr (G >= 4) v += quad_perm<kSwap2>(v);
+    return v;
 }
 
-// The kernel --------------------------------------------------------------------------------
+// Timesteps per sub-tile: 8/NPL keeps a sub-tile's B and C at 16 values per lane; a pair of
+// sub-tiles must hold a whole epilogue group of G timesteps.
+constexpr int sub_len(int G, int NPL) {
+    const int u = NPL >= 8 ? 1 : 8 / NPL;
+    return (2 * u) % G == 0 ? u : G / 2;
+}
+
+// The kernel ---------------------------------------------------------------------------------
 //
-// One workgroup: 64 channels (one per lane) of batch row bi, time segment `seg`, GW wavefronts
-// (wave w owns states [w*NPL, (w+1)*NPL)). Per tile of kTile timesteps:
-//   scan (LDS only) -> barrier -> store the prefetched next tile into LDS, epilogue of this tile,
-//   issue the global loads of the tile after next -> barrier.
-// The tile's x and Δ rows, and its B and C rows (one contiguous run of kTile*N elements each),
-// are fetched one tile ahead into registers with 16-byte loads and widened to fp32 on the way
-// into LDS, so the scan never touches global memory.
-template <typename T, int NPL, int GW, bool AGG>
-__global__ __launch_bounds__(kWave *GW) void scan_fwd_kernel(FwdArgs a) {
+// T: storage type (float or bf16 bits); G: lanes per channel (1, 2, 4); NPL: states per lane
+// (4, 8, 16); AGG: aggregate pass (segment end state from zero and Π Ā, no readout).
+template <typename T, int G, int NPL, bool AGG>
+__global__ __launch_bounds__(kWave) void scan_fwd_kernel(FwdArgs a) {
     constexpr int E = Chunk<T>::kElems;
-    constexpr int kThreads = kWave * GW;
-    constexpr int kChunksPerRow = kTile / E;
-    constexpr int kCPT = kGroupRows * kChunksPerRow / kThreads;                 // x/Δ chunks per thread
-    constexpr int kEPT = kGroupRows * kTile / kThreads;                         // epilogue elements per thread
-    constexpr int NPAD = NPL * GW;                                              // states held in LDS per timestep
-    constexpr int kBCF = kTile * NPAD;                                          // floats per B or C plane
-    constexpr int kBCT = (kBCF / E + kThreads - 1) / kThreads;                  // B/C chunks per thread
-    __shared__ __attribute__((aligned(16))) float xs[kRowsF];
-    __shared__ __attribute__((aligned(16))) float dsh[kRowsF];
-    __shared__ __attribute__((aligned(16))) float Bs[kBCF];
-    __shared__ __attribute__((aligned(16))) float Cs[AGG ? 4 : kBCF];
-    __shared__ __attribute__((aligned(16))) float part[AGG ? 4 : GW * kRowsF];
+    constexpr int CW = kWave / G;                       // channels per wavefront
+    constexpr int NPAD = G * NPL;                        // states held per timestep in LDS
+    constexpr int kRowChunks = kTile / E;                // 16-byte chunks per row per tile
+    constexpr int kXC = (CW * kRowChunks + kWave - 1) / kWave;      // row chunks per lane per tensor
+    constexpr int kBF = kTile * NPAD;                    // floats of one B or C plane
+    constexpr int kBC = (kBF / E + kWave - 1) / kWave;   // run chunks per lane per tensor
+    constexpr int U = sub_len(G, NPL);
+    constexpr int NSUB = kTile / U;                      // a pair of sub-tiles spans 2U steps
+    static_assert((2 * U) % G == 0, "an epilogue group must fit a pair of sub-tiles");
+    static_assert(NSUB % 2 == 0, "sub-tiles are processed in pairs");
+    __shared__ __attribute__((aligned(16))) float xs[CW * kPitch];
+    __shared__ __attribute__((aligned(16))) float dsh[CW * kPitch];
+    __shared__ __attribute__((aligned(16))) float zs[AGG ? 4 : CW * kPitch];
+    __shared__ __attribute__((aligned(16))) float Bs[kBF];
+    __shared__ __attribute__((aligned(16))) float Cs[AGG ? 4 : kBF];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = threadIdx.x;
+    const int c = lane / G;  // channel within the wave
+    const int g = lane % G;  // state group within the channel
 
-    const int64_t ncb = a.b * a.n_db;
+    const int64_t ncb = a.b * a.n_cw;
     const int64_t blk = blockIdx.x;
     const int64_t seg = blk / ncb;
     const int64_t cb = blk - seg * ncb;
-    const int64_t bi = cb / a.n_db;
-    const int64_t d0 = (cb - bi * a.n_db) * kGroupRows;
+    const int64_t bi = cb / a.n_cw;
+    const int64_t d0 = (cb - bi * a.n_cw) * CW;
     const int64_t t_begin = seg * a.seg_len;
     const int64_t t_end = (t_begin + a.seg_len < a.L) ? t_begin + a.seg_len : a.L;
     const int ntiles = (int)((t_end - t_begin + kTile - 1) / kTile);
@@ -244,12 +198,13 @@ __global__ __launch_bounds__(kWave *GW) void scan_fwd_kernel(FwdArgs a) {
     const T *__restrict__ Bg = static_cast<const T *>(a.B) + bi * a.L * a.N;
     const T *__restrict__ Cg = static_cast<const T *>(a.C) + bi * a.L * a.N;
     T *__restrict__ yg = static_cast<T *>(a.y);
+    const bool gate = !AGG && zg != nullptr;
 
-    // ---- per-lane channel constants for this wave's state group ----
-    const int64_t ch = d0 + lane;
+    // ---- per-lane channel constants for this lane's state group ----
+    const int64_t ch = d0 + c;
     const bool ch_ok = ch < a.d;
-    const int n0 = wave * NPL;
-    const int nvalid = (N - n0) < NPL ? (N - n0) : NPL;  // <= 0 for a wave past the last state
+    const int n0 = g * NPL;
+    const int nvalid = (N - n0) < NPL ? (N - n0) : NPL;  // <= 0 for a lane past the last state
     const int64_t row = bi * a.d + ch;
     float Av[NPL], a2[NPL], ia[NPL], s[NPL];
     bool small_a = false;
@@ -278,54 +233,57 @@ __global__ __launch_bounds__(kWave *GW) void scan_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < NPL; ++j) s[j] *= Av[j];  // scaled state s = A·h
     }
-    const float dskip = (!AGG && wave == 0 && ch_ok && a.D) ? a.D[ch] : 0.0f;
+    const float dskip = (!AGG && g == 0 && ch_ok && a.D) ? a.D[ch] : 0.0f;
+    const int64_t ybase = row * a.L;
 
-    // ---- tile prefetch (registers) and its store into LDS ----
-    uint4 px[kCPT], pd[kCPT], pb[kBCT], pc[kBCT];
+    // ---- tile prefetch into registers, and from there into LDS ----
+    uint4 px[kXC], pd[kXC], pz[kXC], pb[kBC], pc[kBC];
     auto load_tile = [&](int64_t t0) {
 #pragma unroll
-        for (int i = 0; i < kCPT; ++i) {
-            const int c = tid + i * kThreads;
-            const int r = c / kChunksPerRow;
-            const int64_t tt = t0 + (c % kChunksPerRow) * E;
-            const bool rok = d0 + r < a.d;
+        for (int i = 0; i < kXC; ++i) {
+            const int k = lane + i * kWave;
+            const int r = k / kRowChunks;
+            const int64_t tt = t0 + (k % kRowChunks) * E;
+            const bool rok = k < CW * kRowChunks && d0 + r < a.d;
             const int64_t off = rok ? (bi * a.d + d0 + r) * a.L : 0;
             px[i] = get_chunk<T>(xg + off, tt, t_end, rok, a.vec_rows);
             pd[i] = get_chunk<T>(dg + off, tt, t_end, rok, a.vec_rows);
+            if (gate) pz[i] = get_chunk<T>(zg + off, tt, t_end, rok, a.vec_rows);
         }
         // B and C rows t0 .. t0 + kTile − 1 form one run of kTile * N elements; rows at or past L
         // are not read (their Δ is 0, so their values do not matter: zeros keep them finite).
         const int64_t rows = (a.L - t0) < kTile ? (a.L - t0) : kTile;
         const int64_t nel = rows * a.N;
 #pragma unroll
-        for (int i = 0; i < kBCT; ++i) {
-            const int c = tid + i * kThreads;
-            const int64_t e0 = (int64_t)c * E;
-            pb[i] = get_chunk<T>(Bg + t0 * a.N, e0, nel, e0 < (int64_t)kBCF, a.vec_bc);
-            if constexpr (!AGG) pc[i] = get_chunk<T>(Cg + t0 * a.N, e0, nel, e0 < (int64_t)kBCF, a.vec_bc);
+        for (int i = 0; i < kBC; ++i) {
+            const int64_t e0 = (int64_t)(lane + i * kWave) * E;
+            const bool ok = e0 < (int64_t)kTile * N;
+            pb[i] = get_chunk<T>(Bg + t0 * a.N, e0, nel, ok, a.vec_bc);
+            if constexpr (!AGG) pc[i] = get_chunk<T>(Cg + t0 * a.N, e0, nel, ok, a.vec_bc);
         }
     };
     auto store_tile = [&]() {
 #pragma unroll
-        for (int i = 0; i < kCPT; ++i) {
-            const int c = tid + i * kThreads;
-            const int r = c / kChunksPerRow;
-            const int col = (c % kChunksPerRow) * E;
+        for (int i = 0; i < kXC; ++i) {
+            const int k = lane + i * kWave;
+            if (k >= CW * kRowChunks) break;
+            const int r = k / kRowChunks;
+            const int col = (k % kRowChunks) * E;
             put_chunk<T>(xs + r * kPitch + col, px[i]);
             put_chunk<T>(dsh + r * kPitch + col, pd[i]);
+            if (gate) put_chunk<T>(zs + r * kPitch + col, pz[i]);
         }
 #pragma unroll
-        for (int i = 0; i < kBCT; ++i) {
-            const int c = tid + i * kThreads;
-            const int e0 = c * E;
-            if (e0 >= kTile * N) continue;
+        for (int i = 0; i < kBC; ++i) {
+            const int e0 = (lane + i * kWave) * E;
+            if (e0 >= kTile * N) break;
             if (N == NPAD) {  // the run maps onto the [kTile][NPAD] plane one to one
                 put_chunk<T>(Bs + e0, pb[i]);
                 if constexpr (!AGG) put_chunk<T>(Cs + e0, pc[i]);
-            } else {          // scatter element by element; columns N .. NPAD−1 stay zero
+            } else {          // element by element; columns N .. NPAD−1 stay zero
                 float vb[E], vc[E];
-                put_chunk_regs<T>(vb, pb[i]);
-                if constexpr (!AGG) put_chunk_regs<T>(vc, pc[i]);
+                chunk_to_regs<T>(vb, pb[i]);
+                if constexpr (!AGG) chunk_to_regs<T>(vc, pc[i]);
 #pragma unroll
                 for (int q = 0; q < E; ++q) {
                     const int e = e0 + q;
@@ -340,70 +298,115 @@ __global__ __launch_bounds__(kWave *GW) void scan_fwd_kernel(FwdArgs a) {
     };
 
     if (N != NPAD) {  // padding columns of the B/C planes must read as zero
-        for (int i = tid; i < kBCF; i += kThreads) {
+        for (int i = lane; i < kBF; i += kWave) {
             Bs[i] = 0.0f;
             if constexpr (!AGG) Cs[i] = 0.0f;
         }
-        __syncthreads();
     }
 
-    float zv[kEPT];
-    auto load_z = [&](int64_t t0) {
-        if constexpr (!AGG) {
+    // ---- the scan of one tile, with the epilogue folded in ----
+    struct Sub {
+        float x[U], d[U], B[U][NPL], C[U][NPL];
+    };
+    const float *xrow = xs + c * kPitch;
+    const float *drow = dsh + c * kPitch;
+    const float *zrow = zs + c * kPitch;
+    const float *Bn = Bs + n0;
+    const float *Cn = Cs + n0;
+    auto load_sub = [&](int u, Sub &o) {
+        lds_get<U>(xrow + u * U, o.x);
+        lds_get<U>(drow + u * U, o.d);
 #pragma unroll
-            for (int i = 0; i < kEPT; ++i) {
-                const int e = tid + i * kThreads;
-                const int r = e / kTile;
-                const int64_t tg = t0 + (e % kTile);
-                zv[i] = 0.0f;
-                if (zg && d0 + r < a.d && tg < t_end) zv[i] = widen(zg[(bi * a.d + d0 + r) * a.L + tg]);
+        for (int k = 0; k < U; ++k) {
+#pragma unroll
+            for (int j = 0; j < NPL; j += 4) {
+                const float4 bv = *reinterpret_cast<const float4 *>(Bn + (u * U + k) * NPAD + j);
+                o.B[k][j] = bv.x; o.B[k][j + 1] = bv.y; o.B[k][j + 2] = bv.z; o.B[k][j + 3] = bv.w;
+                if constexpr (!AGG) {
+                    const float4 cv = *reinterpret_cast<const float4 *>(Cn + (u * U + k) * NPAD + j);
+                    o.C[k][j] = cv.x; o.C[k][j + 1] = cv.y; o.C[k][j + 2] = cv.z; o.C[k][j + 3] = cv.w;
+                }
             }
         }
     };
-
     float dsum = 0.0f;
+    // One sub-tile: the recurrence for U timesteps; ysum[k] receives timestep k's channel readout.
+    auto compute_sub = [&](const Sub &cur, float (&ysum)[U], auto safe_tag) {
+        constexpr bool SAFE = decltype(safe_tag)::value;
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const float xt = cur.x[k], dt = cur.d[k];
+            float acc = dskip * xt;
+#pragma unroll
+            for (int j = 0; j < NPL; ++j) {
+                const float abar = exp2_fast(dt * a2[j]);
+                if constexpr (!SAFE) {
+                    const float pre = __builtin_fmaf(cur.B[k][j], xt, s[j]);  // s + B x
+                    s[j] = __builtin_fmaf(abar - 1.0f, pre, s[j]);            // s + (Ā − 1)(s + B x)
+                    if constexpr (!AGG) acc = __builtin_fmaf(cur.C[k][j] * ia[j], s[j], acc);
+                } else {
+                    const float kc = zoh_input_coef(dt, Av[j], abar, ia[j]);
+                    s[j] = __builtin_fmaf(abar, s[j], kc * (cur.B[k][j] * xt));  // Ā h + B̄ x
+                    if constexpr (!AGG) acc = __builtin_fmaf(cur.C[k][j], s[j], acc);
+                }
+            }
+            if constexpr (AGG) dsum += dt;
+            if constexpr (!AGG) ysum[k] = group_sum<G>(acc);
+        }
+    };
+    // Epilogue of the 2U timesteps of a sub-tile pair starting at tile column `col0`: lane g takes
+    // the timesteps col0 + q*G + g.
+    auto epilogue = [&](int col0, int64_t t0, const float (&y0)[U], const float (&y1)[U]) {
+        float yy[2 * U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) { yy[k] = y0[k]; yy[U + k] = y1[k]; }
+#pragma unroll
+        for (int q = 0; q < 2 * U / G; ++q) {
+            float v = yy[q * G];
+#pragma unroll
+            for (int r = 1; r < G; ++r) v = (g == r) ? yy[q * G + r] : v;
+            const int col = col0 + q * G + g;
+            const int64_t tg = t0 + col;
+            if (gate) v *= silu(zrow[col]);
+            if (ch_ok && tg < t_end) yg[ybase + tg] = narrow<T>(v);
+        }
+    };
+    auto scan_tile = [&](int64_t t0, auto safe_tag) {
+        Sub s0, s1;
+        float y0[U], y1[U];
+        load_sub(0, s0);
+#pragma unroll 1
+        for (int u = 0; u < NSUB; u += 2) {
+            load_sub(u + 1, s1);
+            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
+            compute_sub(s0, y0, safe_tag);
+            load_sub(u + 2 < NSUB ? u + 2 : u + 1, s0);  // the last pass re-reads a sub-tile it has
+            __builtin_amdgcn_sched_barrier(0);
+            compute_sub(s1, y1, safe_tag);
+            if constexpr (!AGG) epilogue(u * U, t0, y0, y1);
+        }
+    };
+
     load_tile(t_begin);
     store_tile();
     if (ntiles > 1) load_tile(t_begin + kTile);
-    load_z(t_begin);
-    __syncthreads();
-
-    const float *xrow = xs + lane * kPitch;
-    const float *drow = dsh + lane * kPitch;
-    float *prow = AGG ? part : part + wave * kRowsF + lane * kPitch;
+    wave_sync();
 #pragma unroll 1
     for (int it = 0; it < ntiles; ++it) {
         const int64_t t0 = t_begin + (int64_t)it * kTile;
         if (!safe)
-            scan_tile<NPL, NPAD, false, AGG>(xrow, drow, Bs + n0, Cs + n0, prow, dskip, a2, Av, ia, s, dsum);
+            scan_tile(t0, std::integral_constant<bool, false>{});
         else
-            scan_tile<NPL, NPAD, true, AGG>(xrow, drow, Bs + n0, Cs + n0, prow, dskip, a2, Av, ia, s, dsum);
-        __syncthreads();
-
-        if (it + 1 < ntiles) store_tile();
-        if constexpr (!AGG) {
-            // Epilogue, time-major: consecutive lanes take consecutive timesteps of one row.
-#pragma unroll
-            for (int i = 0; i < kEPT; ++i) {
-                const int e = tid + i * kThreads;
-                const int r = e / kTile;
-                const int col = e % kTile;
-                const int64_t tg = t0 + col;
-                if (d0 + r < a.d && tg < t_end) {
-                    float v = part[r * kPitch + col];
-#pragma unroll
-                    for (int w = 1; w < GW; ++w) v += part[w * kRowsF + r * kPitch + col];
-                    if (zg) v *= silu(zv[i]);
-                    yg[(bi * a.d + d0 + r) * a.L + tg] = narrow<T>(v);
-                }
-            }
+            scan_tile(t0, std::integral_constant<bool, true>{});
+        if (it + 1 < ntiles) {
+            wave_sync();   // the scan's last reads of tile it come before the stores of tile it + 1
+            store_tile();
+            wave_sync();
         }
         if (it + 2 < ntiles) load_tile(t0 + 2 * kTile);
-        if (it + 1 < ntiles) load_z(t0 + kTile);
-        __syncthreads();
     }
 
-    // ---- segment results ----
+    // ---- segment results: this lane's NPL states ----
     if (ch_ok) {
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
@@ -438,11 +441,11 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ p, i
     if (i < n) p[i] = 0.0f;
 }
 
-template <typename T, int NPL, int GW>
+template <typename T, int G, int NPL>
 hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLaunch &p, hipStream_t stream) {
     if (n_seg > 1) {
         const int64_t grid = (int64_t)(n_seg - 1) * ncb;
-        hipLaunchKernelGGL((scan_fwd_kernel<T, NPL, GW, true>), dim3((unsigned)grid), dim3(kWave * GW), 0, stream, args);
+        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, true>), dim3((unsigned)grid), dim3(kWave), 0, stream, args);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t bdn = p.b * p.d * p.N;
@@ -456,7 +459,7 @@ hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLa
         if (e != hipSuccess) return e;
     }
     const int64_t grid = (int64_t)n_seg * ncb;
-    hipLaunchKernelGGL((scan_fwd_kernel<T, NPL, GW, false>), dim3((unsigned)grid), dim3(kWave * GW), 0, stream, args);
+    hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false>), dim3((unsigned)grid), dim3(kWave), 0, stream, args);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.ev_end) e = hipEventRecord(p.ev_end, stream);
@@ -465,11 +468,11 @@ hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLa
 
 template <typename T>
 hipError_t dispatch_shape(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLaunch &p, hipStream_t stream) {
-#define SSM_CASE(NPL_, GW_) \
-    if (p.states_per_wave == NPL_ && p.waves == GW_) return launch_typed<T, NPL_, GW_>(args, n_seg, ncb, p, stream);
-    SSM_CASE(4, 1) SSM_CASE(4, 2) SSM_CASE(4, 4)
-    SSM_CASE(8, 1) SSM_CASE(8, 2) SSM_CASE(8, 4)
-    SSM_CASE(16, 1) SSM_CASE(16, 2) SSM_CASE(16, 4)
+#define SSM_CASE(G_, NPL_) \
+    if (p.lanes_per_channel == G_ && p.states_per_lane == NPL_) return launch_typed<T, G_, NPL_>(args, n_seg, ncb, p, stream);
+    SSM_CASE(1, 4) SSM_CASE(1, 8) SSM_CASE(1, 16)
+    SSM_CASE(2, 4) SSM_CASE(2, 8) SSM_CASE(2, 16)
+    SSM_CASE(4, 4) SSM_CASE(4, 8) SSM_CASE(4, 16)
 #undef SSM_CASE
     return hipErrorInvalidValue;
 }
@@ -483,11 +486,12 @@ hipError_t launch_scan_fwd(const FwdLaunch &p, hipStream_t stream) {
     a.init_state = p.init_state;
     a.b = p.b; a.d = p.d; a.L = p.L; a.N = p.N;
     a.seg_len = p.seg_len;
-    a.n_db = (p.d + kGroupRows - 1) / kGroupRows;
+    const int cw = kWave / p.lanes_per_channel;
+    a.n_cw = (p.d + cw - 1) / cw;
     const int64_t esize = p.bf16 ? 2 : 4;
     auto aligned16 = [](const void *q) { return q == nullptr || (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
     a.vec_rows = ((p.L * esize) % 16 == 0) && aligned16(p.x) && aligned16(p.delta) && aligned16(p.z);
-    // a tile's B/C run starts at element (bi*L + t0)*N with t0 a multiple of 32
+    // a tile's B/C run starts at element (bi*L + t0)*N with t0 a multiple of the tile length
     a.vec_bc = ((p.L * p.N * esize) % 16 == 0) && aligned16(p.B) && aligned16(p.C);
     if (p.n_seg > 1) {
         const int64_t per = (int64_t)(p.n_seg - 1) * p.b * p.d * p.N;
@@ -495,7 +499,7 @@ hipError_t launch_scan_fwd(const FwdLaunch &p, hipStream_t stream) {
         a.agg_E = p.scratch + per;
         a.h_in = p.scratch + 2 * per;
     }
-    const int64_t ncb = p.b * a.n_db;
+    const int64_t ncb = p.b * a.n_cw;
     if (p.bf16) return dispatch_shape<uint16_t>(a, p.n_seg, ncb, p, stream);
     return dispatch_shape<float>(a, p.n_seg, ncb, p, stream);
 }

@@ -68,12 +68,12 @@ def test_aliasing_output_rejected():
     assert _fwd(fs=ctypes.c_void_p(0x900000)) == 5  # final_state overlaps y
 
 
-@pytest.mark.parametrize("field,value", [("states_per_wave", 5), ("states_per_wave", 4), ("seg_len", 33),
-                                         ("seg_len", -32)])
+@pytest.mark.parametrize("field,value", [("lanes_per_channel", 3), ("lanes_per_channel", 8),
+                                         ("lanes_per_channel", 1), ("seg_len", 33), ("seg_len", -32)])
 def test_bad_options_rejected(field, value):
     o = api.FwdOpts()
     setattr(o, field, value)
-    n = 32 if (field, value) == ("states_per_wave", 4) else 4  # 32 states need > 4 waves of 4
+    n = 32 if (field, value) == ("lanes_per_channel", 1) else 4  # one lane holds at most 16 states
     assert _fwd(N=n, opts=o) == 3
 
 
@@ -91,11 +91,14 @@ def test_step_validation():
 
 def test_plan_shapes():
     p = api.ssm_scan_fwd_plan(1, 8, 128, 4)
-    assert p["n_segments"] == 1 and p["waves_per_group"] == 1 and p["scratch_bytes"] == 0
+    assert p["n_segments"] == 1 and p["lanes_per_channel"] == 4 and p["states_per_lane"] == 4
+    assert p["scratch_bytes"] == 0 and p["waves_per_segment"] == 1
     p = api.ssm_scan_fwd_plan(1, 2048, 131072, 16)
     assert p["n_segments"] > 1 and p["seg_len"] % 32 == 0
     assert p["seg_len"] * p["n_segments"] >= 131072
     assert p["scratch_bytes"] == 3 * (p["n_segments"] - 1) * 2048 * 16 * 4
-    p = api.ssm_scan_fwd_plan(8, 4096, 4096, 16, seg_len=1024, states_per_wave=8)
-    assert p["n_segments"] == 4 and p["states_per_wave"] == 8 and p["waves_per_group"] == 2
-    assert p["groups_output_pass"] == 4 * 8 * 64 and p["groups_aggregate_pass"] == 3 * 8 * 64
+    p = api.ssm_scan_fwd_plan(8, 4096, 4096, 16, seg_len=1024, lanes_per_channel=2)
+    assert p["n_segments"] == 4 and p["states_per_lane"] == 8 and p["waves_per_segment"] == 8 * 128
+    assert p["groups_output_pass"] == 4 * 8 * 128 and p["groups_aggregate_pass"] == 3 * 8 * 128
+    p = api.ssm_scan_fwd_plan(2, 100, 64, 64)
+    assert p["lanes_per_channel"] == 4 and p["states_per_lane"] == 16

@@ -113,9 +113,11 @@ SMALL = [
     (3, 64, 257, 16, "f32", True, True, {"seg_len": 64}),
     (3, 64, 257, 16, "bf16", True, True, {"seg_len": 96}),
     (2, 70, 300, 16, "f32", True, True, {"seg_len": 32}),
-    (1, 64, 512, 16, "f32", True, True, {"states_per_wave": 8}),
-    (1, 64, 512, 16, "f32", True, True, {"states_per_wave": 16}),
-    (1, 64, 512, 16, "bf16", True, True, {"states_per_wave": 16, "seg_len": 128}),
+    (1, 64, 512, 16, "f32", True, True, {"lanes_per_channel": 2}),
+    (1, 70, 512, 16, "f32", True, True, {"lanes_per_channel": 1}),
+    (1, 64, 512, 16, "bf16", True, True, {"lanes_per_channel": 1, "seg_len": 128}),
+    (2, 33, 200, 12, "bf16", True, True, {"lanes_per_channel": 2, "seg_len": 64}),
+    (1, 19, 96, 7, "f32", True, True, {"lanes_per_channel": 1}),
     (2, 33, 200, 33, "f32", True, True, {}),
     (1, 40, 150, 64, "f32", True, True, {}),
     (1, 40, 150, 64, "bf16", False, True, {"seg_len": 64}),
