@@ -16,28 +16,30 @@
 //     rounding of s + Bx. Waves holding a channel with |A| < 2^-10 use an unscaled path whose input
 //     coefficient comes from the series of (e^v − 1)/v near v = 0 (the A = 0 limit is Δ·B).
 //   * The readout over a channel's G lanes is an xor butterfly of DPP quad permutes (the same sum
-//     lands on every lane); lane g then finishes timestep t ≡ g (mod G): + D·x (folded into lane 0's
-//     partial), · silu(z), rounding, store. The epilogue thus costs each element once.
+//     lands on every lane); lane g then finishes timestep t ≡ g (mod G): + D·x, · silu(z), rounding,
+//     store. The epilogue thus costs each element once.
 //   * Each tile of kTile timesteps (x, Δ, z rows of the wave's channels; the B and C rows, one
 //     contiguous run) is fetched one tile ahead with 16-byte loads into registers, widened to fp32
 //     into the wave's private LDS, and read back as wave-uniform (B, C) or per-channel (x, Δ, z)
-//     LDS broadcasts, prefetched one sub-tile ahead. LDS operations of one wave complete in order,
-//     so nothing else is needed to order them.
+//     LDS broadcasts, prefetched one sub-tile ahead. LDS operations of one wave execute in order,
+//     so a compiler fence (wave_sync) is all that orders the tile stores against the scan's reads.
+//   * Waves whose channels all have |A| >= 2^-10 run the scaled-state kernel; the others run a
+//     separate instantiation of the unscaled path. Both are launched over the same grid and each
+//     wave leaves at once when it belongs to the other one, so the fast path keeps its registers.
 //   * Long sequences are cut into time segments (page "Mambaとは？…", section Selective Scanは
 //     選択機構そのものではない: affine maps (A, b) compose associatively). An aggregate pass gives
 //     each segment's (Π Ā, end state from zero); a carry pass chains them per (b, d, n); the output
 //     pass then rescans every segment from its true carry-in.
-#include <type_traits>
-
 #include "device_common.h"
 #include "launch.h"
 
 namespace ssm {
 namespace {
 
-constexpr int kTile = 32;                    // timesteps per tile
-constexpr int kPitch = kTile + 4;            // floats per LDS row of x, Δ, z (16-byte pad)
 constexpr float kSafeAbsA = 1.0f / 1024.0f;  // |A| below this takes the unscaled path
+
+// Timesteps per tile: 64 bytes of every row per tile for either storage type.
+template <typename T> constexpr int tile_len() { return sizeof(T) == 2 ? 32 : 16; }
 
 struct FwdArgs {
     const void *x, *delta;
@@ -157,8 +159,13 @@ constexpr int sub_len(int G, int NPL) {
 //
 // T: storage type (float or bf16 bits); G: lanes per channel (1, 2, 4); NPL: states per lane
 // (4, 8, 16); AGG: aggregate pass (segment end state from zero and Π Ā, no readout).
-template <typename T, int G, int NPL, bool AGG>
-__global__ __launch_bounds__(kWave) void scan_fwd_kernel(FwdArgs a) {
+// SAFE: the unscaled path for waves holding a channel with |A| < 2^-10. Both variants are
+// launched over the same grid and a wavefront leaves at once unless the variant is its own;
+// keeping the rare path out of the common kernel keeps the latter's register budget small.
+template <typename T, int G, int NPL, bool AGG, bool SAFE>
+__global__ __launch_bounds__(kWave, (G == 4 && NPL == 4 && !SAFE) ? 3 : 1) void scan_fwd_kernel(FwdArgs a) {
+    constexpr int kTile = tile_len<T>();
+    constexpr int kPitch = kTile + 4;                    // floats per LDS row of x, Δ, z (16-byte pad)
     constexpr int E = Chunk<T>::kElems;
     constexpr int CW = kWave / G;                       // channels per wavefront
     constexpr int NPAD = G * NPL;                        // states held per timestep in LDS
@@ -228,12 +235,12 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(FwdArgs a) {
         }
         s[j] = h0;
     }
-    const bool safe = __any(small_a);  // wave-uniform choice of path
-    if (!safe) {
+    if (__any(small_a) != SAFE) return;  // wave-uniform: the other variant owns this wavefront
+    if constexpr (!SAFE) {
 #pragma unroll
         for (int j = 0; j < NPL; ++j) s[j] *= Av[j];  // scaled state s = A·h
     }
-    const float dskip = (!AGG && g == 0 && ch_ok && a.D) ? a.D[ch] : 0.0f;
+    const float dskip = (!AGG && ch_ok && a.D) ? a.D[ch] : 0.0f;
     const int64_t ybase = row * a.L;
 
     // ---- tile prefetch into registers, and from there into LDS ----
@@ -331,12 +338,11 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(FwdArgs a) {
     };
     float dsum = 0.0f;
     // One sub-tile: the recurrence for U timesteps; ysum[k] receives timestep k's channel readout.
-    auto compute_sub = [&](const Sub &cur, float (&ysum)[U], auto safe_tag) {
-        constexpr bool SAFE = decltype(safe_tag)::value;
+    auto compute_sub = [&](const Sub &cur, float (&ysum)[U]) {
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             const float xt = cur.x[k], dt = cur.d[k];
-            float acc = dskip * xt;
+            float acc = 0.0f;
 #pragma unroll
             for (int j = 0; j < NPL; ++j) {
                 const float abar = exp2_fast(dt * a2[j]);
@@ -367,11 +373,12 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(FwdArgs a) {
             for (int r = 1; r < G; ++r) v = (g == r) ? yy[q * G + r] : v;
             const int col = col0 + q * G + g;
             const int64_t tg = t0 + col;
+            v = __builtin_fmaf(dskip, xrow[col], v);  // + D·x
             if (gate) v *= silu(zrow[col]);
             if (ch_ok && tg < t_end) yg[ybase + tg] = narrow<T>(v);
         }
     };
-    auto scan_tile = [&](int64_t t0, auto safe_tag) {
+    auto scan_tile = [&](int64_t t0) {
         Sub s0, s1;
         float y0[U], y1[U];
         load_sub(0, s0);
@@ -379,10 +386,10 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(FwdArgs a) {
         for (int u = 0; u < NSUB; u += 2) {
             load_sub(u + 1, s1);
             __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
-            compute_sub(s0, y0, safe_tag);
+            compute_sub(s0, y0);
             load_sub(u + 2 < NSUB ? u + 2 : u + 1, s0);  // the last pass re-reads a sub-tile it has
             __builtin_amdgcn_sched_barrier(0);
-            compute_sub(s1, y1, safe_tag);
+            compute_sub(s1, y1);
             if constexpr (!AGG) epilogue(u * U, t0, y0, y1);
         }
     };
@@ -394,10 +401,7 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(FwdArgs a) {
 #pragma unroll 1
     for (int it = 0; it < ntiles; ++it) {
         const int64_t t0 = t_begin + (int64_t)it * kTile;
-        if (!safe)
-            scan_tile(t0, std::integral_constant<bool, false>{});
-        else
-            scan_tile(t0, std::integral_constant<bool, true>{});
+        scan_tile(t0);
         if (it + 1 < ntiles) {
             wave_sync();   // the scan's last reads of tile it come before the stores of tile it + 1
             store_tile();
@@ -411,7 +415,7 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
             if (j >= nvalid) continue;
-            const float h = safe ? s[j] : s[j] * ia[j];
+            const float h = SAFE ? s[j] : s[j] * ia[j];
             const int64_t idx = row * a.N + n0 + j;
             if constexpr (AGG) {
                 a.agg_P[seg * bd * a.N + idx] = exp2_fast(a2[j] * dsum);  // Π Ā = exp(A ΣΔ)
@@ -445,7 +449,10 @@ template <typename T, int G, int NPL>
 hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLaunch &p, hipStream_t stream) {
     if (n_seg > 1) {
         const int64_t grid = (int64_t)(n_seg - 1) * ncb;
-        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, true>), dim3((unsigned)grid), dim3(kWave), 0, stream, args);
+        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, true, false>), dim3((unsigned)grid), dim3(kWave), 0, stream,
+                           args);
+        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, true, true>), dim3((unsigned)grid), dim3(kWave), 0, stream,
+                           args);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t bdn = p.b * p.d * p.N;
@@ -459,7 +466,8 @@ hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLa
         if (e != hipSuccess) return e;
     }
     const int64_t grid = (int64_t)n_seg * ncb;
-    hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false>), dim3((unsigned)grid), dim3(kWave), 0, stream, args);
+    hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false, false>), dim3((unsigned)grid), dim3(kWave), 0, stream, args);
+    hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false, true>), dim3((unsigned)grid), dim3(kWave), 0, stream, args);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.ev_end) e = hipEventRecord(p.ev_end, stream);
