@@ -95,14 +95,17 @@ def bench_prefill(name, steps, warmup, rotate=0, quiet=False):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / steps
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    kern = np.array([a.elapsed_time(b) for a, b in ev])
+    kern_ms = float(np.mean(kern))
     plan = api.ssm_scan_fwd_plan(w.b, w.d, w.L, w.N, torch.float32 if w.dtype == "f32" else torch.bfloat16)
     elems = w.b * w.d * w.L
     slots = elems * valu_slots_per_element(w.N, w.gate)
     res = {
         "workload": name, "ms_per_call": ms, "GBps": nbytes / (ms * 1e-3) / 1e9,
         "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "elements_per_s": elems / (ms * 1e-3),
-        "output_kernel_ms": kern_ms, "algorithmic_bytes": nbytes, "rotating_sets": rotate, "plan": plan,
+        "output_kernel_ms": kern_ms, "output_kernel_ms_p10_p50_p90": [round(float(q), 5) for q in
+                                                                      np.percentile(kern, [10, 50, 90])],
+        "algorithmic_bytes": nbytes, "rotating_sets": rotate, "plan": plan,
         "valu_slots_per_element": valu_slots_per_element(w.N, w.gate),
         "kernel_valu_Tslot_s": slots / (kern_ms * 1e-3) / 1e12,
         "kernel_GBps": nbytes / (kern_ms * 1e-3) / 1e9, "input_gen_s": gen_s,
@@ -187,12 +190,37 @@ def cpu_baseline(inp, name, threads):
     with cf.ThreadPoolExecutor(threads) as ex:
         list(ex.map(one, chunks))
     wall = time.perf_counter() - t0
+    # one host thread on the first 128 channels of batch row 0
+    t0 = time.perf_counter()
+    one(chunks[0])
+    wall1 = time.perf_counter() - t0
+    rows1 = chunks[0][2] - chunks[0][1]
     esize = 4 if dt == "f32" else 2
     nbytes = algorithmic_bytes(w.b, w.d, w.L, w.N, esize, w.gate)
     return {"value": nbytes / wall / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole workload ({w.b * w.d} (b,d) rows x {w.L} steps x {w.N} states), "
                       f"fp64 sequential rows on {threads} host threads, {wall:.2f} s wall",
-            "elements_per_s": w.b * w.d * w.L / wall}
+            "elements_per_s": w.b * w.d * w.L / wall,
+            "single_thread_elements_per_s": rows1 * w.L / wall1,
+            "single_thread_sample": f"{rows1} (b,d) rows x {w.L} steps on one thread, {wall1:.3f} s"}
+
+
+def copy_bandwidth(nbytes=1 << 30, reps=5):
+    """Device-to-device copy rate (GB/s, bytes read + written), the practical HBM ceiling."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbps
 
 
 def copy_probe(nbytes):
@@ -210,7 +238,7 @@ def copy_probe(nbytes):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--extra", default="decode,mamba1p4b_bf16_b8_d4096_L4096_N16",
@@ -235,6 +263,8 @@ def main():
 
     from selective_state_space_82_amd import inputs as I
 
+    copy_gbps = copy_bandwidth()
+    print(f"# device copy: {copy_gbps:.0f} GB/s (read + write)", file=sys.stderr, flush=True)
     head, inp = bench_prefill(args.workload, args.steps, args.warmup, args.rotate)
     w = I.WORKLOADS[args.workload]
     extra = []
@@ -284,11 +314,14 @@ def main():
         "config": {"workload": args.workload, "b": w.b, "d": w.d, "L": w.L, "N": w.N, "gate": w.gate,
                    "state": "f32", "plan": head["plan"], "rotating_sets": head["rotating_sets"]},
         "hbm_frac": round(head["hbm_frac"], 4),
+        "copy_GBps": round(copy_gbps, 1),
+        "copy_frac": round(head["GBps"] / copy_gbps, 4),
         "elements_per_s": head["elements_per_s"],
         "roofline": {"bound": "alu", "achieved": round(slots / kern_s / 1e12, 3), "peak": round(VALU_PEAK_TSLOT, 3),
                      "unit": "Tslot/s", "frac": round(slots / kern_s / 1e12 / VALU_PEAK_TSLOT, 4),
                      "traffic": traffic, "kernel": "scan_fwd_kernel (output pass)",
                      "kernel_us": round(head["output_kernel_ms"] * 1e3, 2),
+                     "kernel_us_p10_p50_p90": [round(q * 1e3, 2) for q in head["output_kernel_ms_p10_p50_p90"]],
                      "kernel_hbm_frac": round(head["kernel_GBps"] / HBM_PEAK_GBS, 4)},
         "cpu_baseline": cpu,
         "extra": extra,

@@ -98,9 +98,12 @@ ssm_status_t make_plan(int64_t b, int64_t d, int64_t L, int64_t N, const ssm_fwd
     if (seg_len < 0 || (seg_len % ssm::kSegQuantum) != 0) return SSM_ERR_UNSUPPORTED;
     const int64_t Lr = ((L + ssm::kSegQuantum - 1) / ssm::kSegQuantum) * ssm::kSegQuantum;
     if (seg_len == 0) {
-        // about two wavefronts per SIMD (4 SIMDs per compute unit); segments of at least 256 steps
-        const int64_t want = (int64_t)cus * 4 * 2;
-        int64_t S = (want + ncb - 1) / ncb;
+        // A split in time adds an aggregate pass over (S-1)/S of the sequence (about half the
+        // cost of the output pass), so it only pays when one segment gives fewer wavefronts than
+        // the chip has SIMDs (4 per compute unit). Then aim at about eight wavefronts per SIMD
+        // over the grid, with segments of at least 256 steps.
+        const int64_t simds = (int64_t)cus * 4;
+        int64_t S = ncb >= simds ? 1 : (simds * 8 + ncb - 1) / ncb;
         const int64_t max_seg = Lr / 256 > 0 ? Lr / 256 : 1;
         if (S > max_seg) S = max_seg;
         if (S > 64) S = 64;

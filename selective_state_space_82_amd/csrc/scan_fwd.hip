@@ -461,14 +461,18 @@ hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLa
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (p.ev_begin) {
-        hipError_t e = hipEventRecord(p.ev_begin, stream);
-        if (e != hipSuccess) return e;
-    }
+    // The small-|A| instantiation goes first so that the events bracket the fast-path kernel alone
+    // (the two write disjoint channels, so their order does not matter).
     const int64_t grid = (int64_t)n_seg * ncb;
-    hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false, false>), dim3((unsigned)grid), dim3(kWave), 0, stream, args);
     hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false, true>), dim3((unsigned)grid), dim3(kWave), 0, stream, args);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (p.ev_begin) {
+        e = hipEventRecord(p.ev_begin, stream);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false, false>), dim3((unsigned)grid), dim3(kWave), 0, stream, args);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.ev_end) e = hipEventRecord(p.ev_end, stream);
     return e;

@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from selective_state_space_82_amd import api
 
@@ -100,5 +101,10 @@ def test_plan_shapes():
     p = api.ssm_scan_fwd_plan(8, 4096, 4096, 16, seg_len=1024, lanes_per_channel=2)
     assert p["n_segments"] == 4 and p["states_per_lane"] == 8 and p["waves_per_segment"] == 8 * 128
     assert p["groups_output_pass"] == 4 * 8 * 128 and p["groups_aggregate_pass"] == 3 * 8 * 128
+    # automatic time split (planned for 256 compute units): none when one segment already gives a
+    # wavefront per SIMD, else about eight wavefronts per SIMD with segments of >= 256 steps
+    assert api.ssm_scan_fwd_plan(8, 4096, 4096, 16, torch.bfloat16)["n_segments"] == 1
+    assert api.ssm_scan_fwd_plan(4, 1536, 2048, 16)["n_segments"] == 8
+    assert api.ssm_scan_fwd_plan(1, 2048, 131072, 16, torch.bfloat16)["n_segments"] == 64
     p = api.ssm_scan_fwd_plan(2, 100, 64, 64)
     assert p["lanes_per_channel"] == 4 and p["states_per_lane"] == 16
