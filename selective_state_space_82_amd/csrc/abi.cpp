@@ -116,8 +116,9 @@ ssm_status_t make_plan(int64_t b, int64_t d, int64_t L, int64_t N, const ssm_fwd
     int64_t scratch = 0;
     if (n_seg > 1) {
         int64_t per = 0;
-        if (!mul_ok((n_seg - 1) * b, d * N, &per)) return SSM_ERR_SHAPE;
-        scratch = 3 * per * (int64_t)sizeof(float);
+        if (!mul_ok((n_seg - 1) * b, d * N, &per) || !mul_ok(per, 3 * (int64_t)sizeof(float), &scratch))
+            return SSM_ERR_SHAPE;
+        scratch = ssm::scratch_floats(n_seg, b, d, N) * (int64_t)sizeof(float);
     }
     pl->lanes = lanes;
     pl->npl = npl;

@@ -47,4 +47,13 @@ __device__ __forceinline__ float zoh_input_coef(float dt, float a, float abar, f
     return __builtin_fabsf(v) < 0.0625f ? near0 : far;
 }
 
+// The same coefficient from u = Δ·a·log2(e) (the argument already formed for exp2), so the
+// caller need not keep a itself: v = u·ln 2.
+__device__ __forceinline__ float zoh_input_coef_log2(float dt, float u, float abar, float inv_a) {
+    const float v = u * 0.69314718055994530942f;
+    const float near0 = dt * expm1_over_v_small(v);
+    const float far = (abar - 1.0f) * inv_a;  // NaN at a = 0, never selected there
+    return __builtin_fabsf(v) < 0.0625f ? near0 : far;
+}
+
 }  // namespace ssm

@@ -22,7 +22,7 @@ struct FwdLaunch {
     int states_per_lane;      // 4, 8 or 16, with lanes_per_channel * states_per_lane >= N
     int64_t seg_len;          // multiple of kSegQuantum
     int n_seg;                // ceil(L / seg_len) >= 1
-    float *scratch;           // 3 * (n_seg - 1) * b * d * N floats when n_seg > 1
+    float *scratch;           // scratch_floats(n_seg, b, d, N) floats
     hipEvent_t ev_begin, ev_end;
 };
 
@@ -43,5 +43,13 @@ hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t stream);
 hipError_t launch_scan_step(const StepLaunch &p, hipStream_t stream);
 
 constexpr int kSegQuantum = 32; // time segments are multiples of this many steps
+constexpr int kFoldMaxSeg = 64; // up to this many segments the output pass chains the carry itself
+
+// Scratch floats of a time-split prefill: aggregates P and E, plus the carries when a separate
+// carry kernel chains them.
+inline int64_t scratch_floats(int64_t n_seg, int64_t b, int64_t d, int64_t N) {
+    if (n_seg <= 1) return 0;
+    return (n_seg > kFoldMaxSeg ? 3 : 2) * (n_seg - 1) * b * d * N;
+}
 
 }  // namespace ssm

@@ -1,5 +1,5 @@
 // scan_fwd.hip — prefill selective scan for gfx950: fused ZOH discretisation + recurrence + readout
-// + gate/skip epilogue, an aggregate pass and a chunk-carry pass for sequences split in time.
+// + gate/skip epilogue, an aggregate pass and a chunk carry for sequences split in time.
 //
 // Method (page "Mambaとは？Transformer以外の系列モデル", sections 状態空間モデルを一つの式から理解する
 // and Mambaの核心は入力依存のDelta、B、C; page "State Space Models（SSM）とMamba" §2.2, §4.2–§4.3):
@@ -13,23 +13,28 @@
 //   * Per (t, n) the fast path issues one exp and six fp32 VALU operations. With the scaled state
 //     s = A·h the ZOH input needs no division:  s_t = s_{t−1} + (Ā − 1)·(s_{t−1} + B x),
 //     and the readout is Σ_n (C_n / A_n)·s_n. Ā − 1 is exact in fp32 (Sterbenz) and damps the
-//     rounding of s + Bx. Waves holding a channel with |A| < 2^-10 use an unscaled path whose input
-//     coefficient comes from the series of (e^v − 1)/v near v = 0 (the A = 0 limit is Δ·B).
-//   * The readout over a channel's G lanes is an xor butterfly of DPP quad permutes (the same sum
-//     lands on every lane); lane g then finishes timestep t ≡ g (mod G): + D·x, · silu(z), rounding,
-//     store. The epilogue thus costs each element once.
+//     rounding of s + Bx. A wavefront holding a channel with |A| < 2^-10 takes (by a wave-uniform
+//     branch) an unscaled path whose input coefficient comes from the series of (e^v − 1)/v near
+//     v = 0 (the A = 0 limit is Δ·B).
+//   * Readout across the G lanes of a channel: each lane writes its partial sums of a group of 2U
+//     timesteps to LDS, and lane g reads back the G partials of the timesteps ≡ g (mod G) — a
+//     transpose through LDS that costs G − 1 adds per element instead of a butterfly on every
+//     lane. That lane then finishes its timesteps: + D·x, · silu(z), rounding. The reads of one
+//     group are issued before the next group's arithmetic, which hides the LDS round trip.
 //   * Each tile of kTile timesteps (x, Δ, z rows of the wave's channels; the B and C rows, one
-//     contiguous run) is fetched one tile ahead with 16-byte loads into registers, widened to fp32
-//     into the wave's private LDS, and read back as wave-uniform (B, C) or per-channel (x, Δ, z)
-//     LDS broadcasts, prefetched one sub-tile ahead. LDS operations of one wave execute in order,
-//     so a compiler fence (wave_sync) is all that orders the tile stores against the scan's reads.
-//   * Waves whose channels all have |A| >= 2^-10 run the scaled-state kernel; the others run a
-//     separate instantiation of the unscaled path. Both are launched over the same grid and each
-//     wave leaves at once when it belongs to the other one, so the fast path keeps its registers.
+//     contiguous run) is fetched one tile ahead with 16-byte loads into registers, then written
+//     into the wave's private LDS (x, Δ, B, C widened to fp32; z kept in its storage type), and
+//     read back as wave-uniform (B, C) or per-channel (x, Δ, z) LDS broadcasts, prefetched one
+//     sub-tile ahead. Outputs collect in an LDS window of two tiles (128 bytes of each row) and
+//     leave as whole 128-byte lines. LDS operations of one wave execute in order, so a compiler
+//     fence (wave_sync) is all that orders the hand-offs between lanes.
 //   * Long sequences are cut into time segments (page "Mambaとは？…", section Selective Scanは
-//     選択機構そのものではない: affine maps (A, b) compose associatively). An aggregate pass gives
-//     each segment's (Π Ā, end state from zero); a carry pass chains them per (b, d, n); the output
-//     pass then rescans every segment from its true carry-in.
+//     選択機構そのものではない: affine maps h ↦ a·h + b compose associatively). An aggregate pass
+//     gives each segment's (Π Ā, end state from zero); the output pass then rescans every segment
+//     from its true carry-in, which each wavefront chains from the aggregates of the segments
+//     before it (or, for many segments, a carry kernel chains once per (b, d, n)).
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -50,14 +55,15 @@ struct FwdArgs {
     void *y;
     float *final_state;
     const float *init_state;  // segment 0 carry-in (nullable)
-    const float *h_in;        // carry-in of segments 1.. : [n_seg-1][b][d][N] (output pass)
+    const float *h_in;        // carry-in of segments 1.. [n_seg-1][b][d][N], or null: chain the aggregates
     float *agg_P;             // aggregate pass outputs [n_seg-1][b][d][N]
     float *agg_E;
     int64_t b, d, L, N;
     int64_t seg_len;
     int64_t n_cw;             // channel blocks (of 64/G channels) per batch row
-    int vec_rows;             // x/Δ/z rows allow 16-byte loads at every tile
+    int vec_rows;             // x/Δ/z/y rows allow 16-byte accesses at every tile
     int vec_bc;               // B/C tile runs allow 16-byte loads
+    int vec_state;            // state rows allow 16-byte accesses (N % 4 == 0, aligned)
 };
 
 template <typename T> struct Chunk;  // 16 bytes of a row or run
@@ -123,72 +129,49 @@ __device__ __forceinline__ void lds_get(const float *p, float (&o)[U]) {
 }
 
 // Orders this wave's LDS accesses around a hand-off between its lanes (tile stores -> scan
-// reads, scan reads -> next tile stores). One wave's LDS operations already execute in order,
-// so this only fences the compiler; it emits no wait.
+// reads, partial sums -> transposed reads, outputs -> line stores). One wave's LDS operations
+// execute in order, so this only fences the compiler; it emits no wait.
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Value of `v` held by lane (lane ^ 1) or (lane ^ 2) of the same quad: DPP quad permutes.
-template <int CTRL>
-__device__ __forceinline__ float quad_perm(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-constexpr int kSwap1 = 0xB1;  // quad_perm [1, 0, 3, 2]
-constexpr int kSwap2 = 0x4E;  // quad_perm [2, 3, 0, 1]
-
-// Sum over the G lanes of a channel. Floating-point addition is commutative, so every lane of
-// the group ends with bitwise the same value.
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-    if constexpr (G >= 2) v += quad_perm<kSwap1>(v);
-    if constexpr (G >= 4) v += quad_perm<kSwap2>(v);
-    return v;
-}
-
-// Timesteps per sub-tile: 8/NPL keeps a sub-tile's B and C at 16 values per lane; a pair of
-// sub-tiles must hold a whole epilogue group of G timesteps.
-constexpr int sub_len(int G, int NPL) {
-    const int u = NPL >= 8 ? 1 : 8 / NPL;
-    return (2 * u) % G == 0 ? u : G / 2;
-}
-
 // The kernel ---------------------------------------------------------------------------------
 //
 // T: storage type (float or bf16 bits); G: lanes per channel (1, 2, 4); NPL: states per lane
 // (4, 8, 16); AGG: aggregate pass (segment end state from zero and Π Ā, no readout).
-// SAFE: the unscaled path for waves holding a channel with |A| < 2^-10. Both variants are
-// launched over the same grid and a wavefront leaves at once unless the variant is its own;
-// keeping the rare path out of the common kernel keeps the latter's register budget small.
 template <typename T, int G, int NPL, bool AGG, bool SAFE>
-__global__ __launch_bounds__(kWave, (G == 4 && NPL == 4 && !SAFE) ? 3 : 1) void scan_fwd_kernel(FwdArgs a) {
+__device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
     constexpr int kTile = tile_len<T>();
-    constexpr int kPitch = kTile + 4;                    // floats per LDS row of x, Δ, z (16-byte pad)
+    constexpr int kPitch = kTile + 4;                    // floats per LDS row of x, Δ (16-byte pad)
     constexpr int E = Chunk<T>::kElems;
+    constexpr int kZPitch = kTile + (sizeof(T) == 4 ? 4 : 0);  // T elements per LDS row of z
     constexpr int CW = kWave / G;                       // channels per wavefront
     constexpr int NPAD = G * NPL;                        // states held per timestep in LDS
     constexpr int kRowChunks = kTile / E;                // 16-byte chunks per row per tile
     constexpr int kXC = (CW * kRowChunks + kWave - 1) / kWave;      // row chunks per lane per tensor
     constexpr int kBF = kTile * NPAD;                    // floats of one B or C plane
     constexpr int kBC = (kBF / E + kWave - 1) / kWave;   // run chunks per lane per tensor
-    constexpr int U = sub_len(G, NPL);
-    constexpr int NSUB = kTile / U;                      // a pair of sub-tiles spans 2U steps
-    static_assert((2 * U) % G == 0, "an epilogue group must fit a pair of sub-tiles");
-    static_assert(NSUB % 2 == 0, "sub-tiles are processed in pairs");
+    constexpr int kGrp = G > 2 ? G : 2;                  // timesteps per readout group (even)
+    constexpr int kRS = kGrp * G + (G > 1 ? 4 : 0);      // floats per channel in the partial-sum buffer
+    constexpr int kYWin = 2 * kTile;                     // timesteps per output window (128 bytes)
+    constexpr int kYPitch = kYWin + 4 / sizeof(T);       // T per LDS row of the window (+1 word: no conflicts)
+    static_assert(kGrp % G == 0 && kTile % kGrp == 0, "readout groups tile the tile");
+    static_assert(kYWin * sizeof(T) == 128, "an output window is one 128-byte line per row");
     __shared__ __attribute__((aligned(16))) float xs[CW * kPitch];
     __shared__ __attribute__((aligned(16))) float dsh[CW * kPitch];
-    __shared__ __attribute__((aligned(16))) float zs[AGG ? 4 : CW * kPitch];
+    __shared__ __attribute__((aligned(16))) T zs[AGG ? 8 : CW * kZPitch];
     __shared__ __attribute__((aligned(16))) float Bs[kBF];
     __shared__ __attribute__((aligned(16))) float Cs[AGG ? 4 : kBF];
+    __shared__ __attribute__((aligned(16))) float red[(AGG || G == 1) ? 4 : CW * kRS];
+    __shared__ __attribute__((aligned(16))) T ybuf[AGG ? 8 : CW * kYPitch];
 
     const int lane = threadIdx.x;
     const int c = lane / G;  // channel within the wave
     const int g = lane % G;  // state group within the channel
 
     const int64_t ncb = a.b * a.n_cw;
-    const int64_t blk = blockIdx.x;
     const int64_t seg = blk / ncb;
     const int64_t cb = blk - seg * ncb;
     const int64_t bi = cb / a.n_cw;
@@ -213,6 +196,8 @@ __global__ __launch_bounds__(kWave, (G == 4 && NPL == 4 && !SAFE) ? 3 : 1) void 
     const int n0 = g * NPL;
     const int nvalid = (N - n0) < NPL ? (N - n0) : NPL;  // <= 0 for a lane past the last state
     const int64_t row = bi * a.d + ch;
+    const int64_t sidx = row * a.N + n0;                  // this lane's first state in [b][d][N]
+    const bool vstate = a.vec_state && ch_ok && nvalid == NPL;
     float Av[NPL], a2[NPL], ia[NPL], s[NPL];
     bool small_a = false;
 #pragma unroll
@@ -223,25 +208,47 @@ __global__ __launch_bounds__(kWave, (G == 4 && NPL == 4 && !SAFE) ? 3 : 1) void 
         a2[j] = av * kLog2e;
         ia[j] = 1.0f / av;
         small_a |= __builtin_fabsf(av) < kSafeAbsA;
-        float h0 = 0.0f;  // the aggregate pass always scans its segment from the zero state
-        if constexpr (!AGG) {
-            if (ok) {
-                if (seg == 0) {
-                    if (a.init_state) h0 = a.init_state[row * a.N + n0 + j];
-                } else {
-                    h0 = a.h_in[((seg - 1) * bd + row) * a.N + n0 + j];
+        s[j] = 0.0f;  // the aggregate pass always scans its segment from the zero state
+    }
+    if (__any(small_a) != SAFE) return;  // wave-uniform: the other variant owns this unit
+    // carry-in of the output pass: the initial state, a stored carry, or the chain of the aggregates
+    // of the segments before this one: h ← P_k·h + E_k for k = 0 .. seg−1
+    auto load_state = [&](const float *p, float (&o)[NPL]) {
+        if (vstate) {
+#pragma unroll
+            for (int j = 0; j < NPL; j += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(p + j);
+                o[j] = v.x; o[j + 1] = v.y; o[j + 2] = v.z; o[j + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NPL; ++j) o[j] = (ch_ok && j < nvalid) ? p[j] : 0.0f;
+        }
+    };
+    if constexpr (!AGG) {
+        if (seg == 0 || a.h_in == nullptr) {
+            if (a.init_state) load_state(a.init_state + sidx, s);
+        }
+        if (seg > 0) {
+            if (a.h_in) {
+                load_state(a.h_in + (seg - 1) * bd * a.N + sidx, s);
+            } else {
+#pragma unroll 2
+                for (int64_t k = 0; k < seg; ++k) {
+                    float P[NPL], Eend[NPL];
+                    load_state(a.agg_P + k * bd * a.N + sidx, P);
+                    load_state(a.agg_E + k * bd * a.N + sidx, Eend);
+#pragma unroll
+                    for (int j = 0; j < NPL; ++j) s[j] = __builtin_fmaf(P[j], s[j], Eend[j]);
                 }
             }
         }
-        s[j] = h0;
     }
-    if (__any(small_a) != SAFE) return;  // wave-uniform: the other variant owns this wavefront
     if constexpr (!SAFE) {
 #pragma unroll
         for (int j = 0; j < NPL; ++j) s[j] *= Av[j];  // scaled state s = A·h
     }
     const float dskip = (!AGG && ch_ok && a.D) ? a.D[ch] : 0.0f;
-    const int64_t ybase = row * a.L;
 
     // ---- tile prefetch into registers, and from there into LDS ----
     uint4 px[kXC], pd[kXC], pz[kXC], pb[kBC], pc[kBC];
@@ -278,7 +285,7 @@ __global__ __launch_bounds__(kWave, (G == 4 && NPL == 4 && !SAFE) ? 3 : 1) void 
             const int col = (k % kRowChunks) * E;
             put_chunk<T>(xs + r * kPitch + col, px[i]);
             put_chunk<T>(dsh + r * kPitch + col, pd[i]);
-            if (gate) put_chunk<T>(zs + r * kPitch + col, pz[i]);
+            if (gate) *reinterpret_cast<uint4 *>(zs + r * kZPitch + col) = pz[i];
         }
 #pragma unroll
         for (int i = 0; i < kBC; ++i) {
@@ -311,104 +318,179 @@ __global__ __launch_bounds__(kWave, (G == 4 && NPL == 4 && !SAFE) ? 3 : 1) void 
         }
     }
 
-    // ---- the scan of one tile, with the epilogue folded in ----
-    struct Sub {
-        float x[U], d[U], B[U][NPL], C[U][NPL];
+    // The output window starting at step tw0 (nt valid steps) leaves as whole 128-byte lines: lane
+    // l stores 16-byte chunk l % 8 of rows l / 8 + 8i.
+    constexpr int EY = 16 / sizeof(T);                   // elements per 16-byte chunk
+    constexpr int kYC = kYWin / EY;                      // chunks per row (8)
+    constexpr int kYI = CW * kYC / kWave;                // chunks per lane
+    static_assert(kWave % kYC == 0 && (CW * kYC) % kWave == 0, "whole rows per flush pass");
+    constexpr int kWordsPerRow = kYPitch * (int)sizeof(T) / 4;
+    const int yq = lane % kYC;
+    const int yr0 = lane / kYC;
+    T *const ylane = yg + (bi * a.d + d0 + yr0) * a.L + yq * EY;
+    const uint32_t *const yword = reinterpret_cast<const uint32_t *>(ybuf) + yr0 * kWordsPerRow + yq * 4;
+    auto flush_y = [&](int64_t tw0, int nt) {
+        const bool full = a.vec_rows && nt == kYWin;
+#pragma unroll
+        for (int i = 0; i < kYI; ++i) {
+            const int r = yr0 + i * (kWave / kYC);
+            if (d0 + r >= a.d) break;  // rows only grow with i
+            T *dst = ylane + (int64_t)i * (kWave / kYC) * a.L + tw0;
+            const uint32_t *w = yword + i * (kWave / kYC) * kWordsPerRow;  // rows are word-aligned only
+            if (full) {
+                *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+            } else {
+                const T *src = reinterpret_cast<const T *>(w);
+#pragma unroll
+                for (int e = 0; e < EY; ++e)
+                    if (yq * EY + e < nt) dst[e] = src[e];
+            }
+        }
+    };
+
+    // ---- the scan of one tile, with the readout and epilogue folded in ----
+    struct Sub {  // one timestep's operands, read from LDS one step ahead of their use
+        float x, d, B[NPL], C[NPL];
     };
     const float *xrow = xs + c * kPitch;
     const float *drow = dsh + c * kPitch;
-    const float *zrow = zs + c * kPitch;
     const float *Bn = Bs + n0;
     const float *Cn = Cs + n0;
-    auto load_sub = [&](int u, Sub &o) {
-        lds_get<U>(xrow + u * U, o.x);
-        lds_get<U>(drow + u * U, o.d);
+    auto load_sub = [&](int t, Sub &o) {
+        o.x = xrow[t];
+        o.d = drow[t];
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-#pragma unroll
-            for (int j = 0; j < NPL; j += 4) {
-                const float4 bv = *reinterpret_cast<const float4 *>(Bn + (u * U + k) * NPAD + j);
-                o.B[k][j] = bv.x; o.B[k][j + 1] = bv.y; o.B[k][j + 2] = bv.z; o.B[k][j + 3] = bv.w;
-                if constexpr (!AGG) {
-                    const float4 cv = *reinterpret_cast<const float4 *>(Cn + (u * U + k) * NPAD + j);
-                    o.C[k][j] = cv.x; o.C[k][j + 1] = cv.y; o.C[k][j + 2] = cv.z; o.C[k][j + 3] = cv.w;
-                }
+        for (int j = 0; j < NPL; j += 4) {
+            const float4 bv = *reinterpret_cast<const float4 *>(Bn + t * NPAD + j);
+            o.B[j] = bv.x; o.B[j + 1] = bv.y; o.B[j + 2] = bv.z; o.B[j + 3] = bv.w;
+            if constexpr (!AGG) {
+                const float4 cv = *reinterpret_cast<const float4 *>(Cn + t * NPAD + j);
+                o.C[j] = cv.x; o.C[j + 1] = cv.y; o.C[j + 2] = cv.z; o.C[j + 3] = cv.w;
             }
         }
     };
     float dsum = 0.0f;
-    // One sub-tile: the recurrence for U timesteps; ysum[k] receives timestep k's channel readout.
-    auto compute_sub = [&](const Sub &cur, float (&ysum)[U]) {
+    // One timestep of the recurrence; returns this lane's share of the readout.
+    auto compute_step = [&](const Sub &cur) {
+        const float xt = cur.x, dt = cur.d;
+        float acc = 0.0f;
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const float xt = cur.x[k], dt = cur.d[k];
-            float acc = 0.0f;
+        for (int j = 0; j < NPL; ++j) {
+            const float u = dt * a2[j];            // Δ·A·log2(e)
+            const float abar = exp2_fast(u);
+            if constexpr (!SAFE) {
+                const float pre = __builtin_fmaf(cur.B[j], xt, s[j]);  // s + B x
+                s[j] = __builtin_fmaf(abar - 1.0f, pre, s[j]);         // s + (Ā − 1)(s + B x)
+                if constexpr (!AGG) acc = __builtin_fmaf(cur.C[j] * ia[j], s[j], acc);
+            } else {
+                const float kc = zoh_input_coef_log2(dt, u, abar, ia[j]);
+                s[j] = __builtin_fmaf(abar, s[j], kc * (cur.B[j] * xt));  // Ā h + B̄ x
+                if constexpr (!AGG) acc = __builtin_fmaf(cur.C[j], s[j], acc);
+            }
+        }
+        if constexpr (AGG) dsum += dt;
+        return acc;
+    };
+    // Readout transpose: this lane's partials of a group -> LDS; the partials of the timesteps
+    // this lane finishes <- LDS.
+    float *const red_w = red + c * kRS + g;
+    const float *const red_r = red + c * kRS + g * G;
+    auto red_write = [&](const float (&p)[kGrp]) {
 #pragma unroll
-            for (int j = 0; j < NPL; ++j) {
-                const float abar = exp2_fast(dt * a2[j]);
-                if constexpr (!SAFE) {
-                    const float pre = __builtin_fmaf(cur.B[k][j], xt, s[j]);  // s + B x
-                    s[j] = __builtin_fmaf(abar - 1.0f, pre, s[j]);            // s + (Ā − 1)(s + B x)
-                    if constexpr (!AGG) acc = __builtin_fmaf(cur.C[k][j] * ia[j], s[j], acc);
+        for (int kk = 0; kk < kGrp; ++kk) red_w[kk * G] = p[kk];
+    };
+    auto red_read = [&](float (&r)[kGrp]) {  // r[q*G + i]: partial of lane i for step q*G + g
+#pragma unroll
+        for (int q = 0; q < kGrp / G; ++q) {
+            if constexpr (G == 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(red_r + q * G * G);
+                r[q * G] = v.x; r[q * G + 1] = v.y; r[q * G + 2] = v.z; r[q * G + 3] = v.w;
+            } else if constexpr (G == 2) {
+                const float2 v = *reinterpret_cast<const float2 *>(red_r + q * G * G);
+                r[q * G] = v.x; r[q * G + 1] = v.y;
+            }
+        }
+    };
+    // Epilogue of the group starting at tile column col0: lane g finishes steps col0 + q*G + g.
+    const float *const xfin = xrow + g;
+    const T *const zfin = zs + c * kZPitch + g;
+    auto finish = [&](int col0, const float (&r)[kGrp], T *ywin) {
+#pragma unroll
+        for (int q = 0; q < kGrp / G; ++q) {
+            float v = r[q * G];
+#pragma unroll
+            for (int i = 1; i < G; ++i) v += r[q * G + i];
+            const int col = col0 + q * G;  // + g, in the lane's base pointers
+            v = __builtin_fmaf(dskip, xfin[col], v);  // + D·x
+            if (gate) v *= silu(widen(zfin[col]));
+            ywin[col] = narrow<T>(v);
+        }
+    };
+    auto scan_tile = [&](int it) {
+        T *const ywin = ybuf + c * kYPitch + (it & 1) * kTile + g;
+        float p[kGrp], r[kGrp];
+        // Operands are read from LDS one step ahead of their use: across the whole tile (fp32
+        // storage), or within each readout group (bf16 storage, which then needs fewer registers;
+        // both choices measured fastest for their type).
+        constexpr bool kGroupLocal = sizeof(T) == 2;
+        Sub sb[2];
+        if constexpr (!kGroupLocal) load_sub(0, sb[0]);
+        // the output pass unrolls the tile (LDS offsets become immediates); the aggregate pass
+        // keeps a loop, which holds its register need down
+        constexpr int kUnroll = AGG ? 1 : kTile / kGrp;
+#pragma unroll kUnroll
+        for (int t = 0; t < kTile; t += kGrp) {
+            if constexpr (kGroupLocal) load_sub(t, sb[0]);
+#pragma unroll
+            for (int k = 0; k < kGrp; ++k) {
+                if constexpr (kGroupLocal) {
+                    if (k + 1 < kGrp) load_sub(t + k + 1, sb[(k + 1) & 1]);
                 } else {
-                    const float kc = zoh_input_coef(dt, Av[j], abar, ia[j]);
-                    s[j] = __builtin_fmaf(abar, s[j], kc * (cur.B[k][j] * xt));  // Ā h + B̄ x
-                    if constexpr (!AGG) acc = __builtin_fmaf(cur.C[k][j], s[j], acc);
+                    const int tn = t + k + 1 < kTile ? t + k + 1 : kTile - 1;  // the last step re-reads itself
+                    load_sub(tn, sb[(k + 1) & 1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
+                p[k] = compute_step(sb[k & 1]);
+            }
+            if constexpr (!AGG) {
+                if constexpr (G == 1) {
+                    finish(t, p, ywin);
+                } else {
+                    wave_sync();
+                    red_write(p);
+                    wave_sync();
+                    red_read(r);
+                    finish(t, r, ywin);
                 }
             }
-            if constexpr (AGG) dsum += dt;
-            if constexpr (!AGG) ysum[k] = group_sum<G>(acc);
         }
     };
-    // Epilogue of the 2U timesteps of a sub-tile pair starting at tile column `col0`: lane g takes
-    // the timesteps col0 + q*G + g.
-    auto epilogue = [&](int col0, int64_t t0, const float (&y0)[U], const float (&y1)[U]) {
-        float yy[2 * U];
-#pragma unroll
-        for (int k = 0; k < U; ++k) { yy[k] = y0[k]; yy[U + k] = y1[k]; }
-#pragma unroll
-        for (int q = 0; q < 2 * U / G; ++q) {
-            float v = yy[q * G];
-#pragma unroll
-            for (int r = 1; r < G; ++r) v = (g == r) ? yy[q * G + r] : v;
-            const int col = col0 + q * G + g;
-            const int64_t tg = t0 + col;
-            v = __builtin_fmaf(dskip, xrow[col], v);  // + D·x
-            if (gate) v *= silu(zrow[col]);
-            if (ch_ok && tg < t_end) yg[ybase + tg] = narrow<T>(v);
-        }
-    };
-    auto scan_tile = [&](int64_t t0) {
-        Sub s0, s1;
-        float y0[U], y1[U];
-        load_sub(0, s0);
+    auto run = [&]() {
+        load_tile(t_begin);
+        store_tile();
+        if (ntiles > 1) load_tile(t_begin + kTile);
+        wave_sync();
 #pragma unroll 1
-        for (int u = 0; u < NSUB; u += 2) {
-            load_sub(u + 1, s1);
-            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
-            compute_sub(s0, y0);
-            load_sub(u + 2 < NSUB ? u + 2 : u + 1, s0);  // the last pass re-reads a sub-tile it has
-            __builtin_amdgcn_sched_barrier(0);
-            compute_sub(s1, y1);
-            if constexpr (!AGG) epilogue(u * U, t0, y0, y1);
+        for (int it = 0; it < ntiles; ++it) {
+            const int64_t t0 = t_begin + (int64_t)it * kTile;
+            scan_tile(it);
+            if constexpr (!AGG) {
+                if ((it & 1) || it + 1 == ntiles) {  // the output window is complete
+                    const int64_t tw0 = t0 - (it & 1) * kTile;
+                    const int64_t left = t_end - tw0;
+                    wave_sync();
+                    flush_y(tw0, left < kYWin ? (int)left : kYWin);
+                }
+            }
+            if (it + 1 < ntiles) {
+                wave_sync();   // the scan's last reads of tile it come before the stores of tile it + 1
+                store_tile();
+                wave_sync();
+            }
+            if (it + 2 < ntiles) load_tile(t0 + 2 * kTile);
         }
     };
-
-    load_tile(t_begin);
-    store_tile();
-    if (ntiles > 1) load_tile(t_begin + kTile);
-    wave_sync();
-#pragma unroll 1
-    for (int it = 0; it < ntiles; ++it) {
-        const int64_t t0 = t_begin + (int64_t)it * kTile;
-        scan_tile(t0);
-        if (it + 1 < ntiles) {
-            wave_sync();   // the scan's last reads of tile it come before the stores of tile it + 1
-            store_tile();
-            wave_sync();
-        }
-        if (it + 2 < ntiles) load_tile(t0 + 2 * kTile);
-    }
+    run();
 
     // ---- segment results: this lane's NPL states ----
     if (ch_ok) {
@@ -416,7 +498,7 @@ __global__ __launch_bounds__(kWave, (G == 4 && NPL == 4 && !SAFE) ? 3 : 1) void 
         for (int j = 0; j < NPL; ++j) {
             if (j >= nvalid) continue;
             const float h = SAFE ? s[j] : s[j] * ia[j];
-            const int64_t idx = row * a.N + n0 + j;
+            const int64_t idx = sidx + j;
             if constexpr (AGG) {
                 a.agg_P[seg * bd * a.N + idx] = exp2_fast(a2[j] * dsum);  // Π Ā = exp(A ΣΔ)
                 a.agg_E[seg * bd * a.N + idx] = h;                        // end state from zero
@@ -427,7 +509,46 @@ __global__ __launch_bounds__(kWave, (G == 4 && NPL == 4 && !SAFE) ? 3 : 1) void 
     }
 }
 
-// Chunk carry: h_in[k] = P[k−1]·h_in[k−1] + E[k−1] per (b, d, n), h_in[0] = initial state.
+// One wavefront per unit (a block of 64/G channels of one batch row over one time segment). The
+// fast variant takes every unit whose channels all have |A| >= 2^-10 and leaves the others at once;
+// the small-|A| variant walks kSafeUnits units per wavefront and takes only those others, so its
+// launch stays small when, as usual, it has nothing to do. Keeping the rare path in a kernel of its
+// own keeps the common kernel's register budget small.
+constexpr int kSafeUnits = 8;
+
+// Whether any channel of unit `blk` has |A| < 2^-10 (wave-uniform).
+template <int G, int NPL>
+__device__ __forceinline__ bool unit_has_small_a(const FwdArgs &a, int64_t blk) {
+    constexpr int CW = kWave / G;
+    const int64_t cb = blk % (a.b * a.n_cw);
+    const int64_t ch = (cb % a.n_cw) * CW + threadIdx.x / G;
+    const int n0 = (threadIdx.x % G) * NPL;
+    bool small_a = false;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+        if (ch < a.d && n0 + j < a.N) small_a |= __builtin_fabsf(a.A[ch * a.N + n0 + j]) < kSafeAbsA;
+    return __any(small_a);
+}
+
+template <typename T, int G, int NPL, bool AGG, bool SAFE>
+__global__ __launch_bounds__(kWave, (G == 4 && NPL == 4 && !SAFE) ? 3 : 1) void scan_fwd_kernel(FwdArgs a,
+                                                                                               int64_t units) {
+    if constexpr (!SAFE) {
+        scan_unit<T, G, NPL, AGG, false>(a, blockIdx.x);
+    } else {
+        // test all units first (their loads overlap), then scan the ones that need this path
+        const int64_t u0 = (int64_t)blockIdx.x * kSafeUnits;
+        uint32_t mine = 0;
+#pragma unroll
+        for (int i = 0; i < kSafeUnits; ++i)
+            if (u0 + i < units && unit_has_small_a<G, NPL>(a, u0 + i)) mine |= 1u << i;
+        for (int i = 0; i < kSafeUnits; ++i)
+            if (mine & (1u << i)) scan_unit<T, G, NPL, AGG, true>(a, u0 + i);
+    }
+}
+
+// Chunk carry for many segments: h_in[k] = P[k]·h_in[k−1] + E[k] per (b, d, n), from the
+// initial state.
 __global__ __launch_bounds__(256) void carry_kernel(const float *__restrict__ P, const float *__restrict__ Eend,
                                                     float *__restrict__ Hin, const float *__restrict__ init,
                                                     int64_t bdn, int n_seg) {
@@ -447,35 +568,38 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ p, i
 
 template <typename T, int G, int NPL>
 hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLaunch &p, hipStream_t stream) {
-    if (n_seg > 1) {
-        const int64_t grid = (int64_t)(n_seg - 1) * ncb;
-        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, true, false>), dim3((unsigned)grid), dim3(kWave), 0, stream,
-                           args);
-        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, true, true>), dim3((unsigned)grid), dim3(kWave), 0, stream,
-                           args);
+    auto pass = [&](auto agg_c, int64_t units) {
+        constexpr bool AGG = decltype(agg_c)::value;
+        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, AGG, true>), dim3((unsigned)((units + kSafeUnits - 1) / kSafeUnits)),
+                           dim3(kWave), 0, stream, args, units);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const int64_t bdn = p.b * p.d * p.N;
-        hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((bdn + 255) / 256)), dim3(256), 0, stream, args.agg_P,
-                           args.agg_E, const_cast<float *>(args.h_in), p.init_state, bdn, n_seg);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    // The small-|A| instantiation goes first so that the events bracket the fast-path kernel alone
-    // (the two write disjoint channels, so their order does not matter).
-    const int64_t grid = (int64_t)n_seg * ncb;
-    hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false, true>), dim3((unsigned)grid), dim3(kWave), 0, stream, args);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (p.ev_begin) {
+        if (AGG || !p.ev_begin) {
+            hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, AGG, false>), dim3((unsigned)units), dim3(kWave), 0, stream,
+                               args, units);
+            return hipGetLastError();
+        }
+        // the events bracket the fast output kernel alone
         e = hipEventRecord(p.ev_begin, stream);
         if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, AGG, false>), dim3((unsigned)units), dim3(kWave), 0, stream,
+                           args, units);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return p.ev_end ? hipEventRecord(p.ev_end, stream) : hipSuccess;
+    };
+    if (n_seg > 1) {
+        hipError_t e = pass(std::true_type{}, (int64_t)(n_seg - 1) * ncb);
+        if (e != hipSuccess) return e;
+        if (args.h_in) {
+            const int64_t bdn = p.b * p.d * p.N;
+            hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((bdn + 255) / 256)), dim3(256), 0, stream, args.agg_P,
+                               args.agg_E, const_cast<float *>(args.h_in), p.init_state, bdn, n_seg);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
-    hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false, false>), dim3((unsigned)grid), dim3(kWave), 0, stream, args);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (p.ev_end) e = hipEventRecord(p.ev_end, stream);
-    return e;
+    return pass(std::false_type{}, (int64_t)n_seg * ncb);
 }
 
 template <typename T>
@@ -502,14 +626,16 @@ hipError_t launch_scan_fwd(const FwdLaunch &p, hipStream_t stream) {
     a.n_cw = (p.d + cw - 1) / cw;
     const int64_t esize = p.bf16 ? 2 : 4;
     auto aligned16 = [](const void *q) { return q == nullptr || (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
-    a.vec_rows = ((p.L * esize) % 16 == 0) && aligned16(p.x) && aligned16(p.delta) && aligned16(p.z);
+    a.vec_rows = ((p.L * esize) % 16 == 0) && aligned16(p.x) && aligned16(p.delta) && aligned16(p.z) &&
+                 aligned16(p.y);
     // a tile's B/C run starts at element (bi*L + t0)*N with t0 a multiple of the tile length
     a.vec_bc = ((p.L * p.N * esize) % 16 == 0) && aligned16(p.B) && aligned16(p.C);
+    a.vec_state = (p.N % 4 == 0) && aligned16(p.init_state) && aligned16(p.scratch);
     if (p.n_seg > 1) {
         const int64_t per = (int64_t)(p.n_seg - 1) * p.b * p.d * p.N;
         a.agg_P = p.scratch;
         a.agg_E = p.scratch + per;
-        a.h_in = p.scratch + 2 * per;
+        a.h_in = p.n_seg > kFoldMaxSeg ? p.scratch + 2 * per : nullptr;
     }
     const int64_t ncb = p.b * a.n_cw;
     if (p.bf16) return dispatch_shape<uint16_t>(a, p.n_seg, ncb, p, stream);

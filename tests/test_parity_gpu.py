@@ -177,6 +177,24 @@ def test_segment_length_invariance(dt):
         assert_close(h, outs[0][1], tau, "state across segment lengths")
 
 
+@pytest.mark.parametrize("dt,seg_len", [("f32", 32), ("bf16", 32), ("bf16", 64), ("f32", 0)])
+def test_initial_state_with_time_segments(dt, seg_len):
+    """A given initial state through a time-split plan: more than 64 segments (a separate carry
+    kernel chains the aggregates), fewer (each output wavefront chains them), and the default plan."""
+    b, d, L, N = 2, 72, 2400, 16
+    inp = I.random_prefill(b, d, L, N, dtype=dt, seed=21, delta_mu=-3.0)
+    h0 = (np.random.default_rng(3).standard_normal((b, d, N)) * 0.5).astype(np.float32)
+    t = upload(inp)
+    plan = api.ssm_scan_fwd_plan(b, d, L, N, t["x"].dtype, seg_len=seg_len)
+    y, h = api.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], seg_len=seg_len,
+                            initial_state=torch.from_numpy(h0).cuda())
+    torch.cuda.synchronize()
+    check_rows(inp, from_torch(y), from_torch(h), all_rows(b, d), f"h0 + {plan['n_segments']} segments {dt}",
+               h0=h0.astype(np.float64))
+    if seg_len == 32:
+        assert plan["n_segments"] == 75
+
+
 def test_bitwise_deterministic():
     inp = I.random_prefill(2, 128, 700, 16, dtype="bf16", seed=4)
     a = run_fwd(inp)
