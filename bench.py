@@ -77,6 +77,9 @@ def bench_prefill(name, steps, warmup, rotate=0, quiet=False):
         s["y"] = torch.empty_like(s["x"])
         s["h"] = torch.empty((w.b, w.d, w.N), dtype=torch.float32, device=dev)
         sets.append(s)
+    # the output kernel is timed on every `every`-th call of the timed loop (each event pair adds a
+    # few microseconds of queue drain to the call it brackets)
+    every = max(1, steps // 10)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for e0, e1 in ev:  # materialise the underlying HIP events before handing them to the library
         e0.record(); e1.record()
@@ -91,11 +94,11 @@ def bench_prefill(name, steps, warmup, rotate=0, quiet=False):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        call(i, ev[i])
+        call(i, ev[i] if i % every == 0 else None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / steps
-    kern = np.array([a.elapsed_time(b) for a, b in ev])
+    kern = np.array([a.elapsed_time(b) for i, (a, b) in enumerate(ev) if i % every == 0])
     kern_ms = float(np.mean(kern))
     plan = api.ssm_scan_fwd_plan(w.b, w.d, w.L, w.N, torch.float32 if w.dtype == "f32" else torch.bfloat16)
     elems = w.b * w.d * w.L
@@ -103,7 +106,7 @@ def bench_prefill(name, steps, warmup, rotate=0, quiet=False):
     res = {
         "workload": name, "ms_per_call": ms, "GBps": nbytes / (ms * 1e-3) / 1e9,
         "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "elements_per_s": elems / (ms * 1e-3),
-        "output_kernel_ms": kern_ms, "output_kernel_ms_p10_p50_p90": [round(float(q), 5) for q in
+        "output_kernel_ms": kern_ms, "output_kernel_samples": int(len(kern)), "output_kernel_ms_p10_p50_p90": [round(float(q), 5) for q in
                                                                       np.percentile(kern, [10, 50, 90])],
         "algorithmic_bytes": nbytes, "rotating_sets": rotate, "plan": plan,
         "valu_slots_per_element": valu_slots_per_element(w.N, w.gate),

@@ -114,6 +114,13 @@ __device__ __forceinline__ uint4 get_chunk(const T *__restrict__ row, int64_t t,
     return r;
 }
 
+// p[ok ? i : 0] with the load issued unconditionally (a guarded load would become a branch
+// with a wait behind it), then `fallback` where !ok. p[0] must be readable.
+__device__ __forceinline__ float load_or(const float *p, int64_t i, bool ok, float fallback) {
+    const float v = p[ok ? i : 0];
+    return ok ? v : fallback;
+}
+
 // U consecutive floats from LDS (U = 1, 2 or 4).
 template <int U>
 __device__ __forceinline__ void lds_get(const float *p, float (&o)[U]) {
@@ -171,11 +178,14 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
     const int c = lane / G;  // channel within the wave
     const int g = lane % G;  // state group within the channel
 
-    const int64_t ncb = a.b * a.n_cw;
-    const int64_t seg = blk / ncb;
-    const int64_t cb = blk - seg * ncb;
-    const int64_t bi = cb / a.n_cw;
-    const int64_t d0 = (cb - bi * a.n_cw) * CW;
+    // unit index -> (segment, batch row, channel block); the plan keeps every count below 2^31, so
+    // 32-bit divisions do (64-bit ones are long scalar sequences)
+    const uint32_t ncb = (uint32_t)(a.b * a.n_cw);
+    const uint32_t ublk = (uint32_t)blk;
+    const int64_t seg = ublk / ncb;
+    const uint32_t cb = ublk - (uint32_t)seg * ncb;
+    const int64_t bi = cb / (uint32_t)a.n_cw;
+    const int64_t d0 = (int64_t)(cb - (uint32_t)bi * (uint32_t)a.n_cw) * CW;
     const int64_t t_begin = seg * a.seg_len;
     const int64_t t_end = (t_begin + a.seg_len < a.L) ? t_begin + a.seg_len : a.L;
     const int ntiles = (int)((t_end - t_begin + kTile - 1) / kTile);
@@ -197,13 +207,12 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
     const int nvalid = (N - n0) < NPL ? (N - n0) : NPL;  // <= 0 for a lane past the last state
     const int64_t row = bi * a.d + ch;
     const int64_t sidx = row * a.N + n0;                  // this lane's first state in [b][d][N]
-    const bool vstate = a.vec_state && ch_ok && nvalid == NPL;
     float Av[NPL], a2[NPL], ia[NPL], s[NPL];
     bool small_a = false;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
         const bool ok = ch_ok && j < nvalid;
-        const float av = ok ? a.A[ch * a.N + n0 + j] : -1.0f;  // idle states: A = −1 with B = C = 0
+        const float av = load_or(a.A, ch * a.N + n0 + j, ok, -1.0f);  // idle states: A = −1 with B = C = 0
         Av[j] = av;
         a2[j] = av * kLog2e;
         ia[j] = 1.0f / av;
@@ -213,31 +222,32 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
     if (__any(small_a) != SAFE) return;  // wave-uniform: the other variant owns this unit
     // carry-in of the output pass: the initial state, a stored carry, or the chain of the aggregates
     // of the segments before this one: h ← P_k·h + E_k for k = 0 .. seg−1
-    auto load_state = [&](const float *p, float (&o)[NPL]) {
-        if (vstate) {
+    auto load_state = [&](const float *base, float (&o)[NPL]) {  // o = base[sidx .. sidx + NPL), zeros past N
+        if (a.vec_state) {  // N % 4 == 0: whole 16-byte groups are valid or not
 #pragma unroll
             for (int j = 0; j < NPL; j += 4) {
-                const float4 v = *reinterpret_cast<const float4 *>(p + j);
-                o[j] = v.x; o[j + 1] = v.y; o[j + 2] = v.z; o[j + 3] = v.w;
+                const bool ok = ch_ok && j + 4 <= nvalid;
+                const float4 v = *reinterpret_cast<const float4 *>(base + (ok ? sidx + j : 0));
+                o[j] = ok ? v.x : 0.0f; o[j + 1] = ok ? v.y : 0.0f; o[j + 2] = ok ? v.z : 0.0f; o[j + 3] = ok ? v.w : 0.0f;
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < NPL; ++j) o[j] = (ch_ok && j < nvalid) ? p[j] : 0.0f;
+            for (int j = 0; j < NPL; ++j) o[j] = load_or(base, sidx + j, ch_ok && j < nvalid, 0.0f);
         }
     };
     if constexpr (!AGG) {
         if (seg == 0 || a.h_in == nullptr) {
-            if (a.init_state) load_state(a.init_state + sidx, s);
+            if (a.init_state) load_state(a.init_state, s);
         }
         if (seg > 0) {
             if (a.h_in) {
-                load_state(a.h_in + (seg - 1) * bd * a.N + sidx, s);
+                load_state(a.h_in + (seg - 1) * bd * a.N, s);
             } else {
 #pragma unroll 2
                 for (int64_t k = 0; k < seg; ++k) {
                     float P[NPL], Eend[NPL];
-                    load_state(a.agg_P + k * bd * a.N + sidx, P);
-                    load_state(a.agg_E + k * bd * a.N + sidx, Eend);
+                    load_state(a.agg_P + k * bd * a.N, P);
+                    load_state(a.agg_E + k * bd * a.N, Eend);
 #pragma unroll
                     for (int j = 0; j < NPL; ++j) s[j] = __builtin_fmaf(P[j], s[j], Eend[j]);
                 }
@@ -248,7 +258,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
 #pragma unroll
         for (int j = 0; j < NPL; ++j) s[j] *= Av[j];  // scaled state s = A·h
     }
-    const float dskip = (!AGG && ch_ok && a.D) ? a.D[ch] : 0.0f;
+    const float dskip = (!AGG && a.D) ? load_or(a.D, ch, ch_ok, 0.0f) : 0.0f;
 
     // ---- tile prefetch into registers, and from there into LDS ----
     uint4 px[kXC], pd[kXC], pz[kXC], pb[kBC], pc[kBC];
@@ -510,40 +520,27 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
 }
 
 // One wavefront per unit (a block of 64/G channels of one batch row over one time segment). The
-// fast variant takes every unit whose channels all have |A| >= 2^-10 and leaves the others at once;
-// the small-|A| variant walks kSafeUnits units per wavefront and takes only those others, so its
-// launch stays small when, as usual, it has nothing to do. Keeping the rare path in a kernel of its
-// own keeps the common kernel's register budget small.
-constexpr int kSafeUnits = 8;
-
-// Whether any channel of unit `blk` has |A| < 2^-10 (wave-uniform).
-template <int G, int NPL>
-__device__ __forceinline__ bool unit_has_small_a(const FwdArgs &a, int64_t blk) {
-    constexpr int CW = kWave / G;
-    const int64_t cb = blk % (a.b * a.n_cw);
-    const int64_t ch = (cb % a.n_cw) * CW + threadIdx.x / G;
-    const int n0 = (threadIdx.x % G) * NPL;
-    bool small_a = false;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j)
-        if (ch < a.d && n0 + j < a.N) small_a |= __builtin_fabsf(a.A[ch * a.N + n0 + j]) < kSafeAbsA;
-    return __any(small_a);
-}
-
+// fast variant takes every unit whose channels all have |A| >= 2^-10 and leaves the others at once.
+// The small-|A| variant runs one wavefront per channel block (A depends on nothing else): it tests
+// the block's A once and, only if the test holds, scans every unit of that block in turn, so its
+// launch costs little when, as usual, it has nothing to do. Keeping the rare path in a kernel of
+// its own keeps the common kernel's register budget small.
 template <typename T, int G, int NPL, bool AGG, bool SAFE>
 __global__ __launch_bounds__(kWave, (G == 4 && NPL == 4 && !SAFE) ? 3 : 1) void scan_fwd_kernel(FwdArgs a,
                                                                                                int64_t units) {
     if constexpr (!SAFE) {
         scan_unit<T, G, NPL, AGG, false>(a, blockIdx.x);
     } else {
-        // test all units first (their loads overlap), then scan the ones that need this path
-        const int64_t u0 = (int64_t)blockIdx.x * kSafeUnits;
-        uint32_t mine = 0;
+        constexpr int CW = kWave / G;
+        const int64_t cbi = blockIdx.x;  // channel block within a batch row
+        const int64_t ch = cbi * CW + threadIdx.x / G;
+        const int n0 = (threadIdx.x % G) * NPL;
+        bool small_a = false;
 #pragma unroll
-        for (int i = 0; i < kSafeUnits; ++i)
-            if (u0 + i < units && unit_has_small_a<G, NPL>(a, u0 + i)) mine |= 1u << i;
-        for (int i = 0; i < kSafeUnits; ++i)
-            if (mine & (1u << i)) scan_unit<T, G, NPL, AGG, true>(a, u0 + i);
+        for (int j = 0; j < NPL; ++j)
+            small_a |= __builtin_fabsf(load_or(a.A, ch * a.N + n0 + j, ch < a.d && n0 + j < a.N, -1.0f)) < kSafeAbsA;
+        if (!__any(small_a)) return;
+        for (int64_t u = cbi; u < units; u += a.n_cw) scan_unit<T, G, NPL, AGG, true>(a, u);
     }
 }
 
@@ -570,8 +567,8 @@ template <typename T, int G, int NPL>
 hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLaunch &p, hipStream_t stream) {
     auto pass = [&](auto agg_c, int64_t units) {
         constexpr bool AGG = decltype(agg_c)::value;
-        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, AGG, true>), dim3((unsigned)((units + kSafeUnits - 1) / kSafeUnits)),
-                           dim3(kWave), 0, stream, args, units);
+        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, AGG, true>), dim3((unsigned)args.n_cw), dim3(kWave), 0, stream,
+                           args, units);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (AGG || !p.ev_begin) {
