@@ -522,9 +522,10 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
 // One wavefront per unit (a block of 64/G channels of one batch row over one time segment). The
 // fast variant takes every unit whose channels all have |A| >= 2^-10 and leaves the others at once.
 // The small-|A| variant runs one wavefront per channel block (A depends on nothing else): it tests
-// the block's A once and, only if the test holds, scans every unit of that block in turn, so its
-// launch costs little when, as usual, it has nothing to do. Keeping the rare path in a kernel of
-// its own keeps the common kernel's register budget small.
+// the block's A once and, only if the test holds, scans the block in every batch row in turn, each
+// over the whole sequence as a single segment, so its one launch costs little when, as usual, it
+// has nothing to do. Keeping the rare path in a kernel of its own keeps the common kernel's
+// register budget small.
 template <typename T, int G, int NPL, bool AGG, bool SAFE>
 __global__ __launch_bounds__(kWave, (G == 4 && NPL == 4 && !SAFE) ? 3 : 1) void scan_fwd_kernel(FwdArgs a,
                                                                                                int64_t units) {
@@ -565,28 +566,11 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ p, i
 
 template <typename T, int G, int NPL>
 hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLaunch &p, hipStream_t stream) {
-    auto pass = [&](auto agg_c, int64_t units) {
-        constexpr bool AGG = decltype(agg_c)::value;
-        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, AGG, true>), dim3((unsigned)args.n_cw), dim3(kWave), 0, stream,
-                           args, units);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        if (AGG || !p.ev_begin) {
-            hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, AGG, false>), dim3((unsigned)units), dim3(kWave), 0, stream,
-                               args, units);
-            return hipGetLastError();
-        }
-        // the events bracket the fast output kernel alone
-        e = hipEventRecord(p.ev_begin, stream);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, AGG, false>), dim3((unsigned)units), dim3(kWave), 0, stream,
-                           args, units);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        return p.ev_end ? hipEventRecord(p.ev_end, stream) : hipSuccess;
-    };
+    hipError_t e = hipSuccess;
     if (n_seg > 1) {
-        hipError_t e = pass(std::true_type{}, (int64_t)(n_seg - 1) * ncb);
+        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, true, false>), dim3((unsigned)((n_seg - 1) * ncb)), dim3(kWave),
+                           0, stream, args, (int64_t)(n_seg - 1) * ncb);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (args.h_in) {
             const int64_t bdn = p.b * p.d * p.N;
@@ -596,7 +580,25 @@ hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLa
             if (e != hipSuccess) return e;
         }
     }
-    return pass(std::false_type{}, (int64_t)n_seg * ncb);
+    if (p.ev_begin) {  // the events bracket the fast output kernel alone
+        e = hipEventRecord(p.ev_begin, stream);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false, false>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0, stream,
+                       args, (int64_t)n_seg * ncb);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (p.ev_end) {
+        e = hipEventRecord(p.ev_end, stream);
+        if (e != hipSuccess) return e;
+    }
+    // Channel blocks with a small |A| run as one segment each (no aggregates needed), so a single
+    // launch covers them; it depends on nothing above and writes only their outputs.
+    FwdArgs whole = args;
+    whole.seg_len = p.L;
+    hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false, true>), dim3((unsigned)args.n_cw), dim3(kWave), 0, stream,
+                       whole, ncb);
+    return hipGetLastError();
 }
 
 template <typename T>
