@@ -95,8 +95,8 @@ SSM_API ssm_status_t ssm_scan_fwd(const void *x, const void *delta, const float 
  *   D          [d] fp32             optional
  *   z          [b][d] dtype         optional
  *   y          [b][d] dtype         required output
- *   b, d, N >= 1; N <= SSM_MAX_N. The state is read and written in place (it may not overlap any
- *   other argument). Errors as for ssm_scan_fwd.
+ *   b, d, N >= 1; N <= SSM_MAX_N; b * d < 2^31 (SSM_ERR_SHAPE otherwise). The state is read and
+ *   written in place (it may not overlap any other argument). Errors as for ssm_scan_fwd.
  */
 SSM_API ssm_status_t ssm_scan_step(float *state, const void *x, const void *delta, const float *A,
                            const void *B, const void *C, const float *D, const void *z, void *y,

@@ -262,6 +262,7 @@ ssm_status_t ssm_scan_step(float *state, const void *x, const void *delta, const
     if (N > SSM_MAX_N) return SSM_ERR_UNSUPPORTED;
     int64_t bd = 0, bdn = 0, tmp = 0;
     if (!mul_ok(b, d, &bd) || !mul_ok(bd, N, &bdn) || !mul_ok(bd, 16, &tmp)) return SSM_ERR_SHAPE;
+    if (bd > 0x7fffffffLL) return SSM_ERR_SHAPE;  // (b, d) pairs are indexed in 32 bits
     const int64_t es = dtype == SSM_BF16 ? 2 : 4;
     const Span sy{y, bd * es}, ss{state, bdn * 4};
     const Span ins[] = {{x, bd * es}, {delta, bd * es}, {z, bd * es}, {B, b * N * es}, {C, b * N * es},
