@@ -111,9 +111,9 @@ SSM_API ssm_status_t ssm_scan_step(float *state, const void *x, const void *delt
  *                      0 = chosen from the shape
  *   initial_state    [b][d][N] fp32 device pointer, h_{−1} (NULL = zeros); lets a caller
  *                    continue a sequence that an earlier call ended (pass its final_state)
- *   ev_begin, ev_end hipEvent_t values (may be NULL); when set, recorded on `stream` right before
- *                    and right after the output-pass kernel of the fast (scaled-state) path, for
- *                    timing that kernel alone (the small-|A| output kernel runs just before it)
+ *   ev_begin, ev_end hipEvent_t values (may be NULL); when set, the dispatch of the output-pass
+ *                    kernel of the fast (scaled-state) path sets them at its start and end, for
+ *                    timing that kernel alone (hipExtLaunchKernel's start/stop events)
  */
 typedef struct {
     int32_t seg_len;

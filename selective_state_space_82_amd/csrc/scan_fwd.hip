@@ -33,6 +33,8 @@
 //     gives each segment's (Π Ā, end state from zero); the output pass then rescans every segment
 //     from its true carry-in, which each wavefront chains from the aggregates of the segments
 //     before it (or, for many segments, a carry kernel chains once per (b, d, n)).
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "device_common.h"
@@ -580,18 +582,12 @@ hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLa
             if (e != hipSuccess) return e;
         }
     }
-    if (p.ev_begin) {  // the events bracket the fast output kernel alone
-        e = hipEventRecord(p.ev_begin, stream);
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false, false>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0, stream,
-                       args, (int64_t)n_seg * ncb);
+    // Timing events, when given, are set by the dispatch of the fast output kernel itself (start and
+    // end of that kernel), so they add no packets of their own to the queue.
+    hipExtLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false, false>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0,
+                          stream, p.ev_begin, p.ev_end, 0u, args, (int64_t)n_seg * ncb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (p.ev_end) {
-        e = hipEventRecord(p.ev_end, stream);
-        if (e != hipSuccess) return e;
-    }
     // Channel blocks with a small |A| run as one segment each (no aggregates needed), so a single
     // launch covers them; it depends on nothing above and writes only their outputs.
     FwdArgs whole = args;
