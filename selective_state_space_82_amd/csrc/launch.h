@@ -43,7 +43,7 @@ hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t stream);
 hipError_t launch_scan_step(const StepLaunch &p, hipStream_t stream);
 
 constexpr int kSegQuantum = 32; // time segments are multiples of this many steps
-constexpr int kFoldMaxSeg = 64; // up to this many segments the output pass chains the carry itself
+constexpr int kFoldMaxSeg = 16; // up to this many segments the output pass chains the carry itself
 
 // Scratch floats of a time-split prefill: aggregates P and E, plus the carries when a separate
 // carry kernel chains them.

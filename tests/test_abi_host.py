@@ -97,10 +97,10 @@ def test_plan_shapes():
     p = api.ssm_scan_fwd_plan(1, 2048, 131072, 16)
     assert p["n_segments"] > 1 and p["seg_len"] % 32 == 0
     assert p["seg_len"] * p["n_segments"] >= 131072
-    # aggregates (Π Ā, end state) per segment but the last; up to 64 segments need no carry array
-    assert p["scratch_bytes"] == 2 * (p["n_segments"] - 1) * 2048 * 16 * 4
-    p = api.ssm_scan_fwd_plan(1, 2048, 131072, 16, seg_len=1024)
-    assert p["n_segments"] == 128 and p["scratch_bytes"] == 3 * 127 * 2048 * 16 * 4
+    # aggregates (Π Ā, end state) per segment but the last, plus a carry array beyond 16 segments
+    assert p["n_segments"] == 64 and p["scratch_bytes"] == 3 * 63 * 2048 * 16 * 4
+    p = api.ssm_scan_fwd_plan(1, 2048, 131072, 16, seg_len=16384)
+    assert p["n_segments"] == 8 and p["scratch_bytes"] == 2 * 7 * 2048 * 16 * 4
     p = api.ssm_scan_fwd_plan(8, 4096, 4096, 16, seg_len=1024, lanes_per_channel=2)
     assert p["n_segments"] == 4 and p["states_per_lane"] == 8 and p["waves_per_segment"] == 8 * 128
     assert p["groups_output_pass"] == 4 * 8 * 128 and p["groups_aggregate_pass"] == 3 * 8 * 128

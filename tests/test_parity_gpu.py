@@ -177,9 +177,9 @@ def test_segment_length_invariance(dt):
         assert_close(h, outs[0][1], tau, "state across segment lengths")
 
 
-@pytest.mark.parametrize("dt,seg_len", [("f32", 32), ("bf16", 32), ("bf16", 64), ("f32", 0)])
+@pytest.mark.parametrize("dt,seg_len", [("f32", 32), ("bf16", 32), ("bf16", 64), ("bf16", 160), ("f32", 0)])
 def test_initial_state_with_time_segments(dt, seg_len):
-    """A given initial state through a time-split plan: more than 64 segments (a separate carry
+    """A given initial state through a time-split plan: more than 16 segments (a separate carry
     kernel chains the aggregates), fewer (each output wavefront chains them), and the default plan."""
     b, d, L, N = 2, 72, 2400, 16
     inp = I.random_prefill(b, d, L, N, dtype=dt, seed=21, delta_mu=-3.0)
