@@ -63,6 +63,8 @@ class Oracle:
         lib.oracle_scan_fwd.restype = ctypes.c_int
         lib.oracle_scan_step.argtypes = [_DP] * 9 + [L, L, L]
         lib.oracle_scan_step.restype = ctypes.c_int
+        lib.oracle_scan_bwd.argtypes = [_DP] * 18 + [L, L, L, L]
+        lib.oracle_scan_bwd.restype = ctypes.c_int
         lib.oracle_zoh.argtypes = [ctypes.c_double, ctypes.c_double, _DP, _DP]
         lib.oracle_zoh.restype = None
         self.lib = lib
@@ -99,6 +101,33 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_scan_fwd rejected its arguments")
         return y, h
+
+    def scan_bwd(self, x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_final=None):
+        """Gradients of scan_fwd: a dict of float64 arrays dx, ddelta, dA, dB, dC, dD, dz, dh0
+        (dD / dz are None when D / z are absent)."""
+        x = _f64(x)
+        b, d, L = x.shape
+        A = _f64(A)
+        N = A.shape[1]
+        delta = _f64(delta, (b, d, L))
+        B = _f64(B, (b, L, N))
+        C = _f64(C, (b, L, N))
+        D = _f64(D, (d,))
+        z = _f64(z, (b, d, L))
+        h0 = _f64(h0, (b, d, N))
+        dy = _f64(dy, (b, d, L))
+        dh_final = _f64(dh_final, (b, d, N))
+        out = {"dx": np.empty((b, d, L)), "ddelta": np.empty((b, d, L)), "dA": np.empty((d, N)),
+               "dB": np.empty((b, L, N)), "dC": np.empty((b, L, N)),
+               "dD": None if D is None else np.empty(d), "dz": None if z is None else np.empty((b, d, L)),
+               "dh0": np.empty((b, d, N))}
+        rc = self.lib.oracle_scan_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                      _ptr(h0), _ptr(dy), _ptr(dh_final), _ptr(out["dx"]),
+                                      _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+                                      _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["dh0"]), b, d, L, N)
+        if rc != 0:
+            raise ValueError("oracle_scan_bwd rejected its arguments")
+        return out
 
     def scan_step(self, state, x, delta, A, B, C, D=None, z=None):
         """Decode step: returns (y [b, d], new_state [b, d, N]); `state` itself is not modified."""
@@ -141,3 +170,7 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None):
 
 def scan_step(state, x, delta, A, B, C, D=None, z=None):
     return default().scan_step(state, x, delta, A, B, C, D, z)
+
+
+def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_final=None):
+    return default().scan_bwd(x, delta, A, B, C, D, z, h0, dy, dh_final)

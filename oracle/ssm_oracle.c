@@ -8,6 +8,8 @@
 
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
 
 /* Zero-order hold for one diagonal entry.
  * "State Space Models（SSM）とMamba" §2.2 and "Mambaとは？Transformer以外の系列モデル",
@@ -85,5 +87,122 @@ int oracle_scan_step(double *state, const double *x, const double *delta, const 
                      state + row * (size_t)N, y + row, 1, N);
         }
     }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Gradients of the prefill scan.
+ *
+ * The pages define only the forward computation; its gradients follow from the chain rule applied
+ * to that definition, step by step and in reverse time order. The forward states are recomputed
+ * from the inputs rather than stored ("Mambaとは？…", section hardware-awareとは memory trafficまで
+ * 設計すること: intermediate states are recomputed for the backward pass).
+ *
+ * With β = (e^{Δa} − 1)/a (Δ at a = 0), h_t = Ā_t h_{t−1} + β_t B_t x_t,
+ * ys_t = Σ_n C_tn h_tn + D x_t and y_t = ys_t · silu(z_t) (or ys_t without a gate), and λ_t the
+ * total derivative of the loss with respect to h_t:
+ *   λ_t = dys_t · C_t + Ā_{t+1} λ_{t+1}        (λ after the last step: the given d_final_state)
+ *   dĀ_t = λ_t h_{t−1},  dβ_t = λ_t B_t x_t
+ *   ∂Ā/∂Δ = a Ā,  ∂Ā/∂a = Δ Ā,  ∂β/∂Δ = Ā,  ∂β/∂a = (Δ Ā − β)/a  (Δ²/2 at a = 0)
+ * and d(initial state) = Ā_0 λ_0.
+ * ------------------------------------------------------------------------------------------- */
+
+/* ∂β/∂a for one entry: (Δ·e^{Δa} − β)/a, and its limit Δ²/2 at a = 0. Near 0 the quotient is
+ * a difference of nearly equal terms, so its Taylor series Δ²·Σ_{k≥0} (k+1)(Δa)^k/(k+2)! is summed
+ * there instead (to well below fp64 rounding for |Δa| < 2^-6). */
+static double dbeta_da(double delta, double a, double abar, double beta) {
+    const double v = delta * a;
+    if (fabs(v) < 0.015625) {
+        double term = 0.5, sum = 0.0; /* term_k = (k+1) v^k / (k+2)! */
+        double vk = 1.0, fact = 2.0;  /* v^k, (k+2)! */
+        for (int k = 0; k < 12; ++k) {
+            term = (double)(k + 1) * vk / fact;
+            sum += term;
+            vk *= v;
+            fact *= (double)(k + 3);
+        }
+        return delta * delta * sum;
+    }
+    return (delta * abar - beta) / a;
+}
+
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+int oracle_scan_bwd(const double *x, const double *delta, const double *A, const double *B,
+                    const double *C, const double *D, const double *z, const double *h0,
+                    const double *dy, const double *dh_final, double *dx, double *ddelta,
+                    double *dA, double *dB, double *dC, double *dD, double *dz, double *dh0,
+                    long b, long d, long L, long N) {
+    if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC) return -1;
+    if (b < 0 || d < 0 || L < 0 || N < 0 || N > 4096) return -1;
+    if (z && !dz) return -1;
+    memset(dA, 0, sizeof(double) * (size_t)d * (size_t)N);
+    memset(dB, 0, sizeof(double) * (size_t)b * (size_t)L * (size_t)N);
+    memset(dC, 0, sizeof(double) * (size_t)b * (size_t)L * (size_t)N);
+    if (dD) memset(dD, 0, sizeof(double) * (size_t)d);
+    double *hs = (double *)malloc(sizeof(double) * ((size_t)L + 1) * (size_t)(N > 0 ? N : 1));
+    double *lam = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    if (!hs || !lam) {
+        free(hs);
+        free(lam);
+        return -1;
+    }
+    for (long ib = 0; ib < b; ++ib) {
+        for (long id = 0; id < d; ++id) {
+            const size_t row = (size_t)ib * (size_t)d + (size_t)id;
+            const double *xr = x + row * (size_t)L, *dr = delta + row * (size_t)L;
+            const double *zr = z ? z + row * (size_t)L : NULL, *dyr = dy + row * (size_t)L;
+            const double *a = A + (size_t)id * (size_t)N;
+            const double *Bt = B + (size_t)ib * (size_t)L * (size_t)N;
+            const double *Ct = C + (size_t)ib * (size_t)L * (size_t)N;
+            const double dskip = D ? D[id] : 0.0;
+            /* forward recomputation: hs[t + 1][n] = h_t, hs[0][n] = initial state */
+            for (long n = 0; n < N; ++n) hs[n] = h0 ? h0[row * (size_t)N + (size_t)n] : 0.0;
+            for (long t = 0; t < L; ++t) {
+                for (long n = 0; n < N; ++n) {
+                    double abar, beta;
+                    oracle_zoh(dr[t], a[n], &abar, &beta);
+                    hs[(size_t)(t + 1) * (size_t)N + (size_t)n] =
+                        abar * hs[(size_t)t * (size_t)N + (size_t)n] + beta * Bt[t * N + n] * xr[t];
+                }
+            }
+            /* backward, t = L−1 … 0; lam holds Ā_{t+1} λ_{t+1} on entry to step t */
+            for (long n = 0; n < N; ++n) lam[n] = dh_final ? dh_final[row * (size_t)N + (size_t)n] : 0.0;
+            for (long t = L - 1; t >= 0; --t) {
+                const double xt = xr[t], dt = dr[t];
+                const double *h = hs + (size_t)(t + 1) * (size_t)N;
+                const double *hp = hs + (size_t)t * (size_t)N;
+                double ys = dskip * xt;
+                for (long n = 0; n < N; ++n) ys += Ct[t * N + n] * h[n];
+                double dys = dyr[t];
+                if (zr) {
+                    const double sg = sigmoid(zr[t]);
+                    dys = dyr[t] * zr[t] * sg;                                   /* ∂y/∂ys = silu(z) */
+                    dz[row * (size_t)L + (size_t)t] = dyr[t] * ys * sg * (1.0 + zr[t] * (1.0 - sg));
+                }
+                if (dD) dD[id] += dys * xt;
+                double gx = dys * dskip, gd = 0.0;
+                for (long n = 0; n < N; ++n) {
+                    double abar, beta;
+                    oracle_zoh(dt, a[n], &abar, &beta);
+                    const double ln = dys * Ct[t * N + n] + lam[n];             /* λ_t */
+                    const double dab = ln * hp[n];                              /* ∂L/∂Ā_t */
+                    const double dbe = ln * Bt[t * N + n] * xt;                 /* ∂L/∂β_t */
+                    dC[((size_t)ib * (size_t)L + (size_t)t) * (size_t)N + (size_t)n] += dys * h[n];
+                    dB[((size_t)ib * (size_t)L + (size_t)t) * (size_t)N + (size_t)n] += ln * beta * xt;
+                    gx += ln * beta * Bt[t * N + n];
+                    gd += dab * a[n] * abar + dbe * abar;
+                    dA[(size_t)id * (size_t)N + (size_t)n] += dab * dt * abar + dbe * dbeta_da(dt, a[n], abar, beta);
+                    lam[n] = abar * ln;
+                }
+                dx[row * (size_t)L + (size_t)t] = gx;
+                ddelta[row * (size_t)L + (size_t)t] = gd;
+            }
+            if (dh0)
+                for (long n = 0; n < N; ++n) dh0[row * (size_t)N + (size_t)n] = lam[n];
+        }
+    }
+    free(hs);
+    free(lam);
     return 0;
 }

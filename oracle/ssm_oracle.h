@@ -52,6 +52,17 @@ int oracle_scan_step(double *state, const double *x, const double *delta, const 
                      const double *B, const double *C, const double *D, const double *z,
                      double *y, long b, long d, long N);
 
+/* Gradients of oracle_scan_fwd for an upstream gradient dy [b][d][L] (and, optionally, a
+ * gradient dh_final [b][d][N] on the final state). Outputs: dx, ddelta, dz [b][d][L]; dA [d][N];
+ * dB, dC [b][L][N]; dD [d]; dh0 [b][d][N] (gradient on the initial state). D, z, h0, dh_final, dD,
+ * dh0 may be NULL (dz is required when z is given). Forward states are recomputed.
+ * Returns 0 or -1. */
+int oracle_scan_bwd(const double *x, const double *delta, const double *A, const double *B,
+                    const double *C, const double *D, const double *z, const double *h0,
+                    const double *dy, const double *dh_final, double *dx, double *ddelta,
+                    double *dA, double *dB, double *dC, double *dD, double *dz, double *dh0,
+                    long b, long d, long L, long N);
+
 /* ZOH coefficients of one diagonal entry: *abar = exp(delta·a), *bcoef = (exp(delta·a) − 1)/a
  * (delta at a = 0), so that B̄ = bcoef · B. */
 void oracle_zoh(double delta, double a, double *abar, double *bcoef);

@@ -281,6 +281,90 @@ def pin_linearity(orc):
     _close(y12, 2.0 * y1 - 0.5 * y2, rtol=1e-10, atol=1e-12, what="linearity in x")
 
 
+# ---------------------------------------------------------------------------------------------
+# Gradients: the backward oracle against finite differences of the (pinned) forward oracle, and
+# closed forms. The pages define only the forward map; its derivatives are fixed by it.
+# ---------------------------------------------------------------------------------------------
+def _loss(orc, inp, dy, dhf):
+    y, h = orc.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp.get("D"), z=inp.get("z"),
+                        h0=inp.get("h0"))
+    return float(np.sum(dy * y) + np.sum(dhf * h))
+
+
+def _fd_check(orc, inp, dy, dhf, names, rtol=2e-6, atol=1e-8, only=None):
+    g = orc.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp.get("D"), z=inp.get("z"),
+                     h0=inp.get("h0"), dy=dy, dh_final=dhf)
+    key = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz", "h0": "dh0"}
+    for name in names:
+        arr = inp[name]
+        num = np.zeros_like(arr)
+        idx_list = list(np.ndindex(arr.shape)) if only is None or name not in only else only[name]
+        for idx in idx_list:
+            v = arr[idx]
+            eps = 1e-6 * max(1.0, abs(v))
+            arr[idx] = v + eps
+            lp = _loss(orc, inp, dy, dhf)
+            arr[idx] = v - eps
+            lm = _loss(orc, inp, dy, dhf)
+            arr[idx] = v
+            num[idx] = (lp - lm) / (2 * eps)
+        got = g[key[name]]
+        sel = tuple(np.array(idx_list).T) if idx_list else ()
+        _close(got[sel], num[sel], rtol=rtol, atol=atol, what=f"d{name} vs finite differences")
+    return g
+
+
+def pin_bwd_finite_differences(orc):
+    """Every gradient (x, Δ, A, B, C, D, z, initial state) of L = Σ dy·y + Σ dh·h_final against
+    central differences of the forward oracle, on a small gated problem."""
+    rng = _rng(31)
+    b, d, L, N = 2, 3, 9, 4
+    inp = {"x": rng.normal(size=(b, d, L)), "delta": rng.uniform(0.05, 1.2, size=(b, d, L)),
+           "A": -rng.uniform(0.2, 2.5, size=(d, N)), "B": rng.normal(size=(b, L, N)),
+           "C": rng.normal(size=(b, L, N)), "D": rng.normal(size=d), "z": rng.normal(size=(b, d, L)),
+           "h0": rng.normal(size=(b, d, N)) * 0.5}
+    dy = rng.normal(size=(b, d, L))
+    dhf = rng.normal(size=(b, d, N))
+    _fd_check(orc, inp, dy, dhf, ["x", "delta", "A", "B", "C", "D", "z", "h0"])
+
+
+def pin_bwd_small_and_zero_A(orc):
+    """The A derivative where A = 0 (the ZOH limit, ∂β/∂a → Δ²/2) and where |Δ·A| is tiny (the
+    series branch), against central differences; no gate."""
+    rng = _rng(37)
+    b, d, L, N = 1, 2, 7, 4
+    A = -rng.uniform(0.2, 2.0, size=(d, N))
+    A[0, 1] = 0.0
+    A[1, 2] = -3e-4
+    A[1, 0] = 2e-3
+    inp = {"x": rng.normal(size=(b, d, L)), "delta": rng.uniform(0.1, 1.5, size=(b, d, L)), "A": A,
+           "B": rng.normal(size=(b, L, N)), "C": rng.normal(size=(b, L, N)), "D": rng.normal(size=d)}
+    dy = rng.normal(size=(b, d, L))
+    dhf = np.zeros((b, d, N))
+    _fd_check(orc, inp, dy, dhf, ["A", "delta", "x"], rtol=5e-6, atol=1e-8)
+
+
+def pin_bwd_impulse_closed_form(orc):
+    """Scalar LTI impulse (x = δ_0, B = C = 1, D = 0, constant Δ): y_T = β Ā^T, so
+    ∂y_T/∂x_0 = β Ā^T, ∂y_T/∂a = β'(a) Ā^T + β T Δ Ā^T, ∂y_T/∂Δ_0 = Ā·Ā^T, ∂y_T/∂Δ_t = β a Ā^T (t ≥ 1)."""
+    a, dl, T, L = -0.7, 0.4, 5, 8
+    x = np.zeros((1, 1, L)); x[0, 0, 0] = 1.0
+    delta = np.full((1, 1, L), dl)
+    A = np.array([[a]]); B = np.ones((1, L, 1)); C = np.ones((1, L, 1))
+    dy = np.zeros((1, 1, L)); dy[0, 0, T] = 1.0
+    g = orc.scan_bwd(x, delta, A, B, C, dy=dy)
+    ab = math.exp(dl * a)
+    beta = math.expm1(dl * a) / a
+    dbeta = (dl * ab - beta) / a
+    _close(g["dx"][0, 0, 0], beta * ab ** T, what="dx_0")
+    _close(g["dA"][0, 0], dbeta * ab ** T + beta * T * dl * ab ** T, what="dA")
+    _close(g["ddelta"][0, 0, 0], ab * ab ** T, what="dΔ_0")
+    for t in range(1, T + 1):
+        _close(g["ddelta"][0, 0, t], beta * a * ab ** T, what=f"dΔ_{t}")
+    for t in range(T + 1, L):
+        _close(g["ddelta"][0, 0, t], 0.0, what=f"dΔ_{t} after the observed step")
+
+
 ALL_PINS = [
     pin_scalar_worked_example,
     pin_delta_gate,
@@ -294,4 +378,7 @@ ALL_PINS = [
     pin_prefill_equals_decode,
     pin_skip_and_gate,
     pin_linearity,
+    pin_bwd_finite_differences,
+    pin_bwd_small_and_zero_A,
+    pin_bwd_impulse_closed_form,
 ]

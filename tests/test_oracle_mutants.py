@@ -33,6 +33,17 @@ MUTANTS = {
     "B_batch0": ("B + (size_t)ib * (size_t)L * (size_t)N, C", "B, C"),
     "ignore_h0": ("hrow[n] = h0 ? h0[row * (size_t)N + (size_t)n] : 0.0;", "hrow[n] = 0.0;"),
     "gate_on_skip_only": ("if (z) yt *= silu(z[t]);", "if (z) yt = acc + dskip * xt * silu(z[t]);"),
+    # gradients
+    "bwd_state_after_step": ("const double dab = ln * hp[n];", "const double dab = ln * h[n];"),
+    "bwd_no_adjoint_decay": ("lam[n] = abar * ln;", "lam[n] = ln;"),
+    "bwd_dbeta_da_sign": ("return (delta * abar - beta) / a;", "return (delta * abar + beta) / a;"),
+    "bwd_series_coefficient": ("term = (double)(k + 1) * vk / fact;", "term = vk / fact;"),
+    "bwd_silu_derivative": ("(1.0 + zr[t] * (1.0 - sg))", "(1.0 + zr[t] * sg)"),
+    "bwd_ddelta_drops_beta": ("gd += dab * a[n] * abar + dbe * abar;", "gd += dab * a[n] * abar;"),
+    "bwd_dB_drops_x": ("+= ln * beta * xt;", "+= ln * beta;"),
+    "bwd_dD_ungated": ("if (dD) dD[id] += dys * xt;", "if (dD) dD[id] += dyr[t] * xt;"),
+    "bwd_dC_old_state": ("+= dys * h[n];", "+= dys * hp[n];"),
+    "bwd_dh0_undecayed": ("dh0[row * (size_t)N + (size_t)n] = lam[n];", "dh0[row * (size_t)N + (size_t)n] = lam[n] * 0.5;"),
 }
 
 
