@@ -103,6 +103,34 @@ SSM_API ssm_status_t ssm_scan_step(float *state, const void *x, const void *delt
                            int64_t b, int64_t d, int64_t N, ssm_dtype_t dtype, hipStream_t stream);
 
 /*
+ * Gradients of the prefill scan (ssm_scan_fwd with an optional initial state) for an upstream
+ * gradient dy on y and, optionally, d_final_state on the final state. The forward map is the one
+ * ssm_scan_fwd computes (page "Mambaとは？Transformer以外の系列モデル", section 状態空間モデルを一つの
+ * 式から理解する); its derivatives follow by the chain rule in reverse time, and the forward states are
+ * recomputed rather than stored (same page, section hardware-awareとは memory trafficまで設計すること).
+ *   inputs            as for ssm_scan_fwd (x, delta, A, B, C, D, z), initial_state [b][d][N] fp32
+ *                     or NULL (zeros)
+ *   dy                [b][d][L] dtype, required
+ *   d_final_state     [b][d][N] fp32 or NULL (zeros)
+ *   dx, ddelta        [b][d][L] dtype, required outputs
+ *   dz                [b][d][L] dtype; required when z is given, ignored otherwise
+ *   dA                [d][N] fp32, required (summed over b and t)
+ *   dB, dC            [b][L][N] fp32, required (summed over d)
+ *   dD                [d] fp32 or NULL (summed over b and t; defined also when D is NULL)
+ *   d_initial_state   [b][d][N] fp32 or NULL
+ * The sums dA, dB, dC, dD are accumulated with float atomics, so their last bits can differ from
+ * run to run; everything else is deterministic. Scratch (checkpoints every 64/states_per_lane steps
+ * and the segment aggregates) is taken stream-ordered from `stream` and returned. Outputs may not
+ * overlap inputs or each other. b, d, N >= 1, L >= 1, N <= SSM_MAX_N. Errors as for ssm_scan_fwd.
+ */
+SSM_API ssm_status_t ssm_scan_bwd(const void *x, const void *delta, const float *A, const void *B,
+                                  const void *C, const float *D, const void *z,
+                                  const float *initial_state, const void *dy, const float *d_final_state,
+                                  void *dx, void *ddelta, float *dA, float *dB, float *dC, float *dD,
+                                  void *dz, float *d_initial_state, int64_t b, int64_t d, int64_t L,
+                                  int64_t N, ssm_dtype_t dtype, hipStream_t stream);
+
+/*
  * Options of ssm_scan_fwd_ex. Zero-initialise, then set what you need; zero means "choose".
  *   seg_len            time-segment length (multiple of 32) carried across by the chunk-carry
  *                      pass; 0 = chosen from the shape, >= L = one segment

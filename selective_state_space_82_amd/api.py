@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_fwd_plan.restype = i32
     L.ssm_scan_step.argtypes = [vp] * 9 + [i64, i64, i64, i32, vp]
     L.ssm_scan_step.restype = i32
+    L.ssm_scan_bwd.argtypes = [vp] * 18 + [i64, i64, i64, i64, i32, vp]
+    L.ssm_scan_bwd.restype = i32
     L.ssm_status_string.argtypes = [i32]
     L.ssm_status_string.restype = ctypes.c_char_p
     L.ssm_abi_version.argtypes = []
@@ -190,6 +192,43 @@ def ssm_scan_step(state, x, delta, A, B, C, D=None, z=None, *, y=None):
                                  _ptr(y), b, d, N, code, _stream(dev))
     _raise(status, "ssm_scan_step")
     return y
+
+
+def ssm_scan_bwd(x, delta, A, B, C, D=None, z=None, *, dy, initial_state=None, d_final_state=None,
+                 want_dD=True, want_d_initial_state=True) -> dict:
+    """Gradients of ssm_scan_fwd for an upstream gradient dy [b, d, L] (and optionally d_final_state
+    [b, d, N]). Returns a dict: dx, ddelta, dz ([b, d, L], storage dtype; dz None without z),
+    dA [d, N], dB, dC [b, L, N], dD [d] (None unless want_dD), d_initial_state [b, d, N] (None unless
+    want_d_initial_state), all fp32 except the first three."""
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be [b, d, L] and A [d, N]")
+    b, d, L = x.shape
+    N = A.shape[1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a ROCm GPU")
+    st = x.dtype
+    code = _dtype_code(st)
+    for name, t, shape, dt in (("delta", delta, (b, d, L), st), ("A", A, (d, N), torch.float32),
+                               ("B", B, (b, L, N), st), ("C", C, (b, L, N), st), ("D", D, (d,), torch.float32),
+                               ("z", z, (b, d, L), st), ("dy", dy, (b, d, L), st),
+                               ("initial_state", initial_state, (b, d, N), torch.float32),
+                               ("d_final_state", d_final_state, (b, d, N), torch.float32)):
+        _check(name, t, shape, dt, dev)
+    f32 = torch.float32
+    out = {"dx": torch.empty((b, d, L), dtype=st, device=dev), "ddelta": torch.empty((b, d, L), dtype=st, device=dev),
+           "dz": None if z is None else torch.empty((b, d, L), dtype=st, device=dev),
+           "dA": torch.empty((d, N), dtype=f32, device=dev), "dB": torch.empty((b, L, N), dtype=f32, device=dev),
+           "dC": torch.empty((b, L, N), dtype=f32, device=dev),
+           "dD": torch.empty((d,), dtype=f32, device=dev) if want_dD else None,
+           "d_initial_state": torch.empty((b, d, N), dtype=f32, device=dev) if want_d_initial_state else None}
+    status = lib().ssm_scan_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                _ptr(initial_state), _ptr(dy), _ptr(d_final_state), _ptr(out["dx"]),
+                                _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+                                _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["d_initial_state"]), b, d, L, N, code,
+                                _stream(dev))
+    _raise(status, "ssm_scan_bwd")
+    return out
 
 
 def ssm_scan_fwd_plan(b, d, L, N, dtype=torch.float32, seg_len=0, lanes_per_channel=0) -> dict:

@@ -201,6 +201,51 @@ ssm_status_t fwd_impl(const void *x, const void *delta, const float *A, const vo
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+ssm_status_t bwd_impl(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                      const float *D, const void *z, const float *initial_state, const void *dy,
+                      const float *d_final_state, void *dx, void *ddelta, float *dA, float *dB, float *dC,
+                      float *dD, void *dz, float *d_initial_state, int64_t b, int64_t d, int64_t L, int64_t N,
+                      ssm_dtype_t dtype, hipStream_t stream) {
+    ssm_status_t st = check_fwd_sizes(b, d, L, N, dtype);
+    if (st != SSM_OK) return st;
+    if (L < 1) return SSM_ERR_SHAPE;
+    if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC) return SSM_ERR_NULL;
+    if (z && !dz) return SSM_ERR_NULL;
+    if (!z) dz = nullptr;
+    const int64_t es = dtype == SSM_BF16 ? 2 : 4;
+    const int64_t bdl = b * d * L, bln = b * L * N, bdn = b * d * N;
+    const Span outs[] = {{dx, bdl * es}, {ddelta, bdl * es}, {dz, bdl * es}, {dA, d * N * 4},
+                         {dB, bln * 4}, {dC, bln * 4}, {dD, d * 4}, {d_initial_state, bdn * 4}};
+    const Span ins[] = {{x, bdl * es}, {delta, bdl * es}, {z, bdl * es}, {B, bln * es}, {C, bln * es},
+                        {A, d * N * 4}, {D, d * 4}, {initial_state, bdn * 4}, {dy, bdl * es},
+                        {d_final_state, bdn * 4}};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const Span &s : ins)
+            if (overlaps(outs[i], s)) return SSM_ERR_ALIAS;
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+            if (overlaps(outs[i], outs[j])) return SSM_ERR_ALIAS;
+    }
+    Plan pl{};
+    st = make_plan(b, d, L, N, nullptr, cu_count(), &pl);
+    if (st != SSM_OK) return st;
+    ssm::BwdLaunch p{};
+    p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.init_state = initial_state;
+    p.dy = dy; p.d_final_state = d_final_state; p.dx = dx; p.ddelta = ddelta; p.dz = dz;
+    p.dA = dA; p.dB = dB; p.dC = dC; p.dD = dD; p.d_init_state = d_initial_state;
+    p.b = b; p.d = d; p.L = L; p.N = N; p.bf16 = dtype == SSM_BF16;
+    p.lanes_per_channel = pl.lanes; p.states_per_lane = pl.npl; p.seg_len = pl.seg_len; p.n_seg = pl.n_seg;
+    int64_t floats = 0;
+    if (!mul_ok(b * d, L, &floats)) return SSM_ERR_SHAPE;
+    floats = ssm::bwd_scratch_floats(pl.n_seg, b, d, L, N, pl.npl);
+    void *scratch = nullptr;
+    keep_pool_memory();
+    if (hipMallocAsync(&scratch, (size_t)floats * sizeof(float), stream) != hipSuccess) return SSM_ERR_HIP;
+    p.scratch = static_cast<float *>(scratch);
+    const hipError_t e = ssm::launch_scan_bwd(p, stream);
+    if (hipFreeAsync(scratch, stream) != hipSuccess) return SSM_ERR_HIP;
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -251,6 +296,15 @@ ssm_status_t ssm_scan_fwd_plan(int64_t b, int64_t d, int64_t L, int64_t N, ssm_d
     plan->groups_aggregate_pass = pl.groups_agg;
     plan->scratch_bytes = pl.scratch_bytes;
     return SSM_OK;
+}
+
+ssm_status_t ssm_scan_bwd(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                          const float *D, const void *z, const float *initial_state, const void *dy,
+                          const float *d_final_state, void *dx, void *ddelta, float *dA, float *dB, float *dC,
+                          float *dD, void *dz, float *d_initial_state, int64_t b, int64_t d, int64_t L, int64_t N,
+                          ssm_dtype_t dtype, hipStream_t stream) {
+    return bwd_impl(x, delta, A, B, C, D, z, initial_state, dy, d_final_state, dx, ddelta, dA, dB, dC, dD, dz,
+                    d_initial_state, b, d, L, N, dtype, stream);
 }
 
 ssm_status_t ssm_scan_step(float *state, const void *x, const void *delta, const float *A, const void *B,

@@ -24,7 +24,32 @@ struct FwdLaunch {
     int n_seg;                // ceil(L / seg_len) >= 1
     float *scratch;           // scratch_floats(n_seg, b, d, N) floats
     hipEvent_t ev_begin, ev_end;
+    float *ckpt;              // optional: states entering every ck_len-th step, [b][d][ceil(L/ck_len)][N]
+    int ck_len;               // 64 / states_per_lane when ckpt is set
 };
+
+// Everything the gradient launcher needs (validated by the ABI layer).
+struct BwdLaunch {
+    const void *x, *delta;
+    const float *A;
+    const void *B, *C;
+    const float *D;
+    const void *z;
+    const float *init_state;     // nullable
+    const void *dy;
+    const float *d_final_state;  // nullable
+    void *dx, *ddelta, *dz;      // dz nullable (required when z is given)
+    float *dA, *dB, *dC, *dD;    // dD nullable
+    float *d_init_state;         // nullable
+    int64_t b, d, L, N;
+    bool bf16;
+    int lanes_per_channel, states_per_lane;
+    int64_t seg_len;
+    int n_seg;
+    float *scratch;              // bwd_scratch_floats(...) floats
+};
+
+hipError_t launch_scan_bwd(const BwdLaunch &p, hipStream_t stream);
 
 struct StepLaunch {
     float *state;
@@ -50,6 +75,14 @@ constexpr int kFoldMaxSeg = 16; // up to this many segments the output pass chai
 inline int64_t scratch_floats(int64_t n_seg, int64_t b, int64_t d, int64_t N) {
     if (n_seg <= 1) return 0;
     return (n_seg > kFoldMaxSeg ? 3 : 2) * (n_seg - 1) * b * d * N;
+}
+
+// Gradient pass: checkpoint interval (steps whose states fit one lane's registers) and scratch:
+// the forward pass's scratch, the checkpoints, and the reverse aggregates (Π Ā, adjoint from zero).
+inline int ckpt_len(int states_per_lane) { return 64 / states_per_lane; }
+inline int64_t bwd_scratch_floats(int64_t n_seg, int64_t b, int64_t d, int64_t L, int64_t N, int npl) {
+    const int64_t ck = ckpt_len(npl);
+    return scratch_floats(n_seg, b, d, N) + b * d * ((L + ck - 1) / ck) * N + 2 * (n_seg - 1) * b * d * N;
 }
 
 }  // namespace ssm

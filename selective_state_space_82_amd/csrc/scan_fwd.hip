@@ -39,6 +39,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "tile_common.h"
 
 namespace ssm {
 namespace {
@@ -66,85 +67,10 @@ struct FwdArgs {
     int vec_rows;             // x/Δ/z/y rows allow 16-byte accesses at every tile
     int vec_bc;               // B/C tile runs allow 16-byte loads
     int vec_state;            // state rows allow 16-byte accesses (N % 4 == 0, aligned)
+    float *ckpt;              // output pass: state entering every ck_len-th step [b][d][n_ck][N], or null
+    int64_t n_ck;             // ceil(L / ck_len)
+    int ck_len;               // 4, 8 or 16 (divides both tile lengths)
 };
-
-template <typename T> struct Chunk;  // 16 bytes of a row or run
-template <> struct Chunk<float> { static constexpr int kElems = 4; };
-template <> struct Chunk<uint16_t> { static constexpr int kElems = 8; };
-
-// Widen one 16-byte chunk into `E` floats at dst (LDS).
-template <typename T>
-__device__ __forceinline__ void put_chunk(float *dst, const uint4 &v);
-template <>
-__device__ __forceinline__ void put_chunk<float>(float *dst, const uint4 &v) {
-    *reinterpret_cast<float4 *>(dst) =
-        make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
-}
-template <>
-__device__ __forceinline__ void put_chunk<uint16_t>(float *dst, const uint4 &v) {
-    *reinterpret_cast<float4 *>(dst) = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
-    *reinterpret_cast<float4 *>(dst + 4) = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
-}
-
-// Widen one 16-byte chunk into `E` floats in registers.
-template <typename T>
-__device__ __forceinline__ void chunk_to_regs(float *dst, const uint4 &v);
-template <>
-__device__ __forceinline__ void chunk_to_regs<float>(float *dst, const uint4 &v) {
-    dst[0] = __uint_as_float(v.x); dst[1] = __uint_as_float(v.y);
-    dst[2] = __uint_as_float(v.z); dst[3] = __uint_as_float(v.w);
-}
-template <>
-__device__ __forceinline__ void chunk_to_regs<uint16_t>(float *dst, const uint4 &v) {
-    dst[0] = bf16_lo(v.x); dst[1] = bf16_hi(v.x); dst[2] = bf16_lo(v.y); dst[3] = bf16_hi(v.y);
-    dst[4] = bf16_lo(v.z); dst[5] = bf16_hi(v.z); dst[6] = bf16_lo(v.w); dst[7] = bf16_hi(v.w);
-}
-
-// Load one chunk (E consecutive elements of a row or run starting at element t) with bounds;
-// elements at or past `t_end` read as 0.
-template <typename T>
-__device__ __forceinline__ uint4 get_chunk(const T *__restrict__ row, int64_t t, int64_t t_end, bool row_ok,
-                                           bool vec) {
-    constexpr int E = Chunk<T>::kElems;
-    uint4 r = make_uint4(0u, 0u, 0u, 0u);
-    if (!row_ok) return r;
-    if (vec && t + E <= t_end) return *reinterpret_cast<const uint4 *>(row + t);
-    T tmp[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) tmp[e] = (t + e < t_end) ? row[t + e] : T(0);
-    __builtin_memcpy(&r, tmp, sizeof(r));
-    return r;
-}
-
-// p[ok ? i : 0] with the load issued unconditionally (a guarded load would become a branch
-// with a wait behind it), then `fallback` where !ok. p[0] must be readable.
-__device__ __forceinline__ float load_or(const float *p, int64_t i, bool ok, float fallback) {
-    const float v = p[ok ? i : 0];
-    return ok ? v : fallback;
-}
-
-// U consecutive floats from LDS (U = 1, 2 or 4).
-template <int U>
-__device__ __forceinline__ void lds_get(const float *p, float (&o)[U]) {
-    if constexpr (U == 4) {
-        const float4 v = *reinterpret_cast<const float4 *>(p);
-        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
-    } else if constexpr (U == 2) {
-        const float2 v = *reinterpret_cast<const float2 *>(p);
-        o[0] = v.x; o[1] = v.y;
-    } else {
-        o[0] = *p;
-    }
-}
-
-// Orders this wave's LDS accesses around a hand-off between its lanes (tile stores -> scan
-// reads, partial sums -> transposed reads, outputs -> line stores). One wave's LDS operations
-// execute in order, so this only fences the compiler; it emits no wait.
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // The kernel ---------------------------------------------------------------------------------
 //
@@ -438,7 +364,26 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
             ywin[col] = narrow<T>(v);
         }
     };
+    // the state entering global step k * ck_len (unscaled), for the gradient pass to restart from
+    auto store_ckpt = [&](int64_t k) {
+        if (!ch_ok) return;
+        float *dst = a.ckpt + (row * a.n_ck + k) * a.N + n0;
+#pragma unroll
+        for (int j = 0; j < NPL; j += 4) {
+            float hv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hv[q] = SAFE ? s[j + q] : s[j + q] * ia[j + q];
+            if (a.vec_state && j + 4 <= nvalid) {
+                *reinterpret_cast<float4 *>(dst + j) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (j + q < nvalid) dst[j + q] = hv[q];
+            }
+        }
+    };
     auto scan_tile = [&](int it) {
+        const int64_t t0tile = t_begin + (int64_t)it * kTile;
         T *const ywin = ybuf + c * kYPitch + (it & 1) * kTile + g;
         float p[kGrp], r[kGrp];
         // Operands are read from LDS one step ahead of their use: across the whole tile (fp32
@@ -452,6 +397,9 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
         constexpr int kUnroll = AGG ? 1 : kTile / kGrp;
 #pragma unroll kUnroll
         for (int t = 0; t < kTile; t += kGrp) {
+            if constexpr (!AGG) {
+                if (a.ckpt && t % a.ck_len == 0 && t0tile + t < t_end) store_ckpt((t0tile + t) / a.ck_len);
+            }
             if constexpr (kGroupLocal) load_sub(t, sb[0]);
 #pragma unroll
             for (int k = 0; k < kGrp; ++k) {
@@ -487,7 +435,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
             const int64_t t0 = t_begin + (int64_t)it * kTile;
             scan_tile(it);
             if constexpr (!AGG) {
-                if ((it & 1) || it + 1 == ntiles) {  // the output window is complete
+                if (yg && ((it & 1) || it + 1 == ntiles)) {  // the output window is complete
                     const int64_t tw0 = t0 - (it & 1) * kTile;
                     const int64_t left = t_end - tw0;
                     wave_sync();
@@ -625,7 +573,10 @@ hipError_t launch_scan_fwd(const FwdLaunch &p, hipStream_t stream) {
                  aligned16(p.y);
     // a tile's B/C run starts at element (bi*L + t0)*N with t0 a multiple of the tile length
     a.vec_bc = ((p.L * p.N * esize) % 16 == 0) && aligned16(p.B) && aligned16(p.C);
-    a.vec_state = (p.N % 4 == 0) && aligned16(p.init_state) && aligned16(p.scratch);
+    a.vec_state = (p.N % 4 == 0) && aligned16(p.init_state) && aligned16(p.scratch) && aligned16(p.ckpt);
+    a.ckpt = p.ckpt;
+    a.ck_len = p.ck_len;
+    a.n_ck = p.ck_len > 0 ? (p.L + p.ck_len - 1) / p.ck_len : 0;
     if (p.n_seg > 1) {
         const int64_t per = (int64_t)(p.n_seg - 1) * p.b * p.d * p.N;
         a.agg_P = p.scratch;

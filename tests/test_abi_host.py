@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("ssm_scan_fwd", "ssm_scan_step", "ssm_scan_fwd_ex", "ssm_scan_fwd_plan",
+    for required in ("ssm_scan_fwd", "ssm_scan_step", "ssm_scan_fwd_ex", "ssm_scan_fwd_plan", "ssm_scan_bwd",
                      "ssm_status_string", "ssm_abi_version"):
         assert required in names
 
@@ -111,3 +111,23 @@ def test_plan_shapes():
     assert api.ssm_scan_fwd_plan(1, 2048, 131072, 16, torch.bfloat16)["n_segments"] == 64
     p = api.ssm_scan_fwd_plan(2, 100, 64, 64)
     assert p["lanes_per_channel"] == 4 and p["states_per_lane"] == 16
+
+
+def test_bwd_validation():
+    """The gradient entry point checks its arguments on the host and launches nothing on error."""
+    L = api.lib()
+    out = [ctypes.c_void_p(0x900000 + i * 0x100000) for i in range(8)]
+
+    def bwd(x=FAKE, dy=ctypes.c_void_p(0x800000), dx=out[0], dz=None, z=None, b=1, d=4, Ln=16, N=4, dt=0, dA=out[3]):
+        return L.ssm_scan_bwd(x, FAKE, FAKE, FAKE, FAKE, None, z, None, dy, None, dx, out[1], dA, out[4], out[5],
+                              None, dz, None, b, d, Ln, N, dt, None)
+    assert bwd(x=None) == 1
+    assert bwd(dy=None) == 1
+    assert bwd(dx=None) == 1
+    assert bwd(dA=None) == 1
+    assert bwd(z=ctypes.c_void_p(0x700000)) == 1  # z without dz
+    assert bwd(Ln=0) == 2
+    assert bwd(N=65) == 3
+    assert bwd(dt=9) == 3
+    assert bwd(dx=FAKE) == 5                      # dx overlaps x
+    assert bwd(dx=out[1]) == 5                    # dx overlaps ddelta
