@@ -121,6 +121,61 @@ def bench_prefill(name, steps, warmup, rotate=0, quiet=False):
     return res, inp
 
 
+def grad_slots_per_element(N, gate):
+    """VALU issue slots of the gradient pass per (b, d, t): per state the forward recomputation
+    (Δ·A, exp (2), β, B·x, the update: 8) and the walk back (Ā, β again: 5; λ; ∂L/∂Ā; ∂L/∂β (2);
+    the dB and dC partials (3); the dx, dΔ and dA terms (2 + 2 + 5); the carried adjoint; the readout
+    for dz: 23), plus per element the gate and its derivative (12) and the skip terms (3)."""
+    return 31 * N + (15 if gate else 3)
+
+
+def bench_grad(name, steps, warmup, quiet=False):
+    """The gradient pass (ssm_scan_bwd) on a prefill workload: dy ~ N(0, 1) of y's shape."""
+    import torch
+    from selective_state_space_82_amd import api
+    from selective_state_space_82_amd import inputs as I
+
+    w = I.WORKLOADS[name]
+    inp = I.prefill_inputs(w)
+    esize = 4 if w.dtype == "f32" else 2
+    rows = w.b * w.d * w.L
+    # read x, Δ, z, dy, B, C, A, D; write dx, dΔ, dz, dA, dB, dC (fp32), dD
+    nbytes = rows * esize * (4 if w.gate else 3) + rows * esize * (3 if w.gate else 2) \
+        + 2 * w.b * w.L * w.N * esize + 2 * w.b * w.L * w.N * 4 + 2 * (w.d * w.N * 4 + w.d * 4)
+    rotate = int(min(4, max(1, -(-2 * MALL_BYTES // nbytes))))
+    rng = np.random.default_rng(5)
+    sets = []
+    for _ in range(rotate):
+        s = {k: to_dev(inp[k], "cuda") for k in ("x", "delta", "z", "A", "B", "C", "D")}
+        s["dy"] = to_dev(I.store(rng.standard_normal((w.b, w.d, w.L)), w.dtype), "cuda")
+        sets.append(s)
+
+    def call(i):
+        s = sets[i % rotate]
+        return api.ssm_scan_bwd(s["x"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], dy=s["dy"])
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    slots = rows * grad_slots_per_element(w.N, w.gate)
+    res = {"pass": "gradient", "workload": name, "ms_per_call": ms, "elements_per_s": rows / (ms * 1e-3),
+           "GBps": nbytes / (ms * 1e-3) / 1e9, "algorithmic_bytes": nbytes,
+           "valu_slots_per_element": grad_slots_per_element(w.N, w.gate),
+           "call_valu_Tslot_s": slots / (ms * 1e-3) / 1e12,
+           "call_valu_frac": slots / (ms * 1e-3) / 1e12 / VALU_PEAK_TSLOT}
+    if not quiet:
+        print(f"# gradient {name}: {ms * 1e3:.1f} us/call, {res['elements_per_s']:.3g} elements/s, "
+              f"{res['call_valu_Tslot_s']:.2f} T VALU slot/s over the whole call", file=sys.stderr, flush=True)
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_decode(name, rotate_states, quiet=False):
     """The decode workload: `steps` successive single-token steps, each with fresh inputs, on one
     state (rotate_states = 1, the literal workload) or cycling through several layer states."""
@@ -244,8 +299,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--extra", default="decode,mamba1p4b_bf16_b8_d4096_L4096_N16",
-                    help="comma list: 'decode' and/or prefill workload names ('' for none, 'all' for every one)")
+    ap.add_argument("--extra", default="decode,mamba1p4b_bf16_b8_d4096_L4096_N16,grad",
+                    help="comma list: 'decode', 'grad' (gradient pass on the workload) and/or prefill workload names "
+                         "('' for none, 'all' for every one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=0, help="input/output sets to rotate (0 = enough to exceed the cache)")
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
@@ -278,6 +334,8 @@ def main():
         if n == "decode":
             for r in (1, 4):
                 extra.append(bench_decode(I.DECODE_WORKLOADS[0], r))
+        elif n == "grad":
+            extra.append(bench_grad(args.workload, max(3, args.steps // 5), 2))
         else:
             r, _ = bench_prefill(n, max(3, args.steps // 4), 2)
             extra.append(r)

@@ -119,7 +119,7 @@ SSM_API ssm_status_t ssm_scan_step(float *state, const void *x, const void *delt
  *   dD                [d] fp32 or NULL (summed over b and t; defined also when D is NULL)
  *   d_initial_state   [b][d][N] fp32 or NULL
  * The sums dA, dB, dC, dD are accumulated with float atomics, so their last bits can differ from
- * run to run; everything else is deterministic. Scratch (checkpoints every 64/states_per_lane steps
+ * run to run; everything else is deterministic. Scratch (checkpoints every max(4, 32/states_per_lane) steps
  * and the segment aggregates) is taken stream-ordered from `stream` and returned. Outputs may not
  * overlap inputs or each other. b, d, N >= 1, L >= 1, N <= SSM_MAX_N. Errors as for ssm_scan_fwd.
  */

@@ -79,7 +79,7 @@ inline int64_t scratch_floats(int64_t n_seg, int64_t b, int64_t d, int64_t N) {
 
 // Gradient pass: checkpoint interval (steps whose states fit one lane's registers) and scratch:
 // the forward pass's scratch, the checkpoints, and the reverse aggregates (Π Ā, adjoint from zero).
-inline int ckpt_len(int states_per_lane) { return 64 / states_per_lane; }
+inline int ckpt_len(int states_per_lane) { return (32 / states_per_lane) < 4 ? 4 : 32 / states_per_lane; }
 inline int64_t bwd_scratch_floats(int64_t n_seg, int64_t b, int64_t d, int64_t L, int64_t N, int npl) {
     const int64_t ck = ckpt_len(npl);
     return scratch_floats(n_seg, b, d, N) + b * d * ((L + ck - 1) / ck) * N + 2 * (n_seg - 1) * b * d * N;

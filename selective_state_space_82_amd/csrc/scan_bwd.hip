@@ -9,9 +9,9 @@
 //   dĀ_t = λ_t h_{t−1},  dβ_t = λ_t B_t x_t,  ∂Ā/∂Δ = aĀ, ∂Ā/∂a = ΔĀ, ∂β/∂Δ = Ā,
 //   ∂β/∂a = (ΔĀ − β)/a (Δ²/2 at a = 0).
 // The forward states are not stored: the same page's hardware-aware section recomputes them in the
-// backward pass. Here a forward pass leaves the state entering every K-th step (K = 64 / NPL, so K
-// states of a lane fit its registers); the gradient pass restarts from each checkpoint, recomputes
-// K steps forward, then walks them backward.
+// backward pass. Here a forward pass leaves the state entering every K-th step (K = 32 / NPL, at
+// least 4, so the K·NPL states of a chunk fit a lane's registers with two wavefronts per SIMD); the
+// gradient pass restarts from each checkpoint, recomputes K steps forward, then walks them backward.
 //
 // Mapping onto CDNA4 (as in the prefill kernel): one wavefront per unit = 64/G channels of one
 // batch row over one time segment, G lanes per channel with NPL states each.
@@ -62,12 +62,12 @@ __device__ __forceinline__ float dbeta_da(float dt, float u, float abar, float b
 
 // REV: reverse aggregate pass (no gradients; segments 1 .. S−1), else the gradient pass.
 template <typename T, int G, int NPL, bool REV>
-__global__ __launch_bounds__(kWave, 1) void scan_bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
     constexpr int E = Chunk<T>::kElems;
     constexpr int kPitch = kBT + 4;
     constexpr int CW = kWave / G;
     constexpr int NPAD = G * NPL;
-    constexpr int K = 64 / NPL;                          // steps per checkpoint chunk
+    constexpr int K = (32 / NPL) < 4 ? 4 : 32 / NPL;    // steps per checkpoint chunk
     constexpr int kRowChunks = kBT / E;                  // 16-byte chunks per row per tile
     constexpr int kXC = (CW * kRowChunks + kWave - 1) / kWave;
     constexpr int kBF = kBT * NPAD;
