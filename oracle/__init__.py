@@ -65,6 +65,8 @@ class Oracle:
         lib.oracle_scan_step.restype = ctypes.c_int
         lib.oracle_scan_bwd.argtypes = [_DP] * 18 + [L, L, L, L]
         lib.oracle_scan_bwd.restype = ctypes.c_int
+        lib.oracle_conv1d.argtypes = [_DP, _DP, _DP, _DP, ctypes.c_int, _DP, _DP, L, L, L, L]
+        lib.oracle_conv1d.restype = ctypes.c_int
         lib.oracle_zoh.argtypes = [ctypes.c_double, ctypes.c_double, _DP, _DP]
         lib.oracle_zoh.restype = None
         self.lib = lib
@@ -129,6 +131,23 @@ class Oracle:
             raise ValueError("oracle_scan_bwd rejected its arguments")
         return out
 
+    def conv1d(self, xin, w, bias=None, state=None, silu=True):
+        """Causal depthwise Conv1D (+ SiLU): returns (x [b, d, L], new_state [b, d, W-1])."""
+        xin = _f64(xin)
+        b, d, L = xin.shape
+        w = _f64(w)
+        W = w.shape[1]
+        w = _f64(w, (d, W))
+        bias = _f64(bias, (d,))
+        state = _f64(state, (b, d, W - 1))
+        x = np.empty((b, d, L))
+        st = np.empty((b, d, max(W - 1, 0)))
+        rc = self.lib.oracle_conv1d(_ptr(xin), _ptr(w), _ptr(bias), _ptr(state), int(bool(silu)), _ptr(x),
+                                    _ptr(st) if W > 1 else None, b, d, L, W)
+        if rc != 0:
+            raise ValueError("oracle_conv1d rejected its arguments")
+        return x, st
+
     def scan_step(self, state, x, delta, A, B, C, D=None, z=None):
         """Decode step: returns (y [b, d], new_state [b, d, N]); `state` itself is not modified."""
         st = np.array(_f64(state), dtype=np.float64, copy=True)
@@ -174,3 +193,7 @@ def scan_step(state, x, delta, A, B, C, D=None, z=None):
 
 def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_final=None):
     return default().scan_bwd(x, delta, A, B, C, D, z, h0, dy, dh_final)
+
+
+def conv1d(xin, w, bias=None, state=None, silu=True):
+    return default().conv1d(xin, w, bias, state, silu)

@@ -206,3 +206,37 @@ int oracle_scan_bwd(const double *x, const double *delta, const double *A, const
     free(lam);
     return 0;
 }
+
+/* ---------------------------------------------------------------------------------------------
+ * The short causal depthwise Conv1D that feeds the scan in a Mamba block, and its SiLU
+ * ("Mambaとは？…", section Mamba blockのarchitecture: the main branch mixes neighbouring tokens with a
+ * short causal Conv1D, then applies SiLU, then the selective SSM; section training、prefill、decode:
+ * in decode every layer keeps a Conv1D state next to the SSM state). Per channel d with taps
+ * w[d][0..W) and bias c_d:  u_t = c_d + Σ_{k<W} w[d][k] · xin_{t−(W−1)+k},  x_t = silu(u_t) (or u_t),
+ * where inputs before t = 0 come from the given state (the W−1 preceding inputs, oldest first) or are
+ * zero. The state left behind holds the last W−1 inputs of the extended sequence.
+ * ------------------------------------------------------------------------------------------- */
+int oracle_conv1d(const double *xin, const double *w, const double *bias, const double *state_in, int apply_silu,
+                  double *x_out, double *state_out, long b, long d, long L, long W) {
+    if (!xin || !w || !x_out || b < 0 || d < 0 || L < 0 || W < 1) return -1;
+    const long H = W - 1;
+    double *ext = (double *)malloc(sizeof(double) * (size_t)(L + H > 0 ? L + H : 1));
+    if (!ext) return -1;
+    for (long ib = 0; ib < b; ++ib) {
+        for (long id = 0; id < d; ++id) {
+            const size_t row = (size_t)ib * (size_t)d + (size_t)id;
+            /* the extended input: H values of history, then the L new ones */
+            for (long k = 0; k < H; ++k) ext[k] = state_in ? state_in[row * (size_t)H + (size_t)k] : 0.0;
+            for (long t = 0; t < L; ++t) ext[H + t] = xin[row * (size_t)L + (size_t)t];
+            for (long t = 0; t < L; ++t) {
+                double u = bias ? bias[id] : 0.0;
+                for (long k = 0; k < W; ++k) u += w[(size_t)id * (size_t)W + (size_t)k] * ext[t + k];
+                x_out[row * (size_t)L + (size_t)t] = apply_silu ? silu(u) : u;
+            }
+            if (state_out)
+                for (long k = 0; k < H; ++k) state_out[row * (size_t)H + (size_t)k] = ext[L + k];
+        }
+    }
+    free(ext);
+    return 0;
+}

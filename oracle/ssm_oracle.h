@@ -63,6 +63,12 @@ int oracle_scan_bwd(const double *x, const double *delta, const double *A, const
                     double *dA, double *dB, double *dC, double *dD, double *dz, double *dh0,
                     long b, long d, long L, long N);
 
+/* Causal depthwise Conv1D (+ SiLU when apply_silu) per (b, d) row: xin, x_out [b][d][L]; w [d][W];
+ * bias [d] or NULL; state_in / state_out [b][d][W−1] (the W−1 inputs before the sequence, oldest
+ * first / the last W−1 inputs after it) or NULL (zeros / not written). Returns 0 or -1. */
+int oracle_conv1d(const double *xin, const double *w, const double *bias, const double *state_in, int apply_silu,
+                  double *x_out, double *state_out, long b, long d, long L, long W);
+
 /* ZOH coefficients of one diagonal entry: *abar = exp(delta·a), *bcoef = (exp(delta·a) − 1)/a
  * (delta at a = 0), so that B̄ = bcoef · B. */
 void oracle_zoh(double delta, double a, double *abar, double *bcoef);

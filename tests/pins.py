@@ -365,6 +365,64 @@ def pin_bwd_impulse_closed_form(orc):
         _close(g["ddelta"][0, 0, t], 0.0, what=f"dΔ_{t} after the observed step")
 
 
+# ---------------------------------------------------------------------------------------------
+# The causal depthwise Conv1D + SiLU front end
+# ---------------------------------------------------------------------------------------------
+def pin_conv_identity_and_shift(orc):
+    """Taps (0, …, 0, 1) and no bias pass the input through (then silu); taps (0, …, 1, 0) delay it
+    by one step; a bias alone gives silu(bias) everywhere."""
+    rng = _rng(41)
+    b, d, L, W = 2, 3, 11, 4
+    xin = rng.normal(size=(b, d, L))
+    w = np.zeros((d, W)); w[:, -1] = 1.0
+    x, _ = orc.conv1d(xin, w, silu=False)
+    _close(x, xin, what="identity taps")
+    x, _ = orc.conv1d(xin, w, silu=True)
+    _close(x, silu_lib(xin), what="identity taps + silu")
+    w = np.zeros((d, W)); w[:, -2] = 1.0
+    x, _ = orc.conv1d(xin, w, silu=False)
+    _close(x[:, :, 1:], xin[:, :, :-1], what="one-step delay")
+    _close(x[:, :, 0], np.zeros((b, d)), what="nothing before the sequence")
+    bias = rng.normal(size=d)
+    x, _ = orc.conv1d(np.zeros((b, d, L)), np.zeros((d, W)), bias=bias)
+    _close(x, np.broadcast_to(silu_lib(bias)[None, :, None], (b, d, L)), what="bias only")
+
+
+def pin_conv_impulse_and_causality(orc):
+    """An impulse at t0 reads the taps back in reverse order (u_{t0+j} = w[W-1-j]); changing an input
+    never changes an earlier output (the convolution is causal)."""
+    rng = _rng(43)
+    d, L, W = 2, 12, 4
+    w = rng.normal(size=(d, W))
+    xin = np.zeros((1, d, L)); xin[0, :, 5] = 1.0
+    x, _ = orc.conv1d(xin, w, silu=False)
+    for j in range(W):
+        _close(x[0, :, 5 + j], w[:, W - 1 - j], what=f"impulse response lag {j}")
+    _close(x[0, :, :5], np.zeros((d, 5)), what="before the impulse")
+    _close(x[0, :, 5 + W:], np.zeros((d, L - 5 - W)), what="after the window")
+    xin = rng.normal(size=(1, d, L))
+    xin2 = xin.copy(); xin2[0, :, 7] += 3.0
+    x2, _ = orc.conv1d(xin2, w, bias=None)
+    x1b, _ = orc.conv1d(xin, w, bias=None)
+    _close(x2[:, :, :7], x1b[:, :, :7], what="causality")
+
+
+def pin_conv_state_chaining(orc):
+    """Decode keeps the last W-1 inputs: running the sequence in two calls, the second starting from
+    the first call's state, equals one call (kasblo page, section training、prefill、decode)."""
+    rng = _rng(47)
+    b, d, L, W = 2, 3, 10, 4
+    xin = rng.normal(size=(b, d, L)); w = rng.normal(size=(d, W)); bias = rng.normal(size=d)
+    st0 = rng.normal(size=(b, d, W - 1))
+    x, st = orc.conv1d(xin, w, bias, st0)
+    for cut in (1, 2, 6):
+        xa, sa = orc.conv1d(xin[:, :, :cut], w, bias, st0)
+        xb, sb = orc.conv1d(xin[:, :, cut:], w, bias, sa)
+        _close(np.concatenate([xa, xb], axis=2), x, what=f"chained at {cut}")
+        _close(sb, st, what=f"state chained at {cut}")
+    _close(st, xin[:, :, L - (W - 1):], what="state = last W-1 inputs")
+
+
 ALL_PINS = [
     pin_scalar_worked_example,
     pin_delta_gate,
@@ -381,4 +439,7 @@ ALL_PINS = [
     pin_bwd_finite_differences,
     pin_bwd_small_and_zero_A,
     pin_bwd_impulse_closed_form,
+    pin_conv_identity_and_shift,
+    pin_conv_impulse_and_causality,
+    pin_conv_state_chaining,
 ]

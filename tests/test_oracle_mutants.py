@@ -44,6 +44,15 @@ MUTANTS = {
     "bwd_dD_ungated": ("if (dD) dD[id] += dys * xt;", "if (dD) dD[id] += dyr[t] * xt;"),
     "bwd_dC_old_state": ("+= dys * h[n];", "+= dys * hp[n];"),
     "bwd_dh0_undecayed": ("dh0[row * (size_t)N + (size_t)n] = lam[n];", "dh0[row * (size_t)N + (size_t)n] = lam[n] * 0.5;"),
+    # causal conv1d
+    "conv_taps_reversed": ("u += w[(size_t)id * (size_t)W + (size_t)k] * ext[t + k];",
+                           "u += w[(size_t)id * (size_t)W + (size_t)(W - 1 - k)] * ext[t + k];"),
+    "conv_off_by_one": ("u += w[(size_t)id * (size_t)W + (size_t)k] * ext[t + k];",
+                        "u += w[(size_t)id * (size_t)W + (size_t)k] * ext[t + k + (t + k + 1 < L + H ? 1 : 0)];"),
+    "conv_state_ignored": ("ext[k] = state_in ? state_in[row * (size_t)H + (size_t)k] : 0.0;", "ext[k] = 0.0;"),
+    "conv_state_first_inputs": ("state_out[row * (size_t)H + (size_t)k] = ext[L + k];",
+                                "state_out[row * (size_t)H + (size_t)k] = ext[H + k];"),
+    "conv_bias_dropped": ("double u = bias ? bias[id] : 0.0;", "double u = 0.0;"),
 }
 
 
