@@ -131,6 +131,31 @@ SSM_API ssm_status_t ssm_scan_bwd(const void *x, const void *delta, const float 
                                   int64_t N, ssm_dtype_t dtype, hipStream_t stream);
 
 /*
+ * The short causal depthwise Conv1D (+ SiLU) of the Mamba block's main branch, which produces the
+ * scan's x (page "Mambaとは？Transformer以外の系列モデル", section Mamba blockのarchitecture), and its
+ * decode step with the per-layer Conv1D state (same page, section training、prefill、decodeでは計算の
+ * 姿が違う). Per channel d with taps w[d][0..W) and bias c_d:
+ *     u_t = c_d + Σ_{k<W} w[d][k] · xin_{t−(W−1)+k},   x_t = silu(u_t) if apply_silu, else u_t,
+ * the inputs before t = 0 taken from state_in (zeros when NULL).
+ *   xin, x_out        [b][d][L] dtype (x_out may not overlap xin)
+ *   w                 [d][W] fp32, 1 <= W <= SSM_MAX_CONV_W
+ *   bias              [d] fp32 or NULL
+ *   state_in          [b][d][W−1] fp32 or NULL: the W−1 inputs before the sequence, oldest first
+ *   state_out         [b][d][W−1] fp32 or NULL: the last W−1 inputs after it (may equal state_in)
+ * b, d >= 1, L >= 0. Errors as for ssm_scan_fwd.
+ */
+#define SSM_MAX_CONV_W 8
+SSM_API ssm_status_t ssm_conv1d_fwd(const void *xin, const float *w, const float *bias, const float *state_in,
+                                    void *x_out, float *state_out, int64_t b, int64_t d, int64_t L, int64_t W,
+                                    int32_t apply_silu, ssm_dtype_t dtype, hipStream_t stream);
+
+/* Decode: one new input per (b, d). state [b][d][W−1] fp32 is read and shifted in place (the new
+ * input enters last); xin, x_out [b][d] dtype. Other arguments as for ssm_conv1d_fwd. */
+SSM_API ssm_status_t ssm_conv1d_step(float *state, const void *xin, const float *w, const float *bias,
+                                     void *x_out, int64_t b, int64_t d, int64_t W, int32_t apply_silu,
+                                     ssm_dtype_t dtype, hipStream_t stream);
+
+/*
  * Options of ssm_scan_fwd_ex. Zero-initialise, then set what you need; zero means "choose".
  *   seg_len            time-segment length (multiple of 32) carried across by the chunk-carry
  *                      pass; 0 = chosen from the shape, >= L = one segment

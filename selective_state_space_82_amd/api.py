@@ -70,6 +70,10 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_step.restype = i32
     L.ssm_scan_bwd.argtypes = [vp] * 18 + [i64, i64, i64, i64, i32, vp]
     L.ssm_scan_bwd.restype = i32
+    L.ssm_conv1d_fwd.argtypes = [vp] * 6 + [i64, i64, i64, i64, i32, i32, vp]
+    L.ssm_conv1d_fwd.restype = i32
+    L.ssm_conv1d_step.argtypes = [vp] * 5 + [i64, i64, i64, i32, i32, vp]
+    L.ssm_conv1d_step.restype = i32
     L.ssm_status_string.argtypes = [i32]
     L.ssm_status_string.restype = ctypes.c_char_p
     L.ssm_abi_version.argtypes = []
@@ -229,6 +233,52 @@ def ssm_scan_bwd(x, delta, A, B, C, D=None, z=None, *, dy, initial_state=None, d
                                 _stream(dev))
     _raise(status, "ssm_scan_bwd")
     return out
+
+
+def ssm_conv1d_fwd(xin, w, bias=None, *, state_in=None, x_out=None, state_out=None, return_state=True,
+                   silu=True):
+    """Causal depthwise Conv1D (+ SiLU): xin [b, d, L] (float32 or bfloat16), w [d, W] fp32, bias [d] fp32.
+    Returns (x [b, d, L] in xin's dtype, state [b, d, W-1] fp32 or None)."""
+    if xin.dim() != 3 or w.dim() != 2:
+        raise ValueError("xin must be [b, d, L] and w [d, W]")
+    b, d, L = xin.shape
+    W = w.shape[1]
+    dev = xin.device
+    st = xin.dtype
+    code = _dtype_code(st)
+    _check("xin", xin, (b, d, L), st, dev)
+    _check("w", w, (d, W), torch.float32, dev)
+    _check("bias", bias, (d,), torch.float32, dev)
+    _check("state_in", state_in, (b, d, W - 1), torch.float32, dev)
+    if x_out is None:
+        x_out = torch.empty((b, d, L), dtype=st, device=dev)
+    _check("x_out", x_out, (b, d, L), st, dev)
+    if state_out is None and return_state and W > 1:
+        state_out = torch.empty((b, d, W - 1), dtype=torch.float32, device=dev)
+    _check("state_out", state_out, (b, d, W - 1), torch.float32, dev)
+    status = lib().ssm_conv1d_fwd(_ptr(xin), _ptr(w), _ptr(bias), _ptr(state_in), _ptr(x_out), _ptr(state_out),
+                                  b, d, L, W, int(bool(silu)), code, _stream(dev))
+    _raise(status, "ssm_conv1d_fwd")
+    return x_out, state_out
+
+
+def ssm_conv1d_step(state, xin, w, bias=None, *, x_out=None, silu=True):
+    """Decode step of the Conv1D: state [b, d, W-1] fp32 (shifted in place), xin [b, d]. Returns x [b, d]."""
+    b, d = xin.shape
+    W = w.shape[1]
+    dev = xin.device
+    st = xin.dtype
+    code = _dtype_code(st)
+    _check("state", state, (b, d, W - 1), torch.float32, dev)
+    _check("w", w, (d, W), torch.float32, dev)
+    _check("bias", bias, (d,), torch.float32, dev)
+    if x_out is None:
+        x_out = torch.empty((b, d), dtype=st, device=dev)
+    _check("x_out", x_out, (b, d), st, dev)
+    status = lib().ssm_conv1d_step(_ptr(state), _ptr(xin), _ptr(w), _ptr(bias), _ptr(x_out), b, d, W,
+                                   int(bool(silu)), code, _stream(dev))
+    _raise(status, "ssm_conv1d_step")
+    return x_out
 
 
 def ssm_scan_fwd_plan(b, d, L, N, dtype=torch.float32, seg_len=0, lanes_per_channel=0) -> dict:

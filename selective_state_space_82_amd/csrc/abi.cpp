@@ -307,6 +307,51 @@ ssm_status_t ssm_scan_bwd(const void *x, const void *delta, const float *A, cons
                     d_initial_state, b, d, L, N, dtype, stream);
 }
 
+ssm_status_t ssm_conv1d_fwd(const void *xin, const float *w, const float *bias, const float *state_in, void *x_out,
+                            float *state_out, int64_t b, int64_t d, int64_t L, int64_t W, int32_t apply_silu,
+                            ssm_dtype_t dtype, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return SSM_ERR_UNSUPPORTED;
+    if (b < 1 || d < 1 || L < 0 || W < 1) return SSM_ERR_SHAPE;
+    if (W > SSM_MAX_CONV_W) return SSM_ERR_UNSUPPORTED;
+    int64_t bdl = 0, bd = 0;
+    if (!mul_ok(b, d, &bd) || !mul_ok(bd, L > 0 ? L : 1, &bdl) || !mul_ok(bdl, 16, &bdl)) return SSM_ERR_SHAPE;
+    bdl /= 16;
+    if (!w || (L > 0 && (!xin || !x_out))) return SSM_ERR_NULL;
+    const int64_t es = dtype == SSM_BF16 ? 2 : 4;
+    const Span so{x_out, bdl * es}, ss{state_out, bd * (W - 1) * 4};
+    const Span ins[] = {{xin, bdl * es}, {w, d * W * 4}, {bias, d * 4}};
+    for (const Span &s : ins)
+        if (overlaps(so, s) || overlaps(ss, s)) return SSM_ERR_ALIAS;
+    if (overlaps(so, ss) || overlaps(so, Span{state_in, bd * (W - 1) * 4})) return SSM_ERR_ALIAS;
+    if (state_out && state_in && state_out != state_in && overlaps(ss, Span{state_in, bd * (W - 1) * 4}))
+        return SSM_ERR_ALIAS;
+    ssm::ConvLaunch p{};
+    p.xin = xin; p.w = w; p.bias = bias; p.state_in = state_in; p.xout = x_out; p.state_out = state_out;
+    p.b = b; p.d = d; p.L = L; p.W = (int)W; p.silu_on = apply_silu ? 1 : 0; p.bf16 = dtype == SSM_BF16;
+    return ssm::launch_conv1d(p, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status_t ssm_conv1d_step(float *state, const void *xin, const float *w, const float *bias, void *x_out,
+                             int64_t b, int64_t d, int64_t W, int32_t apply_silu, ssm_dtype_t dtype,
+                             hipStream_t stream) {
+    if (!valid_dtype(dtype)) return SSM_ERR_UNSUPPORTED;
+    if (b < 1 || d < 1 || W < 1) return SSM_ERR_SHAPE;
+    if (W > SSM_MAX_CONV_W) return SSM_ERR_UNSUPPORTED;
+    int64_t bd = 0, tmp = 0;
+    if (!mul_ok(b, d, &bd) || !mul_ok(bd, 16 * W, &tmp)) return SSM_ERR_SHAPE;
+    if (!xin || !w || !x_out || (W > 1 && !state)) return SSM_ERR_NULL;
+    const int64_t es = dtype == SSM_BF16 ? 2 : 4;
+    const Span so{x_out, bd * es}, ss{state, bd * (W - 1) * 4};
+    const Span ins[] = {{xin, bd * es}, {w, d * W * 4}, {bias, d * 4}};
+    for (const Span &s : ins)
+        if (overlaps(so, s) || overlaps(ss, s)) return SSM_ERR_ALIAS;
+    if (overlaps(so, ss)) return SSM_ERR_ALIAS;
+    ssm::ConvStepLaunch p{};
+    p.state = state; p.xin = xin; p.w = w; p.bias = bias; p.xout = x_out;
+    p.b = b; p.d = d; p.W = (int)W; p.silu_on = apply_silu ? 1 : 0; p.bf16 = dtype == SSM_BF16;
+    return ssm::launch_conv_step(p, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 ssm_status_t ssm_scan_step(float *state, const void *x, const void *delta, const float *A, const void *B,
                            const void *C, const float *D, const void *z, void *y, int64_t b, int64_t d,
                            int64_t N, ssm_dtype_t dtype, hipStream_t stream) {

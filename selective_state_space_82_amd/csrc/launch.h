@@ -51,6 +51,29 @@ struct BwdLaunch {
 
 hipError_t launch_scan_bwd(const BwdLaunch &p, hipStream_t stream);
 
+// Causal depthwise Conv1D (+ SiLU) over [b][d][L] rows, and its decode step.
+struct ConvLaunch {
+    const void *xin;
+    const float *w, *bias, *state_in;  // bias, state_in nullable
+    void *xout;
+    float *state_out;                  // nullable; may equal state_in
+    int64_t b, d, L;
+    int W;                             // 1 .. 8 taps
+    int silu_on;
+    bool bf16;
+};
+struct ConvStepLaunch {
+    float *state;                      // [b][d][W-1], updated in place
+    const void *xin;                   // [b][d]
+    const float *w, *bias;
+    void *xout;                        // [b][d]
+    int64_t b, d;
+    int W, silu_on;
+    bool bf16;
+};
+hipError_t launch_conv1d(const ConvLaunch &p, hipStream_t stream);
+hipError_t launch_conv_step(const ConvStepLaunch &p, hipStream_t stream);
+
 struct StepLaunch {
     float *state;
     const void *x, *delta;

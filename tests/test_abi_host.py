@@ -131,3 +131,24 @@ def test_bwd_validation():
     assert bwd(dt=9) == 3
     assert bwd(dx=FAKE) == 5                      # dx overlaps x
     assert bwd(dx=out[1]) == 5                    # dx overlaps ddelta
+
+
+def test_conv_validation():
+    L = api.lib()
+    out = ctypes.c_void_p(0x900000)
+
+    def conv(xin=FAKE, w=ctypes.c_void_p(0x700000), xo=out, so=None, si=None, b=1, d=4, Ln=16, W=4, dt=0):
+        return L.ssm_conv1d_fwd(xin, w, None, si, xo, so, b, d, Ln, W, 1, dt, None)
+    assert conv(xin=None) == 1
+    assert conv(w=None) == 1
+    assert conv(b=0) == 2
+    assert conv(W=0) == 2
+    assert conv(W=9) == 3
+    assert conv(dt=5) == 3
+    assert conv(xo=FAKE) == 5                                        # output overlaps the input
+    assert conv(so=ctypes.c_void_p(0x900000 + 8)) == 5               # state_out overlaps x_out
+    step = lambda st=ctypes.c_void_p(0xA00000), xin=FAKE, xo=out, W=4: L.ssm_conv1d_step(
+        st, xin, ctypes.c_void_p(0x700000), None, xo, 1, 4, W, 1, 0, None)
+    assert step(st=None) == 1
+    assert step(W=9) == 3
+    assert step(xo=FAKE) == 5
