@@ -176,6 +176,50 @@ def bench_grad(name, steps, warmup, quiet=False):
     return res
 
 
+def bench_conv(name, steps, warmup, W=4, quiet=False):
+    """The Conv1D + SiLU front end over the workload's [b, d, L] input (taps N(0, 0.5²), bias N(0, 1)),
+    returning the state; HBM-bound: algorithmic bytes = xin read + x written (+ taps, bias, state)."""
+    import torch
+    from selective_state_space_82_amd import api
+    from selective_state_space_82_amd import inputs as I
+
+    w = I.WORKLOADS[name]
+    inp = I.prefill_inputs(w)
+    esize = 4 if w.dtype == "f32" else 2
+    rows = w.b * w.d * w.L
+    nbytes = 2 * rows * esize + w.d * (W + 1) * 4 + w.b * w.d * (W - 1) * 4
+    rotate = int(min(8, max(1, -(-2 * MALL_BYTES // nbytes))))
+    rng = np.random.default_rng(6)
+    taps = torch.from_numpy((rng.standard_normal((w.d, W)) * 0.5).astype(np.float32)).cuda()
+    bias = torch.from_numpy(rng.standard_normal(w.d).astype(np.float32)).cuda()
+    sets = []
+    for _ in range(rotate):
+        xin = to_dev(inp["x"], "cuda")
+        sets.append((xin, torch.empty_like(xin), torch.empty((w.b, w.d, W - 1), device="cuda")))
+
+    def call(i):
+        xin, xo, so = sets[i % rotate]
+        api.ssm_conv1d_fwd(xin, taps, bias, x_out=xo, state_out=so)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    res = {"pass": "conv1d", "workload": name, "W": W, "us_per_call": ms * 1e3, "algorithmic_bytes": nbytes,
+           "GBps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if not quiet:
+        print(f"# conv1d {name} (W={W}): {ms * 1e3:.1f} us/call, {res['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_decode(name, rotate_states, quiet=False):
     """The decode workload: `steps` successive single-token steps, each with fresh inputs, on one
     state (rotate_states = 1, the literal workload) or cycling through several layer states."""
@@ -299,8 +343,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--extra", default="decode,mamba1p4b_bf16_b8_d4096_L4096_N16,grad",
-                    help="comma list: 'decode', 'grad' (gradient pass on the workload) and/or prefill workload names "
+    ap.add_argument("--extra", default="decode,mamba1p4b_bf16_b8_d4096_L4096_N16,grad,conv",
+                    help="comma list: 'decode', 'grad' (gradient pass on the workload), 'conv' (Conv1D front end) "
+                         "and/or prefill workload names "
                          "('' for none, 'all' for every one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=0, help="input/output sets to rotate (0 = enough to exceed the cache)")
@@ -336,6 +381,9 @@ def main():
                 extra.append(bench_decode(I.DECODE_WORKLOADS[0], r))
         elif n == "grad":
             extra.append(bench_grad(args.workload, max(3, args.steps // 5), 2))
+        elif n == "conv":
+            for cw in dict.fromkeys((args.workload, "mamba1p4b_bf16_b8_d4096_L4096_N16")):
+                extra.append(bench_conv(cw, 20, 3))
         else:
             r, _ = bench_prefill(n, max(3, args.steps // 4), 2)
             extra.append(r)

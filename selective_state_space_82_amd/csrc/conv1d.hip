@@ -8,9 +8,12 @@
 //   u_t = c_d + Σ_{k<W} w[d][k] · xin_{t−(W−1)+k},   x_t = silu(u_t)  (or u_t),
 // inputs before t = 0 coming from the state (the W − 1 preceding inputs, oldest first) or zero.
 //
-// Bound by HBM traffic: each thread produces one 16-byte chunk of a row (4 fp32 or 8 bf16 outputs)
-// from that chunk of the input and the W − 1 inputs before it (the previous chunk, read again by the
-// neighbouring thread through the caches), so a wavefront reads and writes contiguous runs.
+// Bound by HBM traffic. A workgroup of 256 threads covers 256 consecutive 16-byte chunks of one (b, d)
+// row, so the row, the channel, its taps and bias are workgroup-uniform (scalar registers); each thread
+// produces one chunk (4 fp32 or 8 bf16 outputs) from that chunk of the input and the W − 1 inputs before
+// it (the previous chunk, read again by the neighbouring lane through the caches). The output streams out
+// with non-temporal stores (written once, read by a later kernel). Measured on the 1.4B-like shape: more
+// chunks per thread, or larger workgroups, ran slower; non-temporal loads too.
 #include "device_common.h"
 #include "launch.h"
 #include "tile_common.h"
@@ -18,78 +21,94 @@
 namespace ssm {
 namespace {
 
+constexpr int kConvBlock = 256;
+
 struct ConvArgs {
     const void *xin;
     const float *w, *bias, *state_in;
     void *xout;
     float *state_out;
     int64_t b, d, L;
+    int64_t tiles_per_row, n_blocks;
     int silu_on;
-    int vec;  // rows allow 16-byte accesses
+    int vec;         // rows allow 16-byte accesses
+    int fuse_state;  // the conv kernel writes state_out itself (no aliasing, L >= W - 1)
 };
 
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+
 template <typename T, int W>
-__global__ __launch_bounds__(256) void conv1d_kernel(ConvArgs a) {
+__global__ __launch_bounds__(kConvBlock) void conv1d_kernel(ConvArgs a) {
     constexpr int E = Chunk<T>::kElems;
     constexpr int H = W - 1;
     constexpr int P = (H + E - 1) / E;  // previous chunks needed (0 or 1 for W <= E + 1)
-    const int64_t nch = (a.L + E - 1) / E;  // chunks per row
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= a.b * a.d * nch) return;
-    const int64_t row = gid / nch;
-    const int64_t t0 = (gid - row * nch) * E;
-    const int64_t ch = row % a.d;
-    const T *xr = static_cast<const T *>(a.xin) + row * a.L;
+    for (int64_t blk = blockIdx.x; blk < a.n_blocks; blk += gridDim.x) {
+        const int64_t row = blk / a.tiles_per_row;  // uniform across the workgroup
+        const int64_t tile = blk - row * a.tiles_per_row;
+        const int64_t ch = row % a.d;
+        const T *xr = static_cast<const T *>(a.xin) + row * a.L;
+        T *yr = static_cast<T *>(a.xout) + row * a.L;
+        const int64_t t0 = (tile * kConvBlock + threadIdx.x) * E;
+        if (t0 >= a.L) continue;
 
-    // ext[0 .. P*E) = inputs t0 − P*E .. t0 − 1 (from the row, or the state before t = 0); ext[P*E ..) = chunk
-    float ext[(P + 1) * E];
-    const bool full = a.vec && t0 + E <= a.L;
-    if (full) {
-        chunk_to_regs<T>(ext + P * E, *reinterpret_cast<const uint4 *>(xr + t0));
-    } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) ext[P * E + e] = (t0 + e < a.L) ? widen(xr[t0 + e]) : 0.0f;
-    }
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-        const int64_t tp = t0 - (P - p) * E;  // first step of this previous chunk
-        if (tp >= 0 && a.vec) {
-            chunk_to_regs<T>(ext + p * E, *reinterpret_cast<const uint4 *>(xr + tp));
+        // ext[0 .. P*E) = inputs t0 − P*E .. t0 − 1 (from the row, or the state before t = 0);
+        // ext[P*E ..) = the chunk itself
+        float ext[(P + 1) * E];
+        const bool full = a.vec && t0 + E <= a.L;
+        if (full) {
+            chunk_to_regs<T>(ext + P * E, *reinterpret_cast<const uint4 *>(xr + t0));
         } else {
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int64_t t = tp + e;
-                float v = 0.0f;
-                if (t >= 0) v = widen(xr[t]);
-                else if (a.state_in && t >= -H) v = a.state_in[row * H + (H + t)];
-                ext[p * E + e] = v;
+            for (int e = 0; e < E; ++e) ext[P * E + e] = (t0 + e < a.L) ? widen(xr[t0 + e]) : 0.0f;
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int64_t tp = t0 - (P - p) * E;  // first step of this previous chunk
+            if (tp >= 0 && a.vec) {
+                chunk_to_regs<T>(ext + p * E, *reinterpret_cast<const uint4 *>(xr + tp));
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int64_t t = tp + e;
+                    float v = 0.0f;
+                    if (t >= 0) v = widen(xr[t]);
+                    else if (a.state_in && t >= -H) v = a.state_in[row * H + (H + t)];
+                    ext[p * E + e] = v;
+                }
             }
         }
-    }
-    float wk[W];
+        float wk[W];
 #pragma unroll
-    for (int k = 0; k < W; ++k) wk[k] = a.w[ch * W + k];
-    const float c = a.bias ? a.bias[ch] : 0.0f;
-    float out[E];
+        for (int k = 0; k < W; ++k) wk[k] = a.w[ch * W + k];
+        const float c = a.bias ? a.bias[ch] : 0.0f;
+        float out[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        float u = c;
+        for (int e = 0; e < E; ++e) {
+            float u = c;
 #pragma unroll
-        for (int k = 0; k < W; ++k) u = __builtin_fmaf(wk[k], ext[P * E + e - H + k], u);
-        out[e] = a.silu_on ? silu(u) : u;
-    }
-    T *yr = static_cast<T *>(a.xout) + row * a.L;
-    if (full) {
-        T packed[E];
+            for (int k = 0; k < W; ++k) u = __builtin_fmaf(wk[k], ext[P * E + e - H + k], u);
+            out[e] = a.silu_on ? silu(u) : u;
+        }
+        if (full) {
+            T packed[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) packed[e] = narrow<T>(out[e]);
-        uint4 v;
-        __builtin_memcpy(&v, packed, sizeof(v));
-        *reinterpret_cast<uint4 *>(yr + t0) = v;
-    } else {
+            for (int e = 0; e < E; ++e) packed[e] = narrow<T>(out[e]);
+            u4v v;
+            __builtin_memcpy(&v, packed, sizeof(v));
+            __builtin_nontemporal_store(v, reinterpret_cast<u4v *>(yr + t0));
+        } else {
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-            if (t0 + e < a.L) yr[t0 + e] = narrow<T>(out[e]);
+            for (int e = 0; e < E; ++e)
+                if (t0 + e < a.L) yr[t0 + e] = narrow<T>(out[e]);
+        }
+        if (H > 0 && a.fuse_state && t0 + E > a.L - H) {
+            // this chunk holds some of the last W − 1 inputs, which become the state
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int64_t k = t0 + e - (a.L - H);
+                if (k >= 0 && k < H) a.state_out[row * H + k] = ext[P * E + e];
+            }
+        }
     }
 }
 
@@ -135,15 +154,19 @@ __global__ __launch_bounds__(256) void conv_step_kernel(float *__restrict__ stat
 }
 
 template <typename T, int W>
-hipError_t conv_typed(const ConvArgs &a, hipStream_t stream) {
+hipError_t conv_typed(ConvArgs a, hipStream_t stream) {
     constexpr int E = Chunk<T>::kElems;
-    const int64_t n = a.b * a.d * ((a.L + E - 1) / E);
-    if (n > 0) {
-        hipLaunchKernelGGL((conv1d_kernel<T, W>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+    const int64_t nch = (a.L + E - 1) / E;
+    a.tiles_per_row = (nch + kConvBlock - 1) / kConvBlock;
+    a.n_blocks = a.b * a.d * a.tiles_per_row;
+    a.fuse_state = a.state_out && a.state_out != a.state_in && a.L >= W - 1 && a.n_blocks > 0;
+    if (a.n_blocks > 0) {
+        const int64_t grid = a.n_blocks < (int64_t(1) << 30) ? a.n_blocks : (int64_t(1) << 30);
+        hipLaunchKernelGGL((conv1d_kernel<T, W>), dim3((unsigned)grid), dim3(kConvBlock), 0, stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (a.state_out && W > 1) {
+    if (a.state_out && W > 1 && !a.fuse_state) {
         hipLaunchKernelGGL((conv_state_kernel<T, W>), dim3((unsigned)((a.b * a.d + 255) / 256)), dim3(256), 0, stream,
                            a);
         return hipGetLastError();

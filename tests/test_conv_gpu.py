@@ -50,6 +50,9 @@ CASES = [
     (2, 16, 250, 7, "bf16", False, False, True),
     (1, 40, 1000, 2, "bf16", True, True, False),
     (4, 1536, 2048, 4, "f32", True, True, True),  # the 130M-like layer's shape
+    (1, 3, 5000, 4, "f32", True, True, True),     # several workgroup tiles per row
+    (2, 5, 9001, 5, "bf16", True, True, True),    # several tiles, ragged rows (no 16-byte accesses)
+    (1, 2, 8192, 8, "bf16", True, False, True),   # several tiles, 16-byte accesses
 ]
 
 
