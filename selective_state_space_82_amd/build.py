@@ -21,10 +21,15 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=
           "-Wall", "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the library sources (identifies which kernels a stored measurement belongs to)."""
+# The sources that decide the prefill kernels and their launch shapes.
+FWD_KERNEL_SOURCES = ("abi.cpp", "device_common.h", "launch.h", "scan_fwd.hip", "tile_common.h")
+
+
+def kernel_source_hash(names=FWD_KERNEL_SOURCES) -> str:
+    """sha256 over the named library sources (default: those of the prefill kernels), identifying which
+    kernels a stored measurement belongs to."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(names):
         if name.endswith((".hip", ".h", ".cpp")):
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
