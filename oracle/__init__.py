@@ -68,6 +68,10 @@ class Oracle:
         lib.oracle_conv1d.argtypes = [_DP, _DP, _DP, _DP, ctypes.c_int, _DP, _DP, L, L, L, L]
         lib.oracle_conv1d.restype = ctypes.c_int
         lib.oracle_zoh.argtypes = [ctypes.c_double, ctypes.c_double, _DP, _DP]
+        lib.oracle_lti_kernel.argtypes = [_DP] * 5 + [L, L, L]
+        lib.oracle_lti_kernel.restype = ctypes.c_int
+        lib.oracle_lti_conv.argtypes = [_DP] * 5 + [L, L, L]
+        lib.oracle_lti_conv.restype = ctypes.c_int
         lib.oracle_zoh.restype = None
         self.lib = lib
         self.path = lib_path
@@ -169,6 +173,35 @@ class Oracle:
         return y, st
 
 
+    def lti_kernel(self, delta, A, B, C, L):
+        """K̄ [d, L] of the time-invariant system per channel (delta [d]; A, B, C [d, N])."""
+        A = _f64(A)
+        if A.ndim != 2:
+            raise ValueError("A must be [d, N]")
+        d, N = A.shape
+        delta = _f64(delta, (d,))
+        B = _f64(B, (d, N))
+        C = _f64(C, (d, N))
+        K = np.empty((d, int(L)), dtype=np.float64)
+        if self.lib.oracle_lti_kernel(_ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(K), d, int(L), N) != 0:
+            raise ValueError("oracle_lti_kernel rejected its arguments")
+        return K
+
+    def lti_conv(self, x, K, D=None, z=None):
+        """y [b, d, L] = causal x ∗ K̄ + D·x, times silu(z) when z is given."""
+        x = _f64(x)
+        if x.ndim != 3:
+            raise ValueError("x must be [b, d, L]")
+        b, d, L = x.shape
+        K = _f64(K, (d, L))
+        D = _f64(D, (d,))
+        z = _f64(z, (b, d, L))
+        y = np.empty_like(x)
+        if self.lib.oracle_lti_conv(_ptr(x), _ptr(K), _ptr(D), _ptr(z), _ptr(y), b, d, L) != 0:
+            raise ValueError("oracle_lti_conv rejected its arguments")
+        return y
+
+
 _default = None
 
 
@@ -197,3 +230,11 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_final=None)
 
 def conv1d(xin, w, bias=None, state=None, silu=True):
     return default().conv1d(xin, w, bias, state, silu)
+
+
+def lti_kernel(delta, A, B, C, L):
+    return default().lti_kernel(delta, A, B, C, L)
+
+
+def lti_conv(x, K, D=None, z=None):
+    return default().lti_conv(x, K, D, z)

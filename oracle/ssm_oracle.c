@@ -240,3 +240,51 @@ int oracle_conv1d(const double *xin, const double *w, const double *bias, const 
     free(ext);
     return 0;
 }
+
+/* ---------------------------------------------------------------------------------------------
+ * The time-invariant case as a convolution ("State Space Models（SSM）とMamba" §2.3; "Mambaとは？…",
+ * section 固定SSMには「再帰」と「畳み込み」の二つの顔がある): when Ā, B̄ and C are the same at every step,
+ * the zero-state recurrence unrolls into y = x ∗ K̄ with K̄ = (CB̄, CĀB̄, CĀ²B̄, …, CĀ^{L−1}B̄). Here every
+ * channel is its own system with a diagonal A, so K̄_k = Σ_n C_n Ā_n^k B̄_n; Ā^k is the running product.
+ * ------------------------------------------------------------------------------------------- */
+int oracle_lti_kernel(const double *delta, const double *A, const double *B, const double *C, double *K,
+                      long d, long L, long N) {
+    if (!delta || !A || !B || !C || !K || d < 0 || L < 0 || N < 1) return -1;
+    for (long id = 0; id < d; ++id) {
+        double *Kd = K + (size_t)id * (size_t)L;
+        for (long k = 0; k < L; ++k) Kd[k] = 0.0;
+        for (long n = 0; n < N; ++n) {
+            const size_t i = (size_t)id * (size_t)N + (size_t)n;
+            double abar, bcoef;
+            oracle_zoh(delta[id], A[i], &abar, &bcoef);
+            const double cb = C[i] * bcoef * B[i];
+            double power = 1.0; /* Ā^k */
+            for (long k = 0; k < L; ++k) {
+                Kd[k] += cb * power;
+                power *= abar;
+            }
+        }
+    }
+    return 0;
+}
+
+/* y = x ∗ K̄ (causal: y_t = Σ_{s≤t} K̄_{t−s} x_s) plus the skip term D·x, then the gate, as in the
+ * recurrent form's readout (same sources as scan_row). */
+int oracle_lti_conv(const double *x, const double *K, const double *D, const double *z, double *y, long b,
+                    long d, long L) {
+    if (!x || !K || !y || b < 0 || d < 0 || L < 0) return -1;
+    for (long ib = 0; ib < b; ++ib) {
+        for (long id = 0; id < d; ++id) {
+            const size_t row = ((size_t)ib * (size_t)d + (size_t)id) * (size_t)L;
+            const double *Kd = K + (size_t)id * (size_t)L;
+            for (long t = 0; t < L; ++t) {
+                double acc = 0.0;
+                for (long s = 0; s <= t; ++s) acc += Kd[t - s] * x[row + (size_t)s];
+                double yt = acc + (D ? D[id] : 0.0) * x[row + (size_t)t];
+                if (z) yt *= silu(z[row + (size_t)t]);
+                y[row + (size_t)t] = yt;
+            }
+        }
+    }
+    return 0;
+}

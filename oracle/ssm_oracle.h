@@ -8,6 +8,7 @@
  * Sources (page title, then section / equation):
  *   [SSM-intro]  "State Space Models（SSM）とMamba" (hatohato.jp ai_intro):
  *                §2.1 continuous-time SSM, §2.2 ZOH discretisation and the discrete update,
+ *                §2.3 an LTI system as a convolution y = x ∗ K̄, K̄ = (CB̄, CĀB̄, CĀ²B̄, …),
  *                §4.2 selective SSM (per-token Δ, B, C).
  *   [kasblo]     "Mambaとは？Transformer以外の系列モデル" (kasblo.com):
  *                section "状態空間モデルを一つの式から理解する" (ẋ = Ah + Bx, y = Ch + Dx; ZOH for
@@ -68,6 +69,18 @@ int oracle_scan_bwd(const double *x, const double *delta, const double *A, const
  * first / the last W−1 inputs after it) or NULL (zeros / not written). Returns 0 or -1. */
 int oracle_conv1d(const double *xin, const double *w, const double *bias, const double *state_in, int apply_silu,
                   double *x_out, double *state_out, long b, long d, long L, long W);
+
+/* Time-invariant (LTI) convolution kernel per channel: with Ā = exp(Δ_d·A[d][n]) and B̄ the ZOH of
+ * B[d][n] (as in oracle_zoh), K[d][k] = Σ_n C[d][n] · Ā^k · B̄ for k = 0 … L−1. delta [d]; A, B, C
+ * [d][N] (every channel its own single-input single-output system); K [d][L]. Returns 0 or -1. */
+int oracle_lti_kernel(const double *delta, const double *A, const double *B, const double *C, double *K,
+                      long d, long L, long N);
+
+/* LTI output by direct causal convolution: y[b][d][t] = Σ_{s≤t} K[d][t−s]·x[b][d][s] + D[d]·x[b][d][t],
+ * then times silu(z[b][d][t]) when z is given. x, z, y [b][d][L]; K [d][L]; D [d]. D and z may be
+ * NULL. Returns 0 or -1. */
+int oracle_lti_conv(const double *x, const double *K, const double *D, const double *z, double *y, long b,
+                    long d, long L);
 
 /* ZOH coefficients of one diagonal entry: *abar = exp(delta·a), *bcoef = (exp(delta·a) − 1)/a
  * (delta at a = 0), so that B̄ = bcoef · B. */

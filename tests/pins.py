@@ -423,6 +423,67 @@ def pin_conv_state_chaining(orc):
     _close(st, xin[:, :, L - (W - 1):], what="state = last W-1 inputs")
 
 
+def pin_lti_kernel_scalar_example(orc):
+    """kasblo page, scalar example, read as a time-invariant kernel: K̄ for A = -1, Δ = 0.5, B = C = 1
+    starts with the four printed weights, and equals (1 - e^{-1/2}) e^{-k/2} (the page's closed forms)."""
+    g = _golden_pairs("kasblo_scalar_example.txt")
+    half = 0.5 * 10.0 ** (-g["printed_decimals"])
+    L = 12
+    K = orc.lti_kernel([g["delta"]], [[g["A"]]], [[g["B"]]], [[g["C"]]], L)
+    for k in range(4):
+        assert abs(K[0, k] - g[f"weight_lag{k}"]) <= half, (k, K[0, k])
+    _close(K[0], (1.0 - math.exp(-0.5)) * np.exp(-0.5 * np.arange(L)), what="scalar K closed form")
+
+
+def pin_lti_kernel_van_loan(orc):
+    """K̄_k = C Ā^k B̄ ("State Space Models（SSM）とMamba" §2.3) with Ā, B̄ from the block matrix
+    exponential (Van Loan) and Ā^k from a matrix power, per channel; one A entry is 0 (the ZOH limit)."""
+    rng = _rng(53)
+    d, N, L = 3, 5, 40
+    A = -rng.uniform(0.1, 2.5, size=(d, N)); A[1, 3] = 0.0
+    dl = rng.uniform(0.02, 0.9, size=d)
+    B = rng.normal(size=(d, N)); C = rng.normal(size=(d, N))
+    K = orc.lti_kernel(dl, A, B, C, L)
+    want = np.empty((d, L))
+    for idd in range(d):
+        Ab, Bb = zoh_vanloan(A[idd], B[idd], dl[idd])
+        want[idd] = [C[idd] @ np.linalg.matrix_power(Ab, k) @ Bb for k in range(L)]
+    _close(K, want, rtol=1e-10, atol=1e-12, what="LTI kernel")
+
+
+def pin_lti_conv_equals_recurrence(orc):
+    """The two faces of a fixed SSM (kasblo page, section 固定SSMには「再帰」と「畳み込み」の二つの顔がある):
+    the kernel route (K̄, then x ∗ K̄ + D x, gate) equals the recurrent scan run with the same Δ, B, C
+    at every step, channel by channel."""
+    rng = _rng(59)
+    b, d, N, L = 2, 3, 4, 30
+    A = -rng.uniform(0.1, 2.0, size=(d, N)); A[2, 1] = 0.0
+    dl = rng.uniform(0.05, 1.0, size=d)
+    B = rng.normal(size=(d, N)); C = rng.normal(size=(d, N)); D = rng.normal(size=d)
+    x = rng.normal(size=(b, d, L)); z = rng.normal(size=(b, d, L))
+    y = orc.lti_conv(x, orc.lti_kernel(dl, A, B, C, L), D=D, z=z)
+    for idd in range(d):
+        yr, _ = orc.scan_fwd(x[:, idd:idd + 1], np.full((b, 1, L), dl[idd]), A[idd:idd + 1],
+                             np.broadcast_to(B[idd], (b, L, N)), np.broadcast_to(C[idd], (b, L, N)),
+                             D=D[idd:idd + 1], z=z[:, idd:idd + 1])
+        _close(y[:, idd:idd + 1], yr, rtol=1e-10, atol=1e-12, what=f"LTI conv vs recurrence, channel {idd}")
+
+
+def pin_lti_conv_library(orc):
+    """y = x ∗ K̄ + D x (then silu(z)) against numpy's full convolution truncated to L, for arbitrary K̄."""
+    rng = _rng(61)
+    b, d, L = 2, 3, 25
+    x = rng.normal(size=(b, d, L)); K = rng.normal(size=(d, L)); D = rng.normal(size=d)
+    z = rng.normal(size=(b, d, L))
+    want = np.empty((b, d, L))
+    for ib in range(b):
+        for idd in range(d):
+            want[ib, idd] = np.convolve(x[ib, idd], K[idd])[:L] + D[idd] * x[ib, idd]
+    _close(orc.lti_conv(x, K, D=D), want, what="LTI conv, no gate")
+    _close(orc.lti_conv(x, K, D=D, z=z), want * silu_lib(z), what="LTI conv, gated")
+    _close(orc.lti_conv(x, K), want - D[None, :, None] * x, what="LTI conv, no D")
+
+
 ALL_PINS = [
     pin_scalar_worked_example,
     pin_delta_gate,
@@ -442,4 +503,8 @@ ALL_PINS = [
     pin_conv_identity_and_shift,
     pin_conv_impulse_and_causality,
     pin_conv_state_chaining,
+    pin_lti_kernel_scalar_example,
+    pin_lti_kernel_van_loan,
+    pin_lti_conv_equals_recurrence,
+    pin_lti_conv_library,
 ]

@@ -53,6 +53,13 @@ MUTANTS = {
     "conv_state_first_inputs": ("state_out[row * (size_t)H + (size_t)k] = ext[L + k];",
                                 "state_out[row * (size_t)H + (size_t)k] = ext[H + k];"),
     "conv_bias_dropped": ("double u = bias ? bias[id] : 0.0;", "double u = 0.0;"),
+    "lti_power_from_abar": ("double power = 1.0; /* Ā^k */", "double power = abar; /* Ā^k */"),
+    "lti_euler_bbar": ("const double cb = C[i] * bcoef * B[i];", "const double cb = C[i] * delta[id] * B[i];"),
+    "lti_channel0_params": ("const size_t i = (size_t)id * (size_t)N + (size_t)n;", "const size_t i = (size_t)n;"),
+    "lti_kernel_index": ("acc += Kd[t - s] * x[row + (size_t)s];", "acc += Kd[s] * x[row + (size_t)s];"),
+    "lti_drop_D": ("double yt = acc + (D ? D[id] : 0.0) * x[row + (size_t)t];", "double yt = acc;"),
+    "lti_gate_dropped": ("if (z) yt *= silu(z[row + (size_t)t]);\n                y[row + (size_t)t] = yt;",
+                         "y[row + (size_t)t] = yt;"),
 }
 
 
