@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -171,6 +172,73 @@ def bench_grad(name, steps, warmup, quiet=False):
     if not quiet:
         print(f"# gradient {name}: {ms * 1e3:.1f} us/call, {res['elements_per_s']:.3g} elements/s, "
               f"{res['call_valu_Tslot_s']:.2f} T VALU slot/s over the whole call", file=sys.stderr, flush=True)
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def lti_fft_points(L):
+    """Transform size of the LTI convolution for sequence length L (a power of two >= max(2L, 1024))."""
+    m = 1024
+    while m < 2 * L:
+        m *= 2
+    return m
+
+
+def bench_lti(name, steps, warmup, quiet=False):
+    """The time-invariant form (ssm_lti_fwd: K̄, then the FFT convolution) on a layer of the workload's
+    shape with per-channel Δ, B, C (the LTI input recipe), gate and D on."""
+    import torch
+    from selective_state_space_82_amd import api
+    from selective_state_space_82_amd import inputs as I
+
+    w = I.WORKLOADS[name]
+    inp = I.random_lti(w.b, w.d, w.L, w.N, dtype=w.dtype, gate=w.gate, seed=2)
+    esize = 4 if w.dtype == "f32" else 2
+    rows = w.b * w.d * w.L
+    # read x, z; write y; read the parameters (K̄ itself stays in L2-sized scratch per channel block)
+    nbytes = rows * esize * (3 if w.gate else 2) + w.d * (3 * w.N + 2) * 4
+    M = lti_fft_points(w.L)
+    transforms = w.d * (1 + 2 * ((w.b + 1) // 2))
+    flops = transforms * 5 * M * math.log2(M) + w.d * ((w.b + 1) // 2) * 6 * M  # radix-2 count
+    rotate = int(min(8, max(1, -(-2 * MALL_BYTES // nbytes))))
+    par = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).cuda() for k in ("delta", "A", "B", "C", "D")}
+    sets = []
+    for _ in range(rotate):
+        x = to_dev(inp["x"], "cuda")
+        sets.append((x, to_dev(inp["z"], "cuda") if w.gate else None, torch.empty_like(x)))
+    K = api.ssm_lti_kernel(par["delta"], par["A"], par["B"], par["C"], w.L)
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def full(i):
+        x, z, y = sets[i % rotate]
+        api.ssm_lti_fwd(x, par["delta"], par["A"], par["B"], par["C"], par["D"], z, y=y)
+
+    def conv_only(i):
+        x, z, y = sets[i % rotate]
+        api.ssm_lti_conv(x, K, par["D"], z, y=y)
+
+    ms = timed(full)
+    ms_conv = timed(conv_only)
+    res = {"pass": "lti_fft", "workload": name, "us_per_call": ms * 1e3, "us_conv_only": ms_conv * 1e3,
+           "elements_per_s": rows / (ms * 1e-3), "algorithmic_bytes": nbytes,
+           "GBps": nbytes / (ms * 1e-3) / 1e9, "fft_points": M, "transforms": transforms,
+           "fft_TFLOPs_conv": flops / (ms_conv * 1e-3) / 1e12}
+    if not quiet:
+        print(f"# lti {name}: {ms * 1e3:.1f} us/call (convolution alone {ms_conv * 1e3:.1f} us), "
+              f"{res['GBps']:.0f} GB/s, {res['fft_TFLOPs_conv']:.1f} TFLOP/s (5 M log2 M per transform)",
+              file=sys.stderr, flush=True)
     del sets
     torch.cuda.empty_cache()
     return res
@@ -350,8 +418,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--extra", default="decode,mamba1p4b_bf16_b8_d4096_L4096_N16,grad,conv",
-                    help="comma list: 'decode', 'grad' (gradient pass on the workload), 'conv' (Conv1D front end) "
+    ap.add_argument("--extra", default="decode,mamba1p4b_bf16_b8_d4096_L4096_N16,grad,conv,lti",
+                    help="comma list: 'decode', 'grad' (gradient pass on the workload), 'conv' (Conv1D front "
+                         "end), 'lti' (LTI convolution form) "
                          "and/or prefill workload names "
                          "('' for none, 'all' for every one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -388,6 +457,9 @@ def main():
                 extra.append(bench_decode(I.DECODE_WORKLOADS[0], r))
         elif n == "grad":
             extra.append(bench_grad(args.workload, max(3, args.steps // 5), 2))
+        elif n == "lti":
+            for cw in dict.fromkeys((args.workload, "mamba1p4b_bf16_b8_d4096_L4096_N16")):
+                extra.append(bench_lti(cw, 20, 3))
         elif n == "conv":
             for cw in dict.fromkeys((args.workload, "mamba1p4b_bf16_b8_d4096_L4096_N16")):
                 extra.append(bench_conv(cw, 20, 3))

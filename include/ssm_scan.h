@@ -156,6 +156,35 @@ SSM_API ssm_status_t ssm_conv1d_step(float *state, const void *xin, const float 
                                      ssm_dtype_t dtype, hipStream_t stream);
 
 /*
+ * The time-invariant (LTI) case evaluated as a convolution (page "State Space Models（SSM）とMamba" §2.3;
+ * page "Mambaとは？Transformer以外の系列モデル", section 固定SSMには「再帰」と「畳み込み」の二つの顔がある):
+ * when Ā, B̄ and C are the same at every step, the zero-state recurrence is y = x ∗ K̄ with
+ * K̄ = (CB̄, CĀB̄, CĀ²B̄, …), which the FFT evaluates in O(L log L). Every channel is its own system.
+ *
+ * ssm_lti_kernel: K[d][k] = Σ_n C[d][n] · Ā^k · B̄ for k < L, with the ZOH of ssm_scan_fwd
+ * (Ā = exp(delta[d]·A[d][n]), B̄ = (Ā − 1)/A · B[d][n], Δ·B at A = 0).
+ *   delta [d], A, B, C [d][N], K [d][L] (output); all fp32. d, N >= 1, N <= SSM_MAX_N, 0 <= L < 2^24.
+ *
+ * ssm_lti_conv: y[b][d][t] = Σ_{s<=t} K[d][t−s] · x[b][d][s] + D[d] · x[b][d][t], times silu(z) when z
+ * is given, by FFT (two batch rows of a channel per complex transform of 2^⌈log2 2L⌉ >= 1024 points).
+ *   x, z, y [b][d][L] dtype (z may be NULL); K [d][L] fp32 (any kernel, e.g. from ssm_lti_kernel);
+ *   D [d] fp32 or NULL. y may not overlap the inputs. b >= 1, 1 <= d <= 2^22,
+ *   1 <= L <= SSM_LTI_MAX_L (SSM_ERR_UNSUPPORTED above it).
+ *
+ * ssm_lti_fwd: both: K̄ into scratch taken stream-ordered from `stream` (d·L·4 bytes), then the
+ * convolution. No final state is produced (the convolution form has none; ssm_scan_fwd with the
+ * parameters repeated over t gives it). Errors as for ssm_scan_fwd.
+ */
+#define SSM_LTI_MAX_L 8192
+SSM_API ssm_status_t ssm_lti_kernel(const float *delta, const float *A, const float *B, const float *C, float *K,
+                                    int64_t d, int64_t L, int64_t N, hipStream_t stream);
+SSM_API ssm_status_t ssm_lti_conv(const void *x, const float *K, const float *D, const void *z, void *y, int64_t b,
+                                  int64_t d, int64_t L, ssm_dtype_t dtype, hipStream_t stream);
+SSM_API ssm_status_t ssm_lti_fwd(const void *x, const float *delta, const float *A, const float *B, const float *C,
+                                 const float *D, const void *z, void *y, int64_t b, int64_t d, int64_t L, int64_t N,
+                                 ssm_dtype_t dtype, hipStream_t stream);
+
+/*
  * Options of ssm_scan_fwd_ex. Zero-initialise, then set what you need; zero means "choose".
  *   seg_len            time-segment length (multiple of 32) carried across by the chunk-carry
  *                      pass; 0 = chosen from the shape, >= L = one segment

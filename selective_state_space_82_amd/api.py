@@ -74,6 +74,12 @@ def lib() -> ctypes.CDLL:
     L.ssm_conv1d_fwd.restype = i32
     L.ssm_conv1d_step.argtypes = [vp] * 5 + [i64, i64, i64, i32, i32, vp]
     L.ssm_conv1d_step.restype = i32
+    L.ssm_lti_kernel.argtypes = [vp] * 5 + [i64, i64, i64, vp]
+    L.ssm_lti_kernel.restype = i32
+    L.ssm_lti_conv.argtypes = [vp] * 5 + [i64, i64, i64, i32, vp]
+    L.ssm_lti_conv.restype = i32
+    L.ssm_lti_fwd.argtypes = [vp] * 8 + [i64, i64, i64, i64, i32, vp]
+    L.ssm_lti_fwd.restype = i32
     L.ssm_status_string.argtypes = [i32]
     L.ssm_status_string.restype = ctypes.c_char_p
     L.ssm_abi_version.argtypes = []
@@ -260,6 +266,61 @@ def ssm_conv1d_fwd(xin, w, bias=None, *, state_in=None, x_out=None, state_out=No
                                   b, d, L, W, int(bool(silu)), code, _stream(dev))
     _raise(status, "ssm_conv1d_fwd")
     return x_out, state_out
+
+
+def ssm_lti_kernel(delta, A, B, C, L, *, K=None):
+    """K̄ [d, L] fp32 of the time-invariant system per channel: delta [d], A, B, C [d, N], all fp32."""
+    if A.dim() != 2:
+        raise ValueError("A must be [d, N]")
+    d, N = A.shape
+    dev = A.device
+    for name, t, shape in (("delta", delta, (d,)), ("A", A, (d, N)), ("B", B, (d, N)), ("C", C, (d, N))):
+        _check(name, t, shape, torch.float32, dev)
+    if K is None:
+        K = torch.empty((d, int(L)), dtype=torch.float32, device=dev)
+    _check("K", K, (d, int(L)), torch.float32, dev)
+    status = lib().ssm_lti_kernel(_ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(K), d, int(L), N, _stream(dev))
+    _raise(status, "ssm_lti_kernel")
+    return K
+
+
+def ssm_lti_conv(x, K, D=None, z=None, *, y=None):
+    """y = x ∗ K̄ + D·x (· silu(z)) by FFT: x, z [b, d, L] (float32 or bfloat16), K [d, L] fp32, D [d] fp32."""
+    if x.dim() != 3:
+        raise ValueError("x must be [b, d, L]")
+    b, d, L = x.shape
+    dev, st = x.device, x.dtype
+    code = _dtype_code(st)
+    _check("K", K, (d, L), torch.float32, dev)
+    _check("D", D, (d,), torch.float32, dev)
+    _check("z", z, (b, d, L), st, dev)
+    if y is None:
+        y = torch.empty((b, d, L), dtype=st, device=dev)
+    _check("y", y, (b, d, L), st, dev)
+    status = lib().ssm_lti_conv(_ptr(x), _ptr(K), _ptr(D), _ptr(z), _ptr(y), b, d, L, code, _stream(dev))
+    _raise(status, "ssm_lti_conv")
+    return y
+
+
+def ssm_lti_fwd(x, delta, A, B, C, D=None, z=None, *, y=None):
+    """The LTI scan as a convolution in one call: K̄ from (delta [d], A, B, C [d, N]), then ssm_lti_conv."""
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be [b, d, L] and A [d, N]")
+    b, d, L = x.shape
+    N = A.shape[1]
+    dev, st = x.device, x.dtype
+    code = _dtype_code(st)
+    for name, t, shape in (("delta", delta, (d,)), ("A", A, (d, N)), ("B", B, (d, N)), ("C", C, (d, N)),
+                           ("D", D, (d,))):
+        _check(name, t, shape, torch.float32, dev)
+    _check("z", z, (b, d, L), st, dev)
+    if y is None:
+        y = torch.empty((b, d, L), dtype=st, device=dev)
+    _check("y", y, (b, d, L), st, dev)
+    status = lib().ssm_lti_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y),
+                               b, d, L, N, code, _stream(dev))
+    _raise(status, "ssm_lti_fwd")
+    return y
 
 
 def ssm_conv1d_step(state, xin, w, bias=None, *, x_out=None, silu=True):

@@ -246,6 +246,37 @@ ssm_status_t bwd_impl(const void *x, const void *delta, const float *A, const vo
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+ssm_status_t lti_kernel_check(const float *delta, const float *A, const float *B, const float *C, const float *K,
+                              int64_t d, int64_t L, int64_t N) {
+    if (d < 1 || N < 1 || L < 0 || L >= (INT64_C(1) << 24)) return SSM_ERR_SHAPE;
+    if (N > SSM_MAX_N) return SSM_ERR_UNSUPPORTED;
+    int64_t dn = 0, dl = 0;
+    if (!mul_ok(d, N, &dn) || !mul_ok(d, L, &dl) || !mul_ok(dl, 4, &dl)) return SSM_ERR_SHAPE;
+    if (!delta || !A || !B || !C || (L > 0 && !K)) return SSM_ERR_NULL;
+    const Span out{K, dl};
+    const Span ins[] = {{delta, d * 4}, {A, dn * 4}, {B, dn * 4}, {C, dn * 4}};
+    for (const Span &in : ins)
+        if (overlaps(out, in)) return SSM_ERR_ALIAS;
+    return SSM_OK;
+}
+
+// K == nullptr is accepted only when the caller computes K itself (internal).
+ssm_status_t lti_conv_check(const void *x, const float *K, bool k_internal, const float *D, const void *z,
+                            const void *y, int64_t b, int64_t d, int64_t L, ssm_dtype_t dtype) {
+    if (!valid_dtype(dtype)) return SSM_ERR_UNSUPPORTED;
+    if (b < 1 || d < 1 || d > (INT64_C(1) << 22) || L < 1) return SSM_ERR_SHAPE;
+    if (L > SSM_LTI_MAX_L) return SSM_ERR_UNSUPPORTED;
+    int64_t bdl = 0;
+    if (!mul_ok(b, d, &bdl) || !mul_ok(bdl, L, &bdl)) return SSM_ERR_SHAPE;
+    if (!x || (!K && !k_internal) || !y) return SSM_ERR_NULL;
+    const int64_t es = dtype == SSM_BF16 ? 2 : 4;
+    const Span out{y, bdl * es};
+    const Span ins[] = {{x, bdl * es}, {z, bdl * es}, {K, d * L * 4}, {D, d * 4}};
+    for (const Span &in : ins)
+        if (overlaps(out, in)) return SSM_ERR_ALIAS;
+    return SSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -374,6 +405,48 @@ ssm_status_t ssm_scan_step(float *state, const void *x, const void *delta, const
     p.b = b; p.d = d; p.N = N;
     p.bf16 = dtype == SSM_BF16;
     return ssm::launch_scan_step(p, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status_t ssm_lti_kernel(const float *delta, const float *A, const float *B, const float *C, float *K, int64_t d,
+                            int64_t L, int64_t N, hipStream_t stream) {
+    const ssm_status_t st = lti_kernel_check(delta, A, B, C, K, d, L, N);
+    if (st != SSM_OK) return st;
+    const ssm::LtiKernelLaunch p{delta, A, B, C, K, d, L, N};
+    return ssm::launch_lti_kernel(p, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status_t ssm_lti_conv(const void *x, const float *K, const float *D, const void *z, void *y, int64_t b, int64_t d,
+                          int64_t L, ssm_dtype_t dtype, hipStream_t stream) {
+    const ssm_status_t st = lti_conv_check(x, K, false, D, z, y, b, d, L, dtype);
+    if (st != SSM_OK) return st;
+    const ssm::LtiConvLaunch p{x, z, K, D, y, b, d, L, dtype == SSM_BF16};
+    return ssm::launch_lti_conv(p, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status_t ssm_lti_fwd(const void *x, const float *delta, const float *A, const float *B, const float *C,
+                         const float *D, const void *z, void *y, int64_t b, int64_t d, int64_t L, int64_t N,
+                         ssm_dtype_t dtype, hipStream_t stream) {
+    const ssm_status_t st = lti_conv_check(x, nullptr, true, D, z, y, b, d, L, dtype);
+    if (st != SSM_OK) return st;
+    if (!delta || !A || !B || !C) return SSM_ERR_NULL;
+    if (N < 1) return SSM_ERR_SHAPE;
+    if (N > SSM_MAX_N) return SSM_ERR_UNSUPPORTED;
+    const int64_t es = dtype == SSM_BF16 ? 2 : 4;
+    const Span out{y, b * d * L * es};
+    const Span ins[] = {{delta, d * 4}, {A, d * N * 4}, {B, d * N * 4}, {C, d * N * 4}};
+    for (const Span &in : ins)
+        if (overlaps(out, in)) return SSM_ERR_ALIAS;
+    void *K = nullptr;
+    keep_pool_memory();
+    if (hipMallocAsync(&K, (size_t)(d * L) * sizeof(float), stream) != hipSuccess) return SSM_ERR_HIP;
+    const ssm::LtiKernelLaunch pk{delta, A, B, C, static_cast<float *>(K), d, L, N};
+    hipError_t e = ssm::launch_lti_kernel(pk, stream);
+    if (e == hipSuccess) {
+        const ssm::LtiConvLaunch pc{x, z, static_cast<const float *>(K), D, y, b, d, L, dtype == SSM_BF16};
+        e = ssm::launch_lti_conv(pc, stream);
+    }
+    if (hipFreeAsync(K, stream) != hipSuccess) return SSM_ERR_HIP;
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 }  // extern "C"

@@ -72,6 +72,25 @@ struct ConvStepLaunch {
     bool bf16;
 };
 hipError_t launch_conv1d(const ConvLaunch &p, hipStream_t stream);
+
+// LTI convolution form: the kernel K̄ and its FFT convolution with x (transform sizes 2^10 … 2^14).
+constexpr int kLtiMinLog2 = 10;
+constexpr int kLtiMaxLog2 = 14;
+struct LtiKernelLaunch {
+    const float *delta, *A, *B, *C;
+    float *K;
+    int64_t d, L, N;
+};
+struct LtiConvLaunch {
+    const void *x, *z;                 // z nullable
+    const float *K, *D;                // D nullable
+    void *y;
+    int64_t b, d, L;
+    bool bf16;
+};
+int lti_fft_log2(int64_t L);           // log2 of the transform size used for sequence length L
+hipError_t launch_lti_kernel(const LtiKernelLaunch &p, hipStream_t stream);
+hipError_t launch_lti_conv(const LtiConvLaunch &p, hipStream_t stream);
 hipError_t launch_conv_step(const ConvStepLaunch &p, hipStream_t stream);
 
 struct StepLaunch {

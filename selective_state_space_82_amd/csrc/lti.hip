@@ -1,0 +1,401 @@
+// lti.hip — the time-invariant (LTI) form of the SSM, evaluated as a convolution through the FFT.
+//
+// Page "State Space Models（SSM）とMamba" §2.3, and page "Mambaとは？Transformer以外の系列モデル", section
+// 固定SSMには「再帰」と「畳み込み」の二つの顔がある: when Ā, B̄ and C are the same at every step, the
+// zero-state recurrence unrolls into y = x ∗ K̄ with K̄ = (CB̄, CĀB̄, CĀ²B̄, …), K̄ can be computed ahead,
+// and the convolution costs O(L log L) through the FFT. Here every channel d is its own system with a
+// diagonal A[d][·], B[d][·], C[d][·] and step Δ_d, so K̄_d[k] = Σ_n C_n B̄_n Ā_n^k.
+//
+// Two kernels:
+//   lti_kernel_kernel     K̄ [d][L] fp32, one thread per (d, k): Ā^k = 2^{k·Δ·a·log2 e}.
+//   lti_fft_conv_kernel   y = x ∗ K̄ + D·x (· silu(z)), one workgroup per channel. D is folded into the
+//                         kernel's first tap (y_t = Σ_s K'_{t−s} x_s with K'_0 = K̄_0 + D). Two batch rows
+//                         of the channel share one complex transform (x_b1 + i·x_b2; K̄ is real, so the
+//                         real and imaginary parts of the result are the two rows' outputs). The
+//                         transform has M = 2^LOGM ≥ 2L points (zero padding makes the circular
+//                         convolution linear on the first L outputs).
+//
+// The transform (M/16 threads, 16 complex values per thread): a decimation-in-frequency forward pass
+// sequence (natural order in, digit-reversed out) and its exact inverse, a decimation-in-time sequence
+// with conjugate roots (digit-reversed in, natural out), so no reordering is ever done: the product
+// with K̄'s spectrum is taken in the digit-reversed order both forward transforms leave behind, in
+// registers. Each pass is one radix-R step on groups of R values a span apart, with the in-group DFT in
+// registers (radix-2 stages) and the values exchanged through LDS between passes. The first forward
+// pass takes its inputs straight from global memory and the last inverse pass hands its outputs straight
+// to the epilogue. Twiddles W_M^i = e^{−2πi·i/M} come from two small LDS tables (W_M^{64j} and W_M^{j},
+// j < 64, filled with sincospi at the start) and products of their entries.
+#include "device_common.h"
+#include "launch.h"
+
+namespace ssm {
+namespace {
+
+struct LtiKernelArgs {
+    const float *delta, *A, *B, *C;
+    float *K;
+    int64_t d, L, N, blocks_per_channel, n_blocks;
+};
+
+__global__ __launch_bounds__(256) void lti_kernel_kernel(LtiKernelArgs a) {
+    for (int64_t blk = blockIdx.x; blk < a.n_blocks; blk += gridDim.x) {
+        const int64_t id = blk / a.blocks_per_channel;  // uniform across the workgroup
+        const int64_t k = (blk - id * a.blocks_per_channel) * 256 + threadIdx.x;
+        if (k >= a.L) continue;
+        const float dt = a.delta[id];
+        const float kf = (float)k;  // exact for k < 2^24
+        float acc = 0.0f;
+        for (int64_t n = 0; n < a.N; ++n) {
+            const float an = a.A[id * a.N + n];
+            const float u = dt * (an * kLog2e);
+            const float abar = exp2_fast(u);
+            const float coef = zoh_input_coef_log2(dt, u, abar, 1.0f / an);
+            const float cb = a.C[id * a.N + n] * (coef * a.B[id * a.N + n]);
+            acc = __builtin_fmaf(cb, exp2_fast(kf * u), acc);
+        }
+        a.K[id * a.L + k] = acc;
+    }
+}
+
+// ---- complex helpers ----------------------------------------------------------------------------
+__device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+__device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+    return make_float2(__builtin_fmaf(a.x, b.x, -a.y * b.y), __builtin_fmaf(a.x, b.y, a.y * b.x));
+}
+// a · conj(b)
+__device__ __forceinline__ float2 cmulc(float2 a, float2 b) {
+    return make_float2(__builtin_fmaf(a.x, b.x, a.y * b.y), __builtin_fmaf(a.y, b.x, -a.x * b.y));
+}
+
+// v · W_16^k (or · conj(W_16^k) when INV), W_16 = e^{−2πi/16}, k in [0, 8); k is a constant after
+// unrolling, so the switch folds away.
+template <bool INV>
+__device__ __forceinline__ float2 rot16(float2 v, int k) {
+    constexpr float c1 = 0.92387953251128676f;  // cos(π/8)
+    constexpr float s1 = 0.38268343236508977f;  // sin(π/8)
+    constexpr float h = 0.70710678118654752f;   // cos(π/4)
+    float2 w;
+    switch (k) {
+        case 0: return v;
+        case 4: return INV ? make_float2(-v.y, v.x) : make_float2(v.y, -v.x);  // · (±i)
+        case 1: w = make_float2(c1, -s1); break;
+        case 2: w = make_float2(h, -h); break;
+        case 3: w = make_float2(s1, -c1); break;
+        case 5: w = make_float2(-s1, -c1); break;
+        case 6: w = make_float2(-h, -h); break;
+        default: w = make_float2(-c1, -s1); break;  // 7
+    }
+    return INV ? cmulc(v, w) : cmul(v, w);
+}
+
+constexpr int bitrev(int i, int R) {
+    int r = 0;
+    for (int m = 1; m < R; m <<= 1) r = (r << 1) | ((i & m) ? 1 : 0);
+    return r;
+}
+
+// DFT of R values in registers by radix-2 decimation in frequency: natural order in, bit-reversed out.
+template <int R>
+__device__ __forceinline__ void dft_dif(float2 *v) {
+#pragma unroll
+    for (int h = R / 2; h >= 1; h >>= 1)
+#pragma unroll
+        for (int blk = 0; blk < R; blk += 2 * h)
+#pragma unroll
+            for (int i = 0; i < h; ++i) {
+                const float2 p = v[blk + i], q = v[blk + i + h];
+                v[blk + i] = cadd(p, q);
+                v[blk + i + h] = rot16<false>(csub(p, q), i * (8 / h));
+            }
+}
+
+// Inverse DFT (conjugate roots, no 1/R) of R values by radix-2 decimation in time: bit-reversed in,
+// natural out. Undoes dft_dif up to the factor R.
+template <int R>
+__device__ __forceinline__ void idft_dit(float2 *v) {
+#pragma unroll
+    for (int h = 1; h < R; h <<= 1)
+#pragma unroll
+        for (int blk = 0; blk < R; blk += 2 * h)
+#pragma unroll
+            for (int i = 0; i < h; ++i) {
+                const float2 p = v[blk + i], q = rot16<true>(v[blk + i + h], i * (8 / h));
+                v[blk + i] = cadd(p, q);
+                v[blk + i + h] = csub(p, q);
+            }
+}
+
+// LDS index with one pad slot every 16 values (keeps the stride-16 accesses of the short passes off a
+// single bank).
+__device__ __forceinline__ int pad(int e) { return e + (e >> 4); }
+
+template <int LOGM>
+struct Fft {
+    static constexpr int M = 1 << LOGM;
+    static constexpr int NT = M / 16;                               // threads
+    static constexpr int R0 = (LOGM % 4) == 0 ? 16 : (1 << (LOGM % 4));  // radix of the widest pass
+    static constexpr int G0 = 16 / R0;                              // its groups per thread
+    static constexpr int Q0 = M / R0;                               // its span between group values
+    static constexpr int PADDED = M + M / 16;
+
+    float2 *buf, *tw_hi, *tw_lo;
+    int tid;
+
+    // W_M^i for 0 <= i < M
+    __device__ __forceinline__ float2 tw(int i) const { return cmul(tw_hi[i >> 6], tw_lo[i & 63]); }
+
+    // w[k] = W_M^{idx·k} for k < R (idx·(R−1) < M)
+    template <int R>
+    __device__ __forceinline__ void powers(int idx, float2 *w) const {
+        w[0] = make_float2(1.0f, 0.0f);
+        if (R > 1) w[1] = tw(idx);
+        if (R > 2) {
+            w[2] = cmul(w[1], w[1]);
+            w[3] = cmul(w[2], w[1]);
+        }
+        if (R > 4) {
+            const float2 w4 = tw(4 * idx);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[4 + k] = k == 0 ? w4 : cmul(w4, w[k]);
+        }
+        if (R > 8) {
+            const float2 w8 = tw(8 * idx);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) w[8 + k] = k == 0 ? w8 : cmul(w8, w[k]);
+        }
+    }
+
+    // Position of register slot s (= u·R0 + j) in the widest pass: group u of this thread, value j.
+    __device__ __forceinline__ int wide_pos(int s) const {
+        const int u = s / R0, j = s % R0;
+        return tid + NT * (u + j * G0);
+    }
+
+    // Forward, widest pass: v holds the natural-order inputs at wide_pos(s); writes to LDS.
+    __device__ __forceinline__ void fwd_wide(float2 *v) const {
+#pragma unroll
+        for (int u = 0; u < G0; ++u) {
+            float2 *g = v + u * R0;
+            const int r = tid + NT * u;
+            dft_dif<R0>(g);
+            float2 w[R0];
+            powers<R0>(r, w);
+#pragma unroll
+            for (int i = 0; i < R0; ++i) {
+                const int k = bitrev(i, R0);
+                buf[pad(r + k * Q0)] = k == 0 ? g[i] : cmul(g[i], w[k]);
+            }
+        }
+    }
+
+    // Forward radix-16 pass with span 16·Q between group values' blocks; Q > 1 goes LDS → LDS,
+    // Q == 1 (the last) leaves the digit-reversed result in v.
+    template <int Q>
+    __device__ __forceinline__ void fwd16(float2 *v) const {
+        const int r = tid % Q, base = (tid / Q) * (16 * Q) + r;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = buf[pad(base + j * Q)];
+        dft_dif<16>(v);
+        if constexpr (Q > 1) {
+            float2 w[16];
+            powers<16>(r * (M / (16 * Q)), w);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int k = bitrev(i, 16);
+                buf[pad(base + k * Q)] = k == 0 ? v[i] : cmul(v[i], w[k]);
+            }
+        }
+    }
+
+    // Inverse radix-16 pass, the mirror of fwd16<Q>: Q == 1 takes v (digit-reversed) from registers.
+    template <int Q>
+    __device__ __forceinline__ void inv16(float2 *v) const {
+        const int r = tid % Q, base = (tid / Q) * (16 * Q) + r;
+        if constexpr (Q > 1) {
+            float2 w[16];
+            powers<16>(r * (M / (16 * Q)), w);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int k = bitrev(i, 16);
+                const float2 c = buf[pad(base + k * Q)];
+                v[i] = k == 0 ? c : cmulc(c, w[k]);
+            }
+        }
+        idft_dit<16>(v);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) buf[pad(base + j * Q)] = v[j];
+    }
+
+    // Inverse, widest pass: reads LDS, leaves natural-order outputs at wide_pos(s) in v.
+    __device__ __forceinline__ void inv_wide(float2 *v) const {
+#pragma unroll
+        for (int u = 0; u < G0; ++u) {
+            float2 *g = v + u * R0;
+            const int r = tid + NT * u;
+            float2 w[R0];
+            powers<R0>(r, w);
+#pragma unroll
+            for (int i = 0; i < R0; ++i) {
+                const int k = bitrev(i, R0);
+                const float2 c = buf[pad(r + k * Q0)];
+                g[i] = k == 0 ? c : cmulc(c, w[k]);
+            }
+            idft_dit<R0>(g);
+        }
+    }
+
+    // Radix-16 passes below the widest one, spans Q0/16, Q0/256, …, 1.
+    template <int Q>
+    __device__ __forceinline__ void fwd_rest(float2 *v) const {
+        fwd16<Q>(v);
+        if constexpr (Q > 1) {
+            __syncthreads();
+            fwd_rest<Q / 16>(v);
+        }
+    }
+    template <int Q>
+    __device__ __forceinline__ void inv_rest(float2 *v) const {
+        if constexpr (Q > 1) {
+            inv_rest<Q / 16>(v);
+            __syncthreads();
+        }
+        inv16<Q>(v);
+    }
+
+    // Full forward transform of v (natural order at wide_pos) into v (digit-reversed, registers).
+    __device__ __forceinline__ void forward(float2 *v) const {
+        fwd_wide(v);
+        __syncthreads();
+        fwd_rest<Q0 / 16>(v);
+    }
+    // Full inverse transform (times M) of v (digit-reversed, registers) into v (natural, wide_pos).
+    __device__ __forceinline__ void inverse(float2 *v) const {
+        inv_rest<Q0 / 16>(v);
+        __syncthreads();
+        inv_wide(v);
+    }
+};
+
+struct LtiConvArgs {
+    const void *x, *z;
+    const float *K, *D;
+    void *y;
+    int64_t b, d, L;
+};
+
+template <typename T, int LOGM>
+__global__ __launch_bounds__((1 << LOGM) / 16) void lti_fft_conv_kernel(LtiConvArgs a) {
+    using F = Fft<LOGM>;
+    constexpr int M = F::M;
+    __shared__ float2 s_buf[F::PADDED];
+    __shared__ float2 s_hi[M / 64], s_lo[64];
+    F f{s_buf, s_hi, s_lo, (int)threadIdx.x};
+
+    // twiddle tables: s_hi[j] = W_M^{64 j}, s_lo[j] = W_M^{j}
+    for (int j = threadIdx.x; j < M / 64 + 64; j += F::NT) {
+        const int i = j < M / 64 ? 64 * j : j - M / 64;
+        float s, c;
+        sincospif(2.0f * (float)i / (float)M, &s, &c);  // 2i/M is exact
+        (j < M / 64 ? s_hi[j] : s_lo[j - M / 64]) = make_float2(c, -s);
+    }
+    __syncthreads();
+
+    const int64_t id = blockIdx.x;
+    const int L = (int)a.L;
+
+    // spectrum of K' (K̄ with D added to its first tap), kept in registers
+    float2 kf[16];
+    {
+        const float *Kd = a.K + id * a.L;
+        const float dsk = a.D ? a.D[id] : 0.0f;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const int e = f.wide_pos(s);
+            float v = e < L ? Kd[e] : 0.0f;
+            if (e == 0) v += dsk;
+            kf[s] = make_float2(v, 0.0f);
+        }
+        f.forward(kf);
+    }
+
+    const T *xg = static_cast<const T *>(a.x);
+    const T *zg = static_cast<const T *>(a.z);
+    T *yg = static_cast<T *>(a.y);
+    constexpr float inv_m = 1.0f / (float)M;
+    for (int64_t b1 = 0; b1 < a.b; b1 += 2) {
+        const bool two = b1 + 1 < a.b;
+        const int64_t r1 = (b1 * a.d + id) * a.L;
+        const int64_t r2 = two ? r1 + a.d * a.L : r1;
+        float2 v[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const int e = f.wide_pos(s);
+            const bool in = e < L;
+            v[s] = make_float2(in ? widen(xg[r1 + e]) : 0.0f, in && two ? widen(xg[r2 + e]) : 0.0f);
+        }
+        __syncthreads();  // the previous pair's last reads of s_buf are done
+        f.forward(v);
+#pragma unroll
+        for (int s = 0; s < 16; ++s) v[s] = cmul(v[s], kf[s]);
+        f.inverse(v);
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const int e = f.wide_pos(s);
+            if (e < L) {
+                float y1 = v[s].x * inv_m, y2 = v[s].y * inv_m;
+                if (zg) {
+                    y1 *= silu(widen(zg[r1 + e]));
+                    if (two) y2 *= silu(widen(zg[r2 + e]));
+                }
+                yg[r1 + e] = narrow<T>(y1);
+                if (two) yg[r2 + e] = narrow<T>(y2);
+            }
+        }
+    }
+}
+
+template <typename T, int LOGM>
+hipError_t launch_conv_m(const LtiConvArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((lti_fft_conv_kernel<T, LOGM>), dim3((unsigned)a.d), dim3((1 << LOGM) / 16), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_conv_typed(const LtiConvArgs &a, int logm, hipStream_t stream) {
+    switch (logm) {
+        case 10: return launch_conv_m<T, 10>(a, stream);
+        case 11: return launch_conv_m<T, 11>(a, stream);
+        case 12: return launch_conv_m<T, 12>(a, stream);
+        case 13: return launch_conv_m<T, 13>(a, stream);
+        case 14: return launch_conv_m<T, 14>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int lti_fft_log2(int64_t L) {
+    int logm = kLtiMinLog2;
+    while ((int64_t(1) << logm) < 2 * L) ++logm;
+    return logm;
+}
+
+hipError_t launch_lti_kernel(const LtiKernelLaunch &p, hipStream_t stream) {
+    if (p.d == 0 || p.L == 0) return hipSuccess;
+    LtiKernelArgs a{p.delta, p.A, p.B, p.C, p.K, p.d, p.L, p.N, (p.L + 255) / 256, 0};
+    a.n_blocks = p.d * a.blocks_per_channel;
+    const int64_t grid = a.n_blocks < (int64_t(1) << 30) ? a.n_blocks : (int64_t(1) << 30);
+    hipLaunchKernelGGL(lti_kernel_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_lti_conv(const LtiConvLaunch &p, hipStream_t stream) {
+    if (p.b == 0 || p.d == 0 || p.L == 0) return hipSuccess;
+    const LtiConvArgs a{p.x, p.z, p.K, p.D, p.y, p.b, p.d, p.L};
+    const int logm = lti_fft_log2(p.L);
+    if (logm > kLtiMaxLog2) return hipErrorInvalidValue;
+    if (p.bf16) return launch_conv_typed<uint16_t>(a, logm, stream);
+    return launch_conv_typed<float>(a, logm, stream);
+}
+
+}  // namespace ssm

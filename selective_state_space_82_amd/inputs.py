@@ -236,3 +236,26 @@ def random_prefill(b, d, L, N, dtype="f32", gate=True, seed=0, delta_mu=-3.0, de
         "dtype": dtype,
         "shape": (b, d, L, N),
     }
+
+
+def random_lti(b, d, L, N, dtype="f32", gate=True, seed=0, delta_mu=-3.0, delta_sigma=1.0, with_D=True,
+               a_zero_frac=0.0) -> dict:
+    """Inputs of the time-invariant (convolution) form: every channel its own system.
+    x, z [b][d][L] in storage form; delta [d] = softplus(N(mu, sigma)); A [d][N] = -(n+1); B, C [d][N]
+    and D [d] ~ N(0, 1); all parameters fp32. a_zero_frac > 0 zeroes that fraction of A (the ZOH limit)."""
+    tag = f"lti_{b}_{d}_{L}_{N}_{dtype}_{int(gate)}_{delta_mu}_{delta_sigma}_{a_zero_frac}"
+    g = lambda t: _gen(seed, tag, t)
+    A = _a_matrix(seed, tag, d, N, "neg_index")
+    if a_zero_frac > 0:
+        A = np.where(g("A0").uniform(size=(d, N)) < a_zero_frac, np.float32(0.0), A).astype(np.float32)
+    return {
+        "x": store(g("x").standard_normal((b, d, L)), dtype),
+        "z": store(g("z").standard_normal((b, d, L)), dtype) if gate else None,
+        "delta": _softplus(g("delta").normal(delta_mu, delta_sigma, size=d)).astype(np.float32),
+        "A": A,
+        "B": g("B").standard_normal((d, N)).astype(np.float32),
+        "C": g("C").standard_normal((d, N)).astype(np.float32),
+        "D": g("D").standard_normal(d).astype(np.float32) if with_D else None,
+        "dtype": dtype,
+        "shape": (b, d, L, N),
+    }

@@ -152,3 +152,38 @@ def test_conv_validation():
     assert step(st=None) == 1
     assert step(W=9) == 3
     assert step(xo=FAKE) == 5
+
+
+def test_lti_validation():
+    L = api.lib()
+    P = lambda a: ctypes.c_void_p(a)
+
+    def kern(delta=P(0x100000), A=P(0x200000), B=P(0x300000), C=P(0x400000), K=P(0x500000), d=4, Ln=16, N=4):
+        return L.ssm_lti_kernel(delta, A, B, C, K, d, Ln, N, None)
+    assert kern(delta=None) == 1
+    assert kern(K=None) == 1
+    assert kern(d=0) == 2
+    assert kern(N=0) == 2
+    assert kern(N=65) == 3
+    assert kern(Ln=1 << 24) == 2
+    assert kern(K=P(0x200000 + 4)) == 5                              # K overlaps A
+
+    def conv(x=P(0x100000), K=P(0x200000), D=None, z=None, y=P(0x900000), b=2, d=4, Ln=16, dt=0):
+        return L.ssm_lti_conv(x, K, D, z, y, b, d, Ln, dt, None)
+    assert conv(x=None) == 1
+    assert conv(K=None) == 1
+    assert conv(y=None) == 1
+    assert conv(Ln=0) == 2
+    assert conv(d=(1 << 22) + 1) == 2
+    assert conv(Ln=8193) == 3                                        # beyond the largest transform
+    assert conv(dt=7) == 3
+    assert conv(y=P(0x100000 + 64)) == 5                             # y overlaps x
+    assert conv(z=P(0x900000 - 8)) == 5                              # y overlaps z
+
+    def fwd(x=P(0x100000), delta=P(0x200000), y=P(0x900000), N=4, Ln=16):
+        return L.ssm_lti_fwd(x, delta, P(0x300000), P(0x400000), P(0x500000), None, None, y, 2, 4, Ln, N, 0, None)
+    assert fwd(delta=None) == 1
+    assert fwd(N=0) == 2
+    assert fwd(N=65) == 3
+    assert fwd(Ln=9000) == 3
+    assert fwd(y=P(0x200000)) == 5                                   # y overlaps delta
