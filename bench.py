@@ -196,8 +196,8 @@ def bench_lti(name, steps, warmup, quiet=False):
     inp = I.random_lti(w.b, w.d, w.L, w.N, dtype=w.dtype, gate=w.gate, seed=2)
     esize = 4 if w.dtype == "f32" else 2
     rows = w.b * w.d * w.L
-    # read x, z; write y; read the parameters (K̄ itself stays in L2-sized scratch per channel block)
-    nbytes = rows * esize * (3 if w.gate else 2) + w.d * (3 * w.N + 2) * 4
+    # read x, z; write y; read the parameters; K̄ [d][L] fp32 is written once and read once
+    nbytes = rows * esize * (3 if w.gate else 2) + w.d * (3 * w.N + 2) * 4 + 2 * w.d * w.L * 4
     M = lti_fft_points(w.L)
     transforms = w.d * (1 + 2 * ((w.b + 1) // 2))
     flops = transforms * 5 * M * math.log2(M) + w.d * ((w.b + 1) // 2) * 6 * M  # radix-2 count

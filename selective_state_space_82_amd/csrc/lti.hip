@@ -7,7 +7,7 @@
 // diagonal A[d][·], B[d][·], C[d][·] and step Δ_d, so K̄_d[k] = Σ_n C_n B̄_n Ā_n^k.
 //
 // Two kernels:
-//   lti_kernel_kernel     K̄ [d][L] fp32, one thread per (d, k): Ā^k = 2^{k·Δ·a·log2 e}.
+//   lti_kernel_kernel     K̄ [d][L] fp32, eight consecutive taps per thread: Ā^k from 2^{k·Δ·a·log2 e}.
 //   lti_fft_conv_kernel   y = x ∗ K̄ + D·x (· silu(z)), one workgroup per channel. D is folded into the
 //                         kernel's first tap (y_t = Σ_s K'_{t−s} x_s with K'_0 = K̄_0 + D). Two batch rows
 //                         of the channel share one complex transform (x_b1 + i·x_b2; K̄ is real, so the
@@ -26,6 +26,7 @@
 // j < 64, filled with sincospi at the start) and products of their entries.
 #include "device_common.h"
 #include "launch.h"
+#include "ssm_scan.h"
 
 namespace ssm {
 namespace {
@@ -36,23 +37,49 @@ struct LtiKernelArgs {
     int64_t d, L, N, blocks_per_channel, n_blocks;
 };
 
+constexpr int kKgenPerThread = 8;  // consecutive taps per thread
+
+// One workgroup covers 256·8 consecutive taps of one channel: the channel's per-state constants
+// (Ā = 2^u, cb = C·B̄) are formed once into LDS, then each thread takes 2^{k0·u} once per state and
+// walks its 8 taps by products (at most 7 roundings from the exponential).
 __global__ __launch_bounds__(256) void lti_kernel_kernel(LtiKernelArgs a) {
+    __shared__ float s_u[SSM_MAX_N], s_cb[SSM_MAX_N];
     for (int64_t blk = blockIdx.x; blk < a.n_blocks; blk += gridDim.x) {
         const int64_t id = blk / a.blocks_per_channel;  // uniform across the workgroup
-        const int64_t k = (blk - id * a.blocks_per_channel) * 256 + threadIdx.x;
-        if (k >= a.L) continue;
-        const float dt = a.delta[id];
-        const float kf = (float)k;  // exact for k < 2^24
-        float acc = 0.0f;
-        for (int64_t n = 0; n < a.N; ++n) {
+        const int64_t k0 = ((blk - id * a.blocks_per_channel) * 256 + threadIdx.x) * kKgenPerThread;
+        __syncthreads();  // the previous channel's constants are no longer read
+        if (threadIdx.x < a.N) {
+            const int64_t n = threadIdx.x;
+            const float dt = a.delta[id];
             const float an = a.A[id * a.N + n];
             const float u = dt * (an * kLog2e);
             const float abar = exp2_fast(u);
-            const float coef = zoh_input_coef_log2(dt, u, abar, 1.0f / an);
-            const float cb = a.C[id * a.N + n] * (coef * a.B[id * a.N + n]);
-            acc = __builtin_fmaf(cb, exp2_fast(kf * u), acc);
+            s_u[n] = u;
+            s_cb[n] = a.C[id * a.N + n] * (zoh_input_coef_log2(dt, u, abar, 1.0f / an) * a.B[id * a.N + n]);
         }
-        a.K[id * a.L + k] = acc;
+        __syncthreads();
+        if (k0 >= a.L) continue;
+        float acc[kKgenPerThread] = {};
+        for (int n = 0; n < (int)a.N; ++n) {
+            const float u = s_u[n];
+            float p = s_cb[n] * exp2_fast((float)k0 * u);  // k0 < 2^24: exact
+            const float step = exp2_fast(u);
+#pragma unroll
+            for (int j = 0; j < kKgenPerThread; ++j) {
+                acc[j] += p;
+                p *= step;
+            }
+        }
+        float *Kd = a.K + id * a.L;
+        if (k0 + kKgenPerThread <= a.L && (a.L % 4) == 0 && (reinterpret_cast<uintptr_t>(a.K) & 15) == 0) {
+#pragma unroll
+            for (int j = 0; j < kKgenPerThread; j += 4)
+                *reinterpret_cast<float4 *>(Kd + k0 + j) = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kKgenPerThread; ++j)
+                if (k0 + j < a.L) Kd[k0 + j] = acc[j];
+        }
     }
 }
 
@@ -126,8 +153,11 @@ __device__ __forceinline__ void idft_dit(float2 *v) {
 }
 
 // LDS index with one pad slot every 16 values (keeps the stride-16 accesses of the short passes off a
-// single bank).
+// single bank). For a span Q that is 1 or a multiple of 16 and a group start g with g % 16 + 15·Q < 16
+// when Q == 1 (groups of 16 aligned to 16), pad(g + j·Q) = pad(g) + j·padded_stride(Q): the group's
+// values sit at constant offsets from one address.
 __device__ __forceinline__ int pad(int e) { return e + (e >> 4); }
+constexpr int padded_stride(int Q) { return Q == 1 ? 1 : Q + Q / 16; }
 
 template <int LOGM>
 struct Fft {
@@ -144,24 +174,21 @@ struct Fft {
     // W_M^i for 0 <= i < M
     __device__ __forceinline__ float2 tw(int i) const { return cmul(tw_hi[i >> 6], tw_lo[i & 63]); }
 
-    // w[k] = W_M^{idx·k} for k < R (idx·(R−1) < M)
-    template <int R>
-    __device__ __forceinline__ void powers(int idx, float2 *w) const {
-        w[0] = make_float2(1.0f, 0.0f);
-        if (R > 1) w[1] = tw(idx);
-        if (R > 2) {
-            w[2] = cmul(w[1], w[1]);
-            w[3] = cmul(w[2], w[1]);
-        }
-        if (R > 4) {
-            const float2 w4 = tw(4 * idx);
+    // v[bitrev(k)] ·= W_M^{idx·k} (CONJ: its conjugate) for 0 < k < R, idx·(R−1) < M. The powers are
+    // built one product at a time from W_M^{idx}, restarting from a table value every fourth k, so at
+    // most three roundings separate any of them from its exact value and only two stay live.
+    template <int R, bool CONJ>
+    __device__ __forceinline__ void twiddle(float2 *v, int idx) const {
+        if constexpr (R > 1) {
+            const float2 w1 = tw(idx);
+            float2 wk = w1;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) w[4 + k] = k == 0 ? w4 : cmul(w4, w[k]);
-        }
-        if (R > 8) {
-            const float2 w8 = tw(8 * idx);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) w[8 + k] = k == 0 ? w8 : cmul(w8, w[k]);
+            for (int k = 1; k < R; ++k) {
+                if (k % 4 == 0) wk = tw(k * idx);
+                else if (k > 1) wk = cmul(wk, w1);
+                float2 &t = v[bitrev(k, R)];
+                t = CONJ ? cmulc(t, wk) : cmul(t, wk);
+            }
         }
     }
 
@@ -178,13 +205,10 @@ struct Fft {
             float2 *g = v + u * R0;
             const int r = tid + NT * u;
             dft_dif<R0>(g);
-            float2 w[R0];
-            powers<R0>(r, w);
+            twiddle<R0, false>(g, r);
+            float2 *p = buf + pad(r);
 #pragma unroll
-            for (int i = 0; i < R0; ++i) {
-                const int k = bitrev(i, R0);
-                buf[pad(r + k * Q0)] = k == 0 ? g[i] : cmul(g[i], w[k]);
-            }
+            for (int i = 0; i < R0; ++i) p[bitrev(i, R0) * padded_stride(Q0)] = g[i];
         }
     }
 
@@ -193,17 +217,14 @@ struct Fft {
     template <int Q>
     __device__ __forceinline__ void fwd16(float2 *v) const {
         const int r = tid % Q, base = (tid / Q) * (16 * Q) + r;
+        float2 *p = buf + pad(base);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = buf[pad(base + j * Q)];
+        for (int j = 0; j < 16; ++j) v[j] = p[j * padded_stride(Q)];
         dft_dif<16>(v);
         if constexpr (Q > 1) {
-            float2 w[16];
-            powers<16>(r * (M / (16 * Q)), w);
+            twiddle<16, false>(v, r * (M / (16 * Q)));
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int k = bitrev(i, 16);
-                buf[pad(base + k * Q)] = k == 0 ? v[i] : cmul(v[i], w[k]);
-            }
+            for (int i = 0; i < 16; ++i) p[bitrev(i, 16) * padded_stride(Q)] = v[i];
         }
     }
 
@@ -211,19 +232,15 @@ struct Fft {
     template <int Q>
     __device__ __forceinline__ void inv16(float2 *v) const {
         const int r = tid % Q, base = (tid / Q) * (16 * Q) + r;
+        float2 *p = buf + pad(base);
         if constexpr (Q > 1) {
-            float2 w[16];
-            powers<16>(r * (M / (16 * Q)), w);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int k = bitrev(i, 16);
-                const float2 c = buf[pad(base + k * Q)];
-                v[i] = k == 0 ? c : cmulc(c, w[k]);
-            }
+            for (int i = 0; i < 16; ++i) v[i] = p[bitrev(i, 16) * padded_stride(Q)];
+            twiddle<16, true>(v, r * (M / (16 * Q)));
         }
         idft_dit<16>(v);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) buf[pad(base + j * Q)] = v[j];
+        for (int j = 0; j < 16; ++j) p[j * padded_stride(Q)] = v[j];
     }
 
     // Inverse, widest pass: reads LDS, leaves natural-order outputs at wide_pos(s) in v.
@@ -232,14 +249,10 @@ struct Fft {
         for (int u = 0; u < G0; ++u) {
             float2 *g = v + u * R0;
             const int r = tid + NT * u;
-            float2 w[R0];
-            powers<R0>(r, w);
+            const float2 *p = buf + pad(r);
 #pragma unroll
-            for (int i = 0; i < R0; ++i) {
-                const int k = bitrev(i, R0);
-                const float2 c = buf[pad(r + k * Q0)];
-                g[i] = k == 0 ? c : cmulc(c, w[k]);
-            }
+            for (int i = 0; i < R0; ++i) g[i] = p[bitrev(i, R0) * padded_stride(Q0)];
+            twiddle<R0, true>(g, r);
             idft_dit<R0>(g);
         }
     }
@@ -284,7 +297,9 @@ struct LtiConvArgs {
 };
 
 template <typename T, int LOGM>
-__global__ __launch_bounds__((1 << LOGM) / 16) void lti_fft_conv_kernel(LtiConvArgs a) {
+// At most 128 VGPRs (four wavefronts per SIMD), so that four workgroups of 256 threads or two of 512 share
+// a CU; measured: without the bound, 2^13 points ran at 178 VGPRs, one workgroup per CU, and 1.7× slower.
+__global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiConvArgs a) {
     using F = Fft<LOGM>;
     constexpr int M = F::M;
     __shared__ float2 s_buf[F::PADDED];
@@ -299,22 +314,23 @@ __global__ __launch_bounds__((1 << LOGM) / 16) void lti_fft_conv_kernel(LtiConvA
         (j < M / 64 ? s_hi[j] : s_lo[j - M / 64]) = make_float2(c, -s);
     }
     __syncthreads();
-
     const int64_t id = blockIdx.x;
+
     const int L = (int)a.L;
 
     // spectrum of K' (K̄ with D added to its first tap), kept in registers
     float2 kf[16];
     {
-        const float *Kd = a.K + id * a.L;
         const float dsk = a.D ? a.D[id] : 0.0f;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) kf[s] = make_float2(0.0f, 0.0f);
+        const float *Kd = a.K + id * a.L;
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
             const int e = f.wide_pos(s);
-            float v = e < L ? Kd[e] : 0.0f;
-            if (e == 0) v += dsk;
-            kf[s] = make_float2(v, 0.0f);
+            if (e < L) kf[s].x = Kd[e];
         }
+        if (threadIdx.x == 0) kf[0].x += dsk;  // wide_pos(0) of thread 0 is position 0
         f.forward(kf);
     }
 
@@ -324,31 +340,36 @@ __global__ __launch_bounds__((1 << LOGM) / 16) void lti_fft_conv_kernel(LtiConvA
     constexpr float inv_m = 1.0f / (float)M;
     for (int64_t b1 = 0; b1 < a.b; b1 += 2) {
         const bool two = b1 + 1 < a.b;
-        const int64_t r1 = (b1 * a.d + id) * a.L;
-        const int64_t r2 = two ? r1 + a.d * a.L : r1;
+        // the pair's rows (workgroup-uniform pointers; per-lane offsets stay 32-bit)
+        const T *x1 = xg + (b1 * a.d + id) * a.L;
+        const T *x2 = two ? x1 + a.d * a.L : x1;
         float2 v[16];
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
             const int e = f.wide_pos(s);
             const bool in = e < L;
-            v[s] = make_float2(in ? widen(xg[r1 + e]) : 0.0f, in && two ? widen(xg[r2 + e]) : 0.0f);
+            v[s] = make_float2(in ? widen(x1[e]) : 0.0f, in && two ? widen(x2[e]) : 0.0f);
         }
         __syncthreads();  // the previous pair's last reads of s_buf are done
         f.forward(v);
 #pragma unroll
         for (int s = 0; s < 16; ++s) v[s] = cmul(v[s], kf[s]);
         f.inverse(v);
+        const int64_t o1 = (b1 * a.d + id) * a.L;
+        const int64_t o2 = two ? o1 + a.d * a.L : o1;
+        T *y1p = yg + o1, *y2p = yg + o2;
+        const T *z1 = zg ? zg + o1 : nullptr, *z2 = zg ? zg + o2 : nullptr;
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
             const int e = f.wide_pos(s);
             if (e < L) {
                 float y1 = v[s].x * inv_m, y2 = v[s].y * inv_m;
                 if (zg) {
-                    y1 *= silu(widen(zg[r1 + e]));
-                    if (two) y2 *= silu(widen(zg[r2 + e]));
+                    y1 *= silu(widen(z1[e]));
+                    if (two) y2 *= silu(widen(z2[e]));
                 }
-                yg[r1 + e] = narrow<T>(y1);
-                if (two) yg[r2 + e] = narrow<T>(y2);
+                y1p[e] = narrow<T>(y1);
+                if (two) y2p[e] = narrow<T>(y2);
             }
         }
     }
@@ -382,7 +403,8 @@ int lti_fft_log2(int64_t L) {
 
 hipError_t launch_lti_kernel(const LtiKernelLaunch &p, hipStream_t stream) {
     if (p.d == 0 || p.L == 0) return hipSuccess;
-    LtiKernelArgs a{p.delta, p.A, p.B, p.C, p.K, p.d, p.L, p.N, (p.L + 255) / 256, 0};
+    constexpr int64_t per_block = 256 * kKgenPerThread;
+    LtiKernelArgs a{p.delta, p.A, p.B, p.C, p.K, p.d, p.L, p.N, (p.L + per_block - 1) / per_block, 0};
     a.n_blocks = p.d * a.blocks_per_channel;
     const int64_t grid = a.n_blocks < (int64_t(1) << 30) ? a.n_blocks : (int64_t(1) << 30);
     hipLaunchKernelGGL(lti_kernel_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
