@@ -72,6 +72,8 @@ class Oracle:
         lib.oracle_lti_kernel.restype = ctypes.c_int
         lib.oracle_lti_conv.argtypes = [_DP] * 5 + [L, L, L]
         lib.oracle_lti_conv.restype = ctypes.c_int
+        lib.oracle_ssd_quadratic.argtypes = [_DP] * 8 + [L, L, L, L, L]
+        lib.oracle_ssd_quadratic.restype = ctypes.c_int
         lib.oracle_zoh.restype = None
         self.lib = lib
         self.path = lib_path
@@ -202,6 +204,33 @@ class Oracle:
         return y
 
 
+    def ssd_quadratic(self, x, delta, A, B, C, D=None, z=None, heads=None):
+        """y [b, H·P, L] of the scalar-decay SSM in its quadratic form: delta [b, H, L], A [H],
+        B, C [b, L, N], D [H·P]; x, z [b, H·P, L]."""
+        x = _f64(x)
+        delta = _f64(delta)
+        if x.ndim != 3 or delta.ndim != 3:
+            raise ValueError("x must be [b, H*P, L] and delta [b, H, L]")
+        b, d, L = x.shape
+        H = delta.shape[1]
+        if d % H:
+            raise ValueError("channels must split evenly into heads")
+        P = d // H
+        A = _f64(A, (H,))
+        B = _f64(B)
+        N = B.shape[2]
+        B = _f64(B, (b, L, N))
+        C = _f64(C, (b, L, N))
+        D = _f64(D, (d,))
+        z = _f64(z, (b, d, L))
+        y = np.empty_like(x)
+        rc = self.lib.oracle_ssd_quadratic(_ptr(x), _ptr(_f64(delta, (b, H, L))), _ptr(A), _ptr(B), _ptr(C),
+                                           _ptr(D), _ptr(z), _ptr(y), b, H, P, L, N)
+        if rc != 0:
+            raise ValueError("oracle_ssd_quadratic rejected its arguments")
+        return y
+
+
 _default = None
 
 
@@ -238,3 +267,7 @@ def lti_kernel(delta, A, B, C, L):
 
 def lti_conv(x, K, D=None, z=None):
     return default().lti_conv(x, K, D, z)
+
+
+def ssd_quadratic(x, delta, A, B, C, D=None, z=None):
+    return default().ssd_quadratic(x, delta, A, B, C, D, z)

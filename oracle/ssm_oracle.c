@@ -288,3 +288,46 @@ int oracle_lti_conv(const double *x, const double *K, const double *D, const dou
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------------------------------------
+ * The scalar-decay selective SSM written as one matrix acting on the whole sequence. Unrolling the
+ * recurrence ("Mambaとは？…", section Mambaの核心は入力依存のDelta、B、C; "State Space Models（SSM）とMamba"
+ * §4.2) gives y_t = Σ_{s<=t} C_t (Π_{r=s+1..t} Ā_r) B̄_s x_s. When A is one scalar a per head, the product
+ * of the Ā_r is the scalar exp(a Σ Δ_r), so the sequence map is y = (causal mask ∘ decay ∘ C Bᵀ)(β ∘ x):
+ * a masked linear attention with queries C, keys B and values x ("State Space Models（SSM）とMamba" §4.6:
+ * Mamba-2's state space duality relates SSMs and linear attention). Evaluated here entry by entry,
+ * O(L²) per head, with the decay exponent summed afresh for every (t, s).
+ * ------------------------------------------------------------------------------------------- */
+int oracle_ssd_quadratic(const double *x, const double *delta, const double *A, const double *B, const double *C,
+                         const double *D, const double *z, double *y, long b, long H, long P, long L, long N) {
+    if (!x || !delta || !A || !B || !C || !y || b < 0 || H < 0 || P < 1 || L < 0 || N < 1) return -1;
+    const long d = H * P;
+    for (long ib = 0; ib < b; ++ib) {
+        const double *Bb = B + (size_t)ib * (size_t)L * (size_t)N;
+        const double *Cb = C + (size_t)ib * (size_t)L * (size_t)N;
+        for (long h = 0; h < H; ++h) {
+            const double a = A[h];
+            const double *dl = delta + ((size_t)ib * (size_t)H + (size_t)h) * (size_t)L;
+            for (long t = 0; t < L; ++t) {
+                for (long p = 0; p < P; ++p) {
+                    const long ch = h * P + p;
+                    const double *xr = x + ((size_t)ib * (size_t)d + (size_t)ch) * (size_t)L;
+                    double acc = 0.0;
+                    for (long s = 0; s <= t; ++s) {
+                        double cb = 0.0; /* C_t · B_s */
+                        for (long n = 0; n < N; ++n) cb += Cb[(size_t)t * (size_t)N + (size_t)n] * Bb[(size_t)s * (size_t)N + (size_t)n];
+                        double sum = 0.0; /* Σ_{r=s+1..t} Δ_r */
+                        for (long r = s + 1; r <= t; ++r) sum += dl[r];
+                        double abar_s, beta_s;
+                        oracle_zoh(dl[s], a, &abar_s, &beta_s);
+                        acc += cb * exp(a * sum) * beta_s * xr[s];
+                    }
+                    double yt = acc + (D ? D[ch] : 0.0) * xr[t];
+                    if (z) yt *= silu(z[((size_t)ib * (size_t)d + (size_t)ch) * (size_t)L + (size_t)t]);
+                    y[((size_t)ib * (size_t)d + (size_t)ch) * (size_t)L + (size_t)t] = yt;
+                }
+            }
+        }
+    }
+    return 0;
+}

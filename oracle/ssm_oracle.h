@@ -82,6 +82,15 @@ int oracle_lti_kernel(const double *delta, const double *A, const double *B, con
 int oracle_lti_conv(const double *x, const double *K, const double *D, const double *z, double *y, long b,
                     long d, long L);
 
+/* The scalar-decay case in its quadratic ("dual", masked-attention) form. Channels come in H heads of P
+ * (d = H·P, channel h·P + p); every head has one scalar a_h (A = a_h·I for all N states) and one step
+ * delta[b][h][t] shared by its P channels; B, C [b][L][N] as for oracle_scan_fwd. Then
+ *   y[b][hP+p][t] = Σ_{s<=t} (C_t·B_s) · exp(a_h Σ_{r=s+1..t} Δ_r) · β_s · x[b][hP+p][s] + D·x, (· silu(z)),
+ * with β_s = (exp(Δ_s a_h) − 1)/a_h (Δ_s at a_h = 0), the recurrence of oracle_scan_fwd unrolled.
+ * x, z, y [b][H·P][L]; delta [b][H][L]; A [H]; D [H·P] or NULL; z may be NULL. Returns 0 or -1. */
+int oracle_ssd_quadratic(const double *x, const double *delta, const double *A, const double *B, const double *C,
+                         const double *D, const double *z, double *y, long b, long H, long P, long L, long N);
+
 /* ZOH coefficients of one diagonal entry: *abar = exp(delta·a), *bcoef = (exp(delta·a) − 1)/a
  * (delta at a = 0), so that B̄ = bcoef · B. */
 void oracle_zoh(double delta, double a, double *abar, double *bcoef);

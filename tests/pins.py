@@ -484,6 +484,41 @@ def pin_lti_conv_library(orc):
     _close(orc.lti_conv(x, K), want - D[None, :, None] * x, what="LTI conv, no D")
 
 
+def pin_ssd_duality(orc):
+    """Scalar decay per head: the quadratic (masked-attention) form equals the recurrent scan run with
+    Δ repeated over the head's channels and A = a_h on every state (the recurrence unrolled; pages:
+    Mamba-2's state space duality of SSMs and linear attention). One head has a = 0."""
+    rng = _rng(67)
+    b, H, P, L, N = 2, 3, 2, 11, 4
+    x = rng.normal(size=(b, H * P, L)); z = rng.normal(size=(b, H * P, L))
+    dl = rng.uniform(0.05, 1.0, size=(b, H, L))
+    A = -rng.uniform(0.2, 2.0, size=H); A[1] = 0.0
+    B = rng.normal(size=(b, L, N)); C = rng.normal(size=(b, L, N)); D = rng.normal(size=H * P)
+    y = orc.ssd_quadratic(x, dl, A, B, C, D=D, z=z)
+    yr, _ = orc.scan_fwd(x, np.repeat(dl, P, axis=1), np.repeat(A, P)[:, None].repeat(N, axis=1), B, C, D=D, z=z)
+    _close(y, yr, rtol=1e-10, atol=1e-12, what="SSD quadratic form vs recurrence")
+
+
+def pin_ssd_masked_attention(orc):
+    """With A = 0 and Δ = 1 the form is plain causal linear attention, y = tril(C Bᵀ) x (queries C, keys B,
+    values x); with a constant Δ and a ≠ 0 the mask is the Toeplitz decay exp(aΔ(t−s)) and the values
+    carry β = (e^{aΔ} − 1)/a. Both built with numpy matrix products."""
+    rng = _rng(71)
+    b, H, P, L, N = 1, 2, 3, 10, 5
+    x = rng.normal(size=(b, H * P, L)); B = rng.normal(size=(b, L, N)); C = rng.normal(size=(b, L, N))
+    G = np.tril(C[0] @ B[0].T)
+    y = orc.ssd_quadratic(x, np.ones((b, H, L)), np.zeros(H), B, C)
+    _close(y[0], x[0] @ G.T, what="linear attention")
+    a, dlt = np.array([-0.6, -1.7]), 0.3
+    y = orc.ssd_quadratic(x, np.full((b, H, L), dlt), a, B, C)
+    t = np.arange(L)
+    for h in range(H):
+        mask = np.tril(np.exp(a[h] * dlt * (t[:, None] - t[None, :])))
+        beta = np.expm1(a[h] * dlt) / a[h]
+        want = (x[0, h * P:(h + 1) * P] * beta) @ (G * mask).T
+        _close(y[0, h * P:(h + 1) * P], want, what=f"decayed attention, head {h}")
+
+
 ALL_PINS = [
     pin_scalar_worked_example,
     pin_delta_gate,
@@ -507,4 +542,6 @@ ALL_PINS = [
     pin_lti_kernel_van_loan,
     pin_lti_conv_equals_recurrence,
     pin_lti_conv_library,
+    pin_ssd_duality,
+    pin_ssd_masked_attention,
 ]

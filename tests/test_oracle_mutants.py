@@ -60,6 +60,12 @@ MUTANTS = {
     "lti_drop_D": ("double yt = acc + (D ? D[id] : 0.0) * x[row + (size_t)t];", "double yt = acc;"),
     "lti_gate_dropped": ("if (z) yt *= silu(z[row + (size_t)t]);\n                y[row + (size_t)t] = yt;",
                          "y[row + (size_t)t] = yt;"),
+    "ssd_strict_mask": ("for (long s = 0; s <= t; ++s) {", "for (long s = 0; s < t; ++s) {"),
+    "ssd_decay_from_s": ("for (long r = s + 1; r <= t; ++r) sum += dl[r];", "for (long r = s; r <= t; ++r) sum += dl[r];"),
+    "ssd_beta_dropped": ("acc += cb * exp(a * sum) * beta_s * xr[s];", "acc += cb * exp(a * sum) * xr[s];"),
+    "ssd_beta_at_t": ("oracle_zoh(dl[s], a, &abar_s, &beta_s);", "oracle_zoh(dl[t], a, &abar_s, &beta_s);"),
+    "ssd_key_at_t": ("cb += Cb[(size_t)t * (size_t)N + (size_t)n] * Bb[(size_t)s * (size_t)N + (size_t)n];",
+                     "cb += Cb[(size_t)t * (size_t)N + (size_t)n] * Bb[(size_t)t * (size_t)N + (size_t)n];"),
 }
 
 
