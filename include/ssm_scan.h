@@ -185,6 +185,27 @@ SSM_API ssm_status_t ssm_lti_fwd(const void *x, const float *delta, const float 
                                  ssm_dtype_t dtype, hipStream_t stream);
 
 /*
+ * The scalar-decay selective SSM of Mamba-2's state space duality (page "State Space Models（SSM）とMamba"
+ * §4.6 relates SSMs and linear attention; the pages give no formulas, so this is the selective scan of
+ * ssm_scan_fwd with A restricted to one scalar per head). Channels come in H heads of P; head h has the
+ * decay a_h (A[d][n] = a_h for its channels and all states) and one step delta[b][h][t] shared by its P
+ * channels. Unrolled, y = (causal mask ∘ e^{a(c_t − c_s)} ∘ C Bᵀ)(β ∘ x) + D x per head, a masked linear
+ * attention; it is evaluated chunk by chunk (64 steps) with fp32 matrix products on the MFMA units.
+ *   x, z, y           [b][H·P][L] dtype (z may be NULL)
+ *   delta             [b][H][L] dtype
+ *   A                 [H] fp32 (the per-head decay a_h)
+ *   B, C              [b][L][N] dtype (shared by all heads)
+ *   D                 [H·P] fp32 or NULL
+ *   initial_state     [b][H·P][N] fp32 or NULL (zeros); final_state [b][H·P][N] fp32 or NULL
+ * Supported: P = 64, N in {32, 64, 128} (SSM_ERR_UNSUPPORTED otherwise); b, H >= 1, L >= 0. Scratch of
+ * b·H·⌈L/64⌉·(P·N + 1) floats is taken stream-ordered from `stream`. Errors as for ssm_scan_fwd.
+ */
+SSM_API ssm_status_t ssm_ssd_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                                 const float *D, const void *z, const float *initial_state, void *y,
+                                 float *final_state, int64_t b, int64_t H, int64_t P, int64_t L, int64_t N,
+                                 ssm_dtype_t dtype, hipStream_t stream);
+
+/*
  * Options of ssm_scan_fwd_ex. Zero-initialise, then set what you need; zero means "choose".
  *   seg_len            time-segment length (multiple of 32) carried across by the chunk-carry
  *                      pass; 0 = chosen from the shape, >= L = one segment

@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_lti_conv.restype = i32
     L.ssm_lti_fwd.argtypes = [vp] * 8 + [i64, i64, i64, i64, i32, vp]
     L.ssm_lti_fwd.restype = i32
+    L.ssm_ssd_fwd.argtypes = [vp] * 10 + [i64, i64, i64, i64, i64, i32, vp]
+    L.ssm_ssd_fwd.restype = i32
     L.ssm_status_string.argtypes = [i32]
     L.ssm_status_string.restype = ctypes.c_char_p
     L.ssm_abi_version.argtypes = []
@@ -321,6 +323,39 @@ def ssm_lti_fwd(x, delta, A, B, C, D=None, z=None, *, y=None):
                                b, d, L, N, code, _stream(dev))
     _raise(status, "ssm_lti_fwd")
     return y
+
+
+def ssm_ssd_fwd(x, delta, A, B, C, D=None, z=None, *, y=None, initial_state=None, final_state=None,
+                return_final_state=True):
+    """Scalar-decay (state space duality) form, chunked on the MFMA units. x, z: [b, H*P, L] with P = 64;
+    delta: [b, H, L]; A: [H] fp32 (one decay per head); B, C: [b, L, N] with N in {32, 64, 128};
+    D: [H*P] fp32. Returns (y, final_state [b, H*P, N] fp32 or None)."""
+    if x.dim() != 3 or delta.dim() != 3 or B.dim() != 3:
+        raise ValueError("x must be [b, H*P, L], delta [b, H, L], B and C [b, L, N]")
+    b, d, L = x.shape
+    H = delta.shape[1]
+    if d % H:
+        raise ValueError("the channels must split evenly into heads")
+    P, N = d // H, B.shape[2]
+    dev, st = x.device, x.dtype
+    code = _dtype_code(st)
+    _check("delta", delta, (b, H, L), st, dev)
+    _check("A", A, (H,), torch.float32, dev)
+    _check("B", B, (b, L, N), st, dev)
+    _check("C", C, (b, L, N), st, dev)
+    _check("D", D, (d,), torch.float32, dev)
+    _check("z", z, (b, d, L), st, dev)
+    _check("initial_state", initial_state, (b, d, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty((b, d, L), dtype=st, device=dev)
+    _check("y", y, (b, d, L), st, dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((b, d, N), dtype=torch.float32, device=dev)
+    _check("final_state", final_state, (b, d, N), torch.float32, dev)
+    status = lib().ssm_ssd_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                               _ptr(initial_state), _ptr(y), _ptr(final_state), b, H, P, L, N, code, _stream(dev))
+    _raise(status, "ssm_ssd_fwd")
+    return y, final_state
 
 
 def ssm_conv1d_step(state, xin, w, bias=None, *, x_out=None, silu=True):

@@ -449,4 +449,47 @@ ssm_status_t ssm_lti_fwd(const void *x, const float *delta, const float *A, cons
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+ssm_status_t ssm_ssd_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                         const float *D, const void *z, const float *initial_state, void *y, float *final_state,
+                         int64_t b, int64_t H, int64_t P, int64_t L, int64_t N, ssm_dtype_t dtype,
+                         hipStream_t stream) {
+    if (!valid_dtype(dtype)) return SSM_ERR_UNSUPPORTED;
+    if (b < 1 || H < 1 || P < 1 || L < 0 || N < 1) return SSM_ERR_SHAPE;
+    if (P != 64 || (N != 32 && N != 64 && N != 128)) return SSM_ERR_UNSUPPORTED;
+    int64_t bd = 0, bdl = 0, bhl = 0, bln = 0, bdn = 0;
+    if (!mul_ok(b, H * P, &bd) || !mul_ok(bd, L > 0 ? L : 1, &bdl) || !mul_ok(b * H, L > 0 ? L : 1, &bhl) ||
+        !mul_ok(b * L, N, &bln) || !mul_ok(bd, N, &bdn) || bdl > (INT64_C(1) << 40))
+        return SSM_ERR_SHAPE;
+    if (b * H * ((L + 63) / 64) >= (INT64_C(1) << 31)) return SSM_ERR_SHAPE;
+    if (L > 0 && (!x || !delta || !A || !B || !C || !y)) return SSM_ERR_NULL;
+    const int64_t es = dtype == SSM_BF16 ? 2 : 4;
+    const Span outs[] = {{y, bdl * es}, {final_state, bdn * 4}};
+    const Span ins[] = {{x, bdl * es}, {delta, bhl * es}, {A, H * 4}, {B, bln * es}, {C, bln * es},
+                        {D, H * P * 4}, {z, bdl * es}, {initial_state, bdn * 4}};
+    for (const Span &o : outs)
+        for (const Span &in : ins)
+            if (overlaps(o, in)) return SSM_ERR_ALIAS;
+    if (overlaps(outs[0], outs[1])) return SSM_ERR_ALIAS;
+    if (L == 0) {
+        if (final_state) {
+            const hipError_t e = initial_state
+                ? hipMemcpyAsync(final_state, initial_state, (size_t)bdn * 4, hipMemcpyDeviceToDevice, stream)
+                : ssm::launch_fill_zero(final_state, bdn, stream);
+            return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+        }
+        return SSM_OK;
+    }
+    void *scratch = nullptr;
+    keep_pool_memory();
+    const int64_t floats = ssm::ssd_scratch_floats(b, H, L, N);
+    if (hipMallocAsync(&scratch, (size_t)floats * sizeof(float), stream) != hipSuccess) return SSM_ERR_HIP;
+    ssm::SsdLaunch p{};
+    p.x = x; p.delta = delta; p.B = B; p.C = C; p.z = z; p.A = A; p.D = D; p.h0 = initial_state;
+    p.y = y; p.hT = final_state; p.scratch = static_cast<float *>(scratch);
+    p.b = b; p.H = H; p.L = L; p.N = N; p.bf16 = dtype == SSM_BF16;
+    const hipError_t e = ssm::launch_ssd(p, stream);
+    if (hipFreeAsync(scratch, stream) != hipSuccess) return SSM_ERR_HIP;
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 }  // extern "C"

@@ -91,6 +91,19 @@ struct LtiConvLaunch {
 int lti_fft_log2(int64_t L);           // log2 of the transform size used for sequence length L
 hipError_t launch_lti_kernel(const LtiKernelLaunch &p, hipStream_t stream);
 hipError_t launch_lti_conv(const LtiConvLaunch &p, hipStream_t stream);
+
+// Scalar-decay (state space duality) form, chunked on the MFMA units: heads of 64 channels, N in {32, 64, 128}.
+struct SsdLaunch {
+    const void *x, *delta, *B, *C, *z;   // z nullable
+    const float *A, *D, *h0;             // D, h0 nullable
+    void *y;
+    float *hT;                           // nullable
+    float *scratch;                      // ssd_scratch_floats(b, H, L, N)
+    int64_t b, H, L, N;
+    bool bf16;
+};
+int64_t ssd_scratch_floats(int64_t b, int64_t H, int64_t L, int64_t N);
+hipError_t launch_ssd(const SsdLaunch &p, hipStream_t stream);
 hipError_t launch_conv_step(const ConvStepLaunch &p, hipStream_t stream);
 
 struct StepLaunch {

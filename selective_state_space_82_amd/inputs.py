@@ -259,3 +259,26 @@ def random_lti(b, d, L, N, dtype="f32", gate=True, seed=0, delta_mu=-3.0, delta_
         "dtype": dtype,
         "shape": (b, d, L, N),
     }
+
+
+def random_ssd(b, H, L, N, dtype="f32", gate=True, seed=0, delta_mu=-3.0, delta_sigma=1.0, with_D=True,
+               a_zero_heads=(), P=64) -> dict:
+    """Inputs of the scalar-decay (state space duality) form: H heads of P channels.
+    x, z [b][H·P][L] and delta [b][H][L] = softplus(N(mu, sigma)) in storage form; B, C [b][L][N] ~ N(0, 1)
+    in storage form; A [H] = -(h mod 16 + 1) fp32 (0 for the heads listed in a_zero_heads); D [H·P] ~ N(0, 1)."""
+    tag = f"ssd_{b}_{H}_{L}_{N}_{P}_{dtype}_{int(gate)}_{delta_mu}_{delta_sigma}"
+    g = lambda t: _gen(seed, tag, t)
+    A = -((np.arange(H) % 16) + 1.0)
+    for h in a_zero_heads:
+        A[h] = 0.0
+    return {
+        "x": store(g("x").standard_normal((b, H * P, L)), dtype),
+        "z": store(g("z").standard_normal((b, H * P, L)), dtype) if gate else None,
+        "delta": store(_softplus(g("delta").normal(delta_mu, delta_sigma, size=(b, H, L))), dtype),
+        "A": A.astype(np.float32),
+        "B": store(g("B").standard_normal((b, L, N)), dtype),
+        "C": store(g("C").standard_normal((b, L, N)), dtype),
+        "D": g("D").standard_normal(H * P).astype(np.float32) if with_D else None,
+        "dtype": dtype,
+        "shape": (b, H, P, L, N),
+    }

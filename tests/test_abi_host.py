@@ -187,3 +187,22 @@ def test_lti_validation():
     assert fwd(N=65) == 3
     assert fwd(Ln=9000) == 3
     assert fwd(y=P(0x200000)) == 5                                   # y overlaps delta
+
+
+def test_ssd_validation():
+    L = api.lib()
+    P_ = lambda a: ctypes.c_void_p(a)
+
+    def ssd(x=P_(0x100000), delta=P_(0x200000), A=P_(0x300000), B=P_(0x400000), C=P_(0x500000), y=P_(0x900000),
+            fs=None, h0=None, b=1, H=2, P=64, Ln=16, N=64, dt=0):
+        return L.ssm_ssd_fwd(x, delta, A, B, C, None, None, h0, y, fs, b, H, P, Ln, N, dt, None)
+    assert ssd(x=None) == 1
+    assert ssd(y=None) == 1
+    assert ssd(b=0) == 2
+    assert ssd(Ln=-1) == 2
+    assert ssd(P=32) == 3
+    assert ssd(N=16) == 3
+    assert ssd(N=256) == 3
+    assert ssd(dt=4) == 3
+    assert ssd(y=P_(0x100000 + 64)) == 5                             # y overlaps x
+    assert ssd(fs=P_(0x900000 + 128)) == 5                           # final state overlaps y
