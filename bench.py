@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0                        # MI355X HBM3E, published
 VALU_PEAK_TSLOT = 256 * 4 * 16 * 2.4e9 / 1e12  # 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz = 39.32 T lane-slots/s
+MFMA_F32_PEAK_TFLOPS = 157.3                 # MI355X dense fp32 MFMA, published
 MALL_BYTES = 256 << 20
 HEADLINE = "mamba130m_f32_b4_d1536_L2048_N16"
 METRIC = "selective-scan GB/s & % of HBM peak; (b·d·L)/s at N=16; decode steps/s"
@@ -244,6 +245,84 @@ def bench_lti(name, steps, warmup, quiet=False):
     return res
 
 
+SSD_SHAPES = {  # name: (b, H, L, N, dtype); heads of 64 channels
+    "ssd_f32_b4_H24_L2048_N64": (4, 24, 2048, 64, "f32"),
+    "ssd_bf16_b8_H64_L4096_N128": (8, 64, 4096, 128, "bf16"),
+}
+
+
+def ssd_mfma_flops(b, H, L, N, P=64, Q=64):
+    """fp32 MFMA flops the chunked form issues: per (b, head, chunk) the chunk state (2·P·N·Q), C·Bᵀ on the
+    three tiles at or below the diagonal (3·2·32²·N), the decayed products times x (2·32²·(2·32 + 2·64)) and
+    C times the entering state (2·Q·P·N)."""
+    per = 2 * P * N * Q + 6 * 32 * 32 * N + 2 * 32 * 32 * 192 + 2 * Q * P * N
+    return b * H * (-(-L // Q)) * per
+
+
+def bench_ssd(name, steps, warmup, quiet=False):
+    """The scalar-decay (state space duality) form, ssm_ssd_fwd, on a layer of the named shape; for N <= 64
+    the recurrent kernel (ssm_scan_fwd with Δ repeated over each head and A = a_h) is timed beside it."""
+    import torch
+    from selective_state_space_82_amd import api
+    from selective_state_space_82_amd import inputs as I
+
+    b, H, L, N, dt = SSD_SHAPES[name]
+    P = 64
+    inp = I.random_ssd(b, H, L, N, dtype=dt, seed=2)
+    es = 4 if dt == "f32" else 2
+    d = H * P
+    nbytes = b * d * L * es * 3 + b * H * L * es + 2 * b * L * N * es + b * d * N * 4 + d * 4 + H * 4
+    scratch_traffic = 4 * b * H * (-(-L // 64)) * P * N * 4
+    flops = ssd_mfma_flops(b, H, L, N)
+    rotate = int(min(8, max(1, -(-2 * MALL_BYTES // nbytes))))
+    sets = []
+    for _ in range(rotate):
+        t = {k: to_dev(inp[k], "cuda") for k in ("x", "z", "delta", "B", "C")}
+        t["A"] = torch.from_numpy(inp["A"]).cuda()
+        t["D"] = torch.from_numpy(inp["D"]).cuda()
+        t["y"] = torch.empty_like(t["x"])
+        t["h"] = torch.empty((b, d, N), device="cuda")
+        sets.append(t)
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def ssd(i):
+        t = sets[i % rotate]
+        api.ssm_ssd_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], y=t["y"], final_state=t["h"])
+
+    ms = timed(ssd)
+    res = {"pass": "ssd_chunked_mfma", "workload": name, "us_per_call": ms * 1e3, "elements_per_s": b * d * L / (ms * 1e-3),
+           "algorithmic_bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9, "scratch_bytes_moved": scratch_traffic,
+           "mfma_flops": flops, "mfma_TFLOPs": flops / (ms * 1e-3) / 1e12,
+           "mfma_frac_fp32": flops / (ms * 1e-3) / 1e12 / MFMA_F32_PEAK_TFLOPS}
+    if N <= 64:
+        for t in sets:
+            t["dl"] = t["delta"].repeat_interleave(P, dim=1).contiguous()
+            t["A2"] = t["A"].repeat_interleave(P)[:, None].expand(d, N).contiguous()
+
+        def rec(i):
+            t = sets[i % rotate]
+            api.ssm_scan_fwd(t["x"], t["dl"], t["A2"], t["B"], t["C"], t["D"], t["z"], y=t["y"], final_state=t["h"])
+        res["us_recurrent_kernel"] = timed(rec) * 1e3
+    if not quiet:
+        extra = f", recurrent kernel {res['us_recurrent_kernel']:.1f} us" if "us_recurrent_kernel" in res else ""
+        print(f"# ssd {name}: {ms * 1e3:.1f} us/call, {res['GBps']:.0f} GB/s, {res['mfma_TFLOPs']:.1f} TFLOP/s fp32 MFMA"
+              f"{extra}", file=sys.stderr, flush=True)
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_conv(name, steps, warmup, W=4, quiet=False):
     """The Conv1D + SiLU front end over the workload's [b, d, L] input (taps N(0, 0.5²), bias N(0, 1)),
     returning the state; HBM-bound: algorithmic bytes = xin read + x written (+ taps, bias, state)."""
@@ -418,9 +497,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--extra", default="decode,mamba1p4b_bf16_b8_d4096_L4096_N16,grad,conv,lti",
+    ap.add_argument("--extra", default="decode,mamba1p4b_bf16_b8_d4096_L4096_N16,grad,conv,lti,ssd",
                     help="comma list: 'decode', 'grad' (gradient pass on the workload), 'conv' (Conv1D front "
-                         "end), 'lti' (LTI convolution form) "
+                         "end), 'lti' (LTI convolution form), 'ssd' (scalar-decay chunked form) "
                          "and/or prefill workload names "
                          "('' for none, 'all' for every one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -457,6 +536,9 @@ def main():
                 extra.append(bench_decode(I.DECODE_WORKLOADS[0], r))
         elif n == "grad":
             extra.append(bench_grad(args.workload, max(3, args.steps // 5), 2))
+        elif n == "ssd":
+            for sn in SSD_SHAPES:
+                extra.append(bench_ssd(sn, 20, 3))
         elif n == "lti":
             for cw in dict.fromkeys((args.workload, "mamba1p4b_bf16_b8_d4096_L4096_N16")):
                 extra.append(bench_lti(cw, 20, 3))
