@@ -29,7 +29,6 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 
 constexpr int kQ = 64;           // chunk length
 constexpr int kP = 64;           // channels per head
-constexpr int kXP = kQ + 1;      // padded row of x [p][s] and of the decayed products [t][s] in LDS
 constexpr int kThreads = 256;    // four wavefronts
 
 struct SsdArgs {
@@ -40,6 +39,8 @@ struct SsdArgs {
     float *S;      // [b][H][nc][P][N] chunk states, then entering states
     float *decay;  // [b][H][nc]
     int64_t b, H, L, nc;
+    bool vec;      // x rows allow 16-byte (fp32) / 8-byte (bf16) loads at 4-element steps
+    bool vec_bc;   // so do the rows of B and C
 };
 
 __device__ __forceinline__ int lane() { return threadIdx.x & 63; }
@@ -47,6 +48,46 @@ __device__ __forceinline__ int wave() { return threadIdx.x >> 6; }
 
 // Row position of result register r of lane l in a 32×32 tile.
 __device__ __forceinline__ int d_row(int r, int l) { return 8 * (r / 4) + 4 * (l / 32) + (r % 4); }
+
+// Four consecutive elements row[i .. i+3] as fp32, zeros at and past `limit`; one 16-byte (fp32) or
+// 8-byte (bf16) load when `vec` says the row allows it.
+template <typename T>
+__device__ __forceinline__ float4 load4(const T *row, int64_t i, int64_t limit, bool vec) {
+    if (vec && i + 4 <= limit) {
+        if constexpr (sizeof(T) == 4) {
+            return *reinterpret_cast<const float4 *>(row + i);
+        } else {
+            const uint2 w = *reinterpret_cast<const uint2 *>(row + i);
+            return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+        }
+    }
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = i + e < limit ? widen(row[i + e]) : 0.0f;
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// One 32×32 tile product over K = 2W with the K index permuted so that each lane reads a contiguous run:
+// at step j the lower lane half supplies k = j and the upper half k = W + j. fa(j) / fb(j) return the
+// lane's operand values for steps j .. j+3 (its own row, k = hi·W + j .. +3).
+// All operand loads are issued before the first product (fully unrolled), so their latencies overlap.
+template <int W, typename FA, typename FB>
+__device__ __forceinline__ void mfma_tile(f16v &acc, FA fa, FB fb) {
+    float4 a4[W / 4], b4[W / 4];
+#pragma unroll
+    for (int j = 0; j < W / 4; ++j) {
+        a4[j] = fa(4 * j);
+        b4[j] = fb(4 * j);
+    }
+#pragma unroll
+    for (int j = 0; j < W / 4; ++j) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[j].x, b4[j].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[j].y, b4[j].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[j].z, b4[j].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[j].w, b4[j].w, acc, 0, 0, 0);
+    }
+}
+
 
 // Wavefront 0 turns the chunk's Δ into the in-chunk running sum of Δ·a·log2 e (cum, inclusive) and the
 // ZOH input coefficient β; steps past L get Δ = 0 (no decay, no input).
@@ -70,39 +111,49 @@ __device__ __forceinline__ void chunk_scalars(const SsdArgs &a, int64_t bh, int6
     s_beta[i] = beta;
 }
 
-// Rows [t0, t0 + 64) of a [L][N] tensor of batch row ib into LDS rows of stride N + 1 (zeros past L).
-template <typename T, int N>
-__device__ __forceinline__ void load_rows_tn(const void *src, int64_t ib, int64_t t0, int64_t L, float *dst) {
-    const T *g = static_cast<const T *>(src) + (ib * L + t0) * N;
-    for (int idx = threadIdx.x; idx < kQ * N; idx += kThreads) {
-        const int t = idx / N, n = idx % N;
-        dst[t * (N + 1) + n] = t0 + t < L ? widen(g[idx]) : 0.0f;
-    }
-}
+constexpr int kMS = kQ + 4;  // LDS row stride of 64-step rows (16-byte aligned rows)
 
-// x rows of head h, steps [t0, t0 + 64), into LDS [p][s] (stride kXP), each value times w[s] if given.
+// Copy `rows` rows of `cols` elements (a multiple of 4) from global memory (row stride gstride, rows
+// at and past row_limit read as zeros) into LDS rows of stride lstride, as fp32, with 4-element loads
+// spread over the workgroup; each value is multiplied by scale[col] when scale is given.
 template <typename T>
-__device__ __forceinline__ void load_x(const SsdArgs &a, int64_t ib, int64_t h, int64_t t0, const float *w,
-                                       float *dst) {
-    const T *g = static_cast<const T *>(a.x) + ((ib * a.H + h) * kP) * a.L;
-    for (int idx = threadIdx.x; idx < kP * kQ; idx += kThreads) {
-        const int p = idx / kQ, s = idx % kQ;
-        float v = t0 + s < a.L ? widen(g[p * a.L + t0 + s]) : 0.0f;
-        if (w) v *= w[s];
-        dst[p * kXP + s] = v;
+__device__ __forceinline__ void stage_rows(const T *g, int64_t gstride, int rows, int cols, int64_t row_limit,
+                                           int64_t col_limit, bool vec, float *lds, int lstride,
+                                           const float *scale = nullptr) {
+    const int per_row = cols / 4;
+    for (int idx = threadIdx.x; idx < rows * per_row; idx += kThreads) {
+        const int r = idx / per_row, c4 = (idx % per_row) * 4;
+        float4 v = r < row_limit ? load4<T>(g + r * gstride, c4, col_limit, vec) : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (scale) {
+            v.x *= scale[c4]; v.y *= scale[c4 + 1]; v.z *= scale[c4 + 2]; v.w *= scale[c4 + 3];
+        }
+        *reinterpret_cast<float4 *>(lds + r * lstride + c4) = v;
     }
 }
 
 template <typename T, int N>
 __global__ __launch_bounds__(kThreads) void ssd_state_kernel(SsdArgs a) {
-    __shared__ float s_cum[kQ], s_beta[kQ], s_w[kQ];
-    __shared__ float s_x[kP * kXP];
-    __shared__ float s_b[kQ * (N + 1)];
+    __shared__ float s_cum[kQ], s_beta[kQ];
+    __shared__ __align__(16) float s_w[kQ];
+    __shared__ __align__(16) float s_x[kP * kMS];  // x·w [p][s]
+    __shared__ __align__(16) float s_bt[N * kMS];  // Bᵀ [n][s]
     const int64_t c = blockIdx.x % a.nc, bh = blockIdx.x / a.nc;
     const int64_t ib = bh / a.H, h = bh % a.H;
     const int64_t t0 = c * kQ;
     const float ah = a.A[h];
     chunk_scalars<T>(a, bh, t0, ah, s_cum, s_beta);
+    {
+        // Bᵀ: each thread reads 4 consecutive n of one step and writes them down a column
+        const T *g = static_cast<const T *>(a.B) + (ib * a.L + t0) * N;
+        for (int idx = threadIdx.x; idx < kQ * (N / 4); idx += kThreads) {
+            const int t = idx / (N / 4), n4 = (idx % (N / 4)) * 4;
+            const float4 v = t0 + t < a.L ? load4<T>(g + t * N, n4, N, a.vec_bc) : make_float4(0.f, 0.f, 0.f, 0.f);
+            s_bt[(n4 + 0) * kMS + t] = v.x;
+            s_bt[(n4 + 1) * kMS + t] = v.y;
+            s_bt[(n4 + 2) * kMS + t] = v.z;
+            s_bt[(n4 + 3) * kMS + t] = v.w;
+        }
+    }
     __syncthreads();
     if (threadIdx.x < kQ) {
         const float cend = s_cum[kQ - 1];
@@ -110,21 +161,19 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(SsdArgs a) {
         if (threadIdx.x == 0) a.decay[bh * a.nc + c] = exp2_fast(cend);
     }
     __syncthreads();
-    load_x<T>(a, ib, h, t0, s_w, s_x);
-    load_rows_tn<T, N>(a.B, ib, t0, a.L, s_b);
+    stage_rows<T>(static_cast<const T *>(a.x) + ((ib * a.H + h) * kP) * a.L + t0, a.L, kP, kQ, kP, a.L - t0, a.vec,
+                  s_x, kMS, s_w);
     __syncthreads();
-    // S[p][n] = Σ_s x_w[p][s] B[s][n]: 2 × N/32 tiles of 32×32, spread over the four wavefronts
-    const int l = lane();
+    // S[p][n] = Σ_s x[p][s] w_s B[s][n]: 2 × N/32 tiles of 32×32 over the four wavefronts, K = 64 steps
+    const int l = lane(), hi = l / 32;
     float *S = a.S + (bh * a.nc + c) * (int64_t)(kP * N);
     for (int tile = wave(); tile < 2 * (N / 32); tile += 4) {
         const int qp = tile % 2, qn = tile / 2;
+        const float *xr = s_x + (32 * qp + l % 32) * kMS + 32 * hi;
+        const float *br = s_bt + (32 * qn + l % 32) * kMS + 32 * hi;
         f16v acc = {};
-#pragma unroll 8
-        for (int s0 = 0; s0 < kQ; s0 += 2) {
-            const float av = s_x[(32 * qp + l % 32) * kXP + s0 + l / 32];
-            const float bv = s_b[(s0 + l / 32) * (N + 1) + 32 * qn + l % 32];
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
-        }
+        mfma_tile<32>(acc, [&](int j) { return *reinterpret_cast<const float4 *>(xr + j); },
+                      [&](int j) { return *reinterpret_cast<const float4 *>(br + j); });
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[(32 * qp + d_row(r, l)) * N + 32 * qn + l % 32] = acc[r];
     }
@@ -150,38 +199,36 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(SsdArgs a) {
 
 template <typename T, int N>
 __global__ __launch_bounds__(kThreads) void ssd_out_kernel(SsdArgs a) {
-    constexpr int CP = N + 1;
-    constexpr int BM = (kQ * CP > kQ * kXP) ? kQ * CP : kQ * kXP;
+    constexpr int NS = N + 4;                                   // LDS row stride of N-wide rows
+    constexpr int BM = (kQ * NS > kQ * kMS) ? kQ * NS : kQ * kMS;
     __shared__ float s_cum[kQ], s_beta[kQ];
-    __shared__ float s_c[kQ * CP];  // C [t][n]
-    __shared__ float s_bm[BM];      // B [s][n], then the decayed products M [t][s]
-    __shared__ float s_h[kP * CP];  // entering state [p][n]
-    __shared__ float s_x[kP * kXP]; // x [p][s]
+    __shared__ __align__(16) float s_c[BM];       // C [t][n]; at the end the outputs [p][t]
+    __shared__ __align__(16) float s_bm[BM];      // B [s][n], then the decayed products M [t][s]
+    __shared__ __align__(16) float s_h[kP * NS];  // entering state [p][n]
+    __shared__ __align__(16) float s_x[kP * kMS]; // x [p][s]
     const int64_t c = blockIdx.x % a.nc, bh = blockIdx.x / a.nc;
     const int64_t ib = bh / a.H, h = bh % a.H;
     const int64_t t0 = c * kQ;
     const float ah = a.A[h];
     chunk_scalars<T>(a, bh, t0, ah, s_cum, s_beta);
-    load_rows_tn<T, N>(a.C, ib, t0, a.L, s_c);
-    load_rows_tn<T, N>(a.B, ib, t0, a.L, s_bm);
-    load_x<T>(a, ib, h, t0, nullptr, s_x);
-    {
-        const float *Hin = a.S + (bh * a.nc + c) * (int64_t)(kP * N);
-        for (int idx = threadIdx.x; idx < kP * N; idx += kThreads) s_h[(idx / N) * CP + idx % N] = Hin[idx];
-    }
+    const T *xg = static_cast<const T *>(a.x) + ((ib * a.H + h) * kP) * a.L + t0;  // row p at + p·L
+    stage_rows<T>(static_cast<const T *>(a.C) + (ib * a.L + t0) * N, N, kQ, N, a.L - t0, N, a.vec_bc, s_c, NS);
+    stage_rows<T>(static_cast<const T *>(a.B) + (ib * a.L + t0) * N, N, kQ, N, a.L - t0, N, a.vec_bc, s_bm, NS);
+    stage_rows<T>(xg, a.L, kP, kQ, kP, a.L - t0, a.vec, s_x, kMS);
+    stage_rows<float>(a.S + (bh * a.nc + c) * (int64_t)(kP * N), N, kP, N, kP, N, true, s_h, NS);
     __syncthreads();
 
-    const int l = lane(), w = wave();
-    // G = C Bᵀ on the three tiles at or below the diagonal, then M = G ∘ e^{a(c_t − c_s)} β_s (s <= t)
+    const int l = lane(), w = wave(), hi = l / 32;
+    constexpr int HN = N / 2;
+    // G = C Bᵀ on the tiles at or below the diagonal (wavefronts 0..2), then M = G ∘ e^{a(c_t − c_s)} β_s
+    // for s <= t; wavefront 3 clears the tile above the diagonal.
     f16v g = {};
     const int qt = w == 0 ? 0 : 1, qs = w == 2 ? 1 : 0;
     if (w < 3) {
-#pragma unroll 8
-        for (int n0 = 0; n0 < N; n0 += 2) {
-            const float av = s_c[(32 * qt + l % 32) * CP + n0 + l / 32];
-            const float bv = s_bm[(32 * qs + l % 32) * CP + n0 + l / 32];
-            g = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, g, 0, 0, 0);
-        }
+        const float *cr = s_c + (32 * qt + l % 32) * NS + hi * HN;
+        const float *br = s_bm + (32 * qs + l % 32) * NS + hi * HN;
+        mfma_tile<HN>(g, [&](int j) { return *reinterpret_cast<const float4 *>(cr + j); },
+                      [&](int j) { return *reinterpret_cast<const float4 *>(br + j); });
     }
     __syncthreads();  // B is no longer read: its space takes M
     if (w < 3) {
@@ -190,43 +237,68 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(SsdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int t = 32 * qt + d_row(r, l);
-            s_bm[t * kXP + s] = s <= t ? g[r] * exp2_fast(s_cum[t] - cs) * bs : 0.0f;
+            s_bm[t * kMS + s] = s <= t ? g[r] * exp2_fast(s_cum[t] - cs) * bs : 0.0f;
         }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s_bm[d_row(r, l) * kMS + 32 + l % 32] = 0.0f;
     }
     __syncthreads();
 
-    // this wavefront's 32×32 output tile: rows t in [32·ot, +32), channels p in [32·op, +32)
+    // this wavefront's output tile: rows t in [32·ot, +32), channels p in [32·op, +32)
     const int ot = w / 2, op = w % 2;
-    f16v acc = {};
-    const int s_end = 32 * (ot + 1);  // M[t][s] = 0 for s > t
-    for (int s0 = 0; s0 < s_end; s0 += 2) {
-        const float av = s_bm[(32 * ot + l % 32) * kXP + s0 + l / 32];
-        const float bv = s_x[(32 * op + l % 32) * kXP + s0 + l / 32];
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    f16v acc = {}, inter = {};
+    {
+        const float *mr = s_bm + (32 * ot + l % 32) * kMS + 32 * hi;
+        const float *xr = s_x + (32 * op + l % 32) * kMS + 32 * hi;
+        mfma_tile<32>(acc, [&](int j) { return *reinterpret_cast<const float4 *>(mr + j); },
+                      [&](int j) { return *reinterpret_cast<const float4 *>(xr + j); });
+        const float *cr = s_c + (32 * ot + l % 32) * NS + hi * HN;
+        const float *hr = s_h + (32 * op + l % 32) * NS + hi * HN;
+        mfma_tile<HN>(inter, [&](int j) { return *reinterpret_cast<const float4 *>(cr + j); },
+                      [&](int j) { return *reinterpret_cast<const float4 *>(hr + j); });
     }
-    f16v inter = {};
-#pragma unroll 8
-    for (int n0 = 0; n0 < N; n0 += 2) {
-        const float av = s_c[(32 * ot + l % 32) * CP + n0 + l / 32];
-        const float bv = s_h[(32 * op + l % 32) * CP + n0 + l / 32];
-        inter = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, inter, 0, 0, 0);
+    __syncthreads();  // C is no longer read: its space takes the outputs [p][t]
+    {
+        const int p = 32 * op + l % 32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int t = 32 * ot + d_row(r, l);
+            s_c[p * kMS + t] = acc[r] + exp2_fast(s_cum[t]) * inter[r];
+        }
     }
-
-    // epilogue: y = intra + e^{a c_t} (C_t·h_in) + D x, times silu(z); lane l owns channel p and four runs
-    // of four consecutive steps
-    const int p = 32 * op + l % 32;
-    const int64_t ch = h * kP + p;
-    const float dsk = a.D ? a.D[ch] : 0.0f;
-    const int64_t row = (ib * a.H * kP + ch) * a.L;
+    __syncthreads();
+    // y = (that) + D x, times silu(z), written row by row in 4-step pieces
     const T *zg = static_cast<const T *>(a.z);
     T *yg = static_cast<T *>(a.y);
+    const int64_t lim = a.L - t0;
+    for (int idx = threadIdx.x; idx < kP * (kQ / 4); idx += kThreads) {
+        const int p = idx / (kQ / 4), t4 = (idx % (kQ / 4)) * 4;
+        if (t4 >= lim) continue;
+        const int64_t ch = h * kP + p;
+        const int64_t off = (ib * a.H * kP + ch) * a.L + t0 + t4;
+        const float dsk = a.D ? a.D[ch] : 0.0f;
+        const float4 o = *reinterpret_cast<const float4 *>(s_c + p * kMS + t4);
+        const float4 xv = *reinterpret_cast<const float4 *>(s_x + p * kMS + t4);
+        float v[4] = {o.x + dsk * xv.x, o.y + dsk * xv.y, o.z + dsk * xv.z, o.w + dsk * xv.w};
+        if (zg) {
+            const float4 zv = load4<T>(zg + off - t4, t4, lim, a.vec);
+            v[0] *= silu(zv.x); v[1] *= silu(zv.y); v[2] *= silu(zv.z); v[3] *= silu(zv.w);
+        }
+        if (a.vec && t4 + 4 <= lim) {
+            if constexpr (sizeof(T) == 4) {
+                *reinterpret_cast<float4 *>(yg + off) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+                uint2 pk;
+                pk.x = (uint32_t)narrow<T>(v[0]) | ((uint32_t)narrow<T>(v[1]) << 16);
+                pk.y = (uint32_t)narrow<T>(v[2]) | ((uint32_t)narrow<T>(v[3]) << 16);
+                *reinterpret_cast<uint2 *>(yg + off) = pk;
+            }
+        } else {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int t = 32 * ot + d_row(r, l);
-        if (t0 + t >= a.L) continue;
-        float v = acc[r] + exp2_fast(s_cum[t]) * inter[r] + dsk * s_x[p * kXP + t];
-        if (zg) v *= silu(widen(zg[row + t0 + t]));
-        yg[row + t0 + t] = narrow<T>(v);
+            for (int e = 0; e < 4; ++e)
+                if (t4 + e < lim) yg[off + e] = narrow<T>(v[e]);
+        }
     }
 }
 
@@ -269,6 +341,10 @@ hipError_t launch_ssd(const SsdLaunch &p, hipStream_t stream) {
     a.b = p.b; a.H = p.H; a.L = p.L;
     a.nc = (p.L + kQ - 1) / kQ;
     a.S = p.scratch;
+    const int64_t es = p.bf16 ? 2 : 4;
+    auto aligned = [&](const void *q) { return (reinterpret_cast<uintptr_t>(q) & (uintptr_t)(4 * es - 1)) == 0; };
+    a.vec = (p.L % 4) == 0 && aligned(p.x);
+    a.vec_bc = aligned(p.B) && aligned(p.C);  // N is a multiple of 32
     a.decay = p.scratch + a.b * a.H * a.nc * (kP * p.N);
     if (p.bf16) return launch_typed<uint16_t>(a, p.N, stream);
     return launch_typed<float>(a, p.N, stream);
