@@ -9,7 +9,11 @@
 // where c_t = Σ_{r<=t in chunk} Δ_r, β_s the ZOH input coefficient and h_in the state entering the chunk,
 // and the state leaving it is h_out = e^{a c_end} h_in + Σ_s e^{a(c_end − c_s)} β_s B_s x_sᵀ. Per (b, head,
 // chunk) those are dense products: G = C Bᵀ (Q×Q over N), Y = (G ∘ decay) Xᵀ (Q×P over Q), C H_inᵀ (Q×P over
-// N) and the chunk state X_w Bᵀ (P×N over Q), all on v_mfma_f32_32x32x2f32 (fp32 in, fp32 accumulate).
+// N) and the chunk state X_w Bᵀ (P×N over Q). fp32 storage runs them on v_mfma_f32_32x32x2f32 (fp32 in,
+// fp32 accumulate); bf16 storage on v_mfma_f32_32x32x16_bf16 (bf16 in, fp32 accumulate): inputs stored as
+// bf16 enter exactly, and each fp32 operand (the decayed products, the entering state, the weighted
+// inputs) enters as the sum of two bf16 numbers, hi = bf16(v) and lo = bf16(v − hi), in two products,
+// which keeps about 16 bits of it.
 //
 // Three kernels:
 //   ssd_state_kernel   per (b, h, chunk): the chunk's own state contribution S_c [P][N] and its decay.
@@ -17,8 +21,9 @@
 //                      chunk c and writing the final state.
 //   ssd_out_kernel     per (b, h, chunk): the outputs of the chunk from its inputs and entering state.
 //
-// MFMA 32x32x2 f32 lane layout (checked on the device): lane l supplies A[l % 32][l / 32] and
-// B[l / 32][l % 32]; result register r of lane l is D[8(r / 4) + 4(l / 32) + r % 4][l % 32].
+// MFMA lane layouts (checked on the device): 32x32x2 f32: lane l supplies A[l % 32][l / 32] and
+// B[l / 32][l % 32]; 32x32x16 bf16: lane l supplies A[l % 32][8(l / 32) + e] and B[8(l / 32) + e][l % 32],
+// e < 8; for both, result register r of lane l is D[8(r / 4) + 4(l / 32) + r % 4][l % 32].
 #include "device_common.h"
 #include "launch.h"
 
@@ -26,6 +31,7 @@ namespace ssm {
 namespace {
 
 typedef float f16v __attribute__((ext_vector_type(16)));
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 
 constexpr int kQ = 64;           // chunk length
 constexpr int kP = 64;           // channels per head
@@ -41,6 +47,7 @@ struct SsdArgs {
     int64_t b, H, L, nc;
     bool vec;      // x rows allow 16-byte (fp32) / 8-byte (bf16) loads at 4-element steps
     bool vec_bc;   // so do the rows of B and C
+    bool vec8;     // x rows allow 16-byte loads at 8-element steps (bf16)
 };
 
 __device__ __forceinline__ int lane() { return threadIdx.x & 63; }
@@ -302,17 +309,228 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(SsdArgs a) {
     }
 }
 
+// ---- bf16 storage: the same three steps on the bf16 MFMA -------------------------------------------
+
+constexpr int kMH = kQ + 8;  // LDS row stride (bf16 elements) of 64-step rows: 144 bytes, 16-byte aligned
+
+// One 32×32 tile product over K = 2W on the bf16 MFMA, K split across the lane halves as in mfma_tile:
+// at step j the lower half supplies k = 8j .. 8j+7 and the upper half k = W + 8j .. +7, so each lane
+// reads 16 contiguous bytes of its own LDS row per step.
+template <int W>
+__device__ __forceinline__ void mfma_tile_bf16(f16v &acc, const uint16_t *arow, const uint16_t *brow) {
+    bf8v a8[W / 8], b8[W / 8];
+#pragma unroll
+    for (int j = 0; j < W / 8; ++j) {
+        a8[j] = *reinterpret_cast<const bf8v *>(arow + 8 * j);
+        b8[j] = *reinterpret_cast<const bf8v *>(brow + 8 * j);
+    }
+#pragma unroll
+    for (int j = 0; j < W / 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8[j], b8[j], acc, 0, 0, 0);
+}
+
+// Eight fp32 values as bf16 hi = bf16(v) and lo = bf16(v − hi).
+__device__ __forceinline__ void split8(const float *src, bf8v &hi8, bf8v &lo8) {
+    const float4 u = *reinterpret_cast<const float4 *>(src), v = *reinterpret_cast<const float4 *>(src + 4);
+    const float f[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const __bf16 hb = (__bf16)f[e];
+        hi8[e] = hb;
+        lo8[e] = (__bf16)(f[e] - (float)hb);
+    }
+}
+
+// As mfma_tile_bf16 with one operand an fp32 LDS row entering as hi + lo (two products per step);
+// SPLIT_A says which operand is the fp32 one.
+template <int W, bool SPLIT_A>
+__device__ __forceinline__ void mfma_tile_split(f16v &acc, const float *frow, const uint16_t *brow) {
+#pragma unroll
+    for (int j = 0; j < W / 8; ++j) {
+        bf8v h8, l8;
+        split8(frow + 8 * j, h8, l8);
+        const bf8v o8 = *reinterpret_cast<const bf8v *>(brow + 8 * j);
+        if (SPLIT_A) {
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h8, o8, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l8, o8, acc, 0, 0, 0);
+        } else {
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o8, h8, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o8, l8, acc, 0, 0, 0);
+        }
+    }
+}
+
+// Copy rows of `cols` bf16 elements (a multiple of 8) into LDS rows of stride lstride, 16 bytes at a time;
+// rows at and past row_limit and columns at and past col_limit read as zeros.
+__device__ __forceinline__ void stage_rows_bf16(const uint16_t *g, int64_t gstride, int rows, int cols,
+                                                int64_t row_limit, int64_t col_limit, bool vec, uint16_t *lds,
+                                                int lstride) {
+    const int per_row = cols / 8;
+    for (int idx = threadIdx.x; idx < rows * per_row; idx += kThreads) {
+        const int r = idx / per_row, c8 = (idx % per_row) * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r < row_limit) {
+            const uint16_t *src = g + r * gstride + c8;
+            if (vec && c8 + 8 <= col_limit) {
+                v = *reinterpret_cast<const uint4 *>(src);
+            } else {
+                uint16_t e[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) e[k] = c8 + k < col_limit ? src[k] : (uint16_t)0;
+                __builtin_memcpy(&v, e, sizeof(v));
+            }
+        }
+        *reinterpret_cast<uint4 *>(lds + r * lstride + c8) = v;
+    }
+}
+
+template <int N>
+__global__ __launch_bounds__(kThreads) void ssd_state_kernel_bf16(SsdArgs a) {
+    __shared__ float s_cum[kQ], s_beta[kQ], s_w[kQ];
+    __shared__ __align__(16) float s_x[kP * kMS];     // x·w [p][s], fp32
+    __shared__ __align__(16) uint16_t s_bt[N * kMH];  // Bᵀ [n][s]
+    const int64_t c = blockIdx.x % a.nc, bh = blockIdx.x / a.nc;
+    const int64_t ib = bh / a.H, h = bh % a.H;
+    const int64_t t0 = c * kQ;
+    const float ah = a.A[h];
+    chunk_scalars<uint16_t>(a, bh, t0, ah, s_cum, s_beta);
+    {
+        const uint16_t *g = static_cast<const uint16_t *>(a.B) + (ib * a.L + t0) * N;
+        for (int idx = threadIdx.x; idx < kQ * N; idx += kThreads) {
+            const int t = idx / N, n = idx % N;
+            s_bt[n * kMH + t] = t0 + t < a.L ? g[idx] : (uint16_t)0;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < kQ) {
+        const float cend = s_cum[kQ - 1];
+        s_w[threadIdx.x] = exp2_fast(cend - s_cum[threadIdx.x]) * s_beta[threadIdx.x];
+        if (threadIdx.x == 0) a.decay[bh * a.nc + c] = exp2_fast(cend);
+    }
+    __syncthreads();
+    {
+        const uint16_t *xg = static_cast<const uint16_t *>(a.x) + ((ib * a.H + h) * kP) * a.L + t0;
+        for (int idx = threadIdx.x; idx < kP * (kQ / 4); idx += kThreads) {
+            const int p = idx / (kQ / 4), s4 = (idx % (kQ / 4)) * 4;
+            const float4 v = load4<uint16_t>(xg + p * a.L, s4, a.L - t0, a.vec);
+            *reinterpret_cast<float4 *>(s_x + p * kMS + s4) =
+                make_float4(v.x * s_w[s4], v.y * s_w[s4 + 1], v.z * s_w[s4 + 2], v.w * s_w[s4 + 3]);
+        }
+    }
+    __syncthreads();
+    const int l = lane(), hi = l / 32;
+    float *S = a.S + (bh * a.nc + c) * (int64_t)(kP * N);
+    for (int tile = wave(); tile < 2 * (N / 32); tile += 4) {
+        const int qp = tile % 2, qn = tile / 2;
+        f16v acc = {};
+        mfma_tile_split<32, true>(acc, s_x + (32 * qp + l % 32) * kMS + 32 * hi,
+                                  s_bt + (32 * qn + l % 32) * kMH + 32 * hi);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[(32 * qp + d_row(r, l)) * N + 32 * qn + l % 32] = acc[r];
+    }
+}
+
+template <int N>
+__global__ __launch_bounds__(kThreads) void ssd_out_kernel_bf16(SsdArgs a) {
+    constexpr int NH = N + 8;                                   // LDS row stride (bf16) of N-wide rows
+    constexpr int NS = N + 4;                                   // LDS row stride (fp32) of N-wide rows
+    constexpr int OUTF = kP * kMS;                              // fp32 [64][kMS] (M, then the outputs)
+    constexpr int CB = (kQ * NH > OUTF * 2) ? kQ * NH : OUTF * 2;  // bf16 units
+    __shared__ float s_cum[kQ], s_beta[kQ];
+    __shared__ __align__(16) uint16_t s_c[CB];        // C [t][n]; at the end the outputs [p][t] (fp32)
+    __shared__ __align__(16) uint16_t s_bm[CB];       // B [s][n], then M [t][s] (fp32)
+    __shared__ __align__(16) float s_h[kP * NS];      // entering state [p][n], fp32
+    __shared__ __align__(16) uint16_t s_x[kP * kMH];  // x [p][s]
+    const int64_t c = blockIdx.x % a.nc, bh = blockIdx.x / a.nc;
+    const int64_t ib = bh / a.H, h = bh % a.H;
+    const int64_t t0 = c * kQ;
+    const float ah = a.A[h];
+    chunk_scalars<uint16_t>(a, bh, t0, ah, s_cum, s_beta);
+    const uint16_t *xg = static_cast<const uint16_t *>(a.x) + ((ib * a.H + h) * kP) * a.L + t0;
+    stage_rows_bf16(static_cast<const uint16_t *>(a.C) + (ib * a.L + t0) * N, N, kQ, N, a.L - t0, N, a.vec_bc, s_c, NH);
+    stage_rows_bf16(static_cast<const uint16_t *>(a.B) + (ib * a.L + t0) * N, N, kQ, N, a.L - t0, N, a.vec_bc, s_bm, NH);
+    stage_rows_bf16(xg, a.L, kP, kQ, kP, a.L - t0, a.vec8, s_x, kMH);
+    stage_rows<float>(a.S + (bh * a.nc + c) * (int64_t)(kP * N), N, kP, N, kP, N, true, s_h, NS);
+    __syncthreads();
+
+    const int l = lane(), w = wave(), hi = l / 32;
+    constexpr int HN = N / 2;
+    f16v g = {};
+    const int qt = w == 0 ? 0 : 1, qs = w == 2 ? 1 : 0;
+    if (w < 3) mfma_tile_bf16<HN>(g, s_c + (32 * qt + l % 32) * NH + hi * HN, s_bm + (32 * qs + l % 32) * NH + hi * HN);
+    __syncthreads();  // B is no longer read: its space takes M (fp32)
+    float *s_m = reinterpret_cast<float *>(s_bm);
+    if (w < 3) {
+        const int s = 32 * qs + l % 32;
+        const float cs = s_cum[s], bs = s_beta[s];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int t = 32 * qt + d_row(r, l);
+            s_m[t * kMS + s] = s <= t ? g[r] * exp2_fast(s_cum[t] - cs) * bs : 0.0f;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s_m[d_row(r, l) * kMS + 32 + l % 32] = 0.0f;
+    }
+    __syncthreads();
+
+    const int ot = w / 2, op = w % 2;
+    f16v acc = {}, inter = {};
+    mfma_tile_split<32, true>(acc, s_m + (32 * ot + l % 32) * kMS + 32 * hi, s_x + (32 * op + l % 32) * kMH + 32 * hi);
+    mfma_tile_split<HN, false>(inter, s_h + (32 * op + l % 32) * NS + hi * HN, s_c + (32 * ot + l % 32) * NH + hi * HN);
+    __syncthreads();  // C is no longer read: its space takes the outputs
+    float *s_o = reinterpret_cast<float *>(s_c);
+    {
+        const int p = 32 * op + l % 32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int t = 32 * ot + d_row(r, l);
+            s_o[p * kMS + t] = acc[r] + exp2_fast(s_cum[t]) * inter[r];
+        }
+    }
+    __syncthreads();
+    const uint16_t *zg = static_cast<const uint16_t *>(a.z);
+    uint16_t *yg = static_cast<uint16_t *>(a.y);
+    const int64_t lim = a.L - t0;
+    for (int idx = threadIdx.x; idx < kP * (kQ / 4); idx += kThreads) {
+        const int p = idx / (kQ / 4), t4 = (idx % (kQ / 4)) * 4;
+        if (t4 >= lim) continue;
+        const int64_t ch = h * kP + p;
+        const int64_t off = (ib * a.H * kP + ch) * a.L + t0 + t4;
+        const float dsk = a.D ? a.D[ch] : 0.0f;
+        const float4 o = *reinterpret_cast<const float4 *>(s_o + p * kMS + t4);
+        const uint16_t *xs = s_x + p * kMH + t4;
+        float v[4] = {o.x + dsk * widen(xs[0]), o.y + dsk * widen(xs[1]), o.z + dsk * widen(xs[2]),
+                      o.w + dsk * widen(xs[3])};
+        if (zg) {
+            const float4 zv = load4<uint16_t>(zg + off - t4, t4, lim, a.vec);
+            v[0] *= silu(zv.x); v[1] *= silu(zv.y); v[2] *= silu(zv.z); v[3] *= silu(zv.w);
+        }
+        if (a.vec && t4 + 4 <= lim) {
+            uint2 pk;
+            pk.x = (uint32_t)narrow<uint16_t>(v[0]) | ((uint32_t)narrow<uint16_t>(v[1]) << 16);
+            pk.y = (uint32_t)narrow<uint16_t>(v[2]) | ((uint32_t)narrow<uint16_t>(v[3]) << 16);
+            *reinterpret_cast<uint2 *>(yg + off) = pk;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (t4 + e < lim) yg[off + e] = narrow<uint16_t>(v[e]);
+        }
+    }
+}
+
 template <typename T, int N>
 hipError_t launch_n(const SsdArgs &a, hipStream_t stream) {
     const unsigned chunks = (unsigned)(a.b * a.H * a.nc);
-    hipLaunchKernelGGL((ssd_state_kernel<T, N>), dim3(chunks), dim3(kThreads), 0, stream, a);
+    if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((ssd_state_kernel_bf16<N>), dim3(chunks), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((ssd_state_kernel<T, N>), dim3(chunks), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t elems = a.b * a.H * kP * N;
     hipLaunchKernelGGL((ssd_pass_kernel<N>), dim3((unsigned)((elems + 255) / 256)), dim3(256), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((ssd_out_kernel<T, N>), dim3(chunks), dim3(kThreads), 0, stream, a);
+    if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((ssd_out_kernel_bf16<N>), dim3(chunks), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((ssd_out_kernel<T, N>), dim3(chunks), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -345,6 +563,7 @@ hipError_t launch_ssd(const SsdLaunch &p, hipStream_t stream) {
     auto aligned = [&](const void *q) { return (reinterpret_cast<uintptr_t>(q) & (uintptr_t)(4 * es - 1)) == 0; };
     a.vec = (p.L % 4) == 0 && aligned(p.x);
     a.vec_bc = aligned(p.B) && aligned(p.C);  // N is a multiple of 32
+    a.vec8 = p.bf16 && (p.L % 8) == 0 && (reinterpret_cast<uintptr_t>(p.x) & 15) == 0;
     a.decay = p.scratch + a.b * a.H * a.nc * (kP * p.N);
     if (p.bf16) return launch_typed<uint16_t>(a, p.N, stream);
     return launch_typed<float>(a, p.N, stream);
