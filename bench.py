@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0                        # MI355X HBM3E, published
 VALU_PEAK_TSLOT = 256 * 4 * 16 * 2.4e9 / 1e12  # 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz = 39.32 T lane-slots/s
 MFMA_F32_PEAK_TFLOPS = 157.3                 # MI355X dense fp32 MFMA, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0               # MI355X dense bf16 MFMA, published
 MALL_BYTES = 256 << 20
 HEADLINE = "mamba130m_f32_b4_d1536_L2048_N16"
 METRIC = "selective-scan GB/s & % of HBM peak; (b·d·L)/s at N=16; decode steps/s"
@@ -304,7 +305,8 @@ def bench_ssd(name, steps, warmup, quiet=False):
     res = {"pass": "ssd_chunked_mfma", "workload": name, "us_per_call": ms * 1e3, "elements_per_s": b * d * L / (ms * 1e-3),
            "algorithmic_bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9, "scratch_bytes_moved": scratch_traffic,
            "mfma_flops": flops, "mfma_TFLOPs": flops / (ms * 1e-3) / 1e12,
-           "mfma_frac_fp32": flops / (ms * 1e-3) / 1e12 / MFMA_F32_PEAK_TFLOPS}
+           "mfma_instruction": "f32_32x32x2" if dt == "f32" else "bf16_32x32x16 (fp32 operands as hi + lo)",
+           "mfma_frac": flops / (ms * 1e-3) / 1e12 / (MFMA_F32_PEAK_TFLOPS if dt == "f32" else MFMA_BF16_PEAK_TFLOPS)}
     if N <= 64:
         for t in sets:
             t["dl"] = t["delta"].repeat_interleave(P, dim=1).contiguous()
@@ -316,8 +318,8 @@ def bench_ssd(name, steps, warmup, quiet=False):
         res["us_recurrent_kernel"] = timed(rec) * 1e3
     if not quiet:
         extra = f", recurrent kernel {res['us_recurrent_kernel']:.1f} us" if "us_recurrent_kernel" in res else ""
-        print(f"# ssd {name}: {ms * 1e3:.1f} us/call, {res['GBps']:.0f} GB/s, {res['mfma_TFLOPs']:.1f} TFLOP/s fp32 MFMA"
-              f"{extra}", file=sys.stderr, flush=True)
+        print(f"# ssd {name}: {ms * 1e3:.1f} us/call, {res['GBps']:.0f} GB/s, {res['mfma_TFLOPs']:.1f} TFLOP/s of "
+              f"matrix products ({res['mfma_instruction']}){extra}", file=sys.stderr, flush=True)
     del sets
     torch.cuda.empty_cache()
     return res
