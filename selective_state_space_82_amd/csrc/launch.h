@@ -25,7 +25,7 @@ struct FwdLaunch {
     float *scratch;           // scratch_floats(n_seg, b, d, N) floats
     hipEvent_t ev_begin, ev_end;
     float *ckpt;              // optional: states entering every ck_len-th step, [b][d][ceil(L/ck_len)][N]
-    int ck_len;               // 64 / states_per_lane when ckpt is set
+    int ck_len;               // checkpoint interval (ckpt_len) when ckpt is set
 };
 
 // Everything the gradient launcher needs (validated by the ABI layer).

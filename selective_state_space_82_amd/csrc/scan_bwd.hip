@@ -68,6 +68,10 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
     constexpr int CW = kWave / G;
     constexpr int NPAD = G * NPL;
     constexpr int K = (32 / NPL) < 4 ? 4 : 32 / NPL;    // steps per checkpoint chunk
+    // with 4 states per lane, Ā and β of the chunk's last KH steps stay in registers from the forward
+    // recomputation to the walk back, which computes them again for the other steps (register budget)
+    constexpr bool kKeep = NPL <= 4;
+    constexpr int KH = K / 2;
     constexpr int kRowChunks = kBT / E;                  // 16-byte chunks per row per tile
     constexpr int kXC = (CW * kRowChunks + kWave - 1) / kWave;
     constexpr int kBF = kBT * NPAD;
@@ -359,6 +363,7 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
             load_ckpt((t0 + tc) / K, h);
             // forward recomputation of the chunk: hs[k] = state after step tc + k
             float hs[K][NPL];
+            float ab_k[kKeep ? KH : 1][kKeep ? NPL : 1], be_k[kKeep ? KH : 1][kKeep ? NPL : 1];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const int t = tc + k;
@@ -374,6 +379,12 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
                         const float beta = zoh_input_coef_log2(dt, u, abar, ia[j + q]);
                         const float hp = k == 0 ? h[j + q] : hs[k - 1][j + q];
                         hs[k][j + q] = __builtin_fmaf(abar, hp, beta * (bq[q] * xt));
+                        if constexpr (kKeep) {
+                            if (k >= K - KH) {
+                                ab_k[k - (K - KH)][j + q] = abar;
+                                be_k[k - (K - KH)][j + q] = beta;
+                            }
+                        }
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);  // one step at a time: keeps the live ranges short
@@ -386,9 +397,9 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
                 const int t = tc + k;
                 const float xt = xrow[t];
                 float dt = drow[t];
-                // Ā and β are recomputed here rather than kept from the forward walk (K·NPL pairs of
-                // registers); the empty asm hides that they are the same values from the compiler
-                asm volatile("" : "+v"(dt));
+                // where not kept, Ā and β are recomputed here rather than kept from the forward walk
+                // (K·NPL pairs of registers); the empty asm hides that they are the same values
+                if (!kKeep || k < K - KH) asm volatile("" : "+v"(dt));
                 const float dyt = grow[t];
                 float Bv[NPL], Cv[NPL];
 #pragma unroll
@@ -417,8 +428,14 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
 #pragma unroll
                 for (int j = 0; j < NPL; ++j) {
                     const float u = dt * a2[j];
-                    const float abar = exp2_fast(u);
-                    const float beta = zoh_input_coef_log2(dt, u, abar, ia[j]);
+                    float abar, beta;
+                    if (kKeep && k >= K - KH) {
+                        abar = ab_k[kKeep ? k - (K - KH) : 0][j];
+                        beta = be_k[kKeep ? k - (K - KH) : 0][j];
+                    } else {
+                        abar = exp2_fast(u);
+                        beta = zoh_input_coef_log2(dt, u, abar, ia[j]);
+                    }
                     const float hp = k == 0 ? h[j] : hs[k - 1][j];
                     const float lam = __builtin_fmaf(dys, Cv[j], kap[j]);
                     const float dab = lam * hp;                 // ∂L/∂Ā_t
@@ -466,14 +483,35 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
     }
 }
 
-__global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ p, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0.0f;
+// Clears up to four buffers (the summed gradients) in one launch: element i of the concatenation.
+struct ZeroList {
+    float *p[4];
+    int64_t n[4];
+};
+
+__global__ __launch_bounds__(256) void zero_kernel(ZeroList z, int64_t total) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        int64_t k = i;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if (k < z.n[b]) {
+                z.p[b][k] = 0.0f;
+                break;
+            }
+            k -= z.n[b];
+        }
+    }
 }
 
-hipError_t zero(float *p, int64_t n, hipStream_t stream) {
-    if (!p || n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n);
+hipError_t zero4(ZeroList z, hipStream_t stream) {
+    int64_t total = 0;
+    for (int b = 0; b < 4; ++b) {
+        if (!z.p[b] || z.n[b] < 0) z.n[b] = 0;
+        total += z.n[b];
+    }
+    if (total == 0) return hipSuccess;
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, stream, z, total);
     return hipGetLastError();
 }
 
@@ -510,10 +548,8 @@ hipError_t launch_scan_bwd(const BwdLaunch &p, hipStream_t stream) {
     float *rP = ckpt + p.b * p.d * n_ck * p.N;
     float *rE = rP + (int64_t)(p.n_seg - 1) * p.b * p.d * p.N;
 
-    hipError_t e = zero(p.dA, p.d * p.N, stream);
-    if (e == hipSuccess) e = zero(p.dB, p.b * p.L * p.N, stream);
-    if (e == hipSuccess) e = zero(p.dC, p.b * p.L * p.N, stream);
-    if (e == hipSuccess) e = zero(p.dD, p.dD ? p.d : 0, stream);
+    const ZeroList zl{{p.dA, p.dB, p.dC, p.dD}, {p.d * p.N, p.b * p.L * p.N, p.b * p.L * p.N, p.dD ? p.d : 0}};
+    hipError_t e = zero4(zl, stream);
     if (e != hipSuccess) return e;
 
     // forward pass that leaves the checkpoints (no outputs)
