@@ -11,9 +11,10 @@
 // chunk) those are dense products: G = C Bᵀ (Q×Q over N), Y = (G ∘ decay) Xᵀ (Q×P over Q), C H_inᵀ (Q×P over
 // N) and the chunk state X_w Bᵀ (P×N over Q). fp32 storage runs them on v_mfma_f32_32x32x2f32 (fp32 in,
 // fp32 accumulate); bf16 storage on v_mfma_f32_32x32x16_bf16 (bf16 in, fp32 accumulate): inputs stored as
-// bf16 enter exactly, and each fp32 operand (the decayed products, the entering state, the weighted
-// inputs) enters as the sum of two bf16 numbers, hi = bf16(v) and lo = bf16(v − hi), in two products,
-// which keeps about 16 bits of it.
+// bf16 enter exactly, and each fp32 operand (the decayed products, the weighted inputs, the entering state)
+// enters as the sum of two bf16 numbers, hi = bf16(v) and lo = bf16(v − hi), in two products, which keeps
+// about 16 bits of it. Chunk states and entering states pass through HBM as fp32 for both storage types
+// (kept in bf16 they were measured to cost most of the bf16 tolerance).
 //
 // Three kernels:
 //   ssd_state_kernel   per (b, h, chunk): the chunk's own state contribution S_c [P][N] and its decay.
@@ -187,19 +188,31 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(SsdArgs a) {
 }
 
 // One thread per (b, h, p, n): h ← decay_c·h + S_c over the chunks, leaving in S_c the state that enters
-// chunk c; the last value is the final state.
-template <int N>
+// chunk c; the last value is the final state. The chunk states are read eight chunks ahead (they do not
+// depend on h), so the chain waits on one round of loads per eight chunks. SS is the storage type of the
+// chunk states (fp32 here).
+template <typename SS, int N>
 __global__ __launch_bounds__(256) void ssd_pass_kernel(SsdArgs a) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= a.b * a.H * kP * N) return;
     const int64_t pn = gid % (kP * N), bh = gid / (kP * N);
     float hv = a.h0 ? a.h0[bh * (kP * N) + pn] : 0.0f;  // [b][H·P][N] = [b·H][P·N]
-    float *S = a.S + bh * a.nc * (kP * N) + pn;
+    SS *S = reinterpret_cast<SS *>(a.S) + bh * a.nc * (kP * N) + pn;
     const float *dec = a.decay + bh * a.nc;
-    for (int64_t c = 0; c < a.nc; ++c) {
-        const float s = S[c * (kP * N)];
-        S[c * (kP * N)] = hv;
-        hv = __builtin_fmaf(dec[c], hv, s);
+    constexpr int U = 8;
+    for (int64_t c0 = 0; c0 < a.nc; c0 += U) {
+        float sv[U], dv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool in = c0 + u < a.nc;
+            sv[u] = in ? widen(S[(c0 + u) * (kP * N)]) : 0.0f;
+            dv[u] = in ? dec[c0 + u] : 1.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (c0 + u < a.nc) S[(c0 + u) * (kP * N)] = narrow<SS>(hv);
+            hv = __builtin_fmaf(dv[u], hv, sv[u]);
+        }
     }
     if (a.hT) a.hT[bh * (kP * N) + pn] = hv;
 }
@@ -211,22 +224,29 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(SsdArgs a) {
     __shared__ float s_cum[kQ], s_beta[kQ];
     __shared__ __align__(16) float s_c[BM];       // C [t][n]; at the end the outputs [p][t]
     __shared__ __align__(16) float s_bm[BM];      // B [s][n], then the decayed products M [t][s]
-    __shared__ __align__(16) float s_h[kP * NS];  // entering state [p][n]
     __shared__ __align__(16) float s_x[kP * kMS]; // x [p][s]
     const int64_t c = blockIdx.x % a.nc, bh = blockIdx.x / a.nc;
     const int64_t ib = bh / a.H, h = bh % a.H;
     const int64_t t0 = c * kQ;
     const float ah = a.A[h];
+    const int l = lane(), w = wave(), hi = l / 32;
+    constexpr int HN = N / 2;
+    const int ot = w / 2, op = w % 2;  // this wavefront's output tile: rows t in [32·ot, +32), channels [32·op, +32)
+    // the entering-state operand of the C·h_inᵀ product (row p = 32·op + l % 32, n = hi·N/2 ..) goes
+    // straight to registers, its loads issued first so that they overlap the staging below
+    float4 hv[HN / 4];
+    {
+        const float *hr = a.S + (bh * a.nc + c) * (int64_t)(kP * N) + (32 * op + l % 32) * N + hi * HN;
+#pragma unroll
+        for (int j = 0; j < HN / 4; ++j) hv[j] = *reinterpret_cast<const float4 *>(hr + 4 * j);
+    }
     chunk_scalars<T>(a, bh, t0, ah, s_cum, s_beta);
     const T *xg = static_cast<const T *>(a.x) + ((ib * a.H + h) * kP) * a.L + t0;  // row p at + p·L
     stage_rows<T>(static_cast<const T *>(a.C) + (ib * a.L + t0) * N, N, kQ, N, a.L - t0, N, a.vec_bc, s_c, NS);
     stage_rows<T>(static_cast<const T *>(a.B) + (ib * a.L + t0) * N, N, kQ, N, a.L - t0, N, a.vec_bc, s_bm, NS);
     stage_rows<T>(xg, a.L, kP, kQ, kP, a.L - t0, a.vec, s_x, kMS);
-    stage_rows<float>(a.S + (bh * a.nc + c) * (int64_t)(kP * N), N, kP, N, kP, N, true, s_h, NS);
     __syncthreads();
 
-    const int l = lane(), w = wave(), hi = l / 32;
-    constexpr int HN = N / 2;
     // G = C Bᵀ on the tiles at or below the diagonal (wavefronts 0..2), then M = G ∘ e^{a(c_t − c_s)} β_s
     // for s <= t; wavefront 3 clears the tile above the diagonal.
     f16v g = {};
@@ -252,8 +272,6 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(SsdArgs a) {
     }
     __syncthreads();
 
-    // this wavefront's output tile: rows t in [32·ot, +32), channels p in [32·op, +32)
-    const int ot = w / 2, op = w % 2;
     f16v acc = {}, inter = {};
     {
         const float *mr = s_bm + (32 * ot + l % 32) * kMS + 32 * hi;
@@ -261,9 +279,8 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(SsdArgs a) {
         mfma_tile<32>(acc, [&](int j) { return *reinterpret_cast<const float4 *>(mr + j); },
                       [&](int j) { return *reinterpret_cast<const float4 *>(xr + j); });
         const float *cr = s_c + (32 * ot + l % 32) * NS + hi * HN;
-        const float *hr = s_h + (32 * op + l % 32) * NS + hi * HN;
         mfma_tile<HN>(inter, [&](int j) { return *reinterpret_cast<const float4 *>(cr + j); },
-                      [&](int j) { return *reinterpret_cast<const float4 *>(hr + j); });
+                      [&](int j) { return hv[j / 4]; });
     }
     __syncthreads();  // C is no longer read: its space takes the outputs [p][t]
     {
@@ -329,8 +346,7 @@ __device__ __forceinline__ void mfma_tile_bf16(f16v &acc, const uint16_t *arow, 
 }
 
 // Eight fp32 values as bf16 hi = bf16(v) and lo = bf16(v − hi).
-__device__ __forceinline__ void split8(const float *src, bf8v &hi8, bf8v &lo8) {
-    const float4 u = *reinterpret_cast<const float4 *>(src), v = *reinterpret_cast<const float4 *>(src + 4);
+__device__ __forceinline__ void split8(const float4 &u, const float4 &v, bf8v &hi8, bf8v &lo8) {
     const float f[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -347,7 +363,8 @@ __device__ __forceinline__ void mfma_tile_split(f16v &acc, const float *frow, co
 #pragma unroll
     for (int j = 0; j < W / 8; ++j) {
         bf8v h8, l8;
-        split8(frow + 8 * j, h8, l8);
+        split8(*reinterpret_cast<const float4 *>(frow + 8 * j), *reinterpret_cast<const float4 *>(frow + 8 * j + 4),
+               h8, l8);
         const bf8v o8 = *reinterpret_cast<const bf8v *>(brow + 8 * j);
         if (SPLIT_A) {
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h8, o8, acc, 0, 0, 0);
@@ -432,28 +449,33 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel_bf16(SsdArgs a) {
 template <int N>
 __global__ __launch_bounds__(kThreads) void ssd_out_kernel_bf16(SsdArgs a) {
     constexpr int NH = N + 8;                                   // LDS row stride (bf16) of N-wide rows
-    constexpr int NS = N + 4;                                   // LDS row stride (fp32) of N-wide rows
     constexpr int OUTF = kP * kMS;                              // fp32 [64][kMS] (M, then the outputs)
     constexpr int CB = (kQ * NH > OUTF * 2) ? kQ * NH : OUTF * 2;  // bf16 units
     __shared__ float s_cum[kQ], s_beta[kQ];
     __shared__ __align__(16) uint16_t s_c[CB];        // C [t][n]; at the end the outputs [p][t] (fp32)
     __shared__ __align__(16) uint16_t s_bm[CB];       // B [s][n], then M [t][s] (fp32)
-    __shared__ __align__(16) float s_h[kP * NS];      // entering state [p][n], fp32
     __shared__ __align__(16) uint16_t s_x[kP * kMH];  // x [p][s]
     const int64_t c = blockIdx.x % a.nc, bh = blockIdx.x / a.nc;
     const int64_t ib = bh / a.H, h = bh % a.H;
     const int64_t t0 = c * kQ;
     const float ah = a.A[h];
+    const int l = lane(), w = wave(), hi = l / 32;
+    constexpr int HN = N / 2;
+    const int ot = w / 2, op = w % 2;  // this wavefront's output tile
+    // the entering-state operand (row p = 32·op + l % 32, n = hi·N/2 ..) straight to registers, first
+    float4 hv[HN / 4];
+    {
+        const float *hr = a.S + (bh * a.nc + c) * (int64_t)(kP * N) + (32 * op + l % 32) * N + hi * HN;
+#pragma unroll
+        for (int j = 0; j < HN / 4; ++j) hv[j] = *reinterpret_cast<const float4 *>(hr + 4 * j);
+    }
     chunk_scalars<uint16_t>(a, bh, t0, ah, s_cum, s_beta);
     const uint16_t *xg = static_cast<const uint16_t *>(a.x) + ((ib * a.H + h) * kP) * a.L + t0;
     stage_rows_bf16(static_cast<const uint16_t *>(a.C) + (ib * a.L + t0) * N, N, kQ, N, a.L - t0, N, a.vec_bc, s_c, NH);
     stage_rows_bf16(static_cast<const uint16_t *>(a.B) + (ib * a.L + t0) * N, N, kQ, N, a.L - t0, N, a.vec_bc, s_bm, NH);
     stage_rows_bf16(xg, a.L, kP, kQ, kP, a.L - t0, a.vec8, s_x, kMH);
-    stage_rows<float>(a.S + (bh * a.nc + c) * (int64_t)(kP * N), N, kP, N, kP, N, true, s_h, NS);
     __syncthreads();
 
-    const int l = lane(), w = wave(), hi = l / 32;
-    constexpr int HN = N / 2;
     f16v g = {};
     const int qt = w == 0 ? 0 : 1, qs = w == 2 ? 1 : 0;
     if (w < 3) mfma_tile_bf16<HN>(g, s_c + (32 * qt + l % 32) * NH + hi * HN, s_bm + (32 * qs + l % 32) * NH + hi * HN);
@@ -473,10 +495,20 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel_bf16(SsdArgs a) {
     }
     __syncthreads();
 
-    const int ot = w / 2, op = w % 2;
     f16v acc = {}, inter = {};
     mfma_tile_split<32, true>(acc, s_m + (32 * ot + l % 32) * kMS + 32 * hi, s_x + (32 * op + l % 32) * kMH + 32 * hi);
-    mfma_tile_split<HN, false>(inter, s_h + (32 * op + l % 32) * NS + hi * HN, s_c + (32 * ot + l % 32) * NH + hi * HN);
+    {
+        // the entering state (fp32) enters as hi + lo
+        const uint16_t *cr = s_c + (32 * ot + l % 32) * NH + hi * HN;
+#pragma unroll
+        for (int j = 0; j < HN / 8; ++j) {
+            bf8v h8, l8;
+            split8(hv[2 * j], hv[2 * j + 1], h8, l8);
+            const bf8v c8 = *reinterpret_cast<const bf8v *>(cr + 8 * j);
+            inter = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c8, h8, inter, 0, 0, 0);
+            inter = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c8, l8, inter, 0, 0, 0);
+        }
+    }
     __syncthreads();  // C is no longer read: its space takes the outputs
     float *s_o = reinterpret_cast<float *>(s_c);
     {
@@ -526,7 +558,7 @@ hipError_t launch_n(const SsdArgs &a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t elems = a.b * a.H * kP * N;
-    hipLaunchKernelGGL((ssd_pass_kernel<N>), dim3((unsigned)((elems + 255) / 256)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((ssd_pass_kernel<float, N>), dim3((unsigned)((elems + 255) / 256)), dim3(256), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((ssd_out_kernel_bf16<N>), dim3(chunks), dim3(kThreads), 0, stream, a);
