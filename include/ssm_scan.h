@@ -33,8 +33,12 @@
  *     returns without synchronising. Asynchronous device faults surface at the caller's next
  *     synchronisation of that stream.
  *   - Calls are reentrant: the library keeps no per-call global state. Calls on different streams
- *     may run concurrently. Prefill calls whose sequence is split into several time segments
- *     take stream-ordered scratch memory (hipMallocAsync / hipFreeAsync on `stream`).
+ *     may run concurrently. Calls that need scratch (a prefill split into time segments, the
+ *     gradient pass, ssm_lti_fwd, ssm_ssd_fwd) take it from the current device's default
+ *     stream-ordered pool (hipMallocAsync / hipFreeAsync on `stream`). The first such call on a
+ *     device sets that pool's release threshold to its maximum, so freed scratch stays pooled
+ *     instead of being returned at every synchronisation; other users of the device's default pool
+ *     see the same setting.
  *   - NaN and Inf inputs propagate; nothing is clamped.
  */
 #ifndef SSM_SCAN_H
