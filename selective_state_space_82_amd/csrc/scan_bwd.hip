@@ -60,8 +60,16 @@ __device__ __forceinline__ float dbeta_da(float dt, float u, float abar, float b
     return __builtin_fabsf(v) < 0.0625f ? series : direct;
 }
 
-// REV: reverse aggregate pass (no gradients; segments 1 .. S−1), else the gradient pass.
-template <typename T, int G, int NPL, bool REV>
+// Where every |A| of a wavefront's states is at least this, the gradient pass takes β = (Ā − 1)/A as
+// written: Ā comes within a few units in the last place of 1, so β's absolute error is a few times
+// 2^-23/|A| (the same error the prefill's scaled-state path accepts for Ā − 1). The series for small
+// |ΔA| is kept for ∂β/∂a, whose direct form cancels to nothing there.
+constexpr float kDirectBetaAbsA = 0.125f;
+
+// REV: reverse aggregate pass (no gradients; segments 1 .. S−1), else the gradient pass. DIRECT (only
+// for the gradient pass): the variant for wavefronts whose |A| are all at least kDirectBetaAbsA;
+// the two variants run over the same grid and each unit returns at once from the one it does not own.
+template <typename T, int G, int NPL, bool REV, bool DIRECT = false>
 __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
     constexpr int E = Chunk<T>::kElems;
     constexpr int kPitch = kBT + 4;
@@ -128,6 +136,12 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
         ia[j] = 1.0f / av;
         gA[j] = 0.0f;
         kap[j] = 0.0f;
+    }
+    if constexpr (!REV) {
+        bool small_a = false;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) small_a |= !(__builtin_fabsf(Av[j]) >= kDirectBetaAbsA);
+        if (__any(small_a) == DIRECT) return;  // wave-uniform: the other variant owns this unit
     }
     auto load_state = [&](const float *base, float (&o)[NPL]) {
         if (a.vec_state) {
@@ -376,7 +390,7 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
                     for (int q = 0; q < 4; ++q) {
                         const float u = dt * a2[j + q];
                         const float abar = exp2_fast(u);
-                        const float beta = zoh_input_coef_log2(dt, u, abar, ia[j + q]);
+                        const float beta = DIRECT ? (abar - 1.0f) * ia[j + q] : zoh_input_coef_log2(dt, u, abar, ia[j + q]);
                         const float hp = k == 0 ? h[j + q] : hs[k - 1][j + q];
                         hs[k][j + q] = __builtin_fmaf(abar, hp, beta * (bq[q] * xt));
                         if constexpr (kKeep) {
@@ -434,7 +448,7 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
                         beta = be_k[kKeep ? k - (K - KH) : 0][j];
                     } else {
                         abar = exp2_fast(u);
-                        beta = zoh_input_coef_log2(dt, u, abar, ia[j]);
+                        beta = DIRECT ? (abar - 1.0f) * ia[j] : zoh_input_coef_log2(dt, u, abar, ia[j]);
                     }
                     const float hp = k == 0 ? h[j] : hs[k - 1][j];
                     const float lam = __builtin_fmaf(dys, Cv[j], kap[j]);
@@ -523,8 +537,12 @@ hipError_t launch_bwd_typed(BwdArgs args, int64_t ncb, int n_seg, hipStream_t st
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((scan_bwd_kernel<T, G, NPL, false>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0, stream,
-                       args);
+    hipLaunchKernelGGL((scan_bwd_kernel<T, G, NPL, false, true>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0,
+                       stream, args);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((scan_bwd_kernel<T, G, NPL, false, false>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0,
+                       stream, args);
     return hipGetLastError();
 }
 
