@@ -201,6 +201,31 @@ ssm_status_t fwd_impl(const void *x, const void *delta, const float *A, const vo
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+// Time split of the reverse aggregate and gradient passes, as a segment length. The gradient kernel
+// keeps two wavefronts per SIMD resident at 4 states per lane and one above that (its registers and
+// LDS), so its grid runs in rounds of that many wavefronts, and a partial last round leaves SIMDs idle.
+// The split minimises rounds × segment length; a longer split wins only where it saves more than
+// 1/16 of that, since every segment after the first costs a reverse aggregate rescan.
+int64_t grad_seg_len(int64_t b, int64_t d, int64_t L, int lanes, int npl, int cus) {
+    const int64_t q = ssm::kSegQuantum;
+    const int64_t Lr = ((L + q - 1) / q) * q;
+    const int64_t ncb = b * ((d + 64 / lanes - 1) / (64 / lanes));
+    const int64_t resident = (int64_t)cus * 4 * (npl <= 4 ? 2 : 1);
+    int64_t best_len = Lr, best_cost = 0;
+    const int64_t max_seg = Lr / 128 > 1 ? (Lr / 128 < 64 ? Lr / 128 : 64) : 1;
+    for (int64_t S = 1; S <= max_seg; ++S) {
+        const int64_t len = ((Lr / S + q - 1) / q) * q;
+        const int64_t segs = (L + len - 1) / len;
+        const int64_t rounds = (segs * ncb + resident - 1) / resident;
+        const int64_t cost = rounds * len;
+        if (S == 1 || cost * 16 < best_cost * 15) {
+            best_cost = cost;
+            best_len = len;
+        }
+    }
+    return best_len;
+}
+
 ssm_status_t bwd_impl(const void *x, const void *delta, const float *A, const void *B, const void *C,
                       const float *D, const void *z, const float *initial_state, const void *dy,
                       const float *d_final_state, void *dx, void *ddelta, float *dA, float *dB, float *dC,
@@ -234,9 +259,11 @@ ssm_status_t bwd_impl(const void *x, const void *delta, const float *A, const vo
     p.dA = dA; p.dB = dB; p.dC = dC; p.dD = dD; p.d_init_state = d_initial_state;
     p.b = b; p.d = d; p.L = L; p.N = N; p.bf16 = dtype == SSM_BF16;
     p.lanes_per_channel = pl.lanes; p.states_per_lane = pl.npl; p.seg_len = pl.seg_len; p.n_seg = pl.n_seg;
+    p.grad_seg_len = grad_seg_len(b, d, L, pl.lanes, pl.npl, cu_count());
+    p.grad_n_seg = (int)((L + p.grad_seg_len - 1) / p.grad_seg_len);
     int64_t floats = 0;
     if (!mul_ok(b * d, L, &floats)) return SSM_ERR_SHAPE;
-    floats = ssm::bwd_scratch_floats(pl.n_seg, b, d, L, N, pl.npl);
+    floats = ssm::bwd_scratch_floats(pl.n_seg, p.grad_n_seg, b, d, L, N, pl.npl);
     void *scratch = nullptr;
     keep_pool_memory();
     if (hipMallocAsync(&scratch, (size_t)floats * sizeof(float), stream) != hipSuccess) return SSM_ERR_HIP;

@@ -44,8 +44,10 @@ struct BwdLaunch {
     int64_t b, d, L, N;
     bool bf16;
     int lanes_per_channel, states_per_lane;
-    int64_t seg_len;
+    int64_t seg_len;             // time split of the checkpointing forward pass
     int n_seg;
+    int64_t grad_seg_len;        // time split of the reverse aggregate and gradient passes
+    int grad_n_seg;
     float *scratch;              // bwd_scratch_floats(...) floats
 };
 
@@ -135,9 +137,10 @@ inline int64_t scratch_floats(int64_t n_seg, int64_t b, int64_t d, int64_t N) {
 // Gradient pass: checkpoint interval (steps whose states fit one lane's registers) and scratch:
 // the forward pass's scratch, the checkpoints, and the reverse aggregates (Π Ā, adjoint from zero).
 inline int ckpt_len(int states_per_lane) { return (32 / states_per_lane) < 4 ? 4 : 32 / states_per_lane; }
-inline int64_t bwd_scratch_floats(int64_t n_seg, int64_t b, int64_t d, int64_t L, int64_t N, int npl) {
+inline int64_t bwd_scratch_floats(int64_t n_seg, int64_t grad_n_seg, int64_t b, int64_t d, int64_t L, int64_t N,
+                                  int npl) {
     const int64_t ck = ckpt_len(npl);
-    return scratch_floats(n_seg, b, d, N) + b * d * ((L + ck - 1) / ck) * N + 2 * (n_seg - 1) * b * d * N;
+    return scratch_floats(n_seg, b, d, N) + b * d * ((L + ck - 1) / ck) * N + 2 * (grad_n_seg - 1) * b * d * N;
 }
 
 }  // namespace ssm

@@ -564,7 +564,7 @@ hipError_t launch_scan_bwd(const BwdLaunch &p, hipStream_t stream) {
     const int64_t fwd_scratch = scratch_floats(p.n_seg, p.b, p.d, p.N);
     float *ckpt = p.scratch + fwd_scratch;
     float *rP = ckpt + p.b * p.d * n_ck * p.N;
-    float *rE = rP + (int64_t)(p.n_seg - 1) * p.b * p.d * p.N;
+    float *rE = rP + (int64_t)(p.grad_n_seg - 1) * p.b * p.d * p.N;
 
     const ZeroList zl{{p.dA, p.dB, p.dC, p.dD}, {p.d * p.N, p.b * p.L * p.N, p.b * p.L * p.N, p.dD ? p.d : 0}};
     hipError_t e = zero4(zl, stream);
@@ -586,7 +586,7 @@ hipError_t launch_scan_bwd(const BwdLaunch &p, hipStream_t stream) {
     a.dh_final = p.d_final_state; a.ckpt = ckpt; a.rP = rP; a.rE = rE; a.rP_out = rP; a.rE_out = rE;
     a.dx = p.dx; a.ddelta = p.ddelta; a.dz = p.dz; a.dA = p.dA; a.dB = p.dB; a.dC = p.dC; a.dD = p.dD;
     a.dh0 = p.d_init_state;
-    a.b = p.b; a.d = p.d; a.L = p.L; a.N = p.N; a.seg_len = p.seg_len; a.n_seg = p.n_seg;
+    a.b = p.b; a.d = p.d; a.L = p.L; a.N = p.N; a.seg_len = p.grad_seg_len; a.n_seg = p.grad_n_seg;
     const int cw = kWave / p.lanes_per_channel;
     a.n_cw = (p.d + cw - 1) / cw;
     a.n_ck = n_ck; a.ck_len = ck;
@@ -596,8 +596,8 @@ hipError_t launch_scan_bwd(const BwdLaunch &p, hipStream_t stream) {
     a.vec_bc = ((p.L * p.N * esize) % 16 == 0) && al16(p.B) && al16(p.C);
     a.vec_state = (p.N % 4 == 0) && al16(p.d_final_state) && al16(p.scratch) && al16(ckpt) && al16(rP) && al16(rE);
     const int64_t ncb = p.b * a.n_cw;
-    if (p.bf16) return dispatch_bwd<uint16_t>(a, p.lanes_per_channel, npl, ncb, p.n_seg, stream);
-    return dispatch_bwd<float>(a, p.lanes_per_channel, npl, ncb, p.n_seg, stream);
+    if (p.bf16) return dispatch_bwd<uint16_t>(a, p.lanes_per_channel, npl, ncb, p.grad_n_seg, stream);
+    return dispatch_bwd<float>(a, p.lanes_per_channel, npl, ncb, p.grad_n_seg, stream);
 }
 
 }  // namespace ssm
