@@ -378,13 +378,28 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
             // forward recomputation of the chunk: hs[k] = state after step tc + k
             float hs[K][NPL];
             float ab_k[kKeep ? KH : 1][kKeep ? NPL : 1], be_k[kKeep ? KH : 1][kKeep ? NPL : 1];
+            // Both walks read a step's operands from LDS one step ahead of their use, so the wait for
+            // them falls behind a step of arithmetic instead of stalling at the start of each step.
+            float fx = xrow[tc], fd = drow[tc];
+            float4 fb[NPL / 4];
+#pragma unroll
+            for (int j = 0; j < NPL; j += 4) fb[j / 4] = *reinterpret_cast<const float4 *>(Bn + tc * NPAD + j);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const int t = tc + k;
-                const float xt = xrow[t], dt = drow[t];
+                const float xt = fx, dt = fd;
+                float4 bcur[NPL / 4];
+#pragma unroll
+                for (int j = 0; j < NPL; j += 4) bcur[j / 4] = fb[j / 4];
+                if (k + 1 < K) {
+                    fx = xrow[t + 1];
+                    fd = drow[t + 1];
+#pragma unroll
+                    for (int j = 0; j < NPL; j += 4) fb[j / 4] = *reinterpret_cast<const float4 *>(Bn + (t + 1) * NPAD + j);
+                }
 #pragma unroll
                 for (int j = 0; j < NPL; j += 4) {
-                    const float4 bv = *reinterpret_cast<const float4 *>(Bn + t * NPAD + j);
+                    const float4 bv = bcur[j / 4];
                     const float bq[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
@@ -406,23 +421,37 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
             // backward over the chunk. The fence makes the walk re-read its operands from LDS
             // rather than keep the forward walk's copies alive in registers.
             wave_sync();
+            float wx, wd, wg, wz;
+            float4 wb[NPL / 4], wc[NPL / 4];
+            auto read_step = [&](int t) {
+                wx = xrow[t];
+                wd = drow[t];
+                wg = grow[t];
+                wz = gate ? zrow[t] : 0.0f;
+#pragma unroll
+                for (int j = 0; j < NPL; j += 4) {
+                    wb[j / 4] = *reinterpret_cast<const float4 *>(Bn + t * NPAD + j);
+                    wc[j / 4] = *reinterpret_cast<const float4 *>(Cn + t * NPAD + j);
+                }
+            };
+            read_step(tc + K - 1);
 #pragma unroll
             for (int k = K - 1; k >= 0; --k) {
                 const int t = tc + k;
-                const float xt = xrow[t];
-                float dt = drow[t];
-                // where not kept, Ā and β are recomputed here rather than kept from the forward walk
-                // (K·NPL pairs of registers); the empty asm hides that they are the same values
-                if (!kKeep || k < K - KH) asm volatile("" : "+v"(dt));
-                const float dyt = grow[t];
+                const float xt = wx;
+                float dt = wd;
+                const float dyt = wg, zt = wz;
                 float Bv[NPL], Cv[NPL];
 #pragma unroll
                 for (int j = 0; j < NPL; j += 4) {
-                    const float4 bv = *reinterpret_cast<const float4 *>(Bn + t * NPAD + j);
-                    const float4 cv = *reinterpret_cast<const float4 *>(Cn + t * NPAD + j);
+                    const float4 bv = wb[j / 4], cv = wc[j / 4];
                     Bv[j] = bv.x; Bv[j + 1] = bv.y; Bv[j + 2] = bv.z; Bv[j + 3] = bv.w;
                     Cv[j] = cv.x; Cv[j + 1] = cv.y; Cv[j + 2] = cv.z; Cv[j + 3] = cv.w;
                 }
+                if (k > 0) read_step(t - 1);
+                // where not kept, Ā and β are recomputed here rather than kept from the forward walk
+                // (K·NPL pairs of registers); the empty asm hides that they are the same values
+                if (!kKeep || k < K - KH) asm volatile("" : "+v"(dt));
                 // readout ys_t (for dz) and the gated output gradient
                 float ysp = 0.0f;
 #pragma unroll
@@ -430,7 +459,6 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
                 const float ys = __builtin_fmaf(dskip, xt, group_sum<G>(ysp));
                 float dys = dyt, dzt = 0.0f;
                 if (gate) {
-                    const float zt = zrow[t];
                     const float sg = __builtin_amdgcn_rcpf(1.0f + exp2_fast(-kLog2e * zt));
                     dys = dyt * zt * sg;
                     dzt = dyt * ys * sg * __builtin_fmaf(zt, 1.0f - sg, 1.0f);
