@@ -75,9 +75,12 @@ struct FwdArgs {
 // The kernel ---------------------------------------------------------------------------------
 //
 // T: storage type (float or bf16 bits); G: lanes per channel (1, 2, 4); NPL: states per lane
-// (4, 8, 16); AGG: aggregate pass (segment end state from zero and Π Ā, no readout).
-template <typename T, int G, int NPL, bool AGG, bool SAFE>
+// (4, 8, 16); AGG: aggregate pass (segment end state from zero and Π Ā, no readout). CK: the
+// output pass of a call that wants only the checkpoints (the gradient's forward), so it carries the
+// state in and stores it every ck_len steps but has no readout.
+template <typename T, int G, int NPL, bool AGG, bool SAFE, bool CK = false>
 __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
+    constexpr bool RO = !AGG && !CK;                     // readout, gate and y
     constexpr int kTile = tile_len<T>();
     constexpr int kPitch = kTile + 4;                    // floats per LDS row of x, Δ (16-byte pad)
     constexpr int E = Chunk<T>::kElems;
@@ -96,11 +99,11 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
     static_assert(kYWin * sizeof(T) == 128, "an output window is one 128-byte line per row");
     __shared__ __attribute__((aligned(16))) float xs[CW * kPitch];
     __shared__ __attribute__((aligned(16))) float dsh[CW * kPitch];
-    __shared__ __attribute__((aligned(16))) T zs[AGG ? 8 : CW * kZPitch];
+    __shared__ __attribute__((aligned(16))) T zs[RO ? CW * kZPitch : 8];
     __shared__ __attribute__((aligned(16))) float Bs[kBF];
-    __shared__ __attribute__((aligned(16))) float Cs[AGG ? 4 : kBF];
-    __shared__ __attribute__((aligned(16))) float red[(AGG || G == 1) ? 4 : CW * kRS];
-    __shared__ __attribute__((aligned(16))) T ybuf[AGG ? 8 : CW * kYPitch];
+    __shared__ __attribute__((aligned(16))) float Cs[RO ? kBF : 4];
+    __shared__ __attribute__((aligned(16))) float red[(!RO || G == 1) ? 4 : CW * kRS];
+    __shared__ __attribute__((aligned(16))) T ybuf[RO ? CW * kYPitch : 8];
 
     const int lane = threadIdx.x;
     const int c = lane / G;  // channel within the wave
@@ -126,7 +129,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
     const T *__restrict__ Bg = static_cast<const T *>(a.B) + bi * a.L * a.N;
     const T *__restrict__ Cg = static_cast<const T *>(a.C) + bi * a.L * a.N;
     T *__restrict__ yg = static_cast<T *>(a.y);
-    const bool gate = !AGG && zg != nullptr;
+    const bool gate = RO && zg != nullptr;
 
     // ---- per-lane channel constants for this lane's state group ----
     const int64_t ch = d0 + c;
@@ -186,7 +189,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
 #pragma unroll
         for (int j = 0; j < NPL; ++j) s[j] *= Av[j];  // scaled state s = A·h
     }
-    const float dskip = (!AGG && a.D) ? load_or(a.D, ch, ch_ok, 0.0f) : 0.0f;
+    const float dskip = (RO && a.D) ? load_or(a.D, ch, ch_ok, 0.0f) : 0.0f;
 
     // ---- tile prefetch into registers, and from there into LDS ----
     uint4 px[kXC], pd[kXC], pz[kXC], pb[kBC], pc[kBC];
@@ -211,7 +214,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
             const int64_t e0 = (int64_t)(lane + i * kWave) * E;
             const bool ok = e0 < (int64_t)kTile * N;
             pb[i] = get_chunk<T>(Bg + t0 * a.N, e0, nel, ok, a.vec_bc);
-            if constexpr (!AGG) pc[i] = get_chunk<T>(Cg + t0 * a.N, e0, nel, ok, a.vec_bc);
+            if constexpr (RO) pc[i] = get_chunk<T>(Cg + t0 * a.N, e0, nel, ok, a.vec_bc);
         }
     };
     auto store_tile = [&]() {
@@ -231,18 +234,18 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
             if (e0 >= kTile * N) break;
             if (N == NPAD) {  // the run maps onto the [kTile][NPAD] plane one to one
                 put_chunk<T>(Bs + e0, pb[i]);
-                if constexpr (!AGG) put_chunk<T>(Cs + e0, pc[i]);
+                if constexpr (RO) put_chunk<T>(Cs + e0, pc[i]);
             } else {          // element by element; columns N .. NPAD−1 stay zero
                 float vb[E], vc[E];
                 chunk_to_regs<T>(vb, pb[i]);
-                if constexpr (!AGG) chunk_to_regs<T>(vc, pc[i]);
+                if constexpr (RO) chunk_to_regs<T>(vc, pc[i]);
 #pragma unroll
                 for (int q = 0; q < E; ++q) {
                     const int e = e0 + q;
                     if (e < kTile * N) {
                         const int t = e / N, n = e - t * N;
                         Bs[t * NPAD + n] = vb[q];
-                        if constexpr (!AGG) Cs[t * NPAD + n] = vc[q];
+                        if constexpr (RO) Cs[t * NPAD + n] = vc[q];
                     }
                 }
             }
@@ -252,7 +255,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
     if (N != NPAD) {  // padding columns of the B/C planes must read as zero
         for (int i = lane; i < kBF; i += kWave) {
             Bs[i] = 0.0f;
-            if constexpr (!AGG) Cs[i] = 0.0f;
+            if constexpr (RO) Cs[i] = 0.0f;
         }
     }
 
@@ -301,7 +304,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
         for (int j = 0; j < NPL; j += 4) {
             const float4 bv = *reinterpret_cast<const float4 *>(Bn + t * NPAD + j);
             o.B[j] = bv.x; o.B[j + 1] = bv.y; o.B[j + 2] = bv.z; o.B[j + 3] = bv.w;
-            if constexpr (!AGG) {
+            if constexpr (RO) {
                 const float4 cv = *reinterpret_cast<const float4 *>(Cn + t * NPAD + j);
                 o.C[j] = cv.x; o.C[j + 1] = cv.y; o.C[j + 2] = cv.z; o.C[j + 3] = cv.w;
             }
@@ -319,11 +322,11 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
             if constexpr (!SAFE) {
                 const float pre = __builtin_fmaf(cur.B[j], xt, s[j]);  // s + B x
                 s[j] = __builtin_fmaf(abar - 1.0f, pre, s[j]);         // s + (Ā − 1)(s + B x)
-                if constexpr (!AGG) acc = __builtin_fmaf(cur.C[j] * ia[j], s[j], acc);
+                if constexpr (RO) acc = __builtin_fmaf(cur.C[j] * ia[j], s[j], acc);
             } else {
                 const float kc = zoh_input_coef_log2(dt, u, abar, ia[j]);
                 s[j] = __builtin_fmaf(abar, s[j], kc * (cur.B[j] * xt));  // Ā h + B̄ x
-                if constexpr (!AGG) acc = __builtin_fmaf(cur.C[j], s[j], acc);
+                if constexpr (RO) acc = __builtin_fmaf(cur.C[j], s[j], acc);
             }
         }
         if constexpr (AGG) dsum += dt;
@@ -394,7 +397,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
         if constexpr (!kGroupLocal) load_sub(0, sb[0]);
         // the output pass unrolls the tile (LDS offsets become immediates); the aggregate pass
         // keeps a loop, which holds its register need down
-        constexpr int kUnroll = AGG ? 1 : kTile / kGrp;
+        constexpr int kUnroll = RO ? kTile / kGrp : 1;
 #pragma unroll kUnroll
         for (int t = 0; t < kTile; t += kGrp) {
             if constexpr (!AGG) {
@@ -412,7 +415,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
                 __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
                 p[k] = compute_step(sb[k & 1]);
             }
-            if constexpr (!AGG) {
+            if constexpr (RO) {
                 if constexpr (G == 1) {
                     finish(t, p, ywin);
                 } else {
@@ -434,7 +437,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
         for (int it = 0; it < ntiles; ++it) {
             const int64_t t0 = t_begin + (int64_t)it * kTile;
             scan_tile(it);
-            if constexpr (!AGG) {
+            if constexpr (RO) {
                 if (yg && ((it & 1) || it + 1 == ntiles)) {  // the output window is complete
                     const int64_t tw0 = t0 - (it & 1) * kTile;
                     const int64_t left = t_end - tw0;
@@ -495,6 +498,13 @@ __global__ __launch_bounds__(kWave, (G == 4 && NPL == 4 && !SAFE) ? 3 : 1) void 
     }
 }
 
+// Output pass of the gradient's checkpointing forward (fast path): carries the state in and stores it
+// every ck_len steps, with no readout and no y.
+template <typename T, int G, int NPL>
+__global__ __launch_bounds__(kWave, (G == 4 && NPL == 4) ? 3 : 1) void scan_ckpt_kernel(FwdArgs a) {
+    scan_unit<T, G, NPL, false, false, true>(a, blockIdx.x);
+}
+
 // Chunk carry for many segments: h_in[k] = P[k]·h_in[k−1] + E[k] per (b, d, n), from the
 // initial state.
 __global__ __launch_bounds__(256) void carry_kernel(const float *__restrict__ P, const float *__restrict__ Eend,
@@ -532,8 +542,12 @@ hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLa
     }
     // Timing events, when given, are set by the dispatch of the fast output kernel itself (start and
     // end of that kernel), so they add no packets of their own to the queue.
-    hipExtLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false, false>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0,
-                          stream, p.ev_begin, p.ev_end, 0u, args, (int64_t)n_seg * ncb);
+    if (args.y == nullptr && args.ckpt != nullptr) {
+        hipLaunchKernelGGL((scan_ckpt_kernel<T, G, NPL>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0, stream, args);
+    } else {
+        hipExtLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false, false>), dim3((unsigned)(n_seg * ncb)), dim3(kWave),
+                              0, stream, p.ev_begin, p.ev_end, 0u, args, (int64_t)n_seg * ncb);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // Channel blocks with a small |A| run as one segment each (no aggregates needed), so a single
