@@ -23,8 +23,8 @@
 //     channels there, and are added to the outputs with float atomics (so their low bits depend on
 //     the order in which waves finish). dA and dD are per-lane sums added atomically at the end.
 //   * Tiles of 16 steps of x, Δ, z and dy rows (and the B, C runs) are prefetched one tile ahead
-//     (in reverse time order) into registers and staged in the wave's LDS; dx, dΔ, dz collect in LDS
-//     and leave a row segment at a time.
+//     (in reverse time order) into registers and staged in the wave's LDS, z and dy as the gate's two
+//     factors (computed once per element); dx, dΔ, dz collect in LDS and leave a row segment at a time.
 #include "device_common.h"
 #include "launch.h"
 #include "tile_common.h"
@@ -90,8 +90,8 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
     static_assert(kBT % K == 0 && K % kRG == 0, "chunks tile the tile, reduction groups tile the chunk");
     __shared__ __attribute__((aligned(16))) float xs[CW * kPitch];
     __shared__ __attribute__((aligned(16))) float ds[CW * kPitch];
-    __shared__ __attribute__((aligned(16))) float zs[CW * kPitch];
-    __shared__ __attribute__((aligned(16))) float gs[CW * kPitch];   // dy
+    __shared__ __attribute__((aligned(16))) float zs[REV ? 4 : CW * kPitch];  // the gate's dz factor
+    __shared__ __attribute__((aligned(16))) float gs[CW * kPitch];   // ∂L/∂ys (dy through the gate)
     __shared__ __attribute__((aligned(16))) float Bs[REV ? 4 : kBF];
     __shared__ __attribute__((aligned(16))) float Cs[kBF];
     __shared__ __attribute__((aligned(16))) float outs[REV ? 4 : 3 * CW * kPitch];  // dx, dΔ, dz
@@ -205,8 +205,27 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
             const int col = (k % kRowChunks) * E;
             if constexpr (!REV) put_chunk<T>(xs + r * kPitch + col, px[i]);
             put_chunk<T>(ds + r * kPitch + col, pd[i]);
-            if (gate) put_chunk<T>(zs + r * kPitch + col, pz[i]);
-            put_chunk<T>(gs + r * kPitch + col, pg[i]);
+            if (gate) {
+                // the gate's factors, once per element rather than on each of a channel's G lanes:
+                // gs <- dy·silu(z) = ∂L/∂ys, zs <- dy·σ(z)·(1 + z(1 − σ(z))), which times ys is ∂L/∂z
+                float zv[E], gv[E], fz[E];
+                chunk_to_regs<T>(zv, pz[i]);
+                chunk_to_regs<T>(gv, pg[i]);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float sg = __builtin_amdgcn_rcpf(1.0f + exp2_fast(-kLog2e * zv[e]));
+                    fz[e] = gv[e] * sg * __builtin_fmaf(zv[e], 1.0f - sg, 1.0f);
+                    gv[e] = gv[e] * zv[e] * sg;
+                }
+#pragma unroll
+                for (int e = 0; e < E; e += 4) {
+                    *reinterpret_cast<float4 *>(gs + r * kPitch + col + e) = make_float4(gv[e], gv[e + 1], gv[e + 2], gv[e + 3]);
+                    if constexpr (!REV)
+                        *reinterpret_cast<float4 *>(zs + r * kPitch + col + e) = make_float4(fz[e], fz[e + 1], fz[e + 2], fz[e + 3]);
+                }
+            } else {
+                put_chunk<T>(gs + r * kPitch + col, pg[i]);
+            }
         }
 #pragma unroll
         for (int i = 0; i < kBC; ++i) {
@@ -244,12 +263,7 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
     const float *grow = gs + c * kPitch;
     const float *Bn = Bs + n0;
     const float *Cn = Cs + n0;
-    auto dys_of = [&](int t) {  // ∂L/∂ys_t = dy_t · silu(z_t) (dy_t without a gate)
-        const float gy = grow[t];
-        if (!gate) return gy;
-        const float zt = zrow[t];
-        return gy * zt * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-kLog2e * zt));
-    };
+    auto dys_of = [&](int t) { return grow[t]; };  // ∂L/∂ys_t: dy_t·silu(z_t) with a gate, else dy_t
 
     // ---- reverse aggregate pass: κ from zero at the segment's end back to its start ----
     if constexpr (REV) {
@@ -457,12 +471,8 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
 #pragma unroll
                 for (int j = 0; j < NPL; ++j) ysp = __builtin_fmaf(Cv[j], hs[k][j], ysp);
                 const float ys = __builtin_fmaf(dskip, xt, group_sum<G>(ysp));
-                float dys = dyt, dzt = 0.0f;
-                if (gate) {
-                    const float sg = __builtin_amdgcn_rcpf(1.0f + exp2_fast(-kLog2e * zt));
-                    dys = dyt * zt * sg;
-                    dzt = dyt * ys * sg * __builtin_fmaf(zt, 1.0f - sg, 1.0f);
-                }
+                const float dys = dyt;      // the staged ∂L/∂ys
+                const float dzt = ys * zt;  // zero without a gate (zt reads as 0 then)
                 float gx = 0.0f, gd = 0.0f;
                 const int kr = k % kRG;
                 float *rb = red_at(kr, 0);
