@@ -103,6 +103,7 @@ struct SsdLaunch {
     float *scratch;                      // ssd_scratch_floats(b, H, L, N)
     int64_t b, H, L, N;
     bool bf16;
+    int cus;                             // compute units of the device
 };
 int64_t ssd_scratch_floats(int64_t b, int64_t H, int64_t L, int64_t N);
 hipError_t launch_ssd(const SsdLaunch &p, hipStream_t stream);

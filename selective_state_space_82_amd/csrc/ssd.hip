@@ -21,81 +21,21 @@
 //   ssd_pass_kernel    per (b, h, p, n): walks the chunks in order, replacing S_c by the state entering
 //                      chunk c and writing the final state.
 //   ssd_out_kernel     per (b, h, chunk): the outputs of the chunk from its inputs and entering state.
+// Where b·H·N/64 workgroups fill the device, ssd_scan_kernel (ssd_scan.hip) takes the place of the first
+// two: it walks each head's chunks in order with the state in its MFMA accumulators, so the chunk
+// states never pass through HBM.
 //
 // MFMA lane layouts (checked on the device): 32x32x2 f32: lane l supplies A[l % 32][l / 32] and
 // B[l / 32][l % 32]; 32x32x16 bf16: lane l supplies A[l % 32][8(l / 32) + e] and B[8(l / 32) + e][l % 32],
 // e < 8; for both, result register r of lane l is D[8(r / 4) + 4(l / 32) + r % 4][l % 32].
 #include "device_common.h"
 #include "launch.h"
+#include "ssd_common.h"
 
 namespace ssm {
 namespace {
 
-typedef float f16v __attribute__((ext_vector_type(16)));
-typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
-
-constexpr int kQ = 64;           // chunk length
-constexpr int kP = 64;           // channels per head
-constexpr int kThreads = 256;    // four wavefronts
-
-struct SsdArgs {
-    const void *x, *delta, *B, *C, *z;
-    const float *A, *D, *h0;
-    void *y;
-    float *hT;
-    float *S;      // [b][H][nc][P][N] chunk states, then entering states
-    float *decay;  // [b][H][nc]
-    int64_t b, H, L, nc;
-    bool vec;      // x rows allow 16-byte (fp32) / 8-byte (bf16) loads at 4-element steps
-    bool vec_bc;   // so do the rows of B and C
-    bool vec8;     // x rows allow 16-byte loads at 8-element steps (bf16)
-};
-
-__device__ __forceinline__ int lane() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave() { return threadIdx.x >> 6; }
-
-// Row position of result register r of lane l in a 32×32 tile.
-__device__ __forceinline__ int d_row(int r, int l) { return 8 * (r / 4) + 4 * (l / 32) + (r % 4); }
-
-// Four consecutive elements row[i .. i+3] as fp32, zeros at and past `limit`; one 16-byte (fp32) or
-// 8-byte (bf16) load when `vec` says the row allows it.
-template <typename T>
-__device__ __forceinline__ float4 load4(const T *row, int64_t i, int64_t limit, bool vec) {
-    if (vec && i + 4 <= limit) {
-        if constexpr (sizeof(T) == 4) {
-            return *reinterpret_cast<const float4 *>(row + i);
-        } else {
-            const uint2 w = *reinterpret_cast<const uint2 *>(row + i);
-            return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
-        }
-    }
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = i + e < limit ? widen(row[i + e]) : 0.0f;
-    return make_float4(v[0], v[1], v[2], v[3]);
-}
-
-// One 32×32 tile product over K = 2W with the K index permuted so that each lane reads a contiguous run:
-// at step j the lower lane half supplies k = j and the upper half k = W + j. fa(j) / fb(j) return the
-// lane's operand values for steps j .. j+3 (its own row, k = hi·W + j .. +3).
-// All operand loads are issued before the first product (fully unrolled), so their latencies overlap.
-template <int W, typename FA, typename FB>
-__device__ __forceinline__ void mfma_tile(f16v &acc, FA fa, FB fb) {
-    float4 a4[W / 4], b4[W / 4];
-#pragma unroll
-    for (int j = 0; j < W / 4; ++j) {
-        a4[j] = fa(4 * j);
-        b4[j] = fb(4 * j);
-    }
-#pragma unroll
-    for (int j = 0; j < W / 4; ++j) {
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[j].x, b4[j].x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[j].y, b4[j].y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[j].z, b4[j].z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[j].w, b4[j].w, acc, 0, 0, 0);
-    }
-}
-
+using namespace ssd;
 
 // Wavefront 0 turns the chunk's Δ into the in-chunk running sum of Δ·a·log2 e (cum, inclusive) and the
 // ZOH input coefficient β; steps past L get Δ = 0 (no decay, no input).
@@ -118,8 +58,6 @@ __device__ __forceinline__ void chunk_scalars(const SsdArgs &a, int64_t bh, int6
     s_cum[i] = c;
     s_beta[i] = beta;
 }
-
-constexpr int kMS = kQ + 4;  // LDS row stride of 64-step rows (16-byte aligned rows)
 
 // Copy `rows` rows of `cols` elements (a multiple of 4) from global memory (row stride gstride, rows
 // at and past row_limit read as zeros) into LDS rows of stride lstride, as fp32, with 4-element loads
@@ -328,8 +266,6 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(SsdArgs a) {
 
 // ---- bf16 storage: the same three steps on the bf16 MFMA -------------------------------------------
 
-constexpr int kMH = kQ + 8;  // LDS row stride (bf16 elements) of 64-step rows: 144 bytes, 16-byte aligned
-
 // One 32×32 tile product over K = 2W on the bf16 MFMA, K split across the lane halves as in mfma_tile:
 // at step j the lower half supplies k = 8j .. 8j+7 and the upper half k = W + 8j .. +7, so each lane
 // reads 16 contiguous bytes of its own LDS row per step.
@@ -343,17 +279,6 @@ __device__ __forceinline__ void mfma_tile_bf16(f16v &acc, const uint16_t *arow, 
     }
 #pragma unroll
     for (int j = 0; j < W / 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8[j], b8[j], acc, 0, 0, 0);
-}
-
-// Eight fp32 values as bf16 hi = bf16(v) and lo = bf16(v − hi).
-__device__ __forceinline__ void split8(const float4 &u, const float4 &v, bf8v &hi8, bf8v &lo8) {
-    const float f[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const __bf16 hb = (__bf16)f[e];
-        hi8[e] = hb;
-        lo8[e] = (__bf16)(f[e] - (float)hb);
-    }
 }
 
 // As mfma_tile_bf16 with one operand an fp32 LDS row entering as hi + lo (two products per step);
@@ -553,6 +478,15 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel_bf16(SsdArgs a) {
 template <typename T, int N>
 hipError_t launch_n(const SsdArgs &a, hipStream_t stream) {
     const unsigned chunks = (unsigned)(a.b * a.H * a.nc);
+    if constexpr (N % 64 == 0) {
+        if (a.fused) {
+            hipError_t e = launch_state_walk(a, N, sizeof(T) == 2, stream);
+            if (e != hipSuccess) return e;
+            if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((ssd_out_kernel_bf16<N>), dim3(chunks), dim3(kThreads), 0, stream, a);
+            else hipLaunchKernelGGL((ssd_out_kernel<T, N>), dim3(chunks), dim3(kThreads), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
     if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((ssd_state_kernel_bf16<N>), dim3(chunks), dim3(kThreads), 0, stream, a);
     else hipLaunchKernelGGL((ssd_state_kernel<T, N>), dim3(chunks), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
@@ -597,6 +531,9 @@ hipError_t launch_ssd(const SsdLaunch &p, hipStream_t stream) {
     a.vec_bc = aligned(p.B) && aligned(p.C);  // N is a multiple of 32
     a.vec8 = p.bf16 && (p.L % 8) == 0 && (reinterpret_cast<uintptr_t>(p.x) & 15) == 0;
     a.decay = p.scratch + a.b * a.H * a.nc * (kP * p.N);
+    // the fused state walk runs b·H·N/64 workgroups of four wavefronts; it pays once they give every
+    // compute unit two
+    a.fused = p.N % 64 == 0 && a.b * a.H * (p.N / 64) >= 2 * (int64_t)p.cus;
     if (p.bf16) return launch_typed<uint16_t>(a, p.N, stream);
     return launch_typed<float>(a, p.N, stream);
 }

@@ -1,0 +1,201 @@
+// ssd_scan.hip — the chunk states of the scalar-decay chunked form and their pass in one kernel.
+//
+// Page "State Space Models（SSM）とMamba" §4.6 (state space duality) with the unrolled recurrence of page
+// "Mambaとは？Transformer以外の系列モデル", section Mambaの核心は入力依存のDelta、B、C: with A = a·I the
+// state leaving a chunk of Q steps is h_out = e^{a c_end} h_in + Σ_s e^{a(c_end − c_s)} β_s B_s x_sᵀ
+// (c the in-chunk running sum of Δ, β the ZOH input coefficient), a dense product per chunk.
+#include <type_traits>
+
+#include "launch.h"
+#include "ssd_common.h"
+
+namespace ssm {
+namespace ssd {
+namespace {
+
+// ---- chunk states and their pass fused: one workgroup walks the chunks of (b, h) in order ------------
+//
+// Workgroup (b, h, nb) keeps the columns n0 .. n0+63 (n0 = 64·nb) of the head's [P][N] state in its
+// MFMA accumulators (wavefront w: rows 32(w % 2) .., columns n0 + 32(w / 2) ..) and for each chunk c
+// writes them out as the state entering c, then takes h ← e^{a c_end} h + X_w Bᵀ with the chunk's
+// weighted inputs X_w[p][s] = x[p][s]·e^{a(c_end − c_s)} β_s. That replaces the chunk states' round
+// trip through HBM and the separate pass over them. It needs b·H·N/64 workgroups to fill the device, so
+// the three-kernel form serves the shapes with fewer.
+
+// Workgroup barrier ordering LDS only: global loads and stores stay in flight across it (the next
+// chunk's operands arrive while this one is multiplied, and the entering states drain meanwhile).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Four consecutive elements row[i .. i+3] in storage form (fp32: float4, bf16: the 8 bytes as uint2),
+// zeros at and past `limit`.
+template <typename T>
+__device__ __forceinline__ typename std::conditional<sizeof(T) == 2, uint2, float4>::type raw4(
+    const T *row, int64_t i, int64_t limit, bool vec) {
+    if constexpr (sizeof(T) == 4) {
+        return load4<T>(row, i, limit, vec);
+    } else {
+        if (vec && i + 4 <= limit) return *reinterpret_cast<const uint2 *>(row + i);
+        uint16_t e[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) e[k] = i + k < limit ? row[i + k] : (uint16_t)0;
+        uint2 r;
+        __builtin_memcpy(&r, e, sizeof(r));
+        return r;
+    }
+}
+__device__ __forceinline__ void raw_elems(const float4 &v, float (&o)[4]) { o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w; }
+__device__ __forceinline__ void raw_elems(const uint2 &v, float (&o)[4]) {
+    o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+}
+__device__ __forceinline__ void raw_bits(const uint2 &v, uint16_t (&o)[4]) {
+    o[0] = (uint16_t)(v.x & 0xffffu); o[1] = (uint16_t)(v.x >> 16); o[2] = (uint16_t)(v.y & 0xffffu); o[3] = (uint16_t)(v.y >> 16);
+}
+
+// As mfma_tile_split<W, true> with the fp32 operand row scaled elementwise by wrow (same k) on the way in.
+template <int W>
+__device__ __forceinline__ void mfma_tile_split_scaled(f16v &acc, const float *frow, const float *wrow,
+                                                       const uint16_t *brow) {
+#pragma unroll
+    for (int j = 0; j < W / 8; ++j) {
+        float4 u = *reinterpret_cast<const float4 *>(frow + 8 * j), v = *reinterpret_cast<const float4 *>(frow + 8 * j + 4);
+        const float4 wu = *reinterpret_cast<const float4 *>(wrow + 8 * j), wv = *reinterpret_cast<const float4 *>(wrow + 8 * j + 4);
+        u.x *= wu.x; u.y *= wu.y; u.z *= wu.z; u.w *= wu.w;
+        v.x *= wv.x; v.y *= wv.y; v.z *= wv.z; v.w *= wv.w;
+        bf8v h8, l8;
+        split8(u, v, h8, l8);
+        const bf8v o8 = *reinterpret_cast<const bf8v *>(brow + 8 * j);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h8, o8, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l8, o8, acc, 0, 0, 0);
+    }
+}
+
+template <typename T, int N>
+__global__ __launch_bounds__(kThreads) void ssd_scan_kernel(SsdArgs a) {
+    static_assert(N % 64 == 0, "64 state columns per workgroup");
+    constexpr bool BF = sizeof(T) == 2;
+    constexpr int NB = N / 64;
+    constexpr int BS = BF ? kMH : kMS;  // LDS row stride of the Bᵀ rows
+    typedef typename std::conditional<BF, uint16_t, float>::type BT;
+    typedef typename std::conditional<BF, uint2, float4>::type Raw;
+    __shared__ __align__(16) float s_w[kQ];
+    __shared__ float s_dec;
+    __shared__ __align__(16) float s_x[kP * kMS];  // x [p][s] (fp32)
+    __shared__ __align__(16) BT s_bt[64 * BS];      // Bᵀ [n − n0][s] (storage type)
+    const int64_t nb = blockIdx.x % NB, bh = blockIdx.x / NB;
+    const int64_t ib = bh / a.H, h = bh % a.H;
+    const int n0 = 64 * (int)nb;
+    const float ah = a.A[h];
+    const int l = lane(), w = wave(), hi = l / 32;
+    const int qp = w % 2, qn = w / 2;
+    const int tid = threadIdx.x;
+    // this lane's elements of the state tile: acc[r] = h[32 qp + d_row(r, l)][n0 + 32 qn + l % 32]
+    auto st_off = [&](int r) { return (int64_t)(32 * qp + d_row(r, l)) * N + n0 + 32 * qn + l % 32; };
+    f16v acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = a.h0 ? a.h0[bh * (kP * N) + st_off(r)] : 0.0f;
+
+    const T *dg = static_cast<const T *>(a.delta) + bh * a.L;
+    const T *bg = static_cast<const T *>(a.B) + ib * a.L * N + n0;
+    const T *xg = static_cast<const T *>(a.x) + ((ib * a.H + h) * kP) * a.L;
+    // the chunk's operands in registers: Δ of step l (wavefront 0), and for k < 4 four B values (step
+    // sb, columns n4 ..) and four x values (channel px, steps s4 ..), element idx = tid + 256k
+    float dtr = 0.0f;
+    Raw bq[4], xq[4];
+    auto load_chunk = [&](int64_t c) {
+        const int64_t t0 = c * kQ;
+        if (w == 0) dtr = t0 + l < a.L ? widen(dg[t0 + l]) : 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int idx = tid + k * kThreads;
+            const int r = idx / 16, q4 = (idx % 16) * 4;
+            bq[k] = raw4<T>(bg + (t0 + r) * N, q4, t0 + r < a.L ? 64 : 0, a.vec_bc);
+            xq[k] = raw4<T>(xg + r * a.L + t0, q4, a.L - t0, a.vec);
+        }
+    };
+    load_chunk(0);
+    for (int64_t c = 0; c < a.nc; ++c) {
+        if (w == 0) {
+            // in-chunk running sum of Δ·a·log2 e, the ZOH coefficient, and the weights e^{a(c_end − c_s)} β_s
+            const float u = dtr * (ah * kLog2e);
+            const float abar = exp2_fast(u);
+            const float beta = zoh_input_coef_log2(dtr, u, abar, 1.0f / ah);
+            float cu = u;
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) {
+                const float o = __shfl_up(cu, m, 64);
+                if (l >= m) cu += o;
+            }
+            const float cend = __shfl(cu, 63, 64);
+            s_w[l] = exp2_fast(cend - cu) * beta;
+            if (l == 0) s_dec = exp2_fast(cend);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int idx = tid + k * kThreads;
+            const int r = idx / 16, q4 = (idx % 16) * 4;
+            if constexpr (BF) {
+                uint16_t e[4];
+                raw_bits(bq[k], e);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s_bt[(q4 + i) * BS + r] = e[i];
+            } else {
+                float e[4];
+                raw_elems(bq[k], e);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s_bt[(q4 + i) * BS + r] = e[i];
+            }
+            float xv[4];
+            raw_elems(xq[k], xv);
+            *reinterpret_cast<float4 *>(s_x + r * kMS + q4) = make_float4(xv[0], xv[1], xv[2], xv[3]);
+        }
+        if (c + 1 < a.nc) load_chunk(c + 1);
+        lds_barrier();  // x, Bᵀ, the weights and the chunk decay
+        const float dec = s_dec;
+        float *S = a.S + (bh * a.nc + c) * (int64_t)(kP * N);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            S[st_off(r)] = acc[r];
+            acc[r] *= dec;
+        }
+        const float *xr = s_x + (32 * qp + l % 32) * kMS + 32 * hi;
+        const float *wr = s_w + 32 * hi;
+        const BT *br = s_bt + (32 * qn + l % 32) * BS + 32 * hi;
+        if constexpr (BF) {
+            mfma_tile_split_scaled<32>(acc, xr, wr, br);
+        } else {
+            mfma_tile<32>(acc,
+                          [&](int j) {
+                              const float4 xv = *reinterpret_cast<const float4 *>(xr + j);
+                              const float4 wv = *reinterpret_cast<const float4 *>(wr + j);
+                              return make_float4(xv.x * wv.x, xv.y * wv.y, xv.z * wv.z, xv.w * wv.w);
+                          },
+                          [&](int j) { return *reinterpret_cast<const float4 *>(br + j); });
+        }
+        lds_barrier();  // the next chunk's staging overwrites the LDS operands
+    }
+    if (a.hT) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a.hT[bh * (kP * N) + st_off(r)] = acc[r];
+    }
+}
+
+template <typename T, int N>
+hipError_t launch_walk(const SsdArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((ssd_scan_kernel<T, N>), dim3((unsigned)(a.b * a.H * (N / 64))), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_state_walk(const SsdArgs &a, int64_t N, bool bf16, hipStream_t stream) {
+    if (N == 64) return bf16 ? launch_walk<uint16_t, 64>(a, stream) : launch_walk<float, 64>(a, stream);
+    if (N == 128) return bf16 ? launch_walk<uint16_t, 128>(a, stream) : launch_walk<float, 128>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ssd
+}  // namespace ssm

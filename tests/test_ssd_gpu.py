@@ -120,6 +120,28 @@ def test_ssd_matches_recurrent_scan_kernel():
     _close(from_torch(h1), from_torch(h2), 2 * TAU["f32"], "SSD vs recurrent kernel state")
 
 
+# Shapes with b·H·N/64 >= 512 workgroups take the fused state walk (ssd_scan_kernel) on a 256-CU device;
+# the ones above take the three-kernel form. Ragged last chunks, initial states, both storage types.
+FUSED = [
+    # b, H, L, N, dtype, initial state
+    (8, 64, 130, 64, "f32", True),
+    (4, 128, 200, 128, "bf16", True),
+    (8, 64, 64, 64, "bf16", False),
+    (4, 64, 333, 128, "f32", False),
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=lambda c: f"b{c[0]}_H{c[1]}_L{c[2]}_N{c[3]}_{c[4]}_h0{int(c[5])}")
+def test_ssd_fused_state_walk(case):
+    b, H, L, N, dt, h0_on = case
+    inp = I.random_ssd(b, H, L, N, dtype=dt, seed=L + 7 * N, a_zero_heads=(3,))
+    h0 = (np.random.default_rng(L + 1).standard_normal((b, H * P, N)) * 0.5).astype(np.float32) if h0_on else None
+    rng = np.random.default_rng(L)
+    rows = [(0, 0), (b - 1, H * P - 1), (0, 3 * P + 5)] + \
+           [(int(rng.integers(b)), int(rng.integers(H * P))) for _ in range(60)]
+    run_case(inp, h0, rows=rows, what=f"fused b{b} H{H} L{L} N{N} {dt}")
+
+
 @pytest.mark.parametrize("shape", [(4, 24, 2048, 64, "f32"), (8, 64, 4096, 128, "bf16")],
                          ids=["b4_H24_L2048_N64_f32", "b8_H64_L4096_N128_bf16"])
 def test_ssd_full_size_sampled(shape):
