@@ -30,6 +30,25 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront: DPP row shifts within each row of 16 lanes
+// (lanes shifted in from outside the row add 0), then each row adds the totals of the rows before it,
+// read with readlane.
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+    auto shr = [](float x, auto k) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + decltype(k)::value, 0xf, 0xf, false));
+    };
+    v += shr(v, std::integral_constant<int, 1>{});
+    v += shr(v, std::integral_constant<int, 2>{});
+    v += shr(v, std::integral_constant<int, 4>{});
+    v += shr(v, std::integral_constant<int, 8>{});
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 15));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 47));
+    const int row = (threadIdx.x & 63) >> 4;
+    const float before = row == 0 ? 0.0f : row == 1 ? r0 : row == 2 ? r0 + r1 : (r0 + r1) + r2;
+    return v + before;
+}
+
 // Four consecutive elements row[i .. i+3] in storage form (fp32: float4, bf16: the 8 bytes as uint2),
 // zeros at and past `limit`.
 template <typename T>
@@ -81,8 +100,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(SsdArgs a) {
     constexpr int BS = BF ? kMH : kMS;  // LDS row stride of the Bᵀ rows
     typedef typename std::conditional<BF, uint16_t, float>::type BT;
     typedef typename std::conditional<BF, uint2, float4>::type Raw;
-    __shared__ __align__(16) float s_w[kQ];
-    __shared__ float s_dec;
+    __shared__ __align__(16) float s_w[4 * kQ];     // each wavefront's copy of the chunk weights
     __shared__ __align__(16) float s_x[kP * kMS];  // x [p][s] (fp32)
     __shared__ __align__(16) BT s_bt[64 * BS];      // Bᵀ [n − n0][s] (storage type)
     const int64_t nb = blockIdx.x % NB, bh = blockIdx.x / NB;
@@ -101,42 +119,42 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(SsdArgs a) {
     const T *dg = static_cast<const T *>(a.delta) + bh * a.L;
     const T *bg = static_cast<const T *>(a.B) + ib * a.L * N + n0;
     const T *xg = static_cast<const T *>(a.x) + ((ib * a.H + h) * kP) * a.L;
-    // the chunk's operands in registers: Δ of step l (wavefront 0), and for k < 4 four B values (step
-    // sb, columns n4 ..) and four x values (channel px, steps s4 ..), element idx = tid + 256k
+    // the chunk's operands in registers: Δ of step l (every wavefront), and for k < 4 four B values
+    // (step br_, columns bq_ ..: 4 lanes per step, so that the transposed LDS stores below spread over
+    // the banks) and four x values (channel xr_, steps xq_ ..: 16 lanes per channel row)
+    auto br_ = [&](int) { return 16 * w + l / 4; };
+    auto bq_ = [&](int k) { return 16 * k + 4 * (l % 4); };
+    auto xr_ = [&](int k) { return (tid + k * kThreads) / 16; };
+    auto xq_ = [&](int k) { return ((tid + k * kThreads) % 16) * 4; };
     float dtr = 0.0f;
     Raw bq[4], xq[4];
     auto load_chunk = [&](int64_t c) {
         const int64_t t0 = c * kQ;
-        if (w == 0) dtr = t0 + l < a.L ? widen(dg[t0 + l]) : 0.0f;
+        dtr = t0 + l < a.L ? widen(dg[t0 + l]) : 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int idx = tid + k * kThreads;
-            const int r = idx / 16, q4 = (idx % 16) * 4;
-            bq[k] = raw4<T>(bg + (t0 + r) * N, q4, t0 + r < a.L ? 64 : 0, a.vec_bc);
-            xq[k] = raw4<T>(xg + r * a.L + t0, q4, a.L - t0, a.vec);
+            const int r = br_(k);
+            bq[k] = raw4<T>(bg + (t0 + r) * N, bq_(k), t0 + r < a.L ? 64 : 0, a.vec_bc);
+            xq[k] = raw4<T>(xg + xr_(k) * a.L + t0, xq_(k), a.L - t0, a.vec);
         }
     };
     load_chunk(0);
     for (int64_t c = 0; c < a.nc; ++c) {
-        if (w == 0) {
-            // in-chunk running sum of Δ·a·log2 e, the ZOH coefficient, and the weights e^{a(c_end − c_s)} β_s
+        // every wavefront: the in-chunk running sum of Δ·a·log2 e, the ZOH coefficient, the weights
+        // e^{a(c_end − c_s)} β_s (into its own LDS copy) and the chunk decay e^{a c_end}
+        float dec;
+        {
             const float u = dtr * (ah * kLog2e);
             const float abar = exp2_fast(u);
             const float beta = zoh_input_coef_log2(dtr, u, abar, 1.0f / ah);
-            float cu = u;
-#pragma unroll
-            for (int m = 1; m < 64; m <<= 1) {
-                const float o = __shfl_up(cu, m, 64);
-                if (l >= m) cu += o;
-            }
-            const float cend = __shfl(cu, 63, 64);
-            s_w[l] = exp2_fast(cend - cu) * beta;
-            if (l == 0) s_dec = exp2_fast(cend);
+            const float cu = wave_prefix_sum(u);
+            const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cu), 63));
+            s_w[kQ * w + l] = exp2_fast(cend - cu) * beta;
+            dec = exp2_fast(cend);
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int idx = tid + k * kThreads;
-            const int r = idx / 16, q4 = (idx % 16) * 4;
+            const int r = br_(k), q4 = bq_(k);
             if constexpr (BF) {
                 uint16_t e[4];
                 raw_bits(bq[k], e);
@@ -150,11 +168,10 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(SsdArgs a) {
             }
             float xv[4];
             raw_elems(xq[k], xv);
-            *reinterpret_cast<float4 *>(s_x + r * kMS + q4) = make_float4(xv[0], xv[1], xv[2], xv[3]);
+            *reinterpret_cast<float4 *>(s_x + xr_(k) * kMS + xq_(k)) = make_float4(xv[0], xv[1], xv[2], xv[3]);
         }
         if (c + 1 < a.nc) load_chunk(c + 1);
-        lds_barrier();  // x, Bᵀ, the weights and the chunk decay
-        const float dec = s_dec;
+        lds_barrier();  // x and Bᵀ
         float *S = a.S + (bh * a.nc + c) * (int64_t)(kP * N);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -162,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(SsdArgs a) {
             acc[r] *= dec;
         }
         const float *xr = s_x + (32 * qp + l % 32) * kMS + 32 * hi;
-        const float *wr = s_w + 32 * hi;
+        const float *wr = s_w + kQ * w + 32 * hi;
         const BT *br = s_bt + (32 * qn + l % 32) * BS + 32 * hi;
         if constexpr (BF) {
             mfma_tile_split_scaled<32>(acc, xr, wr, br);
