@@ -266,41 +266,6 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(SsdArgs a) {
 
 // ---- bf16 storage: the same three steps on the bf16 MFMA -------------------------------------------
 
-// One 32×32 tile product over K = 2W on the bf16 MFMA, K split across the lane halves as in mfma_tile:
-// at step j the lower half supplies k = 8j .. 8j+7 and the upper half k = W + 8j .. +7, so each lane
-// reads 16 contiguous bytes of its own LDS row per step.
-template <int W>
-__device__ __forceinline__ void mfma_tile_bf16(f16v &acc, const uint16_t *arow, const uint16_t *brow) {
-    bf8v a8[W / 8], b8[W / 8];
-#pragma unroll
-    for (int j = 0; j < W / 8; ++j) {
-        a8[j] = *reinterpret_cast<const bf8v *>(arow + 8 * j);
-        b8[j] = *reinterpret_cast<const bf8v *>(brow + 8 * j);
-    }
-#pragma unroll
-    for (int j = 0; j < W / 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8[j], b8[j], acc, 0, 0, 0);
-}
-
-// As mfma_tile_bf16 with one operand an fp32 LDS row entering as hi + lo (two products per step);
-// SPLIT_A says which operand is the fp32 one.
-template <int W, bool SPLIT_A>
-__device__ __forceinline__ void mfma_tile_split(f16v &acc, const float *frow, const uint16_t *brow) {
-#pragma unroll
-    for (int j = 0; j < W / 8; ++j) {
-        bf8v h8, l8;
-        split8(*reinterpret_cast<const float4 *>(frow + 8 * j), *reinterpret_cast<const float4 *>(frow + 8 * j + 4),
-               h8, l8);
-        const bf8v o8 = *reinterpret_cast<const bf8v *>(brow + 8 * j);
-        if (SPLIT_A) {
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h8, o8, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l8, o8, acc, 0, 0, 0);
-        } else {
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o8, h8, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o8, l8, acc, 0, 0, 0);
-        }
-    }
-}
-
 // Copy rows of `cols` bf16 elements (a multiple of 8) into LDS rows of stride lstride, 16 bytes at a time;
 // rows at and past row_limit and columns at and past col_limit read as zeros.
 __device__ __forceinline__ void stage_rows_bf16(const uint16_t *g, int64_t gstride, int rows, int cols,
@@ -478,6 +443,9 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel_bf16(SsdArgs a) {
 template <typename T, int N>
 hipError_t launch_n(const SsdArgs &a, hipStream_t stream) {
     const unsigned chunks = (unsigned)(a.b * a.H * a.nc);
+    if constexpr (sizeof(T) == 2 && N % 64 == 0) {
+        if (a.fused_all) return launch_fused(a, N, stream);
+    }
     if constexpr (N % 64 == 0) {
         if (a.fused) {
             hipError_t e = launch_state_walk(a, N, sizeof(T) == 2, stream);
@@ -534,6 +502,9 @@ hipError_t launch_ssd(const SsdLaunch &p, hipStream_t stream) {
     // the fused state walk runs b·H·N/64 workgroups of four wavefronts; it pays once they give every
     // compute unit two
     a.fused = p.N % 64 == 0 && a.b * a.H * (p.N / 64) >= 2 * (int64_t)p.cus;
+    a.vec_bc16 = ((reinterpret_cast<uintptr_t>(p.B) | reinterpret_cast<uintptr_t>(p.C)) & 15) == 0;
+    // bf16 storage with b·H >= 2 workgroups per CU: the whole form in one walk per (b, head)
+    a.fused_all = p.bf16 && (p.N == 64 || p.N == 128) && a.b * a.H >= 2 * (int64_t)p.cus;
     if (p.bf16) return launch_typed<uint16_t>(a, p.N, stream);
     return launch_typed<float>(a, p.N, stream);
 }

@@ -30,6 +30,8 @@ struct SsdArgs {
     bool vec_bc;   // so do the rows of B and C
     bool vec8;     // x rows allow 16-byte loads at 8-element steps (bf16)
     bool fused;    // chunk states and their pass in one kernel (ssd_scan_kernel)
+    bool vec_bc16; // B and C allow 16-byte loads (bf16 rows of N >= 64)
+    bool fused_all;// the whole chunked form in one ordered walk per (b, head) (ssd_fused_kernel)
 };
 
 __device__ __forceinline__ int lane() { return threadIdx.x & 63; }
@@ -87,6 +89,44 @@ __device__ __forceinline__ void split8(const float4 &u, const float4 &v, bf8v &h
         lo8[e] = (__bf16)(f[e] - (float)hb);
     }
 }
+
+// One 32×32 tile product over K = 2W on the bf16 MFMA, K split across the lane halves as in mfma_tile:
+// at step j the lower half supplies k = 8j .. 8j+7 and the upper half k = W + 8j .. +7, so each lane
+// reads 16 contiguous bytes of its own LDS row per step.
+template <int W>
+__device__ __forceinline__ void mfma_tile_bf16(f16v &acc, const uint16_t *arow, const uint16_t *brow) {
+    bf8v a8[W / 8], b8[W / 8];
+#pragma unroll
+    for (int j = 0; j < W / 8; ++j) {
+        a8[j] = *reinterpret_cast<const bf8v *>(arow + 8 * j);
+        b8[j] = *reinterpret_cast<const bf8v *>(brow + 8 * j);
+    }
+#pragma unroll
+    for (int j = 0; j < W / 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8[j], b8[j], acc, 0, 0, 0);
+}
+
+// As mfma_tile_bf16 with one operand an fp32 LDS row entering as hi + lo (two products per step);
+// SPLIT_A says which operand is the fp32 one.
+template <int W, bool SPLIT_A>
+__device__ __forceinline__ void mfma_tile_split(f16v &acc, const float *frow, const uint16_t *brow) {
+#pragma unroll
+    for (int j = 0; j < W / 8; ++j) {
+        bf8v h8, l8;
+        split8(*reinterpret_cast<const float4 *>(frow + 8 * j), *reinterpret_cast<const float4 *>(frow + 8 * j + 4),
+               h8, l8);
+        const bf8v o8 = *reinterpret_cast<const bf8v *>(brow + 8 * j);
+        if (SPLIT_A) {
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h8, o8, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l8, o8, acc, 0, 0, 0);
+        } else {
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o8, h8, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o8, l8, acc, 0, 0, 0);
+        }
+    }
+}
+
+// The whole chunked form for bf16 storage in one ordered walk per (b, head) (ssd_scan.hip); N is 64 or 128.
+hipError_t launch_fused(const SsdArgs &a, int64_t N, hipStream_t stream);
 
 // The chunk states' walk of ssd_scan.hip (one launch): the state entering every chunk into a.S and the
 // final state into a.hT. N is 64 or 128.

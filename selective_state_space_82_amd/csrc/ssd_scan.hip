@@ -200,6 +200,244 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(SsdArgs a) {
     }
 }
 
+// ---- the whole chunked form in one ordered walk (bf16 storage) ---------------------------------------
+//
+// Workgroup (b, h) keeps the head's whole [P][N] state in MFMA accumulators (tile τ = w + 4j of the
+// 2·N/32 tiles of 32×32: rows 32(τ % 2) .., columns 32(τ / 2) ..) and, chunk by chunk in order, computes
+// the outputs from the entering state and then advances the state, so neither chunk states nor entering
+// states touch HBM: it reads x, z, Δ, B, C once and writes y once. Per chunk (Q = 64 steps):
+//   G = C Bᵀ on the three 32×32 tiles at or below the diagonal (bf16 products, exact inputs), then
+//     M[t][s] = G e^{a(c_t − c_s)} β_s for s <= t;
+//   Y = M Xᵀ + diag(e^{a c_t}) C H_inᵀ (M and H_in enter the bf16 products as hi + lo);
+//   y = Y + D x, times silu(z);  H ← e^{a c_end} H + X_w Bᵀ with X_w = x e^{a(c_end − c_s)} β_s.
+// The next chunk's Δ, B, C, x and this chunk's z arrive in registers while the current chunk is
+// multiplied. It needs about 2 workgroups per CU (b·H of them, 114 KB of LDS each, one per CU at a time).
+template <int N>
+__global__ __launch_bounds__(kThreads, 1) void ssd_fused_kernel(SsdArgs a) {
+    static_assert(N == 64 || N == 128, "state widths");
+    constexpr int NH = N + 8;       // bf16 row stride of N-wide LDS rows
+    constexpr int NF = N + 4;       // fp32 row stride of N-wide LDS rows
+    constexpr int HN = N / 2;
+    constexpr int TPW = N / 64;     // state tiles per wavefront
+    constexpr int CK = N / 32;      // 16-byte pieces of C (and of B) per thread per chunk
+    __shared__ __align__(16) float s_cum[kQ], s_beta[kQ], s_w[kQ];
+    __shared__ __align__(16) uint16_t s_c[kQ * NH];    // C [t][n]
+    __shared__ __align__(16) uint16_t s_b[kQ * NH];    // B [s][n]
+    __shared__ __align__(16) uint16_t s_bt[N * kMH];   // Bᵀ [n][s]
+    __shared__ __align__(16) uint16_t s_x[kP * kMH];   // x [p][s]
+    __shared__ __align__(16) float s_h[kP * NF];       // entering state [p][n]
+    __shared__ __align__(16) float s_m[kQ * kMS];      // M [t][s], then the outputs [p][t]
+    const int64_t bh = blockIdx.x, ib = bh / a.H, h = bh % a.H;
+    const float ah = a.A[h];
+    const int l = lane(), w = wave(), hi = l / 32, tid = threadIdx.x;
+
+    // the state tiles of this wavefront
+    auto tq_p = [&](int j) { return (w + 4 * j) % 2; };
+    auto tq_n = [&](int j) { return (w + 4 * j) / 2; };
+    auto st_off = [&](int j, int r) {
+        return (int64_t)(32 * tq_p(j) + d_row(r, l)) * N + 32 * tq_n(j) + l % 32;
+    };
+    f16v acc[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] = a.h0 ? a.h0[bh * (kP * N) + st_off(j, r)] : 0.0f;
+
+    const uint16_t *dg = static_cast<const uint16_t *>(a.delta) + bh * a.L;
+    const uint16_t *cg = static_cast<const uint16_t *>(a.C) + ib * a.L * N;
+    const uint16_t *bg = static_cast<const uint16_t *>(a.B) + ib * a.L * N;
+    const uint16_t *xg = static_cast<const uint16_t *>(a.x) + ((ib * a.H + h) * kP) * a.L;
+    const uint16_t *zg = static_cast<const uint16_t *>(a.z);
+    uint16_t *yg = static_cast<uint16_t *>(a.y);
+    // per-thread pieces: C row c_r(k) columns c_c(k) .. +7 (16 lanes per row); B row l, columns
+    // 8(w + 4k) .. +7 (one row per lane, so that the transposed stores spread over the banks); x row
+    // x_r(k), steps x_c(k) .. +7; the epilogue's 4-step groups e_p(k), e_t(k) .. +3
+    auto c_r = [&](int k) { return (tid + k * kThreads) / (N / 8); };
+    auto c_c = [&](int k) { return ((tid + k * kThreads) % (N / 8)) * 8; };
+    auto b_c = [&](int k) { return 8 * (w + 4 * k); };
+    auto x_r = [&](int k) { return (tid + k * kThreads) / 8; };
+    auto x_c = [&](int k) { return ((tid + k * kThreads) % 8) * 8; };
+    auto e_p = [&](int k) { return (tid + k * kThreads) / 16; };
+    auto e_t = [&](int k) { return ((tid + k * kThreads) % 16) * 4; };
+    // 8 consecutive bf16 of a row as raw bits, zeros at and past `limit` (16-byte load when allowed)
+    auto raw8 = [](const uint16_t *row, int64_t i, int64_t limit, bool vec) {
+        if (vec && i + 8 <= limit) return *reinterpret_cast<const uint4 *>(row + i);
+        uint16_t e[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) e[k] = i + k < limit ? row[i + k] : (uint16_t)0;
+        uint4 r;
+        __builtin_memcpy(&r, e, sizeof(r));
+        return r;
+    };
+    float dsk[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dsk[k] = a.D ? a.D[h * kP + e_p(k)] : 0.0f;
+
+    float dtr = 0.0f;
+    uint4 cq[CK], bq[CK], xq[2];
+    uint2 zq[4];
+    auto load_chunk = [&](int64_t c) {
+        const int64_t t0 = c * kQ;
+        dtr = t0 + l < a.L ? widen(dg[t0 + l]) : 0.0f;
+#pragma unroll
+        for (int k = 0; k < CK; ++k) {
+            const int cr = c_r(k);
+            cq[k] = raw8(cg + (t0 + cr) * N, c_c(k), t0 + cr < a.L ? N : 0, a.vec_bc16);
+            bq[k] = raw8(bg + (t0 + l) * N, b_c(k), t0 + l < a.L ? N : 0, a.vec_bc16);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) xq[k] = raw8(xg + x_r(k) * a.L + t0, x_c(k), a.L - t0, a.vec8);
+    };
+    auto load_z = [&](int64_t c) {
+        const int64_t t0 = c * kQ;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            zq[k] = zg ? raw4<uint16_t>(zg + ((ib * a.H + h) * kP + e_p(k)) * a.L + t0, e_t(k), a.L - t0, a.vec)
+                       : make_uint2(0u, 0u);
+    };
+    load_chunk(0);
+    load_z(0);
+    for (int64_t c = 0; c < a.nc; ++c) {
+        const int64_t t0 = c * kQ;
+        const int64_t lim = a.L - t0;
+        // running sums of Δ·a·log2 e, β, the state-update weights and the chunk decay (every wavefront
+        // computes them; wavefront 0 publishes them)
+        float dec;
+        {
+            const float u = dtr * (ah * kLog2e);
+            const float abar = exp2_fast(u);
+            const float beta = zoh_input_coef_log2(dtr, u, abar, 1.0f / ah);
+            const float cu = wave_prefix_sum(u);
+            const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cu), 63));
+            dec = exp2_fast(cend);
+            if (w == 0) {
+                s_cum[l] = cu;
+                s_beta[l] = beta;
+                s_w[l] = exp2_fast(cend - cu) * beta;
+            }
+        }
+        // stage C, B, Bᵀ and x; write out the entering state
+#pragma unroll
+        for (int k = 0; k < CK; ++k) {
+            *reinterpret_cast<uint4 *>(s_c + c_r(k) * NH + c_c(k)) = cq[k];
+            *reinterpret_cast<uint4 *>(s_b + l * NH + b_c(k)) = bq[k];
+            const uint32_t wv[4] = {bq[k].x, bq[k].y, bq[k].z, bq[k].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                s_bt[(b_c(k) + e) * kMH + l] = (uint16_t)((e & 1) ? (wv[e / 2] >> 16) : (wv[e / 2] & 0xffffu));
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) *reinterpret_cast<uint4 *>(s_x + x_r(k) * kMH + x_c(k)) = xq[k];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                s_h[(32 * tq_p(j) + d_row(r, l)) * NF + 32 * tq_n(j) + l % 32] = acc[j][r];
+        if (c + 1 < a.nc) load_chunk(c + 1);
+        lds_barrier();
+
+        // G = C Bᵀ (wavefronts 0..2) and the state update (all)
+        f16v g = {};
+        const int qt = w == 0 ? 0 : 1, qs = w == 2 ? 1 : 0;
+        if (w < 3) mfma_tile_bf16<HN>(g, s_c + (32 * qt + l % 32) * NH + hi * HN, s_b + (32 * qs + l % 32) * NH + hi * HN);
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[j][r] *= dec;
+            const uint16_t *xr = s_x + (32 * tq_p(j) + l % 32) * kMH + 32 * hi;
+            const float *wr = s_w + 32 * hi;
+            const uint16_t *br = s_bt + (32 * tq_n(j) + l % 32) * kMH + 32 * hi;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const uint4 xv = *reinterpret_cast<const uint4 *>(xr + 8 * jj);
+                const float4 w0 = *reinterpret_cast<const float4 *>(wr + 8 * jj), w1 = *reinterpret_cast<const float4 *>(wr + 8 * jj + 4);
+                const float4 u0 = make_float4(bf16_lo(xv.x) * w0.x, bf16_hi(xv.x) * w0.y, bf16_lo(xv.y) * w0.z, bf16_hi(xv.y) * w0.w);
+                const float4 u1 = make_float4(bf16_lo(xv.z) * w1.x, bf16_hi(xv.z) * w1.y, bf16_lo(xv.w) * w1.z, bf16_hi(xv.w) * w1.w);
+                bf8v h8, l8;
+                split8(u0, u1, h8, l8);
+                const bf8v b8 = *reinterpret_cast<const bf8v *>(br + 8 * jj);
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h8, b8, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l8, b8, acc[j], 0, 0, 0);
+            }
+        }
+        if (w < 3) {
+            const int s = 32 * qs + l % 32;
+            const float cs = s_cum[s], bs = s_beta[s];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int t = 32 * qt + d_row(r, l);
+                s_m[t * kMS + s] = s <= t ? g[r] * exp2_fast(s_cum[t] - cs) * bs : 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s_m[d_row(r, l) * kMS + 32 + l % 32] = 0.0f;
+        }
+        lds_barrier();
+
+        // this wavefront's output tile: steps 32·ot .., channels 32·op ..
+        const int ot = w / 2, op = w % 2;
+        f16v yv = {}, inter = {};
+        mfma_tile_split<32, true>(yv, s_m + (32 * ot + l % 32) * kMS + 32 * hi, s_x + (32 * op + l % 32) * kMH + 32 * hi);
+        {
+            const uint16_t *cr = s_c + (32 * ot + l % 32) * NH + hi * HN;
+            const float *hr = s_h + (32 * op + l % 32) * NF + hi * HN;
+#pragma unroll
+            for (int j = 0; j < HN / 8; ++j) {
+                bf8v h8, l8;
+                split8(*reinterpret_cast<const float4 *>(hr + 8 * j), *reinterpret_cast<const float4 *>(hr + 8 * j + 4), h8, l8);
+                const bf8v c8 = *reinterpret_cast<const bf8v *>(cr + 8 * j);
+                inter = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c8, h8, inter, 0, 0, 0);
+                inter = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c8, l8, inter, 0, 0, 0);
+            }
+        }
+        lds_barrier();  // M is no longer read: its space takes the outputs [p][t]
+        {
+            const int p = 32 * op + l % 32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int t = 32 * ot + d_row(r, l);
+                s_m[p * kMS + t] = yv[r] + exp2_fast(s_cum[t]) * inter[r];
+            }
+        }
+        lds_barrier();
+        // y = outputs + D x, times silu(z), in 4-step pieces
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int p = e_p(k), t4 = e_t(k);
+            if (t4 >= lim) continue;
+            const int64_t off = ((ib * a.H + h) * kP + p) * a.L + t0 + t4;
+            const float4 o = *reinterpret_cast<const float4 *>(s_m + p * kMS + t4);
+            const uint16_t *xs = s_x + p * kMH + t4;
+            float v[4] = {o.x + dsk[k] * widen(xs[0]), o.y + dsk[k] * widen(xs[1]), o.z + dsk[k] * widen(xs[2]),
+                          o.w + dsk[k] * widen(xs[3])};
+            if (zg) {
+                float zv[4];
+                raw_elems(zq[k], zv);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] *= silu(zv[e]);
+            }
+            if (a.vec && t4 + 4 <= lim) {
+                uint2 pk;
+                pk.x = (uint32_t)narrow<uint16_t>(v[0]) | ((uint32_t)narrow<uint16_t>(v[1]) << 16);
+                pk.y = (uint32_t)narrow<uint16_t>(v[2]) | ((uint32_t)narrow<uint16_t>(v[3]) << 16);
+                *reinterpret_cast<uint2 *>(yg + off) = pk;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (t4 + e < lim) yg[off + e] = narrow<uint16_t>(v[e]);
+            }
+        }
+        if (c + 1 < a.nc) load_z(c + 1);
+        lds_barrier();  // the next chunk's staging overwrites every LDS operand
+    }
+    if (a.hT) {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) a.hT[bh * (kP * N) + st_off(j, r)] = acc[j][r];
+    }
+}
+
 template <typename T, int N>
 hipError_t launch_walk(const SsdArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((ssd_scan_kernel<T, N>), dim3((unsigned)(a.b * a.H * (N / 64))), dim3(kThreads), 0, stream, a);
@@ -207,6 +445,13 @@ hipError_t launch_walk(const SsdArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_fused(const SsdArgs &a, int64_t N, hipStream_t stream) {
+    if (N == 64) hipLaunchKernelGGL((ssd_fused_kernel<64>), dim3((unsigned)(a.b * a.H)), dim3(kThreads), 0, stream, a);
+    else if (N == 128) hipLaunchKernelGGL((ssd_fused_kernel<128>), dim3((unsigned)(a.b * a.H)), dim3(kThreads), 0, stream, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t launch_state_walk(const SsdArgs &a, int64_t N, bool bf16, hipStream_t stream) {
     if (N == 64) return bf16 ? launch_walk<uint16_t, 64>(a, stream) : launch_walk<float, 64>(a, stream);

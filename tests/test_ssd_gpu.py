@@ -120,14 +120,17 @@ def test_ssd_matches_recurrent_scan_kernel():
     _close(from_torch(h1), from_torch(h2), 2 * TAU["f32"], "SSD vs recurrent kernel state")
 
 
-# Shapes with b·H·N/64 >= 512 workgroups take the fused state walk (ssd_scan_kernel) on a 256-CU device;
-# the ones above take the three-kernel form. Ragged last chunks, initial states, both storage types.
+# On a 256-CU device: bf16 shapes with b·H >= 512 take the single-walk form (ssd_fused_kernel); other
+# shapes with b·H·N/64 >= 512 take the fused state walk (ssd_scan_kernel) with the output kernel; the
+# cases above take the three-kernel form. Ragged last chunks, initial states, both storage types.
 FUSED = [
     # b, H, L, N, dtype, initial state
-    (8, 64, 130, 64, "f32", True),
-    (4, 128, 200, 128, "bf16", True),
-    (8, 64, 64, 64, "bf16", False),
-    (4, 64, 333, 128, "f32", False),
+    (8, 64, 130, 64, "f32", True),      # state walk
+    (4, 128, 200, 128, "bf16", True),   # single walk
+    (8, 64, 64, 64, "bf16", False),     # single walk, one whole chunk
+    (4, 64, 333, 128, "f32", False),    # state walk
+    (4, 64, 150, 128, "bf16", True),    # state walk (b·H = 256)
+    (2, 256, 97, 64, "bf16", False),    # single walk, N = 64
 ]
 
 
