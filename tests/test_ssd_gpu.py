@@ -130,7 +130,8 @@ FUSED = [
     (8, 64, 64, 64, "bf16", False),     # single walk, one whole chunk
     (4, 64, 333, 128, "f32", False),    # state walk
     (4, 64, 150, 128, "bf16", True),    # state walk (b·H = 256)
-    (2, 256, 97, 64, "bf16", False),    # single walk, N = 64
+    (2, 256, 104, 64, "bf16", False),   # single walk, N = 64, ragged last chunk
+    (4, 128, 99, 64, "bf16", True),     # single walk, L not a multiple of 8 (element-wise edges)
 ]
 
 
