@@ -132,6 +132,8 @@ FUSED = [
     (4, 64, 150, 128, "bf16", True),    # state walk (b·H = 256)
     (2, 256, 104, 64, "bf16", False),   # single walk, N = 64, ragged last chunk
     (4, 128, 99, 64, "bf16", True),     # single walk, L not a multiple of 8 (element-wise edges)
+    (4, 128, 1, 64, "bf16", True),      # single walk, one step
+    (8, 64, 1, 64, "f32", True),        # state walk, one step
 ]
 
 
