@@ -511,7 +511,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the scan shards by batch row or "
+        print("bench.py measures one GPU: this library has no multi-GPU path (the scan shards by batch row or "
               "channel with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
