@@ -116,3 +116,30 @@ def test_bwd_mamba130m_workload():
     """The 130M-like fp32 workload at full size, in the plan the library picks for it."""
     inp = I.prefill_inputs(I.WORKLOADS["mamba130m_f32_b4_d1536_L2048_N16"])
     run_case(inp, dy_seed=11, what="mamba130m")
+
+
+def test_bwd_mamba1p4b_sampled_rows():
+    """The 1.4B-like bf16 workload (b 8, d 4096, L 4096, N 16) at full size, in the plan the library picks for
+    it: the per-row gradients (dx, dΔ, dz and the initial-state gradient) of sampled rows against the oracle
+    run on each row alone. The sums over rows (dA, dB, dC, dD) are checked at full size on the 130M-like
+    workload above."""
+    dt = "bf16"
+    inp = I.prefill_inputs(I.WORKLOADS["mamba1p4b_bf16_b8_d4096_L4096_N16"])
+    b, d, L = inp["x"].shape
+    rng = np.random.default_rng(17)
+    dy = I.store(rng.standard_normal((b, d, L)), dt)
+    t = upload(inp)
+    g = api.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], dy=_to_dev(dy, dt))
+    torch.cuda.synchronize()
+    rows = [(0, 0), (b - 1, d - 1)] + [(int(rng.integers(b)), int(rng.integers(d))) for _ in range(14)]
+    tau = TAU[dt]
+    worst = {}
+    for ib, ch in rows:
+        row = lambda arr: I.widen(arr[ib:ib + 1, ch:ch + 1], dt)
+        ref = oracle.scan_bwd(row(inp["x"]), row(inp["delta"]), inp["A"][ch:ch + 1], I.widen(inp["B"][ib:ib + 1], dt),
+                              I.widen(inp["C"][ib:ib + 1], dt), inp["D"][ch:ch + 1], row(inp["z"]), h0=None,
+                              dy=row(dy), dh_final=None)
+        for k, rk in (("dx", "dx"), ("ddelta", "ddelta"), ("dz", "dz"), ("d_initial_state", "dh0")):
+            got = from_torch(g[k][ib, ch])
+            worst[k] = max(worst.get(k, 0.0), _check_elementwise(got, ref[rk][0, 0], tau, f"1.4B-like row ({ib}, {ch}) {k}"))
+    print("[bwd mamba1p4b sampled] " + " ".join(f"{k}={v:.1e}" for k, v in worst.items()), flush=True)
