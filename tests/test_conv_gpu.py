@@ -85,6 +85,22 @@ def test_conv_step_equals_prefill(dt):
     assert torch.equal(state, s_pf), "decode state vs prefill state"
 
 
+def test_conv1d_full_size_sampled():
+    """The 1.4B-like layer (b 8, d 4096, L 4096, W 4, bf16, bias and state in) at full size, in the launch the
+    benchmark times: sampled rows against the oracle run on each row alone, their states bit for bit."""
+    b, d, L, W, dt = 8, 4096, 4096, 4, "bf16"
+    xin, w, bias, st = _case(b, d, L, W, dt, True, True, True, seed=44)
+    x, so = api.ssm_conv1d_fwd(_dev(xin, dt), _dev(w, "f32"), _dev(bias, "f32"), state_in=_dev(st, "f32"))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(45)
+    rows = [(0, 0), (b - 1, d - 1)] + [(int(rng.integers(b)), int(rng.integers(d))) for _ in range(30)]
+    for ib, ch in rows:
+        xr, sr = oracle.conv1d(I.widen(xin[ib:ib + 1, ch:ch + 1], dt), w[ch:ch + 1], bias[ch:ch + 1],
+                               st[ib:ib + 1, ch:ch + 1])
+        assert_close(from_torch(x[ib, ch]), xr[0, 0], TAU[dt], f"conv1d row ({ib}, {ch})")
+        assert np.array_equal(from_torch(so[ib, ch]), sr[0, 0]), f"state of row ({ib}, {ch})"
+
+
 def test_conv_state_in_place():
     b, d, L, W = 2, 20, 3, 6  # L < W - 1, so the new state mixes old state and new inputs
     xin, w, bias, st = _case(b, d, L, W, "f32", True, True, True, seed=9)
