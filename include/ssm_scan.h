@@ -34,7 +34,8 @@
  *     synchronisation of that stream.
  *   - Calls are reentrant: the library keeps no per-call global state. Calls on different streams
  *     may run concurrently. Calls that need scratch (a prefill split into time segments, the
- *     gradient pass, ssm_lti_fwd, ssm_ssd_fwd) take it from the current device's default
+ *     gradient pass, ssm_lti_fwd, ssm_ssd_fwd except bf16 with N of 64 or 128 and b·H at least
+ *     twice the device's compute units) take it from the current device's default
  *     stream-ordered pool (hipMallocAsync / hipFreeAsync on `stream`). The first such call on a
  *     device sets that pool's release threshold to its maximum, so freed scratch stays pooled
  *     instead of being returned at every synchronisation; other users of the device's default pool
@@ -194,7 +195,8 @@ SSM_API ssm_status_t ssm_lti_fwd(const void *x, const float *delta, const float 
  * ssm_scan_fwd with A restricted to one scalar per head). Channels come in H heads of P; head h has the
  * decay a_h (A[d][n] = a_h for its channels and all states) and one step delta[b][h][t] shared by its P
  * channels. Unrolled, y = (causal mask ∘ e^{a(c_t − c_s)} ∘ C Bᵀ)(β ∘ x) + D x per head, a masked linear
- * attention; it is evaluated chunk by chunk (64 steps) with fp32 matrix products on the MFMA units.
+ * attention; it is evaluated chunk by chunk (64 steps) with matrix products on the MFMA units (fp32
+ * products for fp32 storage; bf16 products, fp32 operands entering as bf16 hi + lo, for bf16 storage).
  *   x, z, y           [b][H·P][L] dtype (z may be NULL)
  *   delta             [b][H][L] dtype
  *   A                 [H] fp32 (the per-head decay a_h)
@@ -202,7 +204,9 @@ SSM_API ssm_status_t ssm_lti_fwd(const void *x, const float *delta, const float 
  *   D                 [H·P] fp32 or NULL
  *   initial_state     [b][H·P][N] fp32 or NULL (zeros); final_state [b][H·P][N] fp32 or NULL
  * Supported: P = 64, N in {32, 64, 128} (SSM_ERR_UNSUPPORTED otherwise); b, H >= 1, L >= 0. Scratch of
- * b·H·⌈L/64⌉·(P·N + 1) floats is taken stream-ordered from `stream`. Errors as for ssm_scan_fwd.
+ * b·H·⌈L/64⌉·(P·N + 1) floats is taken stream-ordered from `stream`, except for bf16 storage with N of 64
+ * or 128 and b·H at least twice the device's compute units, which needs none (the whole form then runs
+ * as one ordered walk per (b, head)). Errors as for ssm_scan_fwd.
  */
 SSM_API ssm_status_t ssm_ssd_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C,
                                  const float *D, const void *z, const float *initial_state, void *y,

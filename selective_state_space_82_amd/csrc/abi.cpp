@@ -507,16 +507,19 @@ ssm_status_t ssm_ssd_fwd(const void *x, const void *delta, const float *A, const
         return SSM_OK;
     }
     void *scratch = nullptr;
-    keep_pool_memory();
-    const int64_t floats = ssm::ssd_scratch_floats(b, H, L, N);
-    if (hipMallocAsync(&scratch, (size_t)floats * sizeof(float), stream) != hipSuccess) return SSM_ERR_HIP;
+    const int cus = cu_count();
+    const int64_t floats = ssm::ssd_scratch_floats(b, H, L, N, dtype == SSM_BF16, cus);
+    if (floats > 0) {
+        keep_pool_memory();
+        if (hipMallocAsync(&scratch, (size_t)floats * sizeof(float), stream) != hipSuccess) return SSM_ERR_HIP;
+    }
     ssm::SsdLaunch p{};
     p.x = x; p.delta = delta; p.B = B; p.C = C; p.z = z; p.A = A; p.D = D; p.h0 = initial_state;
     p.y = y; p.hT = final_state; p.scratch = static_cast<float *>(scratch);
     p.b = b; p.H = H; p.L = L; p.N = N; p.bf16 = dtype == SSM_BF16;
-    p.cus = cu_count();
+    p.cus = cus;
     const hipError_t e = ssm::launch_ssd(p, stream);
-    if (hipFreeAsync(scratch, stream) != hipSuccess) return SSM_ERR_HIP;
+    if (scratch && hipFreeAsync(scratch, stream) != hipSuccess) return SSM_ERR_HIP;
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

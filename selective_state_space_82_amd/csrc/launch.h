@@ -100,12 +100,15 @@ struct SsdLaunch {
     const float *A, *D, *h0;             // D, h0 nullable
     void *y;
     float *hT;                           // nullable
-    float *scratch;                      // ssd_scratch_floats(b, H, L, N)
+    float *scratch;                      // ssd_scratch_floats(b, H, L, N, bf16, cus) floats, or null
     int64_t b, H, L, N;
     bool bf16;
     int cus;                             // compute units of the device
 };
-int64_t ssd_scratch_floats(int64_t b, int64_t H, int64_t L, int64_t N);
+// The single walk (ssd_fused_kernel) serves bf16 storage with N of 64 or 128 once b·H gives every CU two
+// workgroups; it needs no scratch. The other forms take ssd_scratch_floats(...) floats.
+bool ssd_single_walk(int64_t b, int64_t H, int64_t N, bool bf16, int cus);
+int64_t ssd_scratch_floats(int64_t b, int64_t H, int64_t L, int64_t N, bool bf16, int cus);
 hipError_t launch_ssd(const SsdLaunch &p, hipStream_t stream);
 hipError_t launch_conv_step(const ConvStepLaunch &p, hipStream_t stream);
 

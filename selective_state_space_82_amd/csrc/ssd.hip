@@ -480,7 +480,12 @@ hipError_t launch_typed(const SsdArgs &a, int64_t N, hipStream_t stream) {
 
 }  // namespace
 
-int64_t ssd_scratch_floats(int64_t b, int64_t H, int64_t L, int64_t N) {
+bool ssd_single_walk(int64_t b, int64_t H, int64_t N, bool bf16, int cus) {
+    return bf16 && (N == 64 || N == 128) && b * H >= 2 * (int64_t)cus;
+}
+
+int64_t ssd_scratch_floats(int64_t b, int64_t H, int64_t L, int64_t N, bool bf16, int cus) {
+    if (ssd_single_walk(b, H, N, bf16, cus)) return 0;
     const int64_t nc = (L + kQ - 1) / kQ;
     return b * H * nc * (kP * N + 1);
 }
@@ -498,13 +503,13 @@ hipError_t launch_ssd(const SsdLaunch &p, hipStream_t stream) {
     a.vec = (p.L % 4) == 0 && aligned(p.x);
     a.vec_bc = aligned(p.B) && aligned(p.C);  // N is a multiple of 32
     a.vec8 = p.bf16 && (p.L % 8) == 0 && (reinterpret_cast<uintptr_t>(p.x) & 15) == 0;
-    a.decay = p.scratch + a.b * a.H * a.nc * (kP * p.N);
+    a.decay = p.scratch ? p.scratch + a.b * a.H * a.nc * (kP * p.N) : nullptr;
     // the fused state walk runs b·H·N/64 workgroups of four wavefronts; it pays once they give every
     // compute unit two
     a.fused = p.N % 64 == 0 && a.b * a.H * (p.N / 64) >= 2 * (int64_t)p.cus;
     a.vec_bc16 = ((reinterpret_cast<uintptr_t>(p.B) | reinterpret_cast<uintptr_t>(p.C)) & 15) == 0;
     // bf16 storage with b·H >= 2 workgroups per CU: the whole form in one walk per (b, head)
-    a.fused_all = p.bf16 && (p.N == 64 || p.N == 128) && a.b * a.H >= 2 * (int64_t)p.cus;
+    a.fused_all = ssd_single_walk(a.b, a.H, p.N, p.bf16, p.cus);
     if (p.bf16) return launch_typed<uint16_t>(a, p.N, stream);
     return launch_typed<float>(a, p.N, stream);
 }
