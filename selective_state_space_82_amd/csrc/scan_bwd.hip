@@ -379,6 +379,28 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
             for (int j = 0; j < NPL; ++j) o[j] = load_or(a.ckpt, idx + j, ch_ok && j < nvalid, 0.0f);
         }
     };
+    // The chunks are walked in descending order, kc_last down to kc_first; the checkpoint of the next
+    // one is loaded a chunk ahead (raw, from an always-valid address, and masked only when used), so
+    // its latency hides behind a chunk of arithmetic.
+    const int64_t kc_first = t_begin / K, kc_last = (t_end - 1) / K;
+    bool ck_ok[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) ck_ok[j] = ch_ok && (a.vec_state ? (j / 4) * 4 + 4 <= nvalid : j < nvalid);
+    float hn[NPL];
+    auto load_ckpt_raw = [&](int64_t kc) {
+        const int64_t idx = (row * a.n_ck + kc) * a.N + n0;
+        if (a.vec_state) {
+#pragma unroll
+            for (int j = 0; j < NPL; j += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(a.ckpt + (ck_ok[j] ? idx + j : 0));
+                hn[j] = v.x; hn[j + 1] = v.y; hn[j + 2] = v.z; hn[j + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NPL; ++j) hn[j] = a.ckpt[ck_ok[j] ? idx + j : 0];
+        }
+    };
+    load_ckpt_raw(kc_last);
 #pragma unroll 1
     for (int it = ntiles - 1; it >= 0; --it) {
         const int64_t t0 = t_begin + (int64_t)it * kBT;
@@ -387,8 +409,11 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
             const int tc = m * K;  // chunk start within the tile
             if (t0 + tc >= t_end) continue;  // all padding (no checkpoint there; nothing would change)
             // state entering the chunk (written by the forward pass)
+            const int64_t kc = (t0 + tc) / K;
             float h[NPL];
-            load_ckpt((t0 + tc) / K, h);
+#pragma unroll
+            for (int j = 0; j < NPL; ++j) h[j] = ck_ok[j] ? hn[j] : 0.0f;
+            if (kc > kc_first) load_ckpt_raw(kc - 1);
             // forward recomputation of the chunk: hs[k] = state after step tc + k
             float hs[K][NPL];
             float ab_k[kKeep ? KH : 1][kKeep ? NPL : 1], be_k[kKeep ? KH : 1][kKeep ? NPL : 1];
