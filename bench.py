@@ -32,6 +32,13 @@ VALU_PEAK_TSLOT = 256 * 4 * 16 * 2.4e9 / 1e12  # 256 CUs x 4 SIMD x 16 lanes x 2
 MFMA_F32_PEAK_TFLOPS = 157.3                 # MI355X dense fp32 MFMA, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0               # MI355X dense bf16 MFMA, published
 MALL_BYTES = 256 << 20
+# The shader clock climbs to its sustained level over tens of milliseconds of back-to-back work, and
+# drops while the GPU idles (as it does while inputs are generated on the host). A headline run with 5
+# warm-up calls read 1.31-1.36 TB/s where 200 or more read 1.50-1.52 TB/s. Hence the default warm-up
+# below, and a warm-up of at least EXTRA_WARM_S seconds before each extra measurement.
+DEFAULT_WARMUP = 500
+DEFAULT_STEPS = 500
+EXTRA_WARM_S = 0.25
 HEADLINE = "mamba130m_f32_b4_d1536_L2048_N16"
 METRIC = "selective-scan GB/s & % of HBM peak; (b·d·L)/s at N=16; decode steps/s"
 
@@ -60,7 +67,20 @@ def to_dev(arr, dev):
     return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
 
 
-def bench_prefill(name, steps, warmup, rotate=0, quiet=False):
+def warm_up(fn, count, min_s=0.0):
+    """`count` untimed calls of fn(i), then more until min_s seconds have passed."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while i < count or time.perf_counter() - t0 < min_s:
+        fn(i)
+        i += 1
+        if i % 8 == 0 and i >= count:
+            torch.cuda.synchronize()  # keep the queue short, so the clock check follows the GPU
+    torch.cuda.synchronize()
+
+
+def bench_prefill(name, steps, warmup, rotate=0, quiet=False, min_warm_s=0.0):
     import torch
     from selective_state_space_82_amd import api
     from selective_state_space_82_amd import inputs as I
@@ -92,9 +112,7 @@ def bench_prefill(name, steps, warmup, rotate=0, quiet=False):
         api.ssm_scan_fwd(s["x"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], y=s["y"], final_state=s["h"],
                          events=events)
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
+    warm_up(call, warmup, min_warm_s)
     t0 = time.perf_counter()
     for i in range(steps):
         call(i, ev[i] if i % every == 0 else None)
@@ -157,9 +175,7 @@ def bench_grad(name, steps, warmup, quiet=False):
         s = sets[i % rotate]
         return api.ssm_scan_bwd(s["x"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], dy=s["dy"])
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
+    warm_up(call, warmup, EXTRA_WARM_S)
     t0 = time.perf_counter()
     for i in range(steps):
         call(i)
@@ -212,9 +228,7 @@ def bench_lti(name, steps, warmup, quiet=False):
     K = api.ssm_lti_kernel(par["delta"], par["A"], par["B"], par["C"], w.L)
 
     def timed(fn):
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
+        warm_up(fn, warmup, EXTRA_WARM_S)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(steps):
@@ -286,9 +300,7 @@ def bench_ssd(name, steps, warmup, quiet=False):
         sets.append(t)
 
     def timed(fn):
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
+        warm_up(fn, warmup, EXTRA_WARM_S)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(steps):
@@ -350,9 +362,7 @@ def bench_conv(name, steps, warmup, W=4, quiet=False):
         xin, xo, so = sets[i % rotate]
         api.ssm_conv1d_fwd(xin, taps, bias, x_out=xo, state_out=so)
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
+    warm_up(call, warmup, EXTRA_WARM_S)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(steps):
@@ -391,8 +401,7 @@ def bench_decode(name, rotate_states, quiet=False):
         api.ssm_scan_step(states[i % rotate_states], t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
                           y=ys[i % 2])
 
-    for i in range(4):
-        step(i)
+    warm_up(step, 4, EXTRA_WARM_S)
     for j, s in enumerate(states):
         s.copy_(st0)
     torch.cuda.synchronize()
@@ -496,8 +505,8 @@ def copy_probe(nbytes):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=DEFAULT_STEPS)
+    ap.add_argument("--warmup", type=int, default=DEFAULT_WARMUP)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--extra", default="decode,mamba1p4b_bf16_b8_d4096_L4096_N16,grad,conv,lti,ssd",
                     help="comma list: 'decode', 'grad' (gradient pass on the workload), 'conv' (Conv1D front "
@@ -537,7 +546,7 @@ def main():
             for r in (1, 4):
                 extra.append(bench_decode(I.DECODE_WORKLOADS[0], r))
         elif n == "grad":
-            extra.append(bench_grad(args.workload, max(3, args.steps // 5), 2))
+            extra.append(bench_grad(args.workload, max(3, min(args.steps, 100)), 2))
         elif n == "ssd":
             for sn in SSD_SHAPES:
                 extra.append(bench_ssd(sn, 20, 3))
@@ -548,7 +557,7 @@ def main():
             for cw in dict.fromkeys((args.workload, "mamba1p4b_bf16_b8_d4096_L4096_N16")):
                 extra.append(bench_conv(cw, 20, 3))
         else:
-            r, _ = bench_prefill(n, max(3, args.steps // 4), 2)
+            r, _ = bench_prefill(n, max(3, min(args.steps, 100)), 2, min_warm_s=EXTRA_WARM_S)
             extra.append(r)
 
     cpu = None
