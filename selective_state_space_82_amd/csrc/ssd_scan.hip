@@ -226,7 +226,8 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_fused_kernel(SsdArgs a) {
     __shared__ __align__(16) uint16_t s_bt[N * kMH];   // Bᵀ [n][s]
     __shared__ __align__(16) uint16_t s_x[kP * kMH];   // x [p][s]
     __shared__ __align__(16) float s_h[kP * NF];       // entering state [p][n]
-    __shared__ __align__(16) float s_m[kQ * kMS];      // M [t][s], then the outputs [p][t]
+    __shared__ __align__(16) float s_m[kQ * kMS];      // M [t][s]
+    __shared__ __align__(16) float s_o[kP * kMS];      // the outputs [p][t]
     const int64_t bh = blockIdx.x, ib = bh / a.H, h = bh % a.H;
     const float ah = a.A[h];
     const int l = lane(), w = wave(), hi = l / 32, tid = threadIdx.x;
@@ -390,13 +391,12 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_fused_kernel(SsdArgs a) {
                 inter = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c8, l8, inter, 0, 0, 0);
             }
         }
-        lds_barrier();  // M is no longer read: its space takes the outputs [p][t]
         {
             const int p = 32 * op + l % 32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int t = 32 * ot + d_row(r, l);
-                s_m[p * kMS + t] = yv[r] + exp2_fast(s_cum[t]) * inter[r];
+                s_o[p * kMS + t] = yv[r] + exp2_fast(s_cum[t]) * inter[r];
             }
         }
         lds_barrier();
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_fused_kernel(SsdArgs a) {
             const int p = e_p(k), t4 = e_t(k);
             if (t4 >= lim) continue;
             const int64_t off = ((ib * a.H + h) * kP + p) * a.L + t0 + t4;
-            const float4 o = *reinterpret_cast<const float4 *>(s_m + p * kMS + t4);
+            const float4 o = *reinterpret_cast<const float4 *>(s_o + p * kMS + t4);
             const uint16_t *xs = s_x + p * kMH + t4;
             float v[4] = {o.x + dsk[k] * widen(xs[0]), o.y + dsk[k] * widen(xs[1]), o.z + dsk[k] * widen(xs[2]),
                           o.w + dsk[k] * widen(xs[3])};
