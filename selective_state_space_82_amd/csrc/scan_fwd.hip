@@ -400,7 +400,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
         constexpr int kUnroll = RO ? kTile / kGrp : 1;
 #pragma unroll kUnroll
         for (int t = 0; t < kTile; t += kGrp) {
-            if constexpr (!AGG) {
+            if constexpr (CK || SAFE) {  // the fast output pass never runs with checkpoints
                 if (a.ckpt && t % a.ck_len == 0 && t0tile + t < t_end) store_ckpt((t0tile + t) / a.ck_len);
             }
             if constexpr (kGroupLocal) load_sub(t, sb[0]);
