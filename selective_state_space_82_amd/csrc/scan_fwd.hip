@@ -363,7 +363,8 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
             for (int i = 1; i < G; ++i) v += r[q * G + i];
             const int col = col0 + q * G;  // + g, in the lane's base pointers
             v = __builtin_fmaf(dskip, xfin[col], v);  // + D·x
-            if (gate) v *= silu(widen(zfin[col]));
+            const float sz = silu(widen(zfin[col]));  // computed either way: no branch in the unrolled tile
+            v *= gate ? sz : 1.0f;
             ywin[col] = narrow<T>(v);
         }
     };
