@@ -396,9 +396,9 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
         constexpr bool kGroupLocal = sizeof(T) == 2;
         Sub sb[2];
         if constexpr (!kGroupLocal) load_sub(0, sb[0]);
-        // the output pass unrolls the tile (LDS offsets become immediates); the aggregate pass
-        // keeps a loop, which holds its register need down
-        constexpr int kUnroll = RO ? kTile / kGrp : 1;
+        // the output pass unrolls the tile (LDS offsets become immediates); the other passes unroll
+        // two readout groups at a time (a whole tile there doubles the fp32 aggregate pass's registers)
+        constexpr int kUnroll = RO ? kTile / kGrp : 2;
 #pragma unroll kUnroll
         for (int t = 0; t < kTile; t += kGrp) {
             if constexpr (CK || SAFE) {  // the fast output pass never runs with checkpoints
