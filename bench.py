@@ -1,16 +1,19 @@
 #!/usr/bin/env python3
 """Throughput of the selective scan on one MI355X.
 
-A step is one ssm_scan_fwd call over one batch of the Mamba-130M-like layer workload
-(b=4, d=1536, L=2048, N=16, fp32 storage, gate on, final state returned): ZOH discretisation,
-recurrence, readout, gate/skip epilogue, and the chunk carry when the plan splits time. Inputs are
-synthetic (seeded draws with the workload's distributions) and resident in HBM before timing.
-Several copies of the inputs and outputs rotate so the 256 MB last-level cache cannot hold them.
+A step is one ssm_scan_fwd call over one batch of the long-context workload (b=1, d=2048,
+L=131072, N=16, bf16 storage with an fp32 state, gate on, final state returned), the largest
+configuration that runs on one GPU: ZOH discretisation, recurrence, readout, gate/skip epilogue, and
+the chunk carry across time segments. Inputs are synthetic (seeded draws with the workload's
+distributions) and resident in HBM before timing; where one set fits the 256 MB last-level cache,
+several copies rotate.
 
 Printed: one JSON line. `value` is GB/s of algorithmic traffic (inputs read once, outputs written
 once) over the whole timed call; `roofline` describes the output-pass kernel, timed with HIP
-events on the launch stream; `cpu_baseline` times the fp64 oracle on the host; `extra` carries
-the decode-step rate and the other prefill workloads.
+events on the launch stream, against the VALU issue rate (the bound of an exact exp per (t, n)),
+with the HBM and ALU fractions of the kernel and of the whole call beside it; `cpu_baseline` times the
+fp64 oracle on the host; `extra` carries every other workload: the tiny one (µs per call), the
+130M-like and 1.4B-like prefills, the decode steps, and the gradient, Conv1D, LTI and SSD forms.
 """
 from __future__ import annotations
 
@@ -39,7 +42,14 @@ MALL_BYTES = 256 << 20
 DEFAULT_WARMUP = 500
 DEFAULT_STEPS = 500
 EXTRA_WARM_S = 0.25
-HEADLINE = "mamba130m_f32_b4_d1536_L2048_N16"
+HEAD_WARM_S = 1.0
+HEADLINE = "longctx_bf16_b1_d2048_L131072_N16"
+# the machine's CPU share for one GPU; the oracle baseline uses at most this many host threads
+HOST_THREAD_CAP = 16
+GRAD_WORKLOAD = "mamba130m_f32_b4_d1536_L2048_N16"
+SIDE_WORKLOADS = ("mamba130m_f32_b4_d1536_L2048_N16", "mamba1p4b_bf16_b8_d4096_L4096_N16")
+DEFAULT_EXTRA = ("tiny_f32_b1_d8_L128_N4,mamba130m_f32_b4_d1536_L2048_N16,mamba1p4b_bf16_b8_d4096_L4096_N16,"
+                 "decode,grad,conv,lti,ssd")
 METRIC = "selective-scan GB/s & % of HBM peak; (b·d·L)/s at N=16; decode steps/s"
 
 
@@ -124,19 +134,27 @@ def bench_prefill(name, steps, warmup, rotate=0, quiet=False, min_warm_s=0.0):
     plan = api.ssm_scan_fwd_plan(w.b, w.d, w.L, w.N, torch.float32 if w.dtype == "f32" else torch.bfloat16)
     elems = w.b * w.d * w.L
     slots = elems * valu_slots_per_element(w.N, w.gate)
+    call_tslot = slots / (ms * 1e-3) / 1e12
+    kern_tslot = slots / (kern_ms * 1e-3) / 1e12
     res = {
-        "workload": name, "ms_per_call": ms, "GBps": nbytes / (ms * 1e-3) / 1e9,
-        "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "elements_per_s": elems / (ms * 1e-3),
-        "output_kernel_ms": kern_ms, "output_kernel_samples": int(len(kern)), "output_kernel_ms_p10_p50_p90": [round(float(q), 5) for q in
-                                                                      np.percentile(kern, [10, 50, 90])],
+        "workload": name, "ms_per_call": ms, "us_per_call": ms * 1e3, "GBps": nbytes / (ms * 1e-3) / 1e9,
+        "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alu_frac": call_tslot / VALU_PEAK_TSLOT,
+        "elements_per_s": elems / (ms * 1e-3),
+        "output_kernel_ms": kern_ms, "output_kernel_samples": int(len(kern)),
+        "output_kernel_ms_p10_p50_p90": [round(float(q), 5) for q in np.percentile(kern, [10, 50, 90])],
+        "output_kernel_share_of_call": kern_ms / ms,
         "algorithmic_bytes": nbytes, "rotating_sets": rotate, "plan": plan,
         "valu_slots_per_element": valu_slots_per_element(w.N, w.gate),
-        "kernel_valu_Tslot_s": slots / (kern_ms * 1e-3) / 1e12,
-        "kernel_GBps": nbytes / (kern_ms * 1e-3) / 1e9, "input_gen_s": gen_s,
+        "call_valu_Tslot_s": call_tslot, "kernel_valu_Tslot_s": kern_tslot,
+        "kernel_alu_frac": kern_tslot / VALU_PEAK_TSLOT,
+        "kernel_GBps": nbytes / (kern_ms * 1e-3) / 1e9,
+        "kernel_hbm_frac": nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "input_gen_s": gen_s,
+        "warmup_calls": warmup, "min_warmup_s": min_warm_s,
     }
     if not quiet:
-        print(f"# {name}: {ms * 1e3:.1f} us/call, {res['GBps']:.0f} GB/s, output kernel {kern_ms * 1e3:.1f} us "
-              f"({res['kernel_valu_Tslot_s']:.2f} T VALU slot/s), plan {plan}", file=sys.stderr, flush=True)
+        print(f"# {name}: {ms * 1e3:.1f} us/call, {res['GBps']:.0f} GB/s ({res['hbm_frac']:.3f} HBM, "
+              f"{res['alu_frac']:.3f} ALU), output kernel {kern_ms * 1e3:.1f} us ({res['kernel_alu_frac']:.3f} ALU), "
+              f"plan {plan}", file=sys.stderr, flush=True)
     del sets
     torch.cuda.empty_cache()
     return res, inp
@@ -428,8 +446,10 @@ def bench_decode(name, rotate_states, quiet=False):
     return res
 
 
-def cpu_baseline(inp, name, threads):
-    """The fp64 oracle on the host over the whole workload (its rows split across threads)."""
+def cpu_baseline(inp, name, threads, target_thread_s=15.0):
+    """The fp64 oracle on the host over a bounded sample of the workload: blocks of 16 channels of a batch
+    row over the whole sequence (each row is sequential in t), spread over `threads` host threads, as many
+    blocks as make about `target_thread_s` seconds of CPU work (one block is timed alone first)."""
     import concurrent.futures as cf
 
     import oracle
@@ -437,7 +457,8 @@ def cpu_baseline(inp, name, threads):
 
     w = I.WORKLOADS[name]
     dt = inp["dtype"]
-    chunks = [(ib, c0, min(w.d, c0 + 128)) for ib in range(w.b) for c0 in range(0, w.d, 128)]
+    blk = 16
+    chunks = [(ib, c0, min(w.d, c0 + blk)) for ib in range(w.b) for c0 in range(0, w.d, blk)]
 
     def one(job):
         ib, c0, c1 = job
@@ -446,30 +467,51 @@ def cpu_baseline(inp, name, threads):
                         I.widen(inp["C"][ib:ib + 1], dt), inp["D"][c0:c1],
                         None if inp["z"] is None else wd(inp["z"]))
 
-    # whole passes over the workload until about 10 s of host CPU time (threads x wall) is spent
-    passes, wall = 0, 0.0
-    while passes < 50 and (passes == 0 or wall * threads < 10.0):
-        t0 = time.perf_counter()
-        with cf.ThreadPoolExecutor(threads) as ex:
-            list(ex.map(one, chunks))
-        wall += time.perf_counter() - t0
-        passes += 1
-    # one host thread on batch row 0 (all channels)
-    row0 = [c for c in chunks if c[0] == 0]
     t0 = time.perf_counter()
-    for c in row0:
-        one(c)
-    wall1 = time.perf_counter() - t0
-    rows1 = w.d
+    one(chunks[0])
+    one_s = time.perf_counter() - t0
+    n = int(target_thread_s / max(one_s, 1e-6))
+    n = max(threads, min(len(chunks), (n // threads) * threads if n >= threads else threads))
+    n = min(n, len(chunks))
+    sample = chunks[:n]
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one, sample))
+    wall = time.perf_counter() - t0
+    rows = sum(c1 - c0 for _, c0, c1 in sample)
+    elems = rows * w.L
     esize = 4 if dt == "f32" else 2
-    nbytes = algorithmic_bytes(w.b, w.d, w.L, w.N, esize, w.gate)
-    return {"value": passes * nbytes / wall / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{passes} passes over the whole workload ({w.b * w.d} (b,d) rows x {w.L} steps x {w.N} "
-                      f"states), fp64 sequential rows on {threads} host threads, {wall:.2f} s wall "
-                      f"({wall * threads:.0f} thread-s)",
-            "elements_per_s": passes * w.b * w.d * w.L / wall,
-            "single_thread_elements_per_s": rows1 * w.L / wall1,
-            "single_thread_sample": f"{rows1} (b,d) rows x {w.L} steps on one thread, {wall1:.3f} s"}
+    per_elem = algorithmic_bytes(w.b, w.d, w.L, w.N, esize, w.gate) / (w.b * w.d * w.L)
+    return {"value": elems * per_elem / wall / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of the workload's {w.b * w.d} (b,d) rows, each over all {w.L} steps x {w.N} states "
+                      f"(fp64, sequential in t), on {threads} host threads: {wall:.2f} s wall, about "
+                      f"{wall * threads:.0f} thread-s; GB/s counts the workload's algorithmic bytes per element",
+            "host_cpu_count": os.cpu_count(),
+            "thread_cap": f"{HOST_THREAD_CAP} (the host's CPU share for one GPU)",
+            "elements_per_s": elems / wall,
+            "single_thread_elements_per_s": (chunks[0][2] - chunks[0][1]) * w.L / one_s,
+            "single_thread_sample": f"{chunks[0][2] - chunks[0][1]} (b,d) rows x {w.L} steps on one thread, {one_s:.3f} s"}
+
+
+def bench_tiny_latency(name, calls=200):
+    """Latency of one call on the tiny workload: host wall time of call + synchronize, per call (median)."""
+    import torch
+    from selective_state_space_82_amd import api
+    from selective_state_space_82_amd import inputs as I
+
+    w = I.WORKLOADS[name]
+    inp = I.prefill_inputs(w)
+    t = {k: to_dev(inp[k], "cuda") for k in ("x", "delta", "z", "A", "B", "C", "D")}
+    y = torch.empty_like(t["x"])
+    h = torch.empty((w.b, w.d, w.N), dtype=torch.float32, device="cuda")
+    lat = []
+    for i in range(calls + 20):
+        t0 = time.perf_counter()
+        api.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], y=y, final_state=h)
+        torch.cuda.synchronize()
+        if i >= 20:
+            lat.append(time.perf_counter() - t0)
+    return float(np.median(lat) * 1e6), [round(float(q) * 1e6, 2) for q in np.percentile(lat, [10, 90])]
 
 
 def copy_bandwidth(nbytes=1 << 30, reps=5):
@@ -508,9 +550,9 @@ def main():
     ap.add_argument("--steps", type=int, default=DEFAULT_STEPS)
     ap.add_argument("--warmup", type=int, default=DEFAULT_WARMUP)
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--extra", default="decode,mamba1p4b_bf16_b8_d4096_L4096_N16,grad,conv,lti,ssd",
-                    help="comma list: 'decode', 'grad' (gradient pass on the workload), 'conv' (Conv1D front "
-                         "end), 'lti' (LTI convolution form), 'ssd' (scalar-decay chunked form) "
+    ap.add_argument("--extra", default=DEFAULT_EXTRA,
+                    help="comma list: 'decode', 'grad' (gradient pass on the 130M-like workload), 'conv' (Conv1D "
+                         "front end), 'lti' (LTI convolution form), 'ssd' (scalar-decay chunked form) "
                          "and/or prefill workload names "
                          "('' for none, 'all' for every one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -535,7 +577,7 @@ def main():
 
     copy_gbps = copy_bandwidth()
     print(f"# device copy: {copy_gbps:.0f} GB/s (read + write)", file=sys.stderr, flush=True)
-    head, inp = bench_prefill(args.workload, args.steps, args.warmup, args.rotate)
+    head, inp = bench_prefill(args.workload, args.steps, args.warmup, args.rotate, min_warm_s=HEAD_WARM_S)
     w = I.WORKLOADS[args.workload]
     extra = []
     names = [n for n in args.extra.split(",") if n]
@@ -546,23 +588,32 @@ def main():
             for r in (1, 4):
                 extra.append(bench_decode(I.DECODE_WORKLOADS[0], r))
         elif n == "grad":
-            extra.append(bench_grad(args.workload, max(3, min(args.steps, 100)), 2))
+            extra.append(bench_grad(GRAD_WORKLOAD, max(3, min(args.steps, 100)), 2))
         elif n == "ssd":
             for sn in SSD_SHAPES:
                 extra.append(bench_ssd(sn, 20, 3))
         elif n == "lti":
-            for cw in dict.fromkeys((args.workload, "mamba1p4b_bf16_b8_d4096_L4096_N16")):
+            for cw in SIDE_WORKLOADS:
                 extra.append(bench_lti(cw, 20, 3))
         elif n == "conv":
-            for cw in dict.fromkeys((args.workload, "mamba1p4b_bf16_b8_d4096_L4096_N16")):
+            for cw in SIDE_WORKLOADS:
                 extra.append(bench_conv(cw, 20, 3))
+        elif n == args.workload:
+            continue
         else:
-            r, _ = bench_prefill(n, max(3, min(args.steps, 100)), 2, min_warm_s=EXTRA_WARM_S)
+            wl = I.WORKLOADS[n]
+            small = wl.b * wl.d * wl.L < (1 << 20)
+            r, _ = bench_prefill(n, 2000 if small else max(3, min(args.steps, 200)), 100 if small else 2,
+                                 min_warm_s=EXTRA_WARM_S)
+            if small:  # latency-bound: report the time of one call, back to back and synchronised
+                r["us_per_call_synchronised"], r["us_per_call_synchronised_p10_p90"] = bench_tiny_latency(n)
+                print(f"# {n}: {r['us_per_call']:.2f} us per call back to back, "
+                      f"{r['us_per_call_synchronised']:.1f} us per synchronised call", file=sys.stderr, flush=True)
             extra.append(r)
 
     cpu = None
     if not args.no_cpu_baseline:
-        threads = int(min(16, os.cpu_count() or 1))
+        threads = int(min(HOST_THREAD_CAP, os.cpu_count() or 1))
         cpu = cpu_baseline(inp, args.workload, threads)
         print(f"# cpu baseline: {cpu['value']:.3f} GB/s on {threads} threads", file=sys.stderr, flush=True)
 
@@ -593,8 +644,10 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded Normal / softplus-Normal draws with the workload's distributions)",
         "config": {"workload": args.workload, "b": w.b, "d": w.d, "L": w.L, "N": w.N, "gate": w.gate,
-                   "state": "f32", "plan": head["plan"], "rotating_sets": head["rotating_sets"]},
+                   "state": "f32", "plan": head["plan"], "rotating_sets": head["rotating_sets"],
+                   "warmup": f"{args.warmup} calls and at least {HEAD_WARM_S} s"},
         "hbm_frac": round(head["hbm_frac"], 4),
+        "alu_frac": round(head["alu_frac"], 4),
         "copy_GBps": round(copy_gbps, 1),
         "copy_frac": round(head["GBps"] / copy_gbps, 4),
         "elements_per_s": head["elements_per_s"],
@@ -603,7 +656,9 @@ def main():
                      "traffic": traffic, "kernel": "scan_fwd_kernel (output pass)",
                      "kernel_us": round(head["output_kernel_ms"] * 1e3, 2),
                      "kernel_us_p10_p50_p90": [round(q * 1e3, 2) for q in head["output_kernel_ms_p10_p50_p90"]],
-                     "kernel_hbm_frac": round(head["kernel_GBps"] / HBM_PEAK_GBS, 4)},
+                     "kernel_hbm_frac": round(head["kernel_hbm_frac"], 4),
+                     "call_alu_frac": round(head["alu_frac"], 4), "call_hbm_frac": round(head["hbm_frac"], 4),
+                     "kernel_share_of_call": round(head["output_kernel_share_of_call"], 4)},
         "cpu_baseline": cpu,
         "extra": extra,
     }

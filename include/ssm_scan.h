@@ -35,11 +35,11 @@
  *   - Calls are reentrant: the library keeps no per-call global state. Calls on different streams
  *     may run concurrently. Calls that need scratch (a prefill split into time segments, the
  *     gradient pass, ssm_lti_fwd, ssm_ssd_fwd except bf16 with N of 64 or 128 and b·H at least
- *     twice the device's compute units) take it from the current device's default
- *     stream-ordered pool (hipMallocAsync / hipFreeAsync on `stream`). The first such call on a
- *     device sets that pool's release threshold to its maximum, so freed scratch stays pooled
- *     instead of being returned at every synchronisation; other users of the device's default pool
- *     see the same setting.
+ *     twice the device's compute units) take it stream-ordered on `stream` from a memory pool the
+ *     library creates on the current device at its first such call, and return it there at the
+ *     end of the call. That pool keeps freed scratch (its release threshold is at the maximum), so
+ *     repeated calls reuse it; it lives until the process ends. The device's default pool is not
+ *     touched.
  *   - NaN and Inf inputs propagate; nothing is clamped.
  */
 #ifndef SSM_SCAN_H

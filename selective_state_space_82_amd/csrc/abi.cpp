@@ -52,21 +52,38 @@ int cu_count() {
     return cache[dev];
 }
 
-// Keep freed stream-ordered scratch in the device's default pool instead of returning it to the
-// driver at every synchronisation, so repeated calls do not pay for re-mapping it. Once per device.
-void keep_pool_memory() {
+// Stream-ordered scratch comes from a memory pool the library creates on each device at first use. Its
+// release threshold is at the maximum, so freed scratch stays in that pool across synchronisations and
+// repeated calls do not pay for re-mapping it. The device's default pool is left as the caller set it.
+// Should the pool not be created, scratch comes from the default pool as it stands.
+hipMemPool_t scratch_pool() {
     static std::mutex mu;
-    static bool done[64] = {false};
+    static hipMemPool_t pools[64] = {};
+    static bool tried[64] = {false};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
     std::lock_guard<std::mutex> lock(mu);
-    if (done[dev]) return;
-    done[dev] = true;
-    hipMemPool_t pool = nullptr;
-    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess && pool) {
-        uint64_t threshold = UINT64_MAX;
-        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+    if (!tried[dev]) {
+        tried[dev] = true;
+        hipMemPoolProps props{};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        if (hipMemPoolCreate(&pool, &props) == hipSuccess && pool) {
+            uint64_t threshold = UINT64_MAX;
+            (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+            pools[dev] = pool;
+        }
     }
+    return pools[dev];
+}
+
+hipError_t scratch_alloc(void **p, size_t bytes, hipStream_t stream) {
+    hipMemPool_t pool = scratch_pool();
+    if (pool) return hipMallocFromPoolAsync(p, bytes, pool, stream);
+    return hipMallocAsync(p, bytes, stream);
 }
 
 struct Plan {
@@ -190,8 +207,7 @@ ssm_status_t fwd_impl(const void *x, const void *delta, const float *A, const vo
     p.ev_end = o ? static_cast<hipEvent_t>(o->ev_end) : nullptr;
     void *scratch = nullptr;
     if (pl.scratch_bytes > 0) {
-        keep_pool_memory();
-        if (hipMallocAsync(&scratch, (size_t)pl.scratch_bytes, stream) != hipSuccess) return SSM_ERR_HIP;
+        if (scratch_alloc(&scratch, (size_t)pl.scratch_bytes, stream) != hipSuccess) return SSM_ERR_HIP;
         p.scratch = static_cast<float *>(scratch);
     }
     const hipError_t e = ssm::launch_scan_fwd(p, stream);
@@ -265,8 +281,7 @@ ssm_status_t bwd_impl(const void *x, const void *delta, const float *A, const vo
     if (!mul_ok(b * d, L, &floats)) return SSM_ERR_SHAPE;
     floats = ssm::bwd_scratch_floats(pl.n_seg, p.grad_n_seg, b, d, L, N, pl.npl);
     void *scratch = nullptr;
-    keep_pool_memory();
-    if (hipMallocAsync(&scratch, (size_t)floats * sizeof(float), stream) != hipSuccess) return SSM_ERR_HIP;
+    if (scratch_alloc(&scratch, (size_t)floats * sizeof(float), stream) != hipSuccess) return SSM_ERR_HIP;
     p.scratch = static_cast<float *>(scratch);
     const hipError_t e = ssm::launch_scan_bwd(p, stream);
     if (hipFreeAsync(scratch, stream) != hipSuccess) return SSM_ERR_HIP;
@@ -464,8 +479,7 @@ ssm_status_t ssm_lti_fwd(const void *x, const float *delta, const float *A, cons
     for (const Span &in : ins)
         if (overlaps(out, in)) return SSM_ERR_ALIAS;
     void *K = nullptr;
-    keep_pool_memory();
-    if (hipMallocAsync(&K, (size_t)(d * L) * sizeof(float), stream) != hipSuccess) return SSM_ERR_HIP;
+    if (scratch_alloc(&K, (size_t)(d * L) * sizeof(float), stream) != hipSuccess) return SSM_ERR_HIP;
     const ssm::LtiKernelLaunch pk{delta, A, B, C, static_cast<float *>(K), d, L, N};
     hipError_t e = ssm::launch_lti_kernel(pk, stream);
     if (e == hipSuccess) {
@@ -510,8 +524,7 @@ ssm_status_t ssm_ssd_fwd(const void *x, const void *delta, const float *A, const
     const int cus = cu_count();
     const int64_t floats = ssm::ssd_scratch_floats(b, H, L, N, dtype == SSM_BF16, cus);
     if (floats > 0) {
-        keep_pool_memory();
-        if (hipMallocAsync(&scratch, (size_t)floats * sizeof(float), stream) != hipSuccess) return SSM_ERR_HIP;
+        if (scratch_alloc(&scratch, (size_t)floats * sizeof(float), stream) != hipSuccess) return SSM_ERR_HIP;
     }
     ssm::SsdLaunch p{};
     p.x = x; p.delta = delta; p.B = B; p.C = C; p.z = z; p.A = A; p.D = D; p.h0 = initial_state;

@@ -37,6 +37,12 @@ __device__ __forceinline__ float expm1_over_v_small(float v) {
     return __builtin_fmaf(v, __builtin_fmaf(v, __builtin_fmaf(v, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f), 1.0f);
 }
 
+// e^v − 1 from u = v·log2(e) and abar = 2^u: the series near v = 0 (no cancellation), else abar − 1.
+__device__ __forceinline__ float expm1_log2(float u, float abar) {
+    const float v = u * 0.69314718055994530942f;
+    return __builtin_fabsf(v) < 0.0625f ? v * expm1_over_v_small(v) : abar - 1.0f;
+}
+
 // ZOH input coefficient (e^{Δa} − 1)/a for one state, given abar = e^{Δa} and inv_a = 1/a.
 // Near Δa = 0 the quotient is taken from its series, so a = 0 yields the limit Δ exactly and
 // tiny |a| does not cancel.

@@ -60,16 +60,10 @@ __device__ __forceinline__ float dbeta_da(float dt, float u, float abar, float b
     return __builtin_fabsf(v) < 0.0625f ? series : direct;
 }
 
-// Where every |A| of a wavefront's states is at least this, the gradient pass takes β = (Ā − 1)/A as
-// written: Ā comes within a few units in the last place of 1, so β's absolute error is a few times
-// 2^-23/|A| (the same error the prefill's scaled-state path accepts for Ā − 1). The series for small
-// |ΔA| is kept for ∂β/∂a, whose direct form cancels to nothing there.
-constexpr float kDirectBetaAbsA = 0.125f;
-
-// REV: reverse aggregate pass (no gradients; segments 1 .. S−1), else the gradient pass. DIRECT (only
-// for the gradient pass): the variant for wavefronts whose |A| are all at least kDirectBetaAbsA;
-// the two variants run over the same grid and each unit returns at once from the one it does not own.
-template <typename T, int G, int NPL, bool REV, bool DIRECT = false>
+// REV: reverse aggregate pass (no gradients; segments 1 .. S−1), else the gradient pass. β always takes
+// the series of (e^v − 1)/v where |v| = |ΔA| < 1/16: (Ā − 1)/A from a float Ā near 1 would carry a
+// relative error of about 2^-24/|ΔA| there, which slow channels (small |ΔA| for many steps) expose.
+template <typename T, int G, int NPL, bool REV>
 __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
     constexpr int E = Chunk<T>::kElems;
     constexpr int kPitch = kBT + 4;
@@ -126,7 +120,14 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
     const int nvalid = (N - n0) < NPL ? (N - n0) : NPL;
     const int64_t row = bi * a.d + ch;
     const int64_t sidx = row * a.N + n0;
-    float Av[NPL], a2[NPL], ia[NPL], kap[NPL], gA[NPL];
+    float Av[NPL], a2[NPL], ia[NPL], gA[NPL];
+    // The adjoint carried to the previous step, in fp64: it sums dys·C over the whole remaining sequence,
+    // undamped where Δ·A is small, and an fp32 carry would round at 2^-24 of its size on every step; the
+    // part that survives in dΔ = Σ_n λ_n B_n x (+ …) shows where that sum over states cancels. For the
+    // same reason the decay is applied as κ = λ + (Ā − 1)·λ with Ā − 1 accurate in relative terms (the
+    // series near ΔA = 0): a float Ā itself is only within 2^-25 of its value, and that error compounds
+    // over the sequence. fp64 adds and multiplies issue at the fp32 rate on this GPU.
+    double kap[NPL];
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
         const bool ok = ch_ok && j < nvalid;
@@ -135,13 +136,7 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
         a2[j] = av * kLog2e;
         ia[j] = 1.0f / av;
         gA[j] = 0.0f;
-        kap[j] = 0.0f;
-    }
-    if constexpr (!REV) {
-        bool small_a = false;
-#pragma unroll
-        for (int j = 0; j < NPL; ++j) small_a |= !(__builtin_fabsf(Av[j]) >= kDirectBetaAbsA);
-        if (__any(small_a) == DIRECT) return;  // wave-uniform: the other variant owns this unit
+        kap[j] = 0.0;
     }
     auto load_state = [&](const float *base, float (&o)[NPL]) {
         if (a.vec_state) {
@@ -159,13 +154,18 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
     if constexpr (!REV) {
         // adjoint entering this segment from the right: the final-state gradient, carried through
         // the aggregates of every later segment (κ ← P_j κ + E_j for j = S−1 down to seg+1)
-        if (a.dh_final) load_state(a.dh_final, kap);
+        if (a.dh_final) {
+            float k0[NPL];
+            load_state(a.dh_final, k0);
+#pragma unroll
+            for (int q = 0; q < NPL; ++q) kap[q] = k0[q];
+        }
         for (int64_t j = a.n_seg - 1; j > seg; --j) {
             float P[NPL], Ej[NPL];
             load_state(a.rP + (j - 1) * bd * a.N, P);
             load_state(a.rE + (j - 1) * bd * a.N, Ej);
 #pragma unroll
-            for (int q = 0; q < NPL; ++q) kap[q] = __builtin_fmaf(P[q], kap[q], Ej[q]);
+            for (int q = 0; q < NPL; ++q) kap[q] = __builtin_fma((double)P[q], kap[q], (double)Ej[q]);
         }
     }
     const float dskip = (!REV && a.D) ? load_or(a.D, ch, ch_ok, 0.0f) : 0.0f;
@@ -286,8 +286,9 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
                 }
 #pragma unroll
                 for (int j = 0; j < NPL; ++j) {
-                    const float abar = exp2_fast(dt * a2[j]);
-                    kap[j] = abar * __builtin_fmaf(dys, Cv[j], kap[j]);
+                    const float u = dt * a2[j];
+                    const double lam = kap[j] + (double)(dys * Cv[j]);
+                    kap[j] = __builtin_fma((double)expm1_log2(u, exp2_fast(u)), lam, lam);
                 }
                 dsum += dt;
             }
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
                 if (j >= nvalid) continue;
                 const int64_t o = (seg - 1) * bd * a.N + sidx + j;
                 a.rP_out[o] = exp2_fast(a2[j] * dsum);
-                a.rE_out[o] = kap[j];
+                a.rE_out[o] = (float)kap[j];
             }
         }
         return;
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
                     for (int q = 0; q < 4; ++q) {
                         const float u = dt * a2[j + q];
                         const float abar = exp2_fast(u);
-                        const float beta = DIRECT ? (abar - 1.0f) * ia[j + q] : zoh_input_coef_log2(dt, u, abar, ia[j + q]);
+                        const float beta = zoh_input_coef_log2(dt, u, abar, ia[j + q]);
                         const float hp = k == 0 ? h[j + q] : hs[k - 1][j + q];
                         hs[k][j + q] = __builtin_fmaf(abar, hp, beta * (bq[q] * xt));
                         if constexpr (kKeep) {
@@ -511,10 +512,11 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
                         beta = be_k[kKeep ? k - (K - KH) : 0][j];
                     } else {
                         abar = exp2_fast(u);
-                        beta = DIRECT ? (abar - 1.0f) * ia[j] : zoh_input_coef_log2(dt, u, abar, ia[j]);
+                        beta = zoh_input_coef_log2(dt, u, abar, ia[j]);
                     }
                     const float hp = k == 0 ? h[j] : hs[k - 1][j];
-                    const float lam = __builtin_fmaf(dys, Cv[j], kap[j]);
+                    const double lam64 = kap[j] + (double)(dys * Cv[j]);
+                    const float lam = (float)lam64;
                     const float dab = lam * hp;                 // ∂L/∂Ā_t
                     const float dbe = lam * (Bv[j] * xt);       // ∂L/∂β_t
                     rb[j] = lam * beta * xt;                    // dB partial (this channel)
@@ -522,7 +524,7 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
                     gx = __builtin_fmaf(lam * beta, Bv[j], gx);
                     gd = __builtin_fmaf(__builtin_fmaf(dab, Av[j], dbe), abar, gd);
                     gA[j] = __builtin_fmaf(dab * abar, dt, __builtin_fmaf(dbe, dbeta_da(dt, u, abar, beta, ia[j]), gA[j]));
-                    kap[j] = abar * lam;
+                    kap[j] = __builtin_fma((double)(beta * Av[j]), lam64, lam64);  // λ + (Ā − 1)·λ
                 }
                 gx = __builtin_fmaf(dys, dskip, group_sum<G>(gx));
                 gd = group_sum<G>(gd);
@@ -555,7 +557,7 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
         if (seg == 0 && a.dh0) {
 #pragma unroll
             for (int j = 0; j < NPL; ++j)
-                if (j < nvalid) a.dh0[sidx + j] = kap[j];
+                if (j < nvalid) a.dh0[sidx + j] = (float)kap[j];
         }
     }
 }
@@ -600,12 +602,8 @@ hipError_t launch_bwd_typed(BwdArgs args, int64_t ncb, int n_seg, hipStream_t st
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((scan_bwd_kernel<T, G, NPL, false, true>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0,
-                       stream, args);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_bwd_kernel<T, G, NPL, false, false>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0,
-                       stream, args);
+    hipLaunchKernelGGL((scan_bwd_kernel<T, G, NPL, false>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0, stream,
+                       args);
     return hipGetLastError();
 }
 

@@ -10,12 +10,18 @@
 //     owns CW = 64 / G channels of one batch row for one time segment; each channel is owned by G
 //     adjacent lanes and lane g keeps the NPL states [g*NPL, (g+1)*NPL) of it in registers, walking
 //     time in order, so the recurrence never leaves registers.
-//   * Per (t, n) the fast path issues one exp and six fp32 VALU operations. With the scaled state
+//   * Per (t, n) the common path issues one exp and six fp32 VALU operations. With the scaled state
 //     s = A·h the ZOH input needs no division:  s_t = s_{t−1} + (Ā − 1)·(s_{t−1} + B x),
-//     and the readout is Σ_n (C_n / A_n)·s_n. Ā − 1 is exact in fp32 (Sterbenz) and damps the
-//     rounding of s + Bx. A wavefront holding a channel with |A| < 2^-10 takes (by a wave-uniform
-//     branch) an unscaled path whose input coefficient comes from the series of (e^v − 1)/v near
-//     v = 0 (the A = 0 limit is Δ·B).
+//     and the readout is Σ_n (C_n / A_n)·s_n. The subtraction Ā − 1 is exact, but Ā itself is a
+//     float near 1 whose last-place error (about 2^-24) becomes a relative error of about
+//     2^-24/|Δ·A| in the input coefficient. So every tile is classified, per wavefront: if some
+//     channel of the wavefront has a mean |Δ·A·log2 e| over the tile below a small threshold, the
+//     tile runs with the coefficient taken per step from the cubic series of 2^u − 1 wherever
+//     |u| < 1/16 (the accurate tile). In a tile that keeps Ā − 1, the per-step errors add in
+//     quadrature against increments of mean size at least the threshold, which bounds the state's
+//     relative error near 2^-24 over the threshold. States with A = 0 (|A| < 2^-64) keep h itself
+//     (scale 1) and take the limit Ā = 1, B̄ = Δ·B; a wavefront holding one runs every tile in a third
+//     mode that adds that case.
 //   * Readout across the G lanes of a channel: each lane writes its partial sums of a group of 2U
 //     timesteps to LDS, and lane g reads back the G partials of the timesteps ≡ g (mod G) — a
 //     transpose through LDS that costs G − 1 adds per element instead of a butterfly on every
@@ -44,7 +50,16 @@
 namespace ssm {
 namespace {
 
-constexpr float kSafeAbsA = 1.0f / 1024.0f;  // |A| below this takes the unscaled path
+constexpr float kZeroAbsA = 5.421010862e-20f;  // 2^-64: |A| below this takes the A = 0 limit
+constexpr float kPolyU = 1.0f / 16.0f;         // |u| below this: 2^u − 1 from its series (accurate tiles)
+// 2^u − 1 = u·(c1 + u·(c2 + u·c3)) + O(u^4): c_k = ln(2)^k / k!; relative error below 4e-6 at |u| = 1/16
+constexpr float kPolyC1 = 0.693147180559945f;
+constexpr float kPolyC2 = 0.240226506959101f;
+constexpr float kPolyC3 = 0.0555041086648216f;
+// A tile runs accurate when some valid state of the wavefront has a mean |u| = |Δ·A·log2 e| over the tile
+// below this. Kept tiles then have a relative state error of about 2^-24 / (threshold · ln 2): 1e-5 for
+// fp32 storage (tolerance 1e-4), 3e-4 for bf16 storage (tolerance 2e-2, itself below bf16's own rounding).
+template <typename T> constexpr float class_mean_u() { return sizeof(T) == 2 ? 1.0f / 4096.0f : 1.0f / 128.0f; }
 
 // Timesteps per tile: 64 bytes of every row per tile for either storage type.
 template <typename T> constexpr int tile_len() { return sizeof(T) == 2 ? 32 : 16; }
@@ -78,7 +93,7 @@ struct FwdArgs {
 // (4, 8, 16); AGG: aggregate pass (segment end state from zero and Π Ā, no readout). CK: the
 // output pass of a call that wants only the checkpoints (the gradient's forward), so it carries the
 // state in and stores it every ck_len steps but has no readout.
-template <typename T, int G, int NPL, bool AGG, bool SAFE, bool CK = false>
+template <typename T, int G, int NPL, bool AGG, bool CK = false>
 __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
     constexpr bool RO = !AGG && !CK;                     // readout, gate and y
     constexpr int kTile = tile_len<T>();
@@ -138,19 +153,29 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
     const int nvalid = (N - n0) < NPL ? (N - n0) : NPL;  // <= 0 for a lane past the last state
     const int64_t row = bi * a.d + ch;
     const int64_t sidx = row * a.N + n0;                  // this lane's first state in [b][d][N]
-    float Av[NPL], a2[NPL], ia[NPL], s[NPL];
-    bool small_a = false;
+    // sc: the state's scale (A, or 1 for a state at the A = 0 limit, which keeps h itself); sm: 1, or
+    // 0 for such a state, whose input B·x does not see the state
+    float sc[NPL], a2[NPL], ia[NPL], sm[NPL], s[NPL];
+    bool zero[NPL];
+    bool zero_any = false;
+    float amin = __builtin_inff();  // smallest |A·log2 e| among this lane's valid states
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
         const bool ok = ch_ok && j < nvalid;
         const float av = load_or(a.A, ch * a.N + n0 + j, ok, -1.0f);  // idle states: A = −1 with B = C = 0
-        Av[j] = av;
-        a2[j] = av * kLog2e;
-        ia[j] = 1.0f / av;
-        small_a |= __builtin_fabsf(av) < kSafeAbsA;
+        zero[j] = __builtin_fabsf(av) < kZeroAbsA;
+        sc[j] = zero[j] ? 1.0f : av;
+        a2[j] = zero[j] ? 0.0f : av * kLog2e;
+        ia[j] = 1.0f / sc[j];
+        sm[j] = zero[j] ? 0.0f : 1.0f;
+        zero_any |= zero[j];
+        if (ok) amin = __builtin_fminf(amin, __builtin_fabsf(a2[j]));
         s[j] = 0.0f;  // the aggregate pass always scans its segment from the zero state
     }
-    if (__any(small_a) != SAFE) return;  // wave-uniform: the other variant owns this unit
+    // a tile whose Δ-sum over this lane's channel falls below thr_sum runs accurate (amin = 0 gives +inf:
+    // always; a lane with no valid state gets 0: never)
+    const float thr_sum = (float)tile_len<T>() * class_mean_u<T>() / amin;
+    const bool wave_zero = __any(zero_any);  // wave-uniform: every tile runs in the A = 0 mode
     // carry-in of the output pass: the initial state, a stored carry, or the chain of the aggregates
     // of the segments before this one: h ← P_k·h + E_k for k = 0 .. seg−1
     auto load_state = [&](const float *base, float (&o)[NPL]) {  // o = base[sidx .. sidx + NPL), zeros past N
@@ -185,10 +210,8 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
             }
         }
     }
-    if constexpr (!SAFE) {
 #pragma unroll
-        for (int j = 0; j < NPL; ++j) s[j] *= Av[j];  // scaled state s = A·h
-    }
+    for (int j = 0; j < NPL; ++j) s[j] *= sc[j];  // scaled state s = A·h (h itself at the A = 0 limit)
     const float dskip = (RO && a.D) ? load_or(a.D, ch, ch_ok, 0.0f) : 0.0f;
 
     // ---- tile prefetch into registers, and from there into LDS ----
@@ -311,23 +334,29 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
         }
     };
     float dsum = 0.0f;
-    // One timestep of the recurrence; returns this lane's share of the readout.
-    auto compute_step = [&](const Sub &cur) {
+    // One timestep of the recurrence; returns this lane's share of the readout. MODE 0 takes the input
+    // coefficient Ā − 1 as computed; 1 takes it from the series of 2^u − 1 where |u| < kPolyU; 2 does as
+    // 1 and gives the states at the A = 0 limit Ā = 1, B̄ = Δ·B.
+    auto compute_step = [&](auto mode_c, const Sub &cur) {
+        constexpr int MODE = decltype(mode_c)::value;
         const float xt = cur.x, dt = cur.d;
         float acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
             const float u = dt * a2[j];            // Δ·A·log2(e)
-            const float abar = exp2_fast(u);
-            if constexpr (!SAFE) {
-                const float pre = __builtin_fmaf(cur.B[j], xt, s[j]);  // s + B x
-                s[j] = __builtin_fmaf(abar - 1.0f, pre, s[j]);         // s + (Ā − 1)(s + B x)
-                if constexpr (RO) acc = __builtin_fmaf(cur.C[j] * ia[j], s[j], acc);
-            } else {
-                const float kc = zoh_input_coef_log2(dt, u, abar, ia[j]);
-                s[j] = __builtin_fmaf(abar, s[j], kc * (cur.B[j] * xt));  // Ā h + B̄ x
-                if constexpr (RO) acc = __builtin_fmaf(cur.C[j], s[j], acc);
+            float em1 = exp2_fast(u) - 1.0f;       // Ā − 1
+            float sj = s[j];
+            if constexpr (MODE >= 1) {
+                const float p = __builtin_fmaf(__builtin_fmaf(u, kPolyC3, kPolyC2), u, kPolyC1);
+                em1 = __builtin_fabsf(u) < kPolyU ? u * p : em1;
             }
+            if constexpr (MODE == 2) {
+                em1 = zero[j] ? dt : em1;
+                sj *= sm[j];
+            }
+            const float pre = __builtin_fmaf(cur.B[j], xt, sj);  // s + B x (B x alone at A = 0)
+            s[j] = __builtin_fmaf(em1, pre, s[j]);              // s + (Ā − 1)(s + B x)
+            if constexpr (RO) acc = __builtin_fmaf(cur.C[j] * ia[j], s[j], acc);
         }
         if constexpr (AGG) dsum += dt;
         return acc;
@@ -376,7 +405,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
         for (int j = 0; j < NPL; j += 4) {
             float hv[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) hv[q] = SAFE ? s[j + q] : s[j + q] * ia[j + q];
+            for (int q = 0; q < 4; ++q) hv[q] = s[j + q] * ia[j + q];
             if (a.vec_state && j + 4 <= nvalid) {
                 *reinterpret_cast<float4 *>(dst + j) = make_float4(hv[0], hv[1], hv[2], hv[3]);
             } else {
@@ -386,7 +415,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
             }
         }
     };
-    auto scan_tile = [&](int it) {
+    auto scan_tile = [&](auto mode_c, int it) {
         const int64_t t0tile = t_begin + (int64_t)it * kTile;
         T *const ywin = ybuf + c * kYPitch + (it & 1) * kTile + g;
         float p[kGrp], r[kGrp];
@@ -396,12 +425,14 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
         constexpr bool kGroupLocal = sizeof(T) == 2;
         Sub sb[2];
         if constexpr (!kGroupLocal) load_sub(0, sb[0]);
-        // the output pass unrolls the tile (LDS offsets become immediates); the other passes unroll
-        // two readout groups at a time (a whole tile there doubles the fp32 aggregate pass's registers)
-        constexpr int kUnroll = RO ? kTile / kGrp : 2;
+        // the output pass unrolls the tile in its common mode (LDS offsets become immediates); the other
+        // passes and the rarer accurate modes unroll two readout groups at a time (whole tiles there
+        // would set the kernel's register budget: the fp32 aggregate pass's doubles)
+        constexpr int MODE = decltype(mode_c)::value;
+        constexpr int kUnroll = (RO && MODE == 0) ? kTile / kGrp : 2;
 #pragma unroll kUnroll
         for (int t = 0; t < kTile; t += kGrp) {
-            if constexpr (CK || SAFE) {  // the fast output pass never runs with checkpoints
+            if constexpr (CK) {  // the output pass never runs with checkpoints
                 if (a.ckpt && t % a.ck_len == 0 && t0tile + t < t_end) store_ckpt((t0tile + t) / a.ck_len);
             }
             if constexpr (kGroupLocal) load_sub(t, sb[0]);
@@ -414,7 +445,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
                     load_sub(tn, sb[(k + 1) & 1]);
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
-                p[k] = compute_step(sb[k & 1]);
+                p[k] = compute_step(mode_c, sb[k & 1]);
             }
             if constexpr (RO) {
                 if constexpr (G == 1) {
@@ -429,6 +460,22 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
             }
         }
     };
+    // Mode of the tile now in LDS: the A = 0 mode for the whole unit when it holds such a state, else
+    // accurate when the Δ-sum of some lane's channel over the tile is below that lane's threshold (the G
+    // lanes of a channel each sum a quarter, half or all of the row, then combine).
+    auto tile_mode = [&]() -> int {
+        if (wave_zero) return 2;
+        constexpr int kPer = kTile / G;
+        const float *dr = drow + g * kPer;
+        float sum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kPer; q += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(dr + q);
+            sum += (v.x + v.y) + (v.z + v.w);
+        }
+        sum = group_sum<G>(sum);
+        return __any(sum < thr_sum) ? 1 : 0;
+    };
     auto run = [&]() {
         load_tile(t_begin);
         store_tile();
@@ -437,7 +484,14 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
 #pragma unroll 1
         for (int it = 0; it < ntiles; ++it) {
             const int64_t t0 = t_begin + (int64_t)it * kTile;
-            scan_tile(it);
+            const int mode = tile_mode();
+            if (mode == 0) {
+                scan_tile(std::integral_constant<int, 0>{}, it);
+            } else if (mode == 1) {
+                scan_tile(std::integral_constant<int, 1>{}, it);
+            } else {
+                scan_tile(std::integral_constant<int, 2>{}, it);
+            }
             if constexpr (RO) {
                 if (yg && ((it & 1) || it + 1 == ntiles)) {  // the output window is complete
                     const int64_t tw0 = t0 - (it & 1) * kTile;
@@ -461,7 +515,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
             if (j >= nvalid) continue;
-            const float h = SAFE ? s[j] : s[j] * ia[j];
+            const float h = s[j] * ia[j];
             const int64_t idx = sidx + j;
             if constexpr (AGG) {
                 a.agg_P[seg * bd * a.N + idx] = exp2_fast(a2[j] * dsum);  // Π Ā = exp(A ΣΔ)
@@ -473,37 +527,17 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
     }
 }
 
-// One wavefront per unit (a block of 64/G channels of one batch row over one time segment). The
-// fast variant takes every unit whose channels all have |A| >= 2^-10 and leaves the others at once.
-// The small-|A| variant runs one wavefront per channel block (A depends on nothing else): it tests
-// the block's A once and, only if the test holds, scans the block in every batch row in turn, each
-// over the whole sequence as a single segment, so its one launch costs little when, as usual, it
-// has nothing to do. Keeping the rare path in a kernel of its own keeps the common kernel's
-// register budget small.
-template <typename T, int G, int NPL, bool AGG, bool SAFE>
-__global__ __launch_bounds__(kWave, (G == 4 && NPL == 4 && !SAFE) ? 3 : 1) void scan_fwd_kernel(FwdArgs a,
-                                                                                               int64_t units) {
-    if constexpr (!SAFE) {
-        scan_unit<T, G, NPL, AGG, false>(a, blockIdx.x);
-    } else {
-        constexpr int CW = kWave / G;
-        const int64_t cbi = blockIdx.x;  // channel block within a batch row
-        const int64_t ch = cbi * CW + threadIdx.x / G;
-        const int n0 = (threadIdx.x % G) * NPL;
-        bool small_a = false;
-#pragma unroll
-        for (int j = 0; j < NPL; ++j)
-            small_a |= __builtin_fabsf(load_or(a.A, ch * a.N + n0 + j, ch < a.d && n0 + j < a.N, -1.0f)) < kSafeAbsA;
-        if (!__any(small_a)) return;
-        for (int64_t u = cbi; u < units; u += a.n_cw) scan_unit<T, G, NPL, AGG, true>(a, u);
-    }
+// One wavefront per unit (a block of 64/G channels of one batch row over one time segment).
+template <typename T, int G, int NPL, bool AGG>
+__global__ __launch_bounds__(kWave, (G == 4 && NPL == 4) ? 3 : 1) void scan_fwd_kernel(FwdArgs a) {
+    scan_unit<T, G, NPL, AGG>(a, blockIdx.x);
 }
 
 // Output pass of the gradient's checkpointing forward (fast path): carries the state in and stores it
 // every ck_len steps, with no readout and no y.
 template <typename T, int G, int NPL>
 __global__ __launch_bounds__(kWave, (G == 4 && NPL == 4) ? 3 : 1) void scan_ckpt_kernel(FwdArgs a) {
-    scan_unit<T, G, NPL, false, false, true>(a, blockIdx.x);
+    scan_unit<T, G, NPL, false, true>(a, blockIdx.x);
 }
 
 // Chunk carry for many segments: h_in[k] = P[k]·h_in[k−1] + E[k] per (b, d, n), from the
@@ -529,8 +563,8 @@ template <typename T, int G, int NPL>
 hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLaunch &p, hipStream_t stream) {
     hipError_t e = hipSuccess;
     if (n_seg > 1) {
-        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, true, false>), dim3((unsigned)((n_seg - 1) * ncb)), dim3(kWave),
-                           0, stream, args, (int64_t)(n_seg - 1) * ncb);
+        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, true>), dim3((unsigned)((n_seg - 1) * ncb)), dim3(kWave), 0,
+                           stream, args);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (args.h_in) {
@@ -546,17 +580,9 @@ hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLa
     if (args.y == nullptr && args.ckpt != nullptr) {
         hipLaunchKernelGGL((scan_ckpt_kernel<T, G, NPL>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0, stream, args);
     } else {
-        hipExtLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false, false>), dim3((unsigned)(n_seg * ncb)), dim3(kWave),
-                              0, stream, p.ev_begin, p.ev_end, 0u, args, (int64_t)n_seg * ncb);
+        hipExtLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0,
+                              stream, p.ev_begin, p.ev_end, 0u, args);
     }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // Channel blocks with a small |A| run as one segment each (no aggregates needed), so a single
-    // launch covers them; it depends on nothing above and writes only their outputs.
-    FwdArgs whole = args;
-    whole.seg_len = p.L;
-    hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false, true>), dim3((unsigned)args.n_cw), dim3(kWave), 0, stream,
-                       whole, ncb);
     return hipGetLastError();
 }
 

@@ -215,19 +215,34 @@ def decode_step_inputs(w: Workload | str, step: int, seed: int = 0) -> dict:
 
 
 def random_prefill(b, d, L, N, dtype="f32", gate=True, seed=0, delta_mu=-3.0, delta_sigma=1.0,
-                   a_kind="neg_index", with_D=True, a_zero_frac=0.0) -> dict:
+                   a_kind="neg_index", with_D=True, a_zero_frac=0.0, a_value=None, delta_value=None) -> dict:
     """Small random prefill inputs with the Mamba-shaped distributions, for edge-case tests.
-    a_zero_frac > 0 sets that fraction of A entries to exactly 0 (the ZOH limit case)."""
+    a_kind: "neg_index" (-(n+1)), "neg_index_u" (-(n+1)·U(0.5, 1.5)), "random" (-U(0.05, 4)) or
+    "small" (-U(2^-10, 0.05), the regime where Δ·A is small). a_value / delta_value, when given, make
+    A / Δ that constant everywhere. a_zero_frac > 0 sets that fraction of A entries to exactly 0 (the
+    ZOH limit case)."""
     tag = f"random_{b}_{d}_{L}_{N}_{dtype}_{int(gate)}_{delta_mu}_{delta_sigma}_{a_kind}_{a_zero_frac}"
+    if a_value is not None or delta_value is not None:
+        tag += f"_{a_value}_{delta_value}"
     g = lambda t: _gen(seed, tag, t)
-    A = _a_matrix(seed, tag, d, N, a_kind) if a_kind != "random" else \
-        (-g("A").uniform(0.05, 4.0, size=(d, N))).astype(np.float32)
+    if a_value is not None:
+        A = np.full((d, N), a_value, dtype=np.float32)
+    elif a_kind == "random":
+        A = (-g("A").uniform(0.05, 4.0, size=(d, N))).astype(np.float32)
+    elif a_kind == "small":
+        A = (-g("A").uniform(2.0 ** -10, 0.05, size=(d, N))).astype(np.float32)
+    else:
+        A = _a_matrix(seed, tag, d, N, a_kind)
     if a_zero_frac > 0:
         mask = g("A0").uniform(size=(d, N)) < a_zero_frac
         A = np.where(mask, np.float32(0.0), A).astype(np.float32)
+    if delta_value is not None:
+        delta = store(np.full((b, d, L), float(delta_value)), dtype)
+    else:
+        delta = store(_softplus(g("delta").normal(delta_mu, delta_sigma, size=(b, d, L))), dtype)
     return {
         "x": store(g("x").standard_normal((b, d, L)), dtype),
-        "delta": store(_softplus(g("delta").normal(delta_mu, delta_sigma, size=(b, d, L))), dtype),
+        "delta": delta,
         "z": store(g("z").standard_normal((b, d, L)), dtype) if gate else None,
         "A": A,
         "B": store(g("B").standard_normal((b, L, N)), dtype),

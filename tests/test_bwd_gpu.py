@@ -1,9 +1,8 @@
 """GPU parity of the gradient pass (ssm_scan_bwd through the C ABI) against the fp64 gradient oracle.
 
-Bar (derived in the design notes): per-element gradients (dx, dΔ, dz, d initial state) within
-τ·(1 + |ref|) element by element; the sums over many terms (dA over b and t, dB and dC over d, dD over
-b and t) within τ·(1 + max|ref|) over the tensor. τ = 1e-4 for fp32 storage, 2e-2 for bf16 storage.
-Every result must be finite.
+Bar: every output element by element within τ·(1 + |ref|): the per-element gradients (dx, dΔ, dz,
+d initial state) and the summed ones (dA over b and t, dB and dC over d, dD over b and t) alike.
+τ = 1e-4 for fp32 storage, 2e-2 for bf16 storage. Every result must be finite.
 """
 import numpy as np
 import pytest
@@ -41,10 +40,12 @@ def _check_elementwise(got, ref, tau, what):
 
 
 def _check_sum(got, ref, tau, what):
-    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    """A summed gradient, element by element like the others (its error relative to the largest
+    entry is printed too, for the record)."""
     scale = 1.0 + float(np.abs(ref).max()) if ref.size else 1.0
-    worst = float(np.abs(got - ref).max()) / scale if ref.size else 0.0
-    assert worst <= tau, f"{what}: max abs err / (1 + max|ref|) = {worst:.3e} > {tau}"
+    tensor_rel = float(np.abs(got - ref).max()) / scale if ref.size else 0.0
+    worst = _check_elementwise(got, ref, tau, what)
+    print(f"  {what}: elementwise {worst:.2e}, against the largest entry {tensor_rel:.2e}", flush=True)
     return worst
 
 
@@ -112,6 +113,16 @@ def test_bwd_zero_and_tiny_A(dt):
     run_case(inp, dy_seed=3, what=f"zero/tiny A {dt}")
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_bwd_slow_channels(dt):
+    """Slow channels (A ~ -U(2^-10, 0.05), Δ = softplus(N(-5, 1))): β keeps its relative accuracy where
+    |ΔA| is small for many steps, in the gradient pass too."""
+    inp = I.random_prefill(2, 48, 1024, 16, dtype=dt, seed=19, a_kind="small", delta_mu=-5.0)
+    rng = np.random.default_rng(9)
+    run_case(inp, h0=(rng.standard_normal((2, 48, 16)) * 0.5).astype(np.float32), dy_seed=5,
+             what=f"slow channels {dt}")
+
+
 def test_bwd_mamba130m_workload():
     """The 130M-like fp32 workload at full size, in the plan the library picks for it."""
     inp = I.prefill_inputs(I.WORKLOADS["mamba130m_f32_b4_d1536_L2048_N16"])
@@ -143,3 +154,42 @@ def test_bwd_mamba1p4b_sampled_rows():
             got = from_torch(g[k][ib, ch])
             worst[k] = max(worst.get(k, 0.0), _check_elementwise(got, ref[rk][0, 0], tau, f"1.4B-like row ({ib}, {ch}) {k}"))
     print("[bwd mamba1p4b sampled] " + " ".join(f"{k}={v:.1e}" for k, v in worst.items()), flush=True)
+
+
+def test_bwd_mamba1p4b_sampled_sums():
+    """The summed gradients at the 1.4B-like bf16 size, on samples the oracle can afford: dA and dD of
+    sampled channels (the oracle over every batch row of each channel) and dB, dC of one whole batch row
+    (the oracle over all 4096 channels of that row, in channel blocks whose sums are added)."""
+    import concurrent.futures as cf
+
+    dt = "bf16"
+    inp = I.prefill_inputs(I.WORKLOADS["mamba1p4b_bf16_b8_d4096_L4096_N16"])
+    b, d, L = inp["x"].shape
+    rng = np.random.default_rng(23)
+    dy = I.store(rng.standard_normal((b, d, L)), dt)
+    t = upload(inp)
+    g = api.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], dy=_to_dev(dy, dt))
+    torch.cuda.synchronize()
+    tau = TAU[dt]
+    w = lambda a, bs, cs: I.widen(a[bs, cs], dt)
+
+    def ref_block(bs, cs):
+        return oracle.scan_bwd(w(inp["x"], bs, cs), w(inp["delta"], bs, cs), inp["A"][cs], I.widen(inp["B"][bs], dt),
+                               I.widen(inp["C"][bs], dt), inp["D"][cs], w(inp["z"], bs, cs), h0=None,
+                               dy=w(dy, bs, cs), dh_final=None)
+
+    chans = [0, d - 1] + [int(c) for c in rng.integers(1, d - 1, size=4)]
+    ib = int(rng.integers(b))
+    blocks = [slice(c0, c0 + 256) for c0 in range(0, d, 256)]
+    with cf.ThreadPoolExecutor(16) as ex:
+        per_chan = list(ex.map(lambda ch: ref_block(slice(0, b), slice(ch, ch + 1)), chans))
+        per_block = list(ex.map(lambda cs: ref_block(slice(ib, ib + 1), cs), blocks))
+    gA, gD = from_torch(g["dA"]), from_torch(g["dD"])
+    worst = {}
+    for ch, ref in zip(chans, per_chan):
+        worst["dA"] = max(worst.get("dA", 0.0), _check_elementwise(gA[ch], ref["dA"][0], tau, f"1.4B-like dA[{ch}]"))
+        worst["dD"] = max(worst.get("dD", 0.0), _check_elementwise(gD[ch:ch + 1], ref["dD"], tau, f"1.4B-like dD[{ch}]"))
+    for k in ("dB", "dC"):
+        ref = sum(r[k][0] for r in per_block)
+        worst[k] = _check_elementwise(from_torch(g[k][ib]), ref, tau, f"1.4B-like {k}[{ib}]")
+    print("[bwd mamba1p4b sampled sums] " + " ".join(f"{k}={v:.1e}" for k, v in worst.items()), flush=True)

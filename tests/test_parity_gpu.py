@@ -136,12 +136,82 @@ def test_small_shapes(case):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_zero_and_tiny_A_take_the_limit(dt):
-    """A = 0 entries (ZOH limit Δ·B) and |A| < 2^-10 entries mixed with ordinary ones."""
+    """A = 0 entries (ZOH limit Δ·B) and tiny |A| entries mixed with ordinary ones."""
     inp = I.random_prefill(2, 96, 300, 16, dtype=dt, seed=5, a_zero_frac=0.25)
     inp["A"][3, :4] = np.float32(1e-7)
     inp["A"][50, 7] = np.float32(-3e-5)
     y, h = run_fwd(inp, seg_len=128)
     check_rows(inp, y, h, all_rows(2, 96), f"zero/tiny A {dt}")
+
+
+# Slow channels: |Δ·A| small for many steps in a row. There B̄ = (Ā − 1)/A·B from a float Ā near 1 would
+# lose its relative accuracy (page "Mambaとは？Transformer以外の系列モデル", section 状態空間モデルを
+# 一つの式から理解する, defines B̄ = (ΔA)⁻¹(exp(ΔA) − I)ΔB); the kernel's accurate tiles must hold the bars.
+SLOW = {
+    "A=-0.01,dt=0.01": dict(L=2048, a_value=-0.01, delta_value=0.01),
+    "A=-0.002,dt=0.005": dict(L=4096, a_value=-0.002, delta_value=0.005),
+    "A~-U(2^-10,0.05),dt=softplus(N(-5,1))": dict(L=2048, a_kind="small", delta_mu=-5.0),
+}
+
+
+def slow_inputs(name, dt, b=2, d=64, seed=31):
+    kw = dict(SLOW[name])
+    L = kw.pop("L")
+    return I.random_prefill(b, d, L, 16, dtype=dt, seed=seed, **kw)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("name", list(SLOW))
+def test_slow_channels_small_delta_a(name, dt):
+    inp = slow_inputs(name, dt)
+    y, h = run_fwd(inp)
+    check_rows(inp, y, h, all_rows(2, 64), f"slow {name} {dt}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_slow_channels_with_time_segments_and_initial_state(dt):
+    """The slow regime through a time split (aggregates from accurate tiles) with an initial state."""
+    inp = slow_inputs("A~-U(2^-10,0.05),dt=softplus(N(-5,1))", dt, b=2, d=48)
+    h0 = (np.random.default_rng(4).standard_normal((2, 48, 16)) * 0.5).astype(np.float32)
+    t = upload(inp)
+    y, h = api.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], seg_len=256,
+                            initial_state=torch.from_numpy(h0).cuda())
+    torch.cuda.synchronize()
+    check_rows(inp, from_torch(y), from_torch(h), all_rows(2, 48), f"slow + 8 segments + h0 {dt}",
+               h0=h0.astype(np.float64))
+
+
+def test_slow_and_fast_channels_in_one_wavefront():
+    """Slow channels (A ~ -U(2^-10, 0.05)) interleaved with ordinary ones (A = -(n+1)) in every
+    wavefront, and an A = 0 state in one channel: tiles switch modes per wavefront."""
+    inp = slow_inputs("A~-U(2^-10,0.05),dt=softplus(N(-5,1))", "f32", b=1, d=96)
+    inp["delta"] = I.store(np.logaddexp(0.0, np.random.default_rng(6).normal(-3.0, 1.5, size=(1, 96, 2048))), "f32")
+    inp["A"][::2] = -(np.arange(16, dtype=np.float32) + 1.0)
+    inp["A"][40:64] = -(np.arange(16, dtype=np.float32) + 1.0)  # a whole wavefront of ordinary channels
+    inp["A"][70, 5] = 0.0
+    y, h = run_fwd(inp, seg_len=512)
+    check_rows(inp, y, h, all_rows(1, 96), "slow/fast mix")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_slow_channels_prefill_equals_decode(dt):
+    """Prefill and decode agree in the slow regime (decode always takes the series near ΔA = 0)."""
+    b, d, L, N = 1, 64, 192, 16
+    inp = I.random_prefill(b, d, L, N, dtype=dt, seed=14, a_kind="small", delta_mu=-5.0)
+    t = upload(inp)
+    y_pf, h_pf = api.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"])
+    state = torch.zeros((b, d, N), dtype=torch.float32, device="cuda")
+    ys = []
+    for s in range(L):
+        ys.append(api.ssm_scan_step(state, t["x"][:, :, s].contiguous(), t["delta"][:, :, s].contiguous(), t["A"],
+                                    t["B"][:, s].contiguous(), t["C"][:, s].contiguous(), t["D"],
+                                    t["z"][:, :, s].contiguous()))
+    torch.cuda.synchronize()
+    tau = TAU[dt]
+    assert_close(from_torch(torch.stack(ys, dim=2)), from_torch(y_pf), tau, "slow decode vs prefill y")
+    assert_close(from_torch(state), from_torch(h_pf), 1e-4, "slow decode vs prefill state")
+    yr, hr = oracle_prefill_rows(inp, all_rows(b, d))
+    assert_close(from_torch(state).reshape(b * d, N), hr, 1e-4, "slow decode state vs oracle")
 
 
 def test_running_sum_is_exact_on_gpu():
