@@ -39,7 +39,7 @@
  *     library creates on the current device at its first such call, and return it there at the
  *     end of the call. That pool keeps freed scratch (its release threshold is at the maximum), so
  *     repeated calls reuse it; it lives until the process ends. The device's default pool is not
- *     touched.
+ *     touched. ssm_scan_fwd_noalloc takes no scratch from any pool (see there).
  *   - NaN and Inf inputs propagate; nothing is clamped.
  */
 #ifndef SSM_SCAN_H
@@ -69,7 +69,8 @@ typedef enum {
     SSM_ERR_SHAPE = 2,       /* a size is out of range (b, d, N < 1; L < 0; overflow)         */
     SSM_ERR_UNSUPPORTED = 3, /* N > SSM_MAX_N, unknown dtype, or an option value not accepted */
     SSM_ERR_HIP = 4,         /* a HIP runtime call or a launch failed                          */
-    SSM_ERR_ALIAS = 5        /* an output overlaps an input or another output                 */
+    SSM_ERR_ALIAS = 5,       /* an output overlaps an input or another output                 */
+    SSM_ERR_SCRATCH = 6      /* ssm_scan_fwd_noalloc: the plan needs more than its fixed scratch */
 } ssm_status_t;
 
 /*
@@ -258,6 +259,25 @@ typedef struct {
 
 SSM_API ssm_status_t ssm_scan_fwd_plan(int64_t b, int64_t d, int64_t L, int64_t N, ssm_dtype_t dtype,
                                const ssm_fwd_opts_t *opts, ssm_fwd_plan_t *plan);
+
+/*
+ * ssm_scan_fwd_ex that allocates nothing, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, and harnesses that forbid allocation. Same arguments, plan,
+ * kernels and results as ssm_scan_fwd_ex. The scratch of a time-split plan (the segment aggregates,
+ * and the carries past 16 segments: ssm_fwd_plan_t.scratch_bytes) lives in a fixed device array of
+ * SSM_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds from its first use until the
+ * process ends; no hipMalloc, hipFree or allocating library routine is called. A plan needing more
+ * returns SSM_ERR_SCRATCH and launches nothing (a longer seg_len in opts shrinks it). Every call on a
+ * GPU shares that GPU's array, which keeps the last call's contents: calls that overlap on one GPU
+ * (different streams, or host threads) race and must be serialised by the caller. Nothing in the
+ * array needs clearing: a call writes every scratch word before reading it. Other errors as for
+ * ssm_scan_fwd.
+ */
+#define SSM_NOALLOC_SCRATCH_BYTES (32ll << 20)
+SSM_API ssm_status_t ssm_scan_fwd_noalloc(const void *x, const void *delta, const float *A, const void *B,
+                                          const void *C, const float *D, const void *z, void *y,
+                                          float *final_state, int64_t b, int64_t d, int64_t L, int64_t N,
+                                          ssm_dtype_t dtype, hipStream_t stream, const ssm_fwd_opts_t *opts);
 
 /* Human-readable name of a status code (static string, never NULL). */
 SSM_API const char *ssm_status_string(ssm_status_t s);

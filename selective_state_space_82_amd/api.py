@@ -17,7 +17,9 @@ _LIB_PATH = os.path.join(_PKG, "libssmscan.so")
 SSM_F32, SSM_BF16 = 0, 1
 SSM_OK = 0
 STATUS_NAMES = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_UNSUPPORTED",
-                4: "SSM_ERR_HIP", 5: "SSM_ERR_ALIAS"}
+                4: "SSM_ERR_HIP", 5: "SSM_ERR_ALIAS", 6: "SSM_ERR_SCRATCH"}
+SSM_ERR_SCRATCH = 6
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class SsmError(RuntimeError):
@@ -64,6 +66,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_fwd.restype = i32
     L.ssm_scan_fwd_ex.argtypes = fwd + [ctypes.POINTER(FwdOpts)]
     L.ssm_scan_fwd_ex.restype = i32
+    L.ssm_scan_fwd_noalloc.argtypes = fwd + [ctypes.POINTER(FwdOpts)]
+    L.ssm_scan_fwd_noalloc.restype = i32
     L.ssm_scan_fwd_plan.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(FwdOpts), ctypes.POINTER(FwdPlan)]
     L.ssm_scan_fwd_plan.restype = i32
     L.ssm_scan_step.argtypes = [vp] * 9 + [i64, i64, i64, i32, vp]
@@ -131,11 +135,13 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, *, y=None, final_state=None, return_final_state=True,
-                 seg_len=0, lanes_per_channel=0, initial_state=None, events=None):
+                 seg_len=0, lanes_per_channel=0, initial_state=None, events=None, noalloc=False):
     """Prefill scan. x, delta, z: [b, d, L]; A: [d, N] fp32; B, C: [b, L, N]; D: [d] fp32.
     x, delta, z, B, C share one storage dtype (float32 or bfloat16); y gets it too.
     Returns (y, final_state) (final_state is None when return_final_state is False and none is given).
-    events: optional (begin, end) torch.cuda.Event pair recorded around the output-pass kernel."""
+    events: optional (begin, end) torch.cuda.Event pair recorded around the output-pass kernel.
+    noalloc: call ssm_scan_fwd_noalloc (scratch in the library's fixed device array; y and final_state
+    should then be given, since allocating them here would defeat the purpose)."""
     if x.dim() != 3:
         raise ValueError("x must be [b, d, L]")
     b, d, L = x.shape
@@ -163,7 +169,7 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, *, y=None, final_state=None,
     _check("final_state", final_state, (b, d, N), torch.float32, dev)
     args = [_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), _ptr(final_state),
             b, d, L, N, code, _stream(dev)]
-    if seg_len or lanes_per_channel or initial_state is not None or events is not None:
+    if noalloc or seg_len or lanes_per_channel or initial_state is not None or events is not None:
         o = FwdOpts()
         o.seg_len = int(seg_len)
         o.lanes_per_channel = int(lanes_per_channel)
@@ -171,10 +177,11 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, *, y=None, final_state=None,
         if events is not None:
             o.ev_begin = events[0].cuda_event
             o.ev_end = events[1].cuda_event
-        status = lib().ssm_scan_fwd_ex(*args, ctypes.byref(o))
+        fn = lib().ssm_scan_fwd_noalloc if noalloc else lib().ssm_scan_fwd_ex
+        status = fn(*args, ctypes.byref(o))
     else:
         status = lib().ssm_scan_fwd(*args)
-    _raise(status, "ssm_scan_fwd")
+    _raise(status, "ssm_scan_fwd_noalloc" if noalloc else "ssm_scan_fwd")
     return y, final_state
 
 

@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssmscan.so")
 SOURCES = ["scan_fwd.hip", "scan_bwd.hip", "scan_step.hip", "conv1d.hip", "lti.hip", "ssd.hip", "ssd_scan.hip",
-           "abi.cpp"]
+           "noalloc.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept out of the generated code.

@@ -170,7 +170,8 @@ ssm_status_t check_opts(int64_t N, const ssm_fwd_opts_t *o) {
 
 ssm_status_t fwd_impl(const void *x, const void *delta, const float *A, const void *B, const void *C,
                       const float *D, const void *z, void *y, float *final_state, int64_t b, int64_t d,
-                      int64_t L, int64_t N, ssm_dtype_t dtype, hipStream_t stream, const ssm_fwd_opts_t *o) {
+                      int64_t L, int64_t N, ssm_dtype_t dtype, hipStream_t stream, const ssm_fwd_opts_t *o,
+                      bool noalloc = false) {
     ssm_status_t st = check_fwd_sizes(b, d, L, N, dtype);
     if (st != SSM_OK) return st;
     // With L = 0 nothing but final_state is touched, so the (empty) sequence tensors may be NULL.
@@ -206,6 +207,13 @@ ssm_status_t fwd_impl(const void *x, const void *delta, const float *A, const vo
     p.ev_begin = o ? static_cast<hipEvent_t>(o->ev_begin) : nullptr;
     p.ev_end = o ? static_cast<hipEvent_t>(o->ev_end) : nullptr;
     void *scratch = nullptr;
+    if (noalloc) {
+        // the fixed device array: nothing allocated, nothing to clear (every scratch word a call reads
+        // is written earlier in the same call)
+        if (pl.scratch_bytes > ssm::kNoAllocScratchBytes) return SSM_ERR_SCRATCH;
+        if (pl.scratch_bytes > 0 && ssm::noalloc_scratch(&p.scratch) != hipSuccess) return SSM_ERR_HIP;
+        return ssm::launch_scan_fwd(p, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    }
     if (pl.scratch_bytes > 0) {
         if (scratch_alloc(&scratch, (size_t)pl.scratch_bytes, stream) != hipSuccess) return SSM_ERR_HIP;
         p.scratch = static_cast<float *>(scratch);
@@ -331,6 +339,9 @@ const char *ssm_status_string(ssm_status_t s) {
         case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: N, dtype or an option value is not supported";
         case SSM_ERR_HIP: return "SSM_ERR_HIP: a HIP runtime call or kernel launch failed";
         case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS: an output overlaps an input or another output";
+        case SSM_ERR_SCRATCH:
+            return "SSM_ERR_SCRATCH: the call needs more scratch than ssm_scan_fwd_noalloc holds "
+                   "(SSM_NOALLOC_SCRATCH_BYTES); use fewer time segments or ssm_scan_fwd_ex";
     }
     return "unknown ssm_status_t";
 }
@@ -348,6 +359,13 @@ ssm_status_t ssm_scan_fwd_ex(const void *x, const void *delta, const float *A, c
                              int64_t L, int64_t N, ssm_dtype_t dtype, hipStream_t stream,
                              const ssm_fwd_opts_t *opts) {
     return fwd_impl(x, delta, A, B, C, D, z, y, final_state, b, d, L, N, dtype, stream, opts);
+}
+
+ssm_status_t ssm_scan_fwd_noalloc(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                                  const float *D, const void *z, void *y, float *final_state, int64_t b, int64_t d,
+                                  int64_t L, int64_t N, ssm_dtype_t dtype, hipStream_t stream,
+                                  const ssm_fwd_opts_t *opts) {
+    return fwd_impl(x, delta, A, B, C, D, z, y, final_state, b, d, L, N, dtype, stream, opts, true);
 }
 
 ssm_status_t ssm_scan_fwd_plan(int64_t b, int64_t d, int64_t L, int64_t N, ssm_dtype_t dtype,

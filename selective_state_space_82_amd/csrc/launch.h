@@ -128,6 +128,11 @@ hipError_t launch_scan_fwd(const FwdLaunch &p, hipStream_t stream);
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t stream);
 hipError_t launch_scan_step(const StepLaunch &p, hipStream_t stream);
 
+// Fixed scratch of ssm_scan_fwd_noalloc (SSM_NOALLOC_SCRATCH_BYTES in the public header): its address on
+// the current device, looked up once per device.
+constexpr int64_t kNoAllocScratchBytes = INT64_C(32) << 20;
+hipError_t noalloc_scratch(float **out);
+
 constexpr int kSegQuantum = 32; // time segments are multiples of this many steps
 constexpr int kFoldMaxSeg = 16; // up to this many segments the output pass chains the carry itself
 
