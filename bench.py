@@ -49,7 +49,7 @@ HOST_THREAD_CAP = 16
 GRAD_WORKLOAD = "mamba130m_f32_b4_d1536_L2048_N16"
 SIDE_WORKLOADS = ("mamba130m_f32_b4_d1536_L2048_N16", "mamba1p4b_bf16_b8_d4096_L4096_N16")
 DEFAULT_EXTRA = ("tiny_f32_b1_d8_L128_N4,mamba130m_f32_b4_d1536_L2048_N16,mamba1p4b_bf16_b8_d4096_L4096_N16,"
-                 "decode,grad,conv,lti,ssd")
+                 "decode,grad,conv,frontend,lti,ssd")
 METRIC = "selective-scan GB/s & % of HBM peak; (b·d·L)/s at N=16; decode steps/s"
 
 
@@ -397,6 +397,68 @@ def bench_conv(name, steps, warmup, W=4, quiet=False):
     return res
 
 
+def bench_frontend(name, steps, warmup, W=4, quiet=False):
+    """The fused front end (ssm_scan_fwd_conv: Conv1D + SiLU folded into the scan's staging) against the two
+    launches it replaces (ssm_conv1d_fwd, then ssm_scan_fwd on its output), on the workload's inputs with
+    the Conv1D input standing in for x; and the fused call with Δ's bias and softplus applied inside."""
+    import torch
+    from selective_state_space_82_amd import api
+    from selective_state_space_82_amd import inputs as I
+
+    w = I.WORKLOADS[name]
+    inp = I.prefill_inputs(w)
+    esize = 4 if w.dtype == "f32" else 2
+    nbytes = algorithmic_bytes(w.b, w.d, w.L, w.N, esize, w.gate) + w.d * (W + 1) * 4 + 2 * w.b * w.d * (W - 1) * 4
+    rotate = int(min(8, max(1, -(-2 * MALL_BYTES // nbytes))))
+    rng = np.random.default_rng(7)
+    taps = torch.from_numpy((rng.standard_normal((w.d, W)) * 0.5).astype(np.float32)).cuda()
+    cbias = torch.from_numpy(rng.standard_normal(w.d).astype(np.float32)).cuda()
+    dbias = torch.from_numpy((rng.standard_normal(w.d) * 0.3).astype(np.float32)).cuda()
+    sets = []
+    for _ in range(rotate):
+        t = {k: to_dev(inp[k], "cuda") for k in ("x", "delta", "z", "A", "B", "C", "D")}
+        t["y"] = torch.empty_like(t["x"])
+        t["xc"] = torch.empty_like(t["x"])
+        t["h"] = torch.empty((w.b, w.d, w.N), device="cuda")
+        t["cs_in"] = torch.zeros((w.b, w.d, W - 1), device="cuda")
+        t["cs_out"] = torch.empty((w.b, w.d, W - 1), device="cuda")
+        sets.append(t)
+
+    def timed(fn):
+        warm_up(fn, warmup, EXTRA_WARM_S)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def fused(i, softplus=False):
+        t = sets[i % rotate]
+        api.ssm_scan_fwd_conv(t["x"], taps, t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], conv_bias=cbias,
+                              conv_state_in=t["cs_in"], delta_bias=dbias if softplus else None,
+                              delta_softplus=softplus, y=t["y"], final_state=t["h"], conv_state_out=t["cs_out"])
+
+    def pair(i):
+        t = sets[i % rotate]
+        api.ssm_conv1d_fwd(t["x"], taps, cbias, state_in=t["cs_in"], x_out=t["xc"], state_out=t["cs_out"])
+        api.ssm_scan_fwd(t["xc"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], y=t["y"], final_state=t["h"])
+
+    ms_pair = timed(pair)
+    ms_fused = timed(fused)
+    ms_fused_sp = timed(lambda i: fused(i, True))
+    res = {"pass": "fused_frontend", "workload": name, "W": W, "us_two_launches": ms_pair * 1e3,
+           "us_fused": ms_fused * 1e3, "us_fused_softplus": ms_fused_sp * 1e3, "speedup": ms_pair / ms_fused,
+           "algorithmic_bytes_fused": nbytes, "GBps_fused": nbytes / (ms_fused * 1e-3) / 1e9}
+    if not quiet:
+        print(f"# fused front end {name} (W={W}): {ms_fused * 1e3:.1f} us fused ({ms_fused_sp * 1e3:.1f} us with Δ bias "
+              f"and softplus) against {ms_pair * 1e3:.1f} us for Conv1D then scan", file=sys.stderr, flush=True)
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_decode(name, rotate_states, quiet=False):
     """The decode workload: `steps` successive single-token steps, each with fresh inputs, on one
     state (rotate_states = 1, the literal workload) or cycling through several layer states."""
@@ -552,7 +614,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--extra", default=DEFAULT_EXTRA,
                     help="comma list: 'decode', 'grad' (gradient pass on the 130M-like workload), 'conv' (Conv1D "
-                         "front end), 'lti' (LTI convolution form), 'ssd' (scalar-decay chunked form) "
+                         "front end), 'frontend' (Conv1D fused into the scan, against the two launches), 'lti' "
+                         "(LTI convolution form), 'ssd' (scalar-decay chunked form) "
                          "and/or prefill workload names "
                          "('' for none, 'all' for every one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -598,6 +661,8 @@ def main():
         elif n == "conv":
             for cw in SIDE_WORKLOADS:
                 extra.append(bench_conv(cw, 20, 3))
+        elif n == "frontend":
+            extra.append(bench_frontend("mamba1p4b_bf16_b8_d4096_L4096_N16", 50, 3))
         elif n == args.workload:
             continue
         else:

@@ -82,8 +82,9 @@ typedef enum {
  *   z          [b][d][L] dtype      optional (NULL = no gate)
  *   y          [b][d][L] dtype      required output; must not overlap any input
  *   final_state[b][d][N] fp32       optional output h_{L−1} (NULL = not written)
- *   b, d, N >= 1; L >= 0; N <= SSM_MAX_N. With L = 0 the call writes zeros to final_state and
- *   touches nothing else, so x, delta, A, B, C, y may then be NULL.
+ *   b, d, N >= 1; L >= 0; N <= SSM_MAX_N. With L = 0 the call writes zeros to final_state (with
+ *   ssm_scan_fwd_ex's initial_state: a copy of it) and touches nothing else, so x, delta, A, B, C, y may
+ *   then be NULL.
  *   Errors: SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_UNSUPPORTED, SSM_ERR_ALIAS (nothing launched);
  *   SSM_ERR_HIP when scratch allocation or a launch fails (work already enqueued may have run).
  */
@@ -160,6 +161,58 @@ SSM_API ssm_status_t ssm_conv1d_fwd(const void *xin, const float *w, const float
 SSM_API ssm_status_t ssm_conv1d_step(float *state, const void *xin, const float *w, const float *bias,
                                      void *x_out, int64_t b, int64_t d, int64_t W, int32_t apply_silu,
                                      ssm_dtype_t dtype, hipStream_t stream);
+
+/*
+ * The main branch of the Mamba block from the Conv1D's input to y in one pass: the Conv1D + SiLU of
+ * ssm_conv1d_fwd (apply_silu on) and the scan of ssm_scan_fwd, with the parameter preprocessing folded
+ * into the scan's tile staging (page "Mambaとは？Transformer以外の系列モデル", section hardware-awareとは
+ * memory trafficまで設計すること: parameter generation, discretisation and scan in one kernel, only the
+ * outputs going back to memory; section Mamba blockのarchitecture: Conv1D, SiLU, then the selective SSM).
+ * Per (b, d) and t:
+ *     x_t = silu(c_d + Σ_{k<W} conv_w[d][k] · xin_{t−(W−1)+k})        (inputs before t = 0 from
+ *                                                                     conv_state_in, else zeros)
+ *     Δ_t = softplus(delta_t + delta_bias[d]) if delta_softplus, else delta_t + delta_bias[d]
+ * then the scan of ssm_scan_fwd on x, Δ from initial_state (zeros when NULL). The convolved x is kept in
+ * fp32 inside the kernel (it is not rounded to the storage type before the scan); x_out, when given,
+ * receives it rounded to the storage type (for the caller's projections of x).
+ *   xin                [b][d][L] dtype, required
+ *   conv_w             [d][W] fp32, required, 1 <= W <= SSM_MAX_FUSED_CONV_W (SSM_ERR_UNSUPPORTED above)
+ *   conv_bias          [d] fp32 or NULL
+ *   conv_state_in      [b][d][W−1] fp32 or NULL: the W−1 inputs before the sequence, oldest first
+ *   delta              [b][d][L] dtype, required: Δ before its bias and softplus
+ *   delta_bias         [d] fp32 or NULL
+ *   A, B, C, D, z      as for ssm_scan_fwd; initial_state [b][d][N] fp32 or NULL
+ *   y, final_state     as for ssm_scan_fwd
+ *   conv_state_out     [b][d][W−1] fp32 or NULL: the last W−1 inputs after the sequence (must not
+ *                      overlap conv_state_in; copy it back for the next call)
+ *   x_out              [b][d][L] dtype or NULL
+ * Scratch as for ssm_scan_fwd. No output may overlap an input or another output. Errors as for
+ * ssm_scan_fwd.
+ */
+#define SSM_MAX_FUSED_CONV_W 4
+SSM_API ssm_status_t ssm_scan_fwd_conv(const void *xin, const float *conv_w, const float *conv_bias,
+                                       const float *conv_state_in, int64_t W, const void *delta,
+                                       const float *delta_bias, int32_t delta_softplus, const float *A,
+                                       const void *B, const void *C, const float *D, const void *z,
+                                       const float *initial_state, void *y, float *final_state,
+                                       float *conv_state_out, void *x_out, int64_t b, int64_t d, int64_t L,
+                                       int64_t N, ssm_dtype_t dtype, hipStream_t stream);
+
+/*
+ * One decode step of the same branch in one launch (page "Mambaとは？Transformer以外の系列モデル", section
+ * training、prefill、decodeでは計算の姿が違う: each layer keeps a Conv1D state and an SSM state): the token's
+ * raw input is convolved with conv_state (the last W−1 inputs, fp32 [b][d][W−1], shifted in place; may be
+ * NULL when W = 1), SiLU, Δ as in ssm_scan_fwd_conv, then the step of ssm_scan_step on state.
+ *   state [b][d][N] fp32 in/out; xin, delta, z, y, x_out (nullable) [b][d] dtype; conv_w [d][W];
+ *   conv_bias, delta_bias [d] or NULL; A, B, C, D as for ssm_scan_step.
+ * The two states and the outputs may not overlap each other or any input. Errors as for ssm_scan_step.
+ */
+SSM_API ssm_status_t ssm_scan_step_conv(float *state, float *conv_state, const void *xin, const float *conv_w,
+                                        const float *conv_bias, int64_t W, const void *delta,
+                                        const float *delta_bias, int32_t delta_softplus, const float *A,
+                                        const void *B, const void *C, const float *D, const void *z, void *y,
+                                        void *x_out, int64_t b, int64_t d, int64_t N, ssm_dtype_t dtype,
+                                        hipStream_t stream);
 
 /*
  * The time-invariant (LTI) case evaluated as a convolution (page "State Space Models（SSM）とMamba" §2.3;

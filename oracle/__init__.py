@@ -204,6 +204,26 @@ class Oracle:
         return y
 
 
+    def scan_fwd_conv(self, xin, conv_w, conv_bias, conv_state_in, delta, delta_bias, delta_softplus, A, B, C,
+                      D=None, z=None, h0=None):
+        """The Mamba block's main branch from the Conv1D's input (page "Mambaとは？Transformer以外の系列モデル",
+        section Mamba blockのarchitecture): x = silu(conv1d(xin) + bias), Δ = delta + delta_bias (softplus
+        when asked), then the prefill scan, all in fp64 with nothing rounded between the steps.
+        Returns (y, h_final, conv_state_out, x)."""
+        x, conv_state_out = self.conv1d(xin, conv_w, conv_bias, conv_state_in, silu=True)
+        y, h = self.scan_fwd(x, delta_preprocess(delta, delta_bias, delta_softplus), A, B, C, D, z, h0)
+        return y, h, conv_state_out, x
+
+    def scan_step_conv(self, state, conv_state, xin, conv_w, conv_bias, delta, delta_bias, delta_softplus, A, B, C,
+                       D=None, z=None):
+        """One decode step of that branch: xin, delta, z [b, d]; conv_state [b, d, W-1] (the section
+        training、prefill、decodeでは計算の姿が違う keeps it beside the SSM state). Returns (y, new_state,
+        new_conv_state, x)."""
+        xin = _f64(xin)
+        x, new_cs = self.conv1d(xin[:, :, None], conv_w, conv_bias, conv_state, silu=True)
+        y, h = self.scan_step(state, x[:, :, 0], delta_preprocess(delta, delta_bias, delta_softplus), A, B, C, D, z)
+        return y, h, new_cs, x[:, :, 0]
+
     def ssd_quadratic(self, x, delta, A, B, C, D=None, z=None, heads=None):
         """y [b, H·P, L] of the scalar-decay SSM in its quadratic form: delta [b, H, L], A [H],
         B, C [b, L, N], D [H·P]; x, z [b, H·P, L]."""
@@ -271,3 +291,36 @@ def lti_conv(x, K, D=None, z=None):
 
 def ssd_quadratic(x, delta, A, B, C, D=None, z=None):
     return default().ssd_quadratic(x, delta, A, B, C, D, z)
+
+
+# ---------------------------------------------------------------------------------------------
+# The fused front end of the Mamba block's main branch (page "Mambaとは？Transformer以外の系列モデル",
+# section Mamba blockのarchitecture: a causal Conv1D, SiLU, then the selective SSM; section hardware-awareとは
+# memory trafficまで設計すること: the parameters are prepared inside the scan's kernel). Written as the
+# composition of the pieces above, in fp64: nothing is rounded between the Conv1D and the scan.
+# ---------------------------------------------------------------------------------------------
+def softplus(v):
+    """log(1 + e^v) in fp64, by numpy's logaddexp(0, v) (no overflow for large v). The pages do not give
+    Δ's preprocessing; softplus of Δ plus a per-channel bias is the option the library offers."""
+    return np.logaddexp(0.0, np.asarray(v, dtype=np.float64))
+
+
+def delta_preprocess(delta, delta_bias=None, delta_softplus=False):
+    """Δ = delta + bias[d] (bias broadcast over b and t), through softplus when asked."""
+    dl = _f64(delta)
+    if delta_bias is not None:
+        shape = (1, -1, 1) if dl.ndim == 3 else (1, -1)
+        dl = dl + _f64(delta_bias).reshape(shape)
+    return softplus(dl) if delta_softplus else dl
+
+
+def scan_fwd_conv(xin, conv_w, conv_bias, conv_state_in, delta, delta_bias, delta_softplus, A, B, C, D=None, z=None,
+                  h0=None):
+    return default().scan_fwd_conv(xin, conv_w, conv_bias, conv_state_in, delta, delta_bias, delta_softplus, A, B, C,
+                                   D, z, h0)
+
+
+def scan_step_conv(state, conv_state, xin, conv_w, conv_bias, delta, delta_bias, delta_softplus, A, B, C, D=None,
+                   z=None):
+    return default().scan_step_conv(state, conv_state, xin, conv_w, conv_bias, delta, delta_bias, delta_softplus, A, B,
+                                    C, D, z)

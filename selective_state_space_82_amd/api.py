@@ -78,6 +78,10 @@ def lib() -> ctypes.CDLL:
     L.ssm_conv1d_fwd.restype = i32
     L.ssm_conv1d_step.argtypes = [vp] * 5 + [i64, i64, i64, i32, i32, vp]
     L.ssm_conv1d_step.restype = i32
+    L.ssm_scan_fwd_conv.argtypes = [vp, vp, vp, vp, i64, vp, vp, i32] + [vp] * 10 + [i64, i64, i64, i64, i32, vp]
+    L.ssm_scan_fwd_conv.restype = i32
+    L.ssm_scan_step_conv.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, i32] + [vp] * 7 + [i64, i64, i64, i32, vp]
+    L.ssm_scan_step_conv.restype = i32
     L.ssm_lti_kernel.argtypes = [vp] * 5 + [i64, i64, i64, vp]
     L.ssm_lti_kernel.restype = i32
     L.ssm_lti_conv.argtypes = [vp] * 5 + [i64, i64, i64, i32, vp]
@@ -183,6 +187,80 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, *, y=None, final_state=None,
         status = lib().ssm_scan_fwd(*args)
     _raise(status, "ssm_scan_fwd_noalloc" if noalloc else "ssm_scan_fwd")
     return y, final_state
+
+
+def ssm_scan_fwd_conv(xin, conv_w, delta, A, B, C, D=None, z=None, *, conv_bias=None, conv_state_in=None,
+                      delta_bias=None, delta_softplus=False, initial_state=None, y=None, final_state=None,
+                      conv_state_out=None, x_out=None, return_states=True, want_x=False):
+    """The Mamba block's main branch in one prefill pass: Conv1D (conv_w [d, W], W <= 4) + SiLU on xin
+    [b, d, L], Δ = delta + delta_bias (softplus when delta_softplus), then the scan. Returns
+    (y, final_state, conv_state_out, x_out); the states are allocated when return_states is set and none is
+    given, x_out (the convolved input) when want_x is set."""
+    if xin.dim() != 3 or conv_w.dim() != 2:
+        raise ValueError("xin must be [b, d, L] and conv_w [d, W]")
+    b, d, L = xin.shape
+    N = A.shape[1]
+    W = conv_w.shape[1]
+    dev = xin.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a ROCm GPU")
+    st = xin.dtype
+    code = _dtype_code(st)
+    f32 = torch.float32
+    for name, t, shape, dt in (("delta", delta, (b, d, L), st), ("A", A, (d, N), f32), ("B", B, (b, L, N), st),
+                               ("C", C, (b, L, N), st), ("D", D, (d,), f32), ("z", z, (b, d, L), st),
+                               ("conv_w", conv_w, (d, W), f32), ("conv_bias", conv_bias, (d,), f32),
+                               ("conv_state_in", conv_state_in, (b, d, W - 1), f32),
+                               ("delta_bias", delta_bias, (d,), f32), ("initial_state", initial_state, (b, d, N), f32),
+                               ("xin", xin, (b, d, L), st)):
+        _check(name, t, shape, dt, dev)
+    if y is None:
+        y = torch.empty((b, d, L), dtype=st, device=dev)
+    if return_states and final_state is None:
+        final_state = torch.empty((b, d, N), dtype=f32, device=dev)
+    if return_states and conv_state_out is None and W > 1:
+        conv_state_out = torch.empty((b, d, W - 1), dtype=f32, device=dev)
+    if want_x and x_out is None:
+        x_out = torch.empty((b, d, L), dtype=st, device=dev)
+    _check("y", y, (b, d, L), st, dev)
+    _check("final_state", final_state, (b, d, N), f32, dev)
+    _check("conv_state_out", conv_state_out, (b, d, W - 1), f32, dev)
+    _check("x_out", x_out, (b, d, L), st, dev)
+    status = lib().ssm_scan_fwd_conv(_ptr(xin), _ptr(conv_w), _ptr(conv_bias), _ptr(conv_state_in), W, _ptr(delta),
+                                     _ptr(delta_bias), int(bool(delta_softplus)), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                     _ptr(z), _ptr(initial_state), _ptr(y), _ptr(final_state), _ptr(conv_state_out),
+                                     _ptr(x_out), b, d, L, N, code, _stream(dev))
+    _raise(status, "ssm_scan_fwd_conv")
+    return y, final_state, conv_state_out, x_out
+
+
+def ssm_scan_step_conv(state, conv_state, xin, conv_w, delta, A, B, C, D=None, z=None, *, conv_bias=None,
+                       delta_bias=None, delta_softplus=False, y=None, x_out=None):
+    """One decode step of the Mamba block's main branch: state [b, d, N] and conv_state [b, d, W-1] (fp32,
+    both updated in place); xin, delta, z [b, d]; conv_w [d, W]. Returns (y, x_out) (x_out None unless
+    given)."""
+    b, d, N = state.shape
+    W = conv_w.shape[1]
+    dev = state.device
+    st = xin.dtype
+    code = _dtype_code(st)
+    f32 = torch.float32
+    for name, t, shape, dt in (("state", state, (b, d, N), f32), ("conv_state", conv_state, (b, d, W - 1), f32),
+                               ("xin", xin, (b, d), st), ("delta", delta, (b, d), st), ("A", A, (d, N), f32),
+                               ("B", B, (b, N), st), ("C", C, (b, N), st), ("D", D, (d,), f32), ("z", z, (b, d), st),
+                               ("conv_w", conv_w, (d, W), f32), ("conv_bias", conv_bias, (d,), f32),
+                               ("delta_bias", delta_bias, (d,), f32)):
+        _check(name, t, shape, dt, dev)
+    if y is None:
+        y = torch.empty((b, d), dtype=st, device=dev)
+    _check("y", y, (b, d), st, dev)
+    _check("x_out", x_out, (b, d), st, dev)
+    status = lib().ssm_scan_step_conv(_ptr(state), _ptr(conv_state) if W > 1 else None, _ptr(xin), _ptr(conv_w),
+                                      _ptr(conv_bias), W, _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
+                                      _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), _ptr(x_out), b, d, N, code,
+                                      _stream(dev))
+    _raise(status, "ssm_scan_step_conv")
+    return y, x_out
 
 
 def ssm_scan_step(state, x, delta, A, B, C, D=None, z=None, *, y=None):

@@ -168,12 +168,44 @@ ssm_status_t check_opts(int64_t N, const ssm_fwd_opts_t *o) {
     return SSM_OK;
 }
 
+// The fused front end of ssm_scan_fwd_conv / ssm_scan_step_conv (conv_w == nullptr: none).
+struct FrontEnd {
+    const float *conv_w, *conv_bias, *conv_state_in, *delta_bias;
+    float *conv_state_out;
+    void *x_out;
+    int64_t W;
+    int softplus;
+};
+
 ssm_status_t fwd_impl(const void *x, const void *delta, const float *A, const void *B, const void *C,
                       const float *D, const void *z, void *y, float *final_state, int64_t b, int64_t d,
                       int64_t L, int64_t N, ssm_dtype_t dtype, hipStream_t stream, const ssm_fwd_opts_t *o,
-                      bool noalloc = false) {
+                      bool noalloc = false, const FrontEnd *fe = nullptr) {
     ssm_status_t st = check_fwd_sizes(b, d, L, N, dtype);
     if (st != SSM_OK) return st;
+    if (fe) {
+        if (fe->W < 1 || fe->W > SSM_MAX_FUSED_CONV_W) return SSM_ERR_UNSUPPORTED;
+        if (!fe->conv_w) return SSM_ERR_NULL;
+        const int64_t es = dtype == SSM_BF16 ? 2 : 4;
+        const int64_t bdl = b * d * L, bdn = b * d * N, bdh = b * d * (fe->W - 1);
+        const Span outs[] = {{y, bdl * es}, {final_state, bdn * 4}, {fe->x_out, bdl * es}, {fe->conv_state_out, bdh * 4}};
+        const Span ins[] = {{x, bdl * es}, {delta, bdl * es}, {z, bdl * es}, {B, b * L * N * es}, {C, b * L * N * es},
+                            {A, d * N * 4}, {D, d * 4}, {o ? o->initial_state : nullptr, bdn * 4},
+                            {fe->conv_w, d * fe->W * 4}, {fe->conv_bias, d * 4}, {fe->conv_state_in, bdh * 4},
+                            {fe->delta_bias, d * 4}};
+        for (size_t i = 0; i < 4; ++i) {
+            for (const Span &s : ins)
+                if (overlaps(outs[i], s)) return SSM_ERR_ALIAS;
+            for (size_t j = i + 1; j < 4; ++j)
+                if (overlaps(outs[i], outs[j])) return SSM_ERR_ALIAS;
+        }
+        if (L == 0 && fe->conv_state_out && fe->W > 1) {  // the state passes through unchanged
+            const hipError_t e = fe->conv_state_in
+                ? hipMemcpyAsync(fe->conv_state_out, fe->conv_state_in, (size_t)bdh * 4, hipMemcpyDeviceToDevice, stream)
+                : ssm::launch_fill_zero(fe->conv_state_out, bdh, stream);
+            if (e != hipSuccess) return SSM_ERR_HIP;
+        }
+    }
     // With L = 0 nothing but final_state is touched, so the (empty) sequence tensors may be NULL.
     if (L > 0 && (!x || !delta || !A || !B || !C || !y)) return SSM_ERR_NULL;
     st = check_opts(N, o);
@@ -187,8 +219,13 @@ ssm_status_t fwd_impl(const void *x, const void *delta, const float *A, const vo
         if (overlaps(sy, s) || overlaps(sf, s)) return SSM_ERR_ALIAS;
     if (overlaps(sy, sf)) return SSM_ERR_ALIAS;
 
-    if (L == 0) {
-        if (final_state && ssm::launch_fill_zero(final_state, bdn, stream) != hipSuccess) return SSM_ERR_HIP;
+    if (L == 0) {  // the state passes through: the initial state, or zeros
+        const float *h0 = o ? o->initial_state : nullptr;
+        if (final_state) {
+            const hipError_t e = h0 ? hipMemcpyAsync(final_state, h0, (size_t)bdn * 4, hipMemcpyDeviceToDevice, stream)
+                                    : ssm::launch_fill_zero(final_state, bdn, stream);
+            if (e != hipSuccess) return SSM_ERR_HIP;
+        }
         return SSM_OK;
     }
     Plan pl{};
@@ -206,6 +243,11 @@ ssm_status_t fwd_impl(const void *x, const void *delta, const float *A, const vo
     p.n_seg = pl.n_seg;
     p.ev_begin = o ? static_cast<hipEvent_t>(o->ev_begin) : nullptr;
     p.ev_end = o ? static_cast<hipEvent_t>(o->ev_end) : nullptr;
+    if (fe) {
+        p.conv_w = fe->conv_w; p.conv_bias = fe->conv_bias; p.conv_state_in = fe->conv_state_in;
+        p.conv_state_out = fe->W > 1 ? fe->conv_state_out : nullptr; p.x_out = fe->x_out;
+        p.delta_bias = fe->delta_bias; p.conv_W = (int)fe->W; p.delta_softplus = fe->softplus ? 1 : 0;
+    }
     void *scratch = nullptr;
     if (noalloc) {
         // the fixed device array: nothing allocated, nothing to clear (every scratch word a call reads
@@ -366,6 +408,48 @@ ssm_status_t ssm_scan_fwd_noalloc(const void *x, const void *delta, const float 
                                   int64_t L, int64_t N, ssm_dtype_t dtype, hipStream_t stream,
                                   const ssm_fwd_opts_t *opts) {
     return fwd_impl(x, delta, A, B, C, D, z, y, final_state, b, d, L, N, dtype, stream, opts, true);
+}
+
+ssm_status_t ssm_scan_fwd_conv(const void *xin, const float *conv_w, const float *conv_bias, const float *conv_state_in,
+                               int64_t W, const void *delta, const float *delta_bias, int32_t delta_softplus,
+                               const float *A, const void *B, const void *C, const float *D, const void *z,
+                               const float *initial_state, void *y, float *final_state, float *conv_state_out,
+                               void *x_out, int64_t b, int64_t d, int64_t L, int64_t N, ssm_dtype_t dtype,
+                               hipStream_t stream) {
+    const FrontEnd fe{conv_w, conv_bias, conv_state_in, delta_bias, conv_state_out, x_out, W, delta_softplus};
+    ssm_fwd_opts_t o{};
+    o.initial_state = initial_state;
+    return fwd_impl(xin, delta, A, B, C, D, z, y, final_state, b, d, L, N, dtype, stream, &o, false, &fe);
+}
+
+ssm_status_t ssm_scan_step_conv(float *state, float *conv_state, const void *xin, const float *conv_w,
+                                const float *conv_bias, int64_t W, const void *delta, const float *delta_bias,
+                                int32_t delta_softplus, const float *A, const void *B, const void *C, const float *D,
+                                const void *z, void *y, void *x_out, int64_t b, int64_t d, int64_t N,
+                                ssm_dtype_t dtype, hipStream_t stream) {
+    if (!state || !xin || !delta || !A || !B || !C || !y || !conv_w || (W > 1 && !conv_state)) return SSM_ERR_NULL;
+    if (!valid_dtype(dtype)) return SSM_ERR_UNSUPPORTED;
+    if (b < 1 || d < 1 || N < 1) return SSM_ERR_SHAPE;
+    if (N > SSM_MAX_N || W < 1 || W > SSM_MAX_FUSED_CONV_W) return SSM_ERR_UNSUPPORTED;
+    int64_t bd = 0, bdn = 0, tmp = 0;
+    if (!mul_ok(b, d, &bd) || !mul_ok(bd, N, &bdn) || !mul_ok(bd, 16, &tmp)) return SSM_ERR_SHAPE;
+    if (bd > 0x7fffffffLL) return SSM_ERR_SHAPE;
+    const int64_t es = dtype == SSM_BF16 ? 2 : 4;
+    const Span outs[] = {{y, bd * es}, {state, bdn * 4}, {conv_state, bd * (W - 1) * 4}, {x_out, bd * es}};
+    const Span ins[] = {{xin, bd * es}, {delta, bd * es}, {z, bd * es}, {B, b * N * es}, {C, b * N * es},
+                        {A, d * N * 4}, {D, d * 4}, {conv_w, d * W * 4}, {conv_bias, d * 4}, {delta_bias, d * 4}};
+    for (size_t i = 0; i < 4; ++i) {
+        for (const Span &s : ins)
+            if (overlaps(outs[i], s)) return SSM_ERR_ALIAS;
+        for (size_t j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], outs[j])) return SSM_ERR_ALIAS;
+    }
+    StepLaunch p{};
+    p.state = state; p.x = xin; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.y = y;
+    p.b = b; p.d = d; p.N = N; p.bf16 = dtype == SSM_BF16;
+    p.conv_state = conv_state; p.conv_w = conv_w; p.conv_bias = conv_bias; p.delta_bias = delta_bias;
+    p.x_out = x_out; p.conv_W = (int)W; p.delta_softplus = delta_softplus ? 1 : 0;
+    return ssm::launch_scan_step(p, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 ssm_status_t ssm_scan_fwd_plan(int64_t b, int64_t d, int64_t L, int64_t N, ssm_dtype_t dtype,

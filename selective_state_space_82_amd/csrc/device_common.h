@@ -32,6 +32,16 @@ __device__ __forceinline__ float silu(float v) {
     return v * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-kLog2e * v));
 }
 
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^{−|v|}), with log1p from its series e − e²/2 + e³/3
+// where e < 2^-5 (relative error below 8e-6; 1 + e would round away most of e there) and from the hardware
+// log of 1 + e elsewhere.
+__device__ __forceinline__ float softplus(float v) {
+    const float e = exp2_fast(-kLog2e * __builtin_fabsf(v));
+    const float series = e * __builtin_fmaf(e, __builtin_fmaf(e, 1.0f / 3.0f, -0.5f), 1.0f);
+    const float direct = __builtin_amdgcn_logf(1.0f + e) * 0.69314718055994530942f;
+    return __builtin_fmaxf(v, 0.0f) + (e < 0.03125f ? series : direct);
+}
+
 // (e^{v} - 1) / v for |v| < 2^-4 by its Taylor series (relative error below 1e-8 there).
 __device__ __forceinline__ float expm1_over_v_small(float v) {
     return __builtin_fmaf(v, __builtin_fmaf(v, __builtin_fmaf(v, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f), 1.0f);

@@ -26,6 +26,12 @@ struct FwdLaunch {
     hipEvent_t ev_begin, ev_end;
     float *ckpt;              // optional: states entering every ck_len-th step, [b][d][ceil(L/ck_len)][N]
     int ck_len;               // checkpoint interval (ckpt_len) when ckpt is set
+    // fused front end (set conv_w to enable; then x is the Conv1D's raw input): Conv1D (conv_W <= 4 taps,
+    // bias) + SiLU gives the scan's x; Δ = delta + delta_bias, through softplus when delta_softplus
+    const float *conv_w, *conv_bias, *conv_state_in, *delta_bias;
+    float *conv_state_out;
+    void *x_out;
+    int conv_W, delta_softplus;
 };
 
 // Everything the gradient launcher needs (validated by the ABI layer).
@@ -122,6 +128,12 @@ struct StepLaunch {
     void *y;
     int64_t b, d, N;
     bool bf16;
+    // fused front end (conv_w set: x is the Conv1D's raw input, conv_state [b][d][conv_W − 1] is shifted in
+    // place, x_out (nullable) receives the convolved input); as in FwdLaunch
+    float *conv_state;
+    const float *conv_w, *conv_bias, *delta_bias;
+    void *x_out;
+    int conv_W, delta_softplus;
 };
 
 hipError_t launch_scan_fwd(const FwdLaunch &p, hipStream_t stream);

@@ -85,6 +85,16 @@ struct FwdArgs {
     float *ckpt;              // output pass: state entering every ck_len-th step [b][d][n_ck][N], or null
     int64_t n_ck;             // ceil(L / ck_len)
     int ck_len;               // 4, 8 or 16 (divides both tile lengths)
+    // fused front end (FE kernels): x is the Conv1D's raw input; the scan's x is silu(conv + bias), and
+    // Δ is delta + delta_bias, through softplus when delta_softplus is set
+    const float *conv_w;          // [d][conv_W]
+    const float *conv_bias;       // [d] or null
+    const float *conv_state_in;   // [b][d][conv_W − 1]: inputs before t = 0, or null (zeros)
+    float *conv_state_out;        // [b][d][conv_W − 1]: the last conv_W − 1 inputs, or null
+    void *x_out;                  // [b][d][L]: the scan's x (rounded to the storage type), or null
+    const float *delta_bias;      // [d] or null
+    int conv_W;                   // 1 .. 4 taps
+    int delta_softplus;
 };
 
 // The kernel ---------------------------------------------------------------------------------
@@ -92,8 +102,14 @@ struct FwdArgs {
 // T: storage type (float or bf16 bits); G: lanes per channel (1, 2, 4); NPL: states per lane
 // (4, 8, 16); AGG: aggregate pass (segment end state from zero and Π Ā, no readout). CK: the
 // output pass of a call that wants only the checkpoints (the gradient's forward), so it carries the
-// state in and stores it every ck_len steps but has no readout.
-template <typename T, int G, int NPL, bool AGG, bool CK = false>
+// state in and stores it every ck_len steps but has no readout. FE: the front end of the Mamba block's
+// main branch is computed while a tile is staged (page "Mambaとは？Transformer以外の系列モデル", section
+// hardware-awareとは memory trafficまで設計すること: parameter generation, discretisation and scan in one
+// kernel; section Mamba blockのarchitecture: causal Conv1D, SiLU, then the selective SSM): each lane turns
+// its 16-byte chunk of the raw input into silu(Σ_k w_k·xin_{t−(W−1)+k} + c) from an LDS row that keeps the
+// previous tile's last inputs before it, so the convolved x never goes to memory; Δ gets its bias and,
+// optionally, softplus.
+template <typename T, int G, int NPL, bool AGG, bool CK = false, bool FE = false>
 __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
     constexpr bool RO = !AGG && !CK;                     // readout, gate and y
     constexpr int kTile = tile_len<T>();
@@ -119,6 +135,11 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
     __shared__ __attribute__((aligned(16))) float Cs[RO ? kBF : 4];
     __shared__ __attribute__((aligned(16))) float red[(!RO || G == 1) ? 4 : CW * kRS];
     __shared__ __attribute__((aligned(16))) T ybuf[RO ? CW * kYPitch : 8];
+    // FE: raw inputs of each row, after kHalo slots that hold the inputs before the tile
+    constexpr int kHalo = 4;
+    constexpr int kRawPitch = kHalo + kTile + 4;
+    __shared__ __attribute__((aligned(16))) float xraw[FE ? CW * kRawPitch : 4];
+    static_assert(!FE || (kXC == 1 && kRowChunks == 4 && !CK), "the front end stages one chunk per lane");
 
     const int lane = threadIdx.x;
     const int c = lane / G;  // channel within the wave
@@ -214,6 +235,34 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
     for (int j = 0; j < NPL; ++j) s[j] *= sc[j];  // scaled state s = A·h (h itself at the A = 0 limit)
     const float dskip = (RO && a.D) ? load_or(a.D, ch, ch_ok, 0.0f) : 0.0f;
 
+    // ---- front end (FE): this lane stages chunk fq of row fr of every tile ----
+    const int fr = lane / kRowChunks;
+    const int fq = lane % kRowChunks;
+    const int64_t fch = d0 + fr;
+    const bool fok = FE && fch < a.d;
+    const int64_t frow = bi * a.d + fch;
+    float wr[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // taps aligned to the right: wr[4 − W + k] = w[k]
+    float cbias = 0.0f, dbias = 0.0f;
+    if constexpr (FE) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = j - (4 - a.conv_W);
+            wr[j] = load_or(a.conv_w, fch * a.conv_W + k, fok && k >= 0, 0.0f);
+        }
+        if (a.conv_bias) cbias = load_or(a.conv_bias, fch, fok, 0.0f);
+        if (a.delta_bias) dbias = load_or(a.delta_bias, fch, fok, 0.0f);
+        // the kHalo inputs just before the segment: from the sequence, or before t = 0 from the Conv1D
+        // state (zeros without one); lane fq fills slot fq
+        const int H = a.conv_W - 1;
+        const int64_t t = t_begin - kHalo + fq;
+        float v = 0.0f;
+        if (fok) {
+            if (t >= 0) v = widen(xg[frow * a.L + t]);
+            else if (a.conv_state_in && t >= -H) v = a.conv_state_in[frow * H + (H + t)];
+        }
+        xraw[fr * kRawPitch + fq] = v;
+    }
+
     // ---- tile prefetch into registers, and from there into LDS ----
     uint4 px[kXC], pd[kXC], pz[kXC], pb[kBC], pc[kBC];
     auto load_tile = [&](int64_t t0) {
@@ -240,16 +289,75 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
             if constexpr (RO) pc[i] = get_chunk<T>(Cg + t0 * a.N, e0, nel, ok, a.vec_bc);
         }
     };
-    auto store_tile = [&]() {
+    // Stages the tile starting at step t0 (first: the unit's first tile, whose halo came from memory).
+    auto store_tile = [&](int64_t t0, bool first) {
+        if constexpr (FE) {
+            if (!first) {  // the previous tile's last inputs become this tile's halo
+                const float tail = xraw[fr * kRawPitch + kTile + fq];
+                wave_sync();
+                xraw[fr * kRawPitch + fq] = tail;
+                wave_sync();
+            }
+        }
 #pragma unroll
         for (int i = 0; i < kXC; ++i) {
             const int k = lane + i * kWave;
             if (k >= CW * kRowChunks) break;
             const int r = k / kRowChunks;
             const int col = (k % kRowChunks) * E;
-            put_chunk<T>(xs + r * kPitch + col, px[i]);
-            put_chunk<T>(dsh + r * kPitch + col, pd[i]);
+            if constexpr (FE) {
+                put_chunk<T>(xraw + r * kRawPitch + kHalo + col, px[i]);
+                // Δ = delta + bias (then softplus); zero past the segment, where the tile is padding
+                float dv[E];
+                chunk_to_regs<T>(dv, pd[i]);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    float v = dv[e] + dbias;
+                    if (a.delta_softplus) v = softplus(v);
+                    dv[e] = t0 + col + e < t_end ? v : 0.0f;
+                }
+#pragma unroll
+                for (int e = 0; e < E; e += 4)
+                    *reinterpret_cast<float4 *>(dsh + r * kPitch + col + e) = make_float4(dv[e], dv[e + 1], dv[e + 2], dv[e + 3]);
+            } else {
+                put_chunk<T>(xs + r * kPitch + col, px[i]);
+                put_chunk<T>(dsh + r * kPitch + col, pd[i]);
+            }
             if (gate) *reinterpret_cast<uint4 *>(zs + r * kZPitch + col) = pz[i];
+        }
+        if constexpr (FE) {
+            wave_sync();  // every raw input of the tile is in LDS before the convolution reads its neighbours'
+            // this lane's E outputs: in[m] is the raw input at column fq·E − kHalo + m
+            const float *xr = xraw + fr * kRawPitch + fq * E;
+            float in[E + 4];
+#pragma unroll
+            for (int m = 0; m < E + 4; m += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(xr + m);
+                in[m] = v.x; in[m + 1] = v.y; in[m + 2] = v.z; in[m + 3] = v.w;
+            }
+            float xo[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                float u = cbias;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) u = __builtin_fmaf(wr[j], in[e + 1 + j], u);
+                xo[e] = t0 + fq * E + e < t_end ? silu(u) : 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < E; e += 4)
+                *reinterpret_cast<float4 *>(xs + fr * kPitch + fq * E + e) = make_float4(xo[e], xo[e + 1], xo[e + 2], xo[e + 3]);
+            if constexpr (RO) {
+                if (a.x_out && fok) {  // the convolved input, for the caller's projections
+                    T *dst = static_cast<T *>(a.x_out) + frow * a.L + t0 + fq * E;
+                    if (a.vec_rows && t0 + fq * E + E <= t_end) {
+                        *reinterpret_cast<uint4 *>(dst) = regs_to_chunk<T>(xo);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            if (t0 + fq * E + e < t_end) dst[e] = narrow<T>(xo[e]);
+                    }
+                }
+            }
         }
 #pragma unroll
         for (int i = 0; i < kBC; ++i) {
@@ -478,7 +586,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
     };
     auto run = [&]() {
         load_tile(t_begin);
-        store_tile();
+        store_tile(t_begin, true);
         if (ntiles > 1) load_tile(t_begin + kTile);
         wave_sync();
 #pragma unroll 1
@@ -502,7 +610,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
             }
             if (it + 1 < ntiles) {
                 wave_sync();   // the scan's last reads of tile it come before the stores of tile it + 1
-                store_tile();
+                store_tile(t0 + kTile, false);
                 wave_sync();
             }
             if (it + 2 < ntiles) load_tile(t0 + 2 * kTile);
@@ -525,12 +633,23 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
             }
         }
     }
+    // the Conv1D state after the sequence: its last W − 1 inputs (earlier ones from the state when L is short)
+    if constexpr (FE && RO) {
+        const int H = a.conv_W - 1;
+        if (a.conv_state_out && t_end == a.L && fok && fq < H) {
+            const int64_t t = a.L - H + fq;
+            float v = 0.0f;
+            if (t >= 0) v = widen(xg[frow * a.L + t]);
+            else if (a.conv_state_in) v = a.conv_state_in[frow * H + (H + t)];
+            a.conv_state_out[frow * H + fq] = v;
+        }
+    }
 }
 
 // One wavefront per unit (a block of 64/G channels of one batch row over one time segment).
-template <typename T, int G, int NPL, bool AGG>
+template <typename T, int G, int NPL, bool AGG, bool FE = false>
 __global__ __launch_bounds__(kWave, (G == 4 && NPL == 4) ? 3 : 1) void scan_fwd_kernel(FwdArgs a) {
-    scan_unit<T, G, NPL, AGG>(a, blockIdx.x);
+    scan_unit<T, G, NPL, AGG, false, FE>(a, blockIdx.x);
 }
 
 // Output pass of the gradient's checkpointing forward (fast path): carries the state in and stores it
@@ -559,11 +678,11 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ p, i
     if (i < n) p[i] = 0.0f;
 }
 
-template <typename T, int G, int NPL>
+template <typename T, int G, int NPL, bool FE = false>
 hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLaunch &p, hipStream_t stream) {
     hipError_t e = hipSuccess;
     if (n_seg > 1) {
-        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, true>), dim3((unsigned)((n_seg - 1) * ncb)), dim3(kWave), 0,
+        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, true, FE>), dim3((unsigned)((n_seg - 1) * ncb)), dim3(kWave), 0,
                            stream, args);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -577,17 +696,27 @@ hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLa
     }
     // Timing events, when given, are set by the dispatch of the fast output kernel itself (start and
     // end of that kernel), so they add no packets of their own to the queue.
-    if (args.y == nullptr && args.ckpt != nullptr) {
-        hipLaunchKernelGGL((scan_ckpt_kernel<T, G, NPL>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0, stream, args);
-    } else {
-        hipExtLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0,
-                              stream, p.ev_begin, p.ev_end, 0u, args);
+    if constexpr (!FE) {
+        if (args.y == nullptr && args.ckpt != nullptr) {
+            hipLaunchKernelGGL((scan_ckpt_kernel<T, G, NPL>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0, stream,
+                               args);
+            return hipGetLastError();
+        }
     }
+    hipExtLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, false, FE>), dim3((unsigned)(n_seg * ncb)), dim3(kWave), 0,
+                          stream, p.ev_begin, p.ev_end, 0u, args);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t dispatch_shape(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLaunch &p, hipStream_t stream) {
+    if (p.conv_w) {  // the fused front end: four lanes per channel
+        if (p.lanes_per_channel != 4) return hipErrorInvalidValue;
+        if (p.states_per_lane == 4) return launch_typed<T, 4, 4, true>(args, n_seg, ncb, p, stream);
+        if (p.states_per_lane == 8) return launch_typed<T, 4, 8, true>(args, n_seg, ncb, p, stream);
+        if (p.states_per_lane == 16) return launch_typed<T, 4, 16, true>(args, n_seg, ncb, p, stream);
+        return hipErrorInvalidValue;
+    }
 #define SSM_CASE(G_, NPL_) \
     if (p.lanes_per_channel == G_ && p.states_per_lane == NPL_) return launch_typed<T, G_, NPL_>(args, n_seg, ncb, p, stream);
     SSM_CASE(1, 4) SSM_CASE(1, 8) SSM_CASE(1, 16)
@@ -611,7 +740,10 @@ hipError_t launch_scan_fwd(const FwdLaunch &p, hipStream_t stream) {
     const int64_t esize = p.bf16 ? 2 : 4;
     auto aligned16 = [](const void *q) { return q == nullptr || (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
     a.vec_rows = ((p.L * esize) % 16 == 0) && aligned16(p.x) && aligned16(p.delta) && aligned16(p.z) &&
-                 aligned16(p.y);
+                 aligned16(p.y) && aligned16(p.x_out);
+    a.conv_w = p.conv_w; a.conv_bias = p.conv_bias; a.conv_state_in = p.conv_state_in;
+    a.conv_state_out = p.conv_state_out; a.x_out = p.x_out; a.delta_bias = p.delta_bias;
+    a.conv_W = p.conv_W; a.delta_softplus = p.delta_softplus;
     // a tile's B/C run starts at element (bi*L + t0)*N with t0 a multiple of the tile length
     a.vec_bc = ((p.L * p.N * esize) % 16 == 0) && aligned16(p.B) && aligned16(p.C);
     a.vec_state = (p.N % 4 == 0) && aligned16(p.init_state) && aligned16(p.scratch) && aligned16(p.ckpt);

@@ -9,6 +9,12 @@
 // states, so a wavefront reads and writes one contiguous run of 64 × 16 bytes of state. The
 // readout partials of the LP lanes are combined by an xor butterfly (identical sum on every lane),
 // and the first lane of the row applies the skip term and gate and stores y.
+//
+// The CONV variant is the whole decode step of the Mamba block's main branch (page "Mambaとは？Transformer
+// 以外の系列モデル", section training、prefill、decodeでは計算の姿が違う: each layer keeps a Conv1D state and
+// an SSM state): the token's raw input goes through the causal Conv1D against the stored last W − 1
+// inputs, plus bias and SiLU, and Δ gets its bias (and softplus); the Conv1D state shifts by one in the
+// same launch.
 #include "device_common.h"
 #include "launch.h"
 
@@ -30,6 +36,11 @@ struct StepArgs {
     int64_t b, d, N;
     int vec;     // N % 4 == 0 and 16-byte aligned state/A rows
     int vec_bc;  // N % 4 == 0 and B/C rows aligned to 4 elements
+    // CONV: x is the raw input; conv_state [b][d][conv_W − 1] fp32, shifted in place
+    float *conv_state;
+    const float *conv_w, *conv_bias, *delta_bias;
+    void *x_out;
+    int conv_W, delta_softplus;
 };
 
 // Four consecutive B or C values (one lane's states) in one load when aligned.
@@ -52,7 +63,7 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 // consecutive pairs, and every lane issues the loads of its R pairs before any arithmetic, so
 // R state reads per lane are in flight at once. The state streams through (read once, written
 // once) with non-temporal accesses.
-template <typename T, int LP, int R>
+template <typename T, int LP, int R, bool CONV = false>
 __global__ __launch_bounds__(256) void scan_step_kernel(StepArgs a) {
     constexpr int PB = 256 / LP;  // pairs per block and round
     const uint32_t bd = (uint32_t)(a.b * a.d);
@@ -70,6 +81,7 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepArgs a) {
     uint32_t pair[R];
     bool ok[R];
     float xt[R], dt[R], zt[R], dsk[R];
+    float raw[R], cs[R][3];  // CONV: the raw input and the stored inputs before it (oldest first)
     float h[R][4], Av[R][4], Bv[R][4], Cv[R][4];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -80,6 +92,22 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepArgs a) {
         const uint32_t ch = pair[r] - bi * d;
         xt[r] = widen(xg[pair[r]]);
         dt[r] = widen(dg[pair[r]]);
+        if constexpr (CONV) {
+            const int H = a.conv_W - 1;
+            const float *st = a.conv_state + (int64_t)pair[r] * H;
+            const float *w = a.conv_w + (int64_t)ch * a.conv_W;
+            raw[r] = xt[r];
+            float u = a.conv_bias ? a.conv_bias[ch] : 0.0f;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                cs[r][k] = k < H ? st[k] : 0.0f;
+                if (k < H) u = __builtin_fmaf(w[k], cs[r][k], u);
+            }
+            u = __builtin_fmaf(w[H], raw[r], u);
+            xt[r] = silu(u);
+            float v = dt[r] + (a.delta_bias ? a.delta_bias[ch] : 0.0f);
+            dt[r] = a.delta_softplus ? softplus(v) : v;
+        }
         zt[r] = zg ? widen(zg[pair[r]]) : 0.0f;
         dsk[r] = a.D ? a.D[ch] : 0.0f;
         const float *st = a.state + (int64_t)pair[r] * a.N + n0;
@@ -136,11 +164,19 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepArgs a) {
             float v = __builtin_fmaf(dsk[r], xt[r], acc);
             if (zg) v *= silu(zt[r]);
             static_cast<T *>(a.y)[pair[r]] = narrow<T>(v);
+            if constexpr (CONV) {  // the Conv1D state moves on by one input; the convolved input goes out
+                const int H = a.conv_W - 1;
+                float *st = a.conv_state + (int64_t)pair[r] * H;
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+                    if (k < H) st[k] = k + 1 < H ? cs[r][k + 1] : raw[r];
+                if (a.x_out) static_cast<T *>(a.x_out)[pair[r]] = narrow<T>(xt[r]);
+            }
         }
     }
 }
 
-template <typename T>
+template <typename T, bool CONV>
 hipError_t launch_step_typed(const StepArgs &a, hipStream_t stream) {
     const int lp_needed = (int)((a.N + 3) / 4);
     int lp = 1;
@@ -149,11 +185,11 @@ hipError_t launch_step_typed(const StepArgs &a, hipStream_t stream) {
     const int64_t per_block = (int64_t)R * (256 / lp);
     const dim3 grid((unsigned)((a.b * a.d + per_block - 1) / per_block)), block(256);
     switch (lp) {
-        case 1: hipLaunchKernelGGL((scan_step_kernel<T, 1, R>), grid, block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((scan_step_kernel<T, 2, R>), grid, block, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((scan_step_kernel<T, 4, R>), grid, block, 0, stream, a); break;
-        case 8: hipLaunchKernelGGL((scan_step_kernel<T, 8, R>), grid, block, 0, stream, a); break;
-        case 16: hipLaunchKernelGGL((scan_step_kernel<T, 16, R>), grid, block, 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((scan_step_kernel<T, 1, R, CONV>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((scan_step_kernel<T, 2, R, CONV>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((scan_step_kernel<T, 4, R, CONV>), grid, block, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((scan_step_kernel<T, 8, R, CONV>), grid, block, 0, stream, a); break;
+        case 16: hipLaunchKernelGGL((scan_step_kernel<T, 16, R, CONV>), grid, block, 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -170,8 +206,11 @@ hipError_t launch_scan_step(const StepLaunch &p, hipStream_t stream) {
     const uintptr_t bc_align = p.bf16 ? 8u : 16u;
     a.vec_bc = (p.N % 4 == 0) && (reinterpret_cast<uintptr_t>(p.B) % bc_align == 0) &&
                (reinterpret_cast<uintptr_t>(p.C) % bc_align == 0);
-    if (p.bf16) return launch_step_typed<uint16_t>(a, stream);
-    return launch_step_typed<float>(a, stream);
+    a.conv_state = p.conv_state; a.conv_w = p.conv_w; a.conv_bias = p.conv_bias; a.delta_bias = p.delta_bias;
+    a.x_out = p.x_out; a.conv_W = p.conv_W; a.delta_softplus = p.delta_softplus;
+    if (p.conv_w) return p.bf16 ? launch_step_typed<uint16_t, true>(a, stream) : launch_step_typed<float, true>(a, stream);
+    if (p.bf16) return launch_step_typed<uint16_t, false>(a, stream);
+    return launch_step_typed<float, false>(a, stream);
 }
 
 }  // namespace ssm

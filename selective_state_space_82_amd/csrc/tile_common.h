@@ -37,6 +37,21 @@ __device__ __forceinline__ void chunk_to_regs<uint16_t>(float *dst, const uint4 
     dst[4] = bf16_lo(v.z); dst[5] = bf16_hi(v.z); dst[6] = bf16_lo(v.w); dst[7] = bf16_hi(v.w);
 }
 
+// Narrow `E` floats into one 16-byte chunk of the storage type (bf16: round to nearest even).
+template <typename T>
+__device__ __forceinline__ uint4 regs_to_chunk(const float *v);
+template <>
+__device__ __forceinline__ uint4 regs_to_chunk<float>(const float *v) {
+    return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+}
+template <>
+__device__ __forceinline__ uint4 regs_to_chunk<uint16_t>(const float *v) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)narrow<uint16_t>(v[2 * i]) | ((uint32_t)narrow<uint16_t>(v[2 * i + 1]) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Load one chunk (E consecutive elements of a row or run starting at element t) with bounds;
 // elements at or past `t_end` read as 0.
 template <typename T>

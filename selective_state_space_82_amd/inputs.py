@@ -297,3 +297,29 @@ def random_ssd(b, H, L, N, dtype="f32", gate=True, seed=0, delta_mu=-3.0, delta_
         "dtype": dtype,
         "shape": (b, H, P, L, N),
     }
+
+
+def random_frontend(b, d, L, N, W=4, dtype="f32", gate=True, seed=0, delta_mu=-3.0, delta_sigma=1.0,
+                    a_kind="neg_index", with_state=True, with_h0=False) -> dict:
+    """Inputs of the fused front end (Conv1D + SiLU, Δ bias and softplus, then the scan): the Conv1D's raw
+    input xin ~ N(0, 1); raw Δ (before its bias and softplus) ~ N(mu, sigma); taps ~ N(0, 0.5²) [d][W];
+    Conv1D bias ~ N(0, 1); Δ bias ~ N(0, 0.3²); the Conv1D state [b][d][W-1] ~ N(0, 1) and an initial SSM
+    state [b][d][N] ~ N(0, 0.5²) when asked; A, B, C, D, z as in random_prefill."""
+    tag = f"frontend_{b}_{d}_{L}_{N}_{W}_{dtype}_{int(gate)}_{delta_mu}_{delta_sigma}_{a_kind}"
+    g = lambda t: _gen(seed, tag, t)
+    return {
+        "xin": store(g("xin").standard_normal((b, d, L)), dtype),
+        "delta": store(g("delta").normal(delta_mu, delta_sigma, size=(b, d, L)), dtype),
+        "z": store(g("z").standard_normal((b, d, L)), dtype) if gate else None,
+        "A": _a_matrix(seed, tag, d, N, a_kind),
+        "B": store(g("B").standard_normal((b, L, N)), dtype),
+        "C": store(g("C").standard_normal((b, L, N)), dtype),
+        "D": g("D").standard_normal(d).astype(np.float32),
+        "conv_w": (g("conv_w").standard_normal((d, W)) * 0.5).astype(np.float32),
+        "conv_bias": g("conv_bias").standard_normal(d).astype(np.float32),
+        "delta_bias": (g("delta_bias").standard_normal(d) * 0.3).astype(np.float32),
+        "conv_state": g("conv_state").standard_normal((b, d, W - 1)).astype(np.float32) if with_state else None,
+        "h0": (g("h0").standard_normal((b, d, N)) * 0.5).astype(np.float32) if with_h0 else None,
+        "dtype": dtype,
+        "shape": (b, d, L, N, W),
+    }

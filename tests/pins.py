@@ -519,6 +519,64 @@ def pin_ssd_masked_attention(orc):
         _close(y[0, h * P:(h + 1) * P], want, what=f"decayed attention, head {h}")
 
 
+def pin_softplus_closed_forms(orc):
+    """softplus(v) = log(1 + e^v): ln 2 at 0; softplus(v) − softplus(−v) = v; the inverse of
+    c ↦ log(e^c − 1); e^v to full relative precision far below 0; v far above 0."""
+    import oracle as O
+    _close(O.softplus(0.0), math.log(2.0), rtol=1e-15, what="softplus(0)")
+    v = _rng(41).normal(0.0, 5.0, size=200)
+    _close(O.softplus(v) - O.softplus(-v), v, rtol=1e-13, atol=1e-13, what="softplus odd part")
+    c = np.array([1e-6, 0.01, 0.5, 3.0, 20.0])
+    _close(O.softplus(np.log(np.expm1(c))), c, rtol=1e-12, what="softplus inverse")
+    _close(O.softplus(-40.0), math.exp(-40.0), rtol=1e-12, atol=0.0, what="softplus far left")
+    _close(O.softplus(800.0), 800.0, rtol=1e-15, what="softplus far right")
+    assert np.all(O.softplus(v) > np.maximum(v, 0.0)), "softplus exceeds max(v, 0)"
+
+
+def pin_fused_front_end_composition(orc):
+    """The Conv1D + SiLU → Δ preprocessing → scan composition: with one unit tap and no biases it is the
+    scan of silu(xin) (library expit) on the raw Δ; its Conv1D state output is the last W − 1 inputs;
+    two calls chained through both states equal one call; L decode steps equal the prefill."""
+    rng = _rng(43)
+    b, d, L, N, W = 2, 5, 30, 4, 4
+    xin = rng.standard_normal((b, d, L))
+    dl = rng.normal(-1.0, 0.7, size=(b, d, L))
+    A = -rng.uniform(0.2, 2.0, size=(d, N))
+    B, C = rng.standard_normal((b, L, N)), rng.standard_normal((b, L, N))
+    D, z = rng.standard_normal(d), rng.standard_normal((b, d, L))
+    # one unit tap, no bias, no softplus: the plain scan of silu(xin)
+    y1, h1, _, x1 = orc.scan_fwd_conv(xin, np.ones((d, 1)), None, None, np.abs(dl), None, False, A, B, C, D, z)
+    y2, h2 = orc.scan_fwd(silu_lib(xin), np.abs(dl), A, B, C, D, z)
+    _close(y1, y2, what="fused, W = 1: y")
+    _close(h1, h2, what="fused, W = 1: state")
+    _close(x1, silu_lib(xin), what="fused, W = 1: x")
+    # W = 4 with biases and softplus: the state output and chaining
+    w = rng.normal(0.0, 0.5, size=(d, W))
+    cb, db = rng.standard_normal(d), rng.normal(0.0, 0.3, size=d)
+    cs0 = rng.standard_normal((b, d, W - 1))
+    h0 = rng.standard_normal((b, d, N)) * 0.3
+    y, h, cs, _ = orc.scan_fwd_conv(xin, w, cb, cs0, dl, db, True, A, B, C, D, z, h0)
+    assert np.array_equal(cs, xin[:, :, L - (W - 1):]), "Conv1D state output is not the last W - 1 inputs"
+    cut = 11
+    ya, ha, csa, _ = orc.scan_fwd_conv(xin[:, :, :cut], w, cb, cs0, dl[:, :, :cut], db, True, A, B[:, :cut],
+                                       C[:, :cut], D, z[:, :, :cut], h0)
+    yb, hb, csb, _ = orc.scan_fwd_conv(xin[:, :, cut:], w, cb, csa, dl[:, :, cut:], db, True, A, B[:, cut:],
+                                       C[:, cut:], D, z[:, :, cut:], ha)
+    _close(np.concatenate([ya, yb], axis=2), y, what="fused chained y")
+    _close(hb, h, what="fused chained state")
+    _close(csb, cs, what="fused chained Conv1D state")
+    # decode steps
+    st, cst = h0.copy(), cs0.copy()
+    ys = []
+    for t in range(L):
+        yt, st, cst, _ = orc.scan_step_conv(st, cst, xin[:, :, t], w, cb, dl[:, :, t], db, True, A, B[:, t], C[:, t],
+                                            D, z[:, :, t])
+        ys.append(yt)
+    _close(np.stack(ys, axis=2), y, what="fused decode steps vs prefill")
+    _close(st, h, what="fused decode state")
+    _close(cst, cs, what="fused decode Conv1D state")
+
+
 ALL_PINS = [
     pin_scalar_worked_example,
     pin_delta_gate,
@@ -544,4 +602,6 @@ ALL_PINS = [
     pin_lti_conv_library,
     pin_ssd_duality,
     pin_ssd_masked_attention,
+    pin_softplus_closed_forms,
+    pin_fused_front_end_composition,
 ]
