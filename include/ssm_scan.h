@@ -61,7 +61,9 @@ extern "C" {
 #else
 #define SSM_API
 #endif
-typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+/* The *_MAX_ENUM members are not values: they give both enums a 32-bit range, so any int a C or FFI
+ * caller passes is a representable value of the type (and is then rejected or named "unknown"). */
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1, SSM_DTYPE_MAX_ENUM = 0x7fffffff } ssm_dtype_t;
 
 typedef enum {
     SSM_OK = 0,
@@ -70,7 +72,8 @@ typedef enum {
     SSM_ERR_UNSUPPORTED = 3, /* N > SSM_MAX_N, unknown dtype, or an option value not accepted */
     SSM_ERR_HIP = 4,         /* a HIP runtime call or a launch failed                          */
     SSM_ERR_ALIAS = 5,       /* an output overlaps an input or another output                 */
-    SSM_ERR_SCRATCH = 6      /* ssm_scan_fwd_noalloc: the plan needs more than its fixed scratch */
+    SSM_ERR_SCRATCH = 6,     /* ssm_scan_fwd_noalloc: the plan needs more than its fixed scratch */
+    SSM_STATUS_MAX_ENUM = 0x7fffffff
 } ssm_status_t;
 
 /*

@@ -24,6 +24,16 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=
 
 # The sources that decide the prefill kernels and their launch shapes.
 FWD_KERNEL_SOURCES = ("abi.cpp", "device_common.h", "launch.h", "scan_fwd.hip", "tile_common.h")
+# The sources behind each group of kernels a profile under profiles/ covers.
+PROFILE_SOURCES = {
+    "scan_fwd": FWD_KERNEL_SOURCES,
+    "scan_step": ("abi.cpp", "device_common.h", "launch.h", "scan_step.hip"),
+    "scan_bwd": ("abi.cpp", "device_common.h", "launch.h", "scan_bwd.hip", "scan_fwd.hip", "tile_common.h"),
+    "conv1d": ("abi.cpp", "device_common.h", "launch.h", "conv1d.hip", "tile_common.h"),
+    "frontend": ("abi.cpp", "conv1d.hip", "device_common.h", "launch.h", "scan_fwd.hip", "tile_common.h"),
+    "lti": ("abi.cpp", "device_common.h", "launch.h", "lti.hip"),
+    "ssd": ("abi.cpp", "device_common.h", "launch.h", "ssd.hip", "ssd_common.h", "ssd_scan.hip"),
+}
 
 
 def kernel_source_hash(names=FWD_KERNEL_SOURCES) -> str:

@@ -381,6 +381,7 @@ const char *ssm_status_string(ssm_status_t s) {
         case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: N, dtype or an option value is not supported";
         case SSM_ERR_HIP: return "SSM_ERR_HIP: a HIP runtime call or kernel launch failed";
         case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS: an output overlaps an input or another output";
+        case SSM_STATUS_MAX_ENUM: break;
         case SSM_ERR_SCRATCH:
             return "SSM_ERR_SCRATCH: the call needs more scratch than ssm_scan_fwd_noalloc holds "
                    "(SSM_NOALLOC_SCRATCH_BYTES); use fewer time segments or ssm_scan_fwd_ex";

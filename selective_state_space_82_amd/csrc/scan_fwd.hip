@@ -220,13 +220,23 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
             if (a.h_in) {
                 load_state(a.h_in + (seg - 1) * bd * a.N, s);
             } else {
-#pragma unroll 2
-                for (int64_t k = 0; k < seg; ++k) {
-                    float P[NPL], Eend[NPL];
-                    load_state(a.agg_P + k * bd * a.N, P);
-                    load_state(a.agg_E + k * bd * a.N, Eend);
+                // four segments' aggregates are loaded before they are folded in, so the chain waits on
+                // memory once per four segments (segments past this one's are read from segment 0: harmless)
+                for (int64_t k = 0; k < seg; k += 4) {
+                    float P[4][NPL], Eend[4][NPL];
 #pragma unroll
-                    for (int j = 0; j < NPL; ++j) s[j] = __builtin_fmaf(P[j], s[j], Eend[j]);
+                    for (int q = 0; q < 4; ++q) {
+                        const int64_t kk = k + q < seg ? k + q : 0;
+                        load_state(a.agg_P + kk * bd * a.N, P[q]);
+                        load_state(a.agg_E + kk * bd * a.N, Eend[q]);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if (k + q < seg) {
+#pragma unroll
+                            for (int j = 0; j < NPL; ++j) s[j] = __builtin_fmaf(P[q][j], s[j], Eend[q][j]);
+                        }
+                    }
                 }
             }
         }
@@ -667,7 +677,22 @@ __global__ __launch_bounds__(256) void carry_kernel(const float *__restrict__ P,
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= bdn) return;
     float h = init ? init[i] : 0.0f;
-    for (int k = 0; k + 1 < n_seg; ++k) {
+    // eight segments' aggregates in flight at a time: one memory round trip per eight steps of the chain
+    int k = 0;
+    for (; k + 8 < n_seg; k += 8) {
+        float p[8], e[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            p[q] = P[(k + q) * bdn + i];
+            e[q] = Eend[(k + q) * bdn + i];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            h = __builtin_fmaf(p[q], h, e[q]);
+            Hin[(k + q) * bdn + i] = h;
+        }
+    }
+    for (; k + 1 < n_seg; ++k) {
         h = __builtin_fmaf(P[k * bdn + i], h, Eend[k * bdn + i]);
         Hin[k * bdn + i] = h;
     }
