@@ -90,7 +90,7 @@ def warm_up(fn, count, min_s=0.0):
     torch.cuda.synchronize()
 
 
-def bench_prefill(name, steps, warmup, rotate=0, quiet=False, min_warm_s=0.0):
+def bench_prefill(name, steps, warmup, rotate=0, quiet=False, min_warm_s=0.0, call_kw=None):
     import torch
     from selective_state_space_82_amd import api
     from selective_state_space_82_amd import inputs as I
@@ -120,7 +120,7 @@ def bench_prefill(name, steps, warmup, rotate=0, quiet=False, min_warm_s=0.0):
     def call(i, events=None):
         s = sets[i % rotate]
         api.ssm_scan_fwd(s["x"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], y=s["y"], final_state=s["h"],
-                         events=events)
+                         events=events, **(call_kw or {}))
 
     warm_up(call, warmup, min_warm_s)
     t0 = time.perf_counter()
@@ -131,7 +131,8 @@ def bench_prefill(name, steps, warmup, rotate=0, quiet=False, min_warm_s=0.0):
     ms = (t1 - t0) * 1e3 / steps
     kern = np.array([a.elapsed_time(b) for i, (a, b) in enumerate(ev) if i % every == 0])
     kern_ms = float(np.mean(kern))
-    plan = api.ssm_scan_fwd_plan(w.b, w.d, w.L, w.N, torch.float32 if w.dtype == "f32" else torch.bfloat16)
+    plan = api.ssm_scan_fwd_plan(w.b, w.d, w.L, w.N, torch.float32 if w.dtype == "f32" else torch.bfloat16,
+                                 **(call_kw or {}))
     elems = w.b * w.d * w.L
     slots = elems * valu_slots_per_element(w.N, w.gate)
     call_tslot = slots / (ms * 1e-3) / 1e12

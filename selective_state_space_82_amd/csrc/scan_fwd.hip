@@ -610,6 +610,15 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
             } else {
                 scan_tile(std::integral_constant<int, 2>{}, it);
             }
+            // The next tile is staged and the one after it requested before this window's outputs are
+            // stored: staging waits for the requested loads, and loads and stores share one counter, so
+            // a store issued just before would be waited for as well.
+            if (it + 1 < ntiles) {
+                wave_sync();   // the scan's last reads of tile it come before the stores of tile it + 1
+                store_tile(t0 + kTile, false);
+                wave_sync();
+            }
+            if (it + 2 < ntiles) load_tile(t0 + 2 * kTile);
             if constexpr (RO) {
                 if (yg && ((it & 1) || it + 1 == ntiles)) {  // the output window is complete
                     const int64_t tw0 = t0 - (it & 1) * kTile;
@@ -618,12 +627,6 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
                     flush_y(tw0, left < kYWin ? (int)left : kYWin);
                 }
             }
-            if (it + 1 < ntiles) {
-                wave_sync();   // the scan's last reads of tile it come before the stores of tile it + 1
-                store_tile(t0 + kTile, false);
-                wave_sync();
-            }
-            if (it + 2 < ntiles) load_tile(t0 + 2 * kTile);
         }
     };
     run();
