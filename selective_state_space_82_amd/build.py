@@ -12,8 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssmscan.so")
-SOURCES = ["scan_fwd.hip", "scan_bwd.hip", "scan_step.hip", "conv1d.hip", "lti.hip", "ssd.hip", "ssd_scan.hip",
-           "noalloc.hip", "abi.cpp"]
+SOURCES = ["scan_fwd.hip", "agg_rev.hip", "scan_bwd.hip", "scan_step.hip", "conv1d.hip", "lti.hip", "ssd.hip",
+           "ssd_scan.hip", "noalloc.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept out of the generated code.
@@ -23,12 +23,13 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=
 
 
 # The sources that decide the prefill kernels and their launch shapes.
-FWD_KERNEL_SOURCES = ("abi.cpp", "device_common.h", "launch.h", "scan_fwd.hip", "tile_common.h")
+FWD_KERNEL_SOURCES = ("abi.cpp", "agg_rev.hip", "device_common.h", "launch.h", "scan_fwd.hip", "tile_common.h")
 # The sources behind each group of kernels a profile under profiles/ covers.
 PROFILE_SOURCES = {
     "scan_fwd": FWD_KERNEL_SOURCES,
     "scan_step": ("abi.cpp", "device_common.h", "launch.h", "scan_step.hip"),
-    "scan_bwd": ("abi.cpp", "device_common.h", "launch.h", "scan_bwd.hip", "scan_fwd.hip", "tile_common.h"),
+    "scan_bwd": ("abi.cpp", "agg_rev.hip", "device_common.h", "launch.h", "scan_bwd.hip", "scan_fwd.hip",
+                 "tile_common.h"),
     "conv1d": ("abi.cpp", "device_common.h", "launch.h", "conv1d.hip", "tile_common.h"),
     "frontend": ("abi.cpp", "conv1d.hip", "device_common.h", "launch.h", "scan_fwd.hip", "tile_common.h"),
     "lti": ("abi.cpp", "device_common.h", "launch.h", "lti.hip"),

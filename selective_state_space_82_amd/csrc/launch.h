@@ -59,6 +59,20 @@ struct BwdLaunch {
 
 hipError_t launch_scan_bwd(const BwdLaunch &p, hipStream_t stream);
 
+// Aggregate pass of a time split (agg_rev.hip): for segments 0 .. n_seg − 2, P = Π Ā = exp(A·ΣΔ) and E, the
+// end state from zero, both [n_seg − 1][b][d][N] fp32, by a backward walk that stops once the decay back
+// to the step reached is at most 2^-30 for every state of a wavefront. N <= 64.
+struct AggLaunch {
+    const void *x, *delta;
+    const float *A;
+    const void *B;
+    float *P, *E;
+    int64_t b, d, L, N, seg_len;
+    int n_seg;
+    bool bf16;
+};
+hipError_t launch_agg_rev(const AggLaunch &p, hipStream_t stream);
+
 // Causal depthwise Conv1D (+ SiLU) over [b][d][L] rows, and its decode step.
 struct ConvLaunch {
     const void *xin;
@@ -95,10 +109,28 @@ struct LtiConvLaunch {
     void *y;
     int64_t b, d, L;
     bool bf16;
+    // Chunked form (chunk > 0): K holds `chunk` taps per channel, every chunk of the sequence is convolved
+    // on its own, and each chunk after the first adds the response Σ_n C_n·Ā_n^{τ+1}·h_n of the state h
+    // entering it: h_in [b][d][n_chunks − 1][N]; delta [d], A, C [d][N] give Ā and C.
+    int64_t chunk;
+    const float *h_in, *delta, *A, *C;
+    int64_t N;
 };
 int lti_fft_log2(int64_t L);           // log2 of the transform size used for sequence length L
 hipError_t launch_lti_kernel(const LtiKernelLaunch &p, hipStream_t stream);
 hipError_t launch_lti_conv(const LtiConvLaunch &p, hipStream_t stream);
+
+// Chunk length of the chunked LTI form (sequences longer than one transform), and the states it passes:
+// H [b][d][n_chunks − 1][N] = the state at the end of chunks 0 .. n_chunks − 2 (from zero at t = 0).
+constexpr int64_t kLtiChunk = 4096;
+struct LtiChunkLaunch {
+    const void *x;
+    const float *delta, *A, *B;
+    float *H;
+    int64_t b, d, L, N, chunk;
+    bool bf16;
+};
+hipError_t launch_lti_chunk_states(const LtiChunkLaunch &p, hipStream_t stream);
 
 // Scalar-decay (state space duality) form, chunked on the MFMA units: heads of 64 channels, N in {32, 64, 128}.
 struct SsdLaunch {

@@ -51,6 +51,7 @@ namespace ssm {
 namespace {
 
 constexpr float kZeroAbsA = 5.421010862e-20f;  // 2^-64: |A| below this takes the A = 0 limit
+constexpr int64_t kAggWalkMinSeg = 1024;       // segments this long take the truncated backward aggregate walk
 constexpr float kPolyU = 1.0f / 16.0f;         // |u| below this: 2^u − 1 from its series (accurate tiles)
 // 2^u − 1 = u·(c1 + u·(c2 + u·c3)) + O(u^4): c_k = ln(2)^k / k!; relative error below 4e-6 at |u| = 1/16
 constexpr float kPolyC1 = 0.693147180559945f;
@@ -710,9 +711,20 @@ template <typename T, int G, int NPL, bool FE = false>
 hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLaunch &p, hipStream_t stream) {
     hipError_t e = hipSuccess;
     if (n_seg > 1) {
-        hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, true, FE>), dim3((unsigned)((n_seg - 1) * ncb)), dim3(kWave), 0,
-                           stream, args);
-        e = hipGetLastError();
+        // Segments of kAggWalkMinSeg steps or more take the truncated backward walk (agg_rev.hip): there a
+        // segment outlasts the decay of most states. Shorter ones (and the fused front end, whose x is the
+        // convolution computed on the way) take the forward aggregate pass: its wavefronts are equally long,
+        // where the walk of the slowest state group would run alone on its SIMD for the whole segment.
+        if (FE || p.seg_len < kAggWalkMinSeg) {
+            hipLaunchKernelGGL((scan_fwd_kernel<T, G, NPL, true, FE>), dim3((unsigned)((n_seg - 1) * ncb)), dim3(kWave),
+                               0, stream, args);
+            e = hipGetLastError();
+        } else {
+            AggLaunch g{};
+            g.x = p.x; g.delta = p.delta; g.A = p.A; g.B = p.B; g.P = args.agg_P; g.E = args.agg_E;
+            g.b = p.b; g.d = p.d; g.L = p.L; g.N = p.N; g.seg_len = p.seg_len; g.n_seg = n_seg; g.bf16 = p.bf16;
+            e = launch_agg_rev(g, stream);
+        }
         if (e != hipSuccess) return e;
         if (args.h_in) {
             const int64_t bdn = p.b * p.d * p.N;

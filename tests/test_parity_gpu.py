@@ -265,6 +265,63 @@ def test_initial_state_with_time_segments(dt, seg_len):
         assert plan["n_segments"] == 75
 
 
+# ------------------------------------------------------------------------------------------
+# Segments of 1024 steps or more take the aggregate pass that walks each segment backward and stops once the
+# decay back to the step reached is at most 2^-30 for every state of its wavefront (one group of four states
+# of 64 channels); P = exp(A·ΣΔ) still covers the whole segment. These cases make the walks stop at
+# different points, or never.
+# ------------------------------------------------------------------------------------------
+TRUNC = {
+    # fast decay: every group stops within a tile or two of the segment end
+    "fast": dict(L=3500, delta_mu=0.5, seg_len=1024),
+    # the Mamba-like spread: group 0 walks far, groups 1-3 stop early
+    "spread": dict(L=4096, delta_mu=-2.0, seg_len=1024),
+    # slow decay (|Δ·A| ~ 1e-4 per step): no walk stops
+    "slow": dict(L=3072, a_value=-0.01, delta_value=0.01, seg_len=1024),
+}
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("name", list(TRUNC))
+def test_truncated_aggregates(name, dt):
+    kw = dict(TRUNC[name])
+    L, seg = kw.pop("L"), kw.pop("seg_len")
+    b, d, N = 2, 96, 16
+    inp = I.random_prefill(b, d, L, N, dtype=dt, seed=41, **kw)
+    h0 = (np.random.default_rng(5).standard_normal((b, d, N)) * 3.0).astype(np.float32)
+    t = upload(inp)
+    y, h = api.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], seg_len=seg,
+                            initial_state=torch.from_numpy(h0).cuda())
+    torch.cuda.synchronize()
+    check_rows(inp, from_torch(y), from_torch(h), all_rows(b, d), f"truncated aggregates {name} {dt}",
+               h0=h0.astype(np.float64))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_truncated_aggregates_negative_delta_before_the_stop(dt):
+    """Δ < 0 (Ā > 1) early in segments whose walk stops before reaching them: the dropped part stays
+    negligible, and P = exp(A·ΣΔ) over the whole segment must still count those steps."""
+    b, d, L, N, seg = 2, 64, 4096, 16, 1024
+    inp = I.random_prefill(b, d, L, N, dtype=dt, seed=43, delta_mu=0.0)
+    dl = I.widen(inp["delta"], dt)
+    for s0 in range(0, L, seg):
+        dl[:, :, s0 + 10:s0 + 14] = -0.08
+    inp["delta"] = I.store(dl, dt)
+    y, h = run_fwd(inp, seg_len=seg)
+    check_rows(inp, y, h, all_rows(b, d), f"truncated aggregates, negative delta {dt}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_truncated_aggregates_odd_groups(dt):
+    """N = 5 and 33 (a last state group with one valid state), A = 0 and A > 0 states that never decay,
+    d not a multiple of 64."""
+    for N in (5, 33):
+        inp = I.random_prefill(2, 70, 2500, N, dtype=dt, seed=44 + N, delta_mu=-1.0, a_zero_frac=0.05)
+        inp["A"][3, N - 1] = np.float32(0.01)
+        y, h = run_fwd(inp, seg_len=1024)
+        check_rows(inp, y, h, all_rows(2, 70), f"truncated aggregates N={N} {dt}")
+
+
 def test_bitwise_deterministic():
     inp = I.random_prefill(2, 128, 700, 16, dtype="bf16", seed=4)
     a = run_fwd(inp)
