@@ -214,6 +214,10 @@ def bench_grad(name, steps, warmup, quiet=False):
     return res
 
 
+LTI_MAX_L = 8192   # one transform's sequence length (SSM_LTI_MAX_L)
+LTI_CHUNK = 4096   # chunk length of the longer, chunked form (SSM_LTI_CHUNK)
+
+
 def lti_fft_points(L):
     """Transform size of the LTI convolution for sequence length L (a power of two >= max(2L, 1024))."""
     m = 1024
@@ -233,18 +237,22 @@ def bench_lti(name, steps, warmup, quiet=False):
     inp = I.random_lti(w.b, w.d, w.L, w.N, dtype=w.dtype, gate=w.gate, seed=2)
     esize = 4 if w.dtype == "f32" else 2
     rows = w.b * w.d * w.L
-    # read x, z; write y; read the parameters; K̄ [d][L] fp32 is written once and read once
-    nbytes = rows * esize * (3 if w.gate else 2) + w.d * (3 * w.N + 2) * 4 + 2 * w.d * w.L * 4
-    M = lti_fft_points(w.L)
-    transforms = w.d * (1 + 2 * ((w.b + 1) // 2))
-    flops = transforms * 5 * M * math.log2(M) + w.d * ((w.b + 1) // 2) * 6 * M  # radix-2 count
+    # beyond one transform, chunks of 4096 steps joined through the state (K̄ over 4096 taps)
+    chunked = w.L > LTI_MAX_L
+    klen = LTI_CHUNK if chunked else w.L
+    n_chunks = -(-w.L // klen)
+    # read x, z; write y; read the parameters; K̄ [d][klen] fp32 is written once and read once per chunk
+    nbytes = rows * esize * (3 if w.gate else 2) + w.d * (3 * w.N + 2) * 4 + w.d * klen * 4 * (1 + n_chunks)
+    M = lti_fft_points(klen)
+    transforms = w.d * n_chunks * (1 + 2 * ((w.b + 1) // 2))
+    flops = transforms * 5 * M * math.log2(M) + w.d * n_chunks * ((w.b + 1) // 2) * 6 * M  # radix-2 count
     rotate = int(min(8, max(1, -(-2 * MALL_BYTES // nbytes))))
     par = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).cuda() for k in ("delta", "A", "B", "C", "D")}
     sets = []
     for _ in range(rotate):
         x = to_dev(inp["x"], "cuda")
         sets.append((x, to_dev(inp["z"], "cuda") if w.gate else None, torch.empty_like(x)))
-    K = api.ssm_lti_kernel(par["delta"], par["A"], par["B"], par["C"], w.L)
+    K = None if chunked else api.ssm_lti_kernel(par["delta"], par["A"], par["B"], par["C"], w.L)
 
     def timed(fn):
         warm_up(fn, warmup, EXTRA_WARM_S)
@@ -265,14 +273,18 @@ def bench_lti(name, steps, warmup, quiet=False):
         api.ssm_lti_conv(x, K, par["D"], z, y=y)
 
     ms = timed(full)
-    ms_conv = timed(conv_only)
-    res = {"pass": "lti_fft", "workload": name, "us_per_call": ms * 1e3, "us_conv_only": ms_conv * 1e3,
-           "elements_per_s": rows / (ms * 1e-3), "algorithmic_bytes": nbytes,
+    # the convolution alone (a given K̄) exists for one transform; the chunked form is timed whole
+    ms_conv = timed(conv_only) if not chunked else None
+    res = {"pass": "lti_fft", "workload": name, "us_per_call": ms * 1e3,
+           "us_conv_only": ms_conv * 1e3 if ms_conv else None, "chunked": chunked, "chunk": klen,
+           "n_chunks": n_chunks, "elements_per_s": rows / (ms * 1e-3), "algorithmic_bytes": nbytes,
            "GBps": nbytes / (ms * 1e-3) / 1e9, "fft_points": M, "transforms": transforms,
-           "fft_TFLOPs_conv": flops / (ms_conv * 1e-3) / 1e12}
+           "fft_TFLOPs_call": flops / (ms * 1e-3) / 1e12,
+           "fft_TFLOPs_conv": flops / (ms_conv * 1e-3) / 1e12 if ms_conv else None}
     if not quiet:
-        print(f"# lti {name}: {ms * 1e3:.1f} us/call (convolution alone {ms_conv * 1e3:.1f} us), "
-              f"{res['GBps']:.0f} GB/s, {res['fft_TFLOPs_conv']:.1f} TFLOP/s (5 M log2 M per transform)",
+        conv_txt = f"convolution alone {ms_conv * 1e3:.1f} us" if ms_conv else f"{n_chunks} chunks of {klen} steps"
+        print(f"# lti {name}: {ms * 1e3:.1f} us/call ({conv_txt}), {res['GBps']:.0f} GB/s, "
+              f"{res['fft_TFLOPs_call']:.1f} TFLOP/s over the call (5 M log2 M per transform)",
               file=sys.stderr, flush=True)
     del sets
     torch.cuda.empty_cache()
@@ -657,7 +669,7 @@ def main():
             for sn in SSD_SHAPES:
                 extra.append(bench_ssd(sn, 20, 3))
         elif n == "lti":
-            for cw in SIDE_WORKLOADS:
+            for cw in SIDE_WORKLOADS + ["longctx_bf16_b1_d2048_L131072_N16"]:
                 extra.append(bench_lti(cw, 20, 3))
         elif n == "conv":
             for cw in SIDE_WORKLOADS:

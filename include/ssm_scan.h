@@ -233,11 +233,17 @@ SSM_API ssm_status_t ssm_scan_step_conv(float *state, float *conv_state, const v
  *   D [d] fp32 or NULL. y may not overlap the inputs. b >= 1, 1 <= d <= 2^22,
  *   1 <= L <= SSM_LTI_MAX_L (SSM_ERR_UNSUPPORTED above it).
  *
- * ssm_lti_fwd: both: K̄ into scratch taken stream-ordered from `stream` (d·L·4 bytes), then the
- * convolution. No final state is produced (the convolution form has none; ssm_scan_fwd with the
- * parameters repeated over t gives it). Errors as for ssm_scan_fwd.
+ * ssm_lti_fwd: both: K̄ into scratch taken stream-ordered from `stream`, then the convolution; any L >= 1
+ * (below 2^40). Up to SSM_LTI_MAX_L steps: K̄ over L taps (d·L·4 bytes of scratch) and one transform per
+ * row pair. Longer: chunks of SSM_LTI_CHUNK steps, each convolved with K̄ over SSM_LTI_CHUNK taps, joined
+ * through the state, the other face of the same system (same page and section): each chunk's end state
+ * from zero, E_n = B̄_n·Σ_s Ā_n^{chunk−1−s}·x_s, is chained by h ← Ā^chunk·h + E into the state entering every
+ * later chunk, whose response Σ_n C_n·Ā_n^{τ+1}·h_n that chunk adds to its output τ steps in (scratch:
+ * d·SSM_LTI_CHUNK + b·d·(n_chunks − 1)·N floats). No final state is produced (the convolution form has none;
+ * ssm_scan_fwd with the parameters repeated over t gives it). Errors as for ssm_scan_fwd.
  */
 #define SSM_LTI_MAX_L 8192
+#define SSM_LTI_CHUNK 4096
 SSM_API ssm_status_t ssm_lti_kernel(const float *delta, const float *A, const float *B, const float *C, float *K,
                                     int64_t d, int64_t L, int64_t N, hipStream_t stream);
 SSM_API ssm_status_t ssm_lti_conv(const void *x, const float *K, const float *D, const void *z, void *y, int64_t b,

@@ -357,13 +357,14 @@ ssm_status_t lti_conv_check(const void *x, const float *K, bool k_internal, cons
                             const void *y, int64_t b, int64_t d, int64_t L, ssm_dtype_t dtype) {
     if (!valid_dtype(dtype)) return SSM_ERR_UNSUPPORTED;
     if (b < 1 || d < 1 || d > (INT64_C(1) << 22) || L < 1) return SSM_ERR_SHAPE;
-    if (L > SSM_LTI_MAX_L) return SSM_ERR_UNSUPPORTED;
+    if (L > SSM_LTI_MAX_L && !k_internal) return SSM_ERR_UNSUPPORTED;  // one transform holds a given K
+    if (L >= (INT64_C(1) << 40)) return SSM_ERR_SHAPE;
     int64_t bdl = 0;
     if (!mul_ok(b, d, &bdl) || !mul_ok(bdl, L, &bdl)) return SSM_ERR_SHAPE;
     if (!x || (!K && !k_internal) || !y) return SSM_ERR_NULL;
     const int64_t es = dtype == SSM_BF16 ? 2 : 4;
     const Span out{y, bdl * es};
-    const Span ins[] = {{x, bdl * es}, {z, bdl * es}, {K, d * L * 4}, {D, d * 4}};
+    const Span ins[] = {{x, bdl * es}, {z, bdl * es}, {K, K ? d * L * 4 : 0}, {D, d * 4}};
     for (const Span &in : ins)
         if (overlaps(out, in)) return SSM_ERR_ALIAS;
     return SSM_OK;
@@ -564,7 +565,8 @@ ssm_status_t ssm_lti_conv(const void *x, const float *K, const float *D, const v
                           int64_t L, ssm_dtype_t dtype, hipStream_t stream) {
     const ssm_status_t st = lti_conv_check(x, K, false, D, z, y, b, d, L, dtype);
     if (st != SSM_OK) return st;
-    const ssm::LtiConvLaunch p{x, z, K, D, y, b, d, L, dtype == SSM_BF16};
+    ssm::LtiConvLaunch p{};
+    p.x = x; p.z = z; p.K = K; p.D = D; p.y = y; p.b = b; p.d = d; p.L = L; p.bf16 = dtype == SSM_BF16;
     return ssm::launch_lti_conv(p, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -581,15 +583,38 @@ ssm_status_t ssm_lti_fwd(const void *x, const float *delta, const float *A, cons
     const Span ins[] = {{delta, d * 4}, {A, d * N * 4}, {B, d * N * 4}, {C, d * N * 4}};
     for (const Span &in : ins)
         if (overlaps(out, in)) return SSM_ERR_ALIAS;
-    void *K = nullptr;
-    if (scratch_alloc(&K, (size_t)(d * L) * sizeof(float), stream) != hipSuccess) return SSM_ERR_HIP;
-    const ssm::LtiKernelLaunch pk{delta, A, B, C, static_cast<float *>(K), d, L, N};
+    // Up to one transform's length: K̄ over the whole sequence, one convolution. Beyond it, the chunked form:
+    // K̄ over one chunk, the states between chunks (each chunk's end state from zero, chained by Ā^chunk),
+    // and a convolution per chunk that adds the response of the state entering it.
+    const bool chunked = L > SSM_LTI_MAX_L;
+    const int64_t klen = chunked ? ssm::kLtiChunk : L;
+    const int64_t n_chunks = (L + klen - 1) / klen;
+    int64_t hfl = 0;
+    if (chunked && (!mul_ok(b * d, (n_chunks - 1) * N, &hfl) || hfl > (INT64_C(1) << 40))) return SSM_ERR_SHAPE;
+    void *K = nullptr, *H = nullptr;
+    if (scratch_alloc(&K, (size_t)(d * klen) * sizeof(float), stream) != hipSuccess) return SSM_ERR_HIP;
+    if (chunked && scratch_alloc(&H, (size_t)hfl * sizeof(float), stream) != hipSuccess) {
+        (void)hipFreeAsync(K, stream);
+        return SSM_ERR_HIP;
+    }
+    const ssm::LtiKernelLaunch pk{delta, A, B, C, static_cast<float *>(K), d, klen, N};
     hipError_t e = ssm::launch_lti_kernel(pk, stream);
+    if (e == hipSuccess && chunked) {
+        const ssm::LtiChunkLaunch ph{x, delta, A, B, static_cast<float *>(H), b, d, L, N, klen, dtype == SSM_BF16};
+        e = ssm::launch_lti_chunk_states(ph, stream);
+    }
     if (e == hipSuccess) {
-        const ssm::LtiConvLaunch pc{x, z, static_cast<const float *>(K), D, y, b, d, L, dtype == SSM_BF16};
+        ssm::LtiConvLaunch pc{};
+        pc.x = x; pc.z = z; pc.K = static_cast<const float *>(K); pc.D = D; pc.y = y;
+        pc.b = b; pc.d = d; pc.L = L; pc.bf16 = dtype == SSM_BF16;
+        if (chunked) {
+            pc.chunk = klen; pc.h_in = static_cast<const float *>(H); pc.delta = delta; pc.A = A; pc.C = C; pc.N = N;
+        }
         e = ssm::launch_lti_conv(pc, stream);
     }
-    if (hipFreeAsync(K, stream) != hipSuccess) return SSM_ERR_HIP;
+    const hipError_t f1 = hipFreeAsync(K, stream);
+    const hipError_t f2 = H ? hipFreeAsync(H, stream) : hipSuccess;
+    if (f1 != hipSuccess || f2 != hipSuccess) return SSM_ERR_HIP;
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

@@ -122,7 +122,7 @@ hipError_t launch_lti_conv(const LtiConvLaunch &p, hipStream_t stream);
 
 // Chunk length of the chunked LTI form (sequences longer than one transform), and the states it passes:
 // H [b][d][n_chunks − 1][N] = the state at the end of chunks 0 .. n_chunks − 2 (from zero at t = 0).
-constexpr int64_t kLtiChunk = 4096;
+constexpr int64_t kLtiChunk = SSM_LTI_CHUNK;
 struct LtiChunkLaunch {
     const void *x;
     const float *delta, *A, *B;

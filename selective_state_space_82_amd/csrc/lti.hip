@@ -294,6 +294,10 @@ struct LtiConvArgs {
     const float *K, *D;
     void *y;
     int64_t b, d, L;
+    // chunked form: `chunk` > 0 steps per transform, n_chunks of them; h_in, delta, A, C as in LtiConvLaunch
+    int64_t chunk, n_chunks;
+    const float *h_in, *delta, *A, *C;
+    int64_t N;
 };
 
 template <typename T, int LOGM>
@@ -313,10 +317,21 @@ __global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiCo
         sincospif(2.0f * (float)i / (float)M, &s, &c);  // 2i/M is exact
         (j < M / 64 ? s_hi[j] : s_lo[j - M / 64]) = make_float2(c, -s);
     }
+    // workgroup -> (chunk j, channel id); one chunk spans the whole sequence when the form is not chunked
+    const int64_t id = blockIdx.x % a.d;
+    const int64_t j = blockIdx.x / a.d;
+    const int64_t klen = a.chunk > 0 ? a.chunk : a.L;  // taps of K per channel
+    const int64_t t0 = j * klen;                         // the chunk's first step
+    const int L = (int)((a.L - t0) < klen ? (a.L - t0) : klen);
+    // chunks after the first add the response of the state entering them: the log2 decays u_n and, per
+    // batch row of the pair, w_n = C_n·h_n
+    __shared__ float s_u[SSM_MAX_N], s_w[2][SSM_MAX_N];
+    const bool resp = a.h_in != nullptr && j > 0;
+    if (resp && threadIdx.x < a.N) {
+        const int64_t n = threadIdx.x;
+        s_u[n] = a.delta[id] * (a.A[id * a.N + n] * kLog2e);
+    }
     __syncthreads();
-    const int64_t id = blockIdx.x;
-
-    const int L = (int)a.L;
 
     // spectrum of K' (K̄ with D added to its first tap), kept in registers
     float2 kf[16];
@@ -324,7 +339,7 @@ __global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiCo
         const float dsk = a.D ? a.D[id] : 0.0f;
 #pragma unroll
         for (int s = 0; s < 16; ++s) kf[s] = make_float2(0.0f, 0.0f);
-        const float *Kd = a.K + id * a.L;
+        const float *Kd = a.K + id * klen;
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
             const int e = f.wide_pos(s);
@@ -341,7 +356,7 @@ __global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiCo
     for (int64_t b1 = 0; b1 < a.b; b1 += 2) {
         const bool two = b1 + 1 < a.b;
         // the pair's rows (workgroup-uniform pointers; per-lane offsets stay 32-bit)
-        const T *x1 = xg + (b1 * a.d + id) * a.L;
+        const T *x1 = xg + (b1 * a.d + id) * a.L + t0;
         const T *x2 = two ? x1 + a.d * a.L : x1;
         float2 v[16];
 #pragma unroll
@@ -350,12 +365,19 @@ __global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiCo
             const bool in = e < L;
             v[s] = make_float2(in ? widen(x1[e]) : 0.0f, in && two ? widen(x2[e]) : 0.0f);
         }
-        __syncthreads();  // the previous pair's last reads of s_buf are done
+        __syncthreads();  // the previous pair's last reads of s_buf (and s_w) are done
+        if (resp && threadIdx.x < a.N) {
+            const int64_t n = threadIdx.x;
+            const float cn = a.C[id * a.N + n];
+            const int64_t hrow = (b1 * a.d + id) * (a.n_chunks - 1) + (j - 1);
+            s_w[0][n] = cn * a.h_in[hrow * a.N + n];
+            s_w[1][n] = two ? cn * a.h_in[(hrow + a.d * (a.n_chunks - 1)) * a.N + n] : 0.0f;
+        }
         f.forward(v);
 #pragma unroll
         for (int s = 0; s < 16; ++s) v[s] = cmul(v[s], kf[s]);
         f.inverse(v);
-        const int64_t o1 = (b1 * a.d + id) * a.L;
+        const int64_t o1 = (b1 * a.d + id) * a.L + t0;
         const int64_t o2 = two ? o1 + a.d * a.L : o1;
         T *y1p = yg + o1, *y2p = yg + o2;
         const T *z1 = zg ? zg + o1 : nullptr, *z2 = zg ? zg + o2 : nullptr;
@@ -364,6 +386,14 @@ __global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiCo
             const int e = f.wide_pos(s);
             if (e < L) {
                 float y1 = v[s].x * inv_m, y2 = v[s].y * inv_m;
+                if (resp) {  // + Σ_n w_n·Ā_n^{e+1} (s_w was written before the transforms' barriers)
+                    const float k1 = (float)(e + 1);  // <= 2^13: exact
+                    for (int n = 0; n < (int)a.N; ++n) {
+                        const float pw = exp2_fast(k1 * s_u[n]);
+                        y1 = __builtin_fmaf(s_w[0][n], pw, y1);
+                        y2 = __builtin_fmaf(s_w[1][n], pw, y2);
+                    }
+                }
                 if (zg) {
                     y1 *= silu(widen(z1[e]));
                     if (two) y2 *= silu(widen(z2[e]));
@@ -377,8 +407,64 @@ __global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiCo
 
 template <typename T, int LOGM>
 hipError_t launch_conv_m(const LtiConvArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((lti_fft_conv_kernel<T, LOGM>), dim3((unsigned)a.d), dim3((1 << LOGM) / 16), 0, stream, a);
+    hipLaunchKernelGGL((lti_fft_conv_kernel<T, LOGM>), dim3((unsigned)(a.d * a.n_chunks)), dim3((1 << LOGM) / 16), 0,
+                       stream, a);
     return hipGetLastError();
+}
+
+// End state of chunk j of row (b, d) from zero, for chunks 0 .. n_chunks − 2 (all of full length):
+// E_n = B̄_n·Σ_s Ā_n^{chunk−1−s}·x_s. A workgroup per (row, chunk); thread i takes 16 consecutive steps by
+// Horner's rule (acc ← acc·Ā + x, so no power is formed) and scales its sum by Ā^{chunk−16−16i} (one exp);
+// the 256 partial sums of each state are added in LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void lti_chunk_agg_kernel(LtiChunkLaunch p, int64_t n_chunks) {
+    constexpr int kPer = 16;
+    __shared__ float s_part[256];
+    __shared__ float s_res[SSM_MAX_N];
+    const int64_t nc1 = n_chunks - 1;
+    const int64_t row = blockIdx.x / nc1;           // b·d + d
+    const int64_t j = blockIdx.x - row * nc1;
+    const int64_t id = row % p.d;
+    const int tid = threadIdx.x;
+    const T *xr = static_cast<const T *>(p.x) + row * p.L + j * p.chunk;
+    const int64_t s0 = (int64_t)tid * kPer;
+    float xv[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) xv[k] = s0 + k < p.chunk ? widen(xr[s0 + k]) : 0.0f;
+    const float dt = p.delta[id];
+    for (int n = 0; n < (int)p.N; ++n) {
+        const float an = p.A[id * p.N + n];
+        const float u = dt * (an * kLog2e);
+        const float abar = exp2_fast(u);
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) acc = __builtin_fmaf(acc, abar, xv[k]);
+        const int64_t rest = p.chunk - kPer - s0;  // steps after this thread's last one
+        s_part[tid] = rest >= 0 ? acc * exp2_fast((float)rest * u) : 0.0f;
+        __syncthreads();
+        for (int w = 128; w > 0; w >>= 1) {
+            if (tid < w) s_part[tid] += s_part[tid + w];
+            __syncthreads();
+        }
+        if (tid == 0) s_res[n] = s_part[0] * (zoh_input_coef_log2(dt, u, abar, 1.0f / an) * p.B[id * p.N + n]);
+        __syncthreads();
+    }
+    if (tid < p.N) p.H[(row * nc1 + j) * p.N + tid] = s_res[tid];
+}
+
+// The states between chunks, in place: H_j ← Ā^chunk·H_{j−1} + H_j per (row, n), walking the chunks in order.
+__global__ __launch_bounds__(256) void lti_chunk_carry_kernel(LtiChunkLaunch p, int64_t n_chunks) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (row, n)
+    if (i >= p.b * p.d * p.N) return;
+    const int64_t row = i / p.N, n = i - row * p.N, id = row % p.d;
+    const float pc = exp2_fast((float)p.chunk * (p.delta[id] * (p.A[id * p.N + n] * kLog2e)));
+    const int64_t nc1 = n_chunks - 1;
+    float *h = p.H + row * nc1 * p.N + n;
+    float acc = 0.0f;
+    for (int64_t j = 0; j < nc1; ++j) {
+        acc = __builtin_fmaf(pc, acc, h[j * p.N]);
+        h[j * p.N] = acc;
+    }
 }
 
 template <typename T>
@@ -413,11 +499,33 @@ hipError_t launch_lti_kernel(const LtiKernelLaunch &p, hipStream_t stream) {
 
 hipError_t launch_lti_conv(const LtiConvLaunch &p, hipStream_t stream) {
     if (p.b == 0 || p.d == 0 || p.L == 0) return hipSuccess;
-    const LtiConvArgs a{p.x, p.z, p.K, p.D, p.y, p.b, p.d, p.L};
-    const int logm = lti_fft_log2(p.L);
+    const int64_t klen = p.chunk > 0 ? p.chunk : p.L;
+    const int64_t n_chunks = (p.L + klen - 1) / klen;
+    const LtiConvArgs a{p.x, p.z, p.K, p.D, p.y, p.b, p.d, p.L, p.chunk, n_chunks,
+                        n_chunks > 1 ? p.h_in : nullptr, p.delta, p.A, p.C, p.N};
+    if (n_chunks > 1 && (!p.h_in || !p.delta || !p.A || !p.C || p.N < 1 || p.N > SSM_MAX_N)) return hipErrorInvalidValue;
+    if (p.d * n_chunks > 0x7fffffffLL) return hipErrorInvalidValue;
+    const int logm = lti_fft_log2(klen);
     if (logm > kLtiMaxLog2) return hipErrorInvalidValue;
     if (p.bf16) return launch_conv_typed<uint16_t>(a, logm, stream);
     return launch_conv_typed<float>(a, logm, stream);
+}
+
+hipError_t launch_lti_chunk_states(const LtiChunkLaunch &p, hipStream_t stream) {
+    const int64_t n_chunks = (p.L + p.chunk - 1) / p.chunk;
+    if (n_chunks <= 1 || p.b == 0 || p.d == 0) return hipSuccess;
+    if (p.chunk > 256 * 16 || p.N < 1 || p.N > SSM_MAX_N) return hipErrorInvalidValue;
+    const int64_t blocks = p.b * p.d * (n_chunks - 1);
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (p.bf16)
+        hipLaunchKernelGGL(lti_chunk_agg_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream, p, n_chunks);
+    else
+        hipLaunchKernelGGL(lti_chunk_agg_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, p, n_chunks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t rows = p.b * p.d * p.N;
+    hipLaunchKernelGGL(lti_chunk_carry_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, p, n_chunks);
+    return hipGetLastError();
 }
 
 }  // namespace ssm

@@ -16,6 +16,7 @@ hipError_t launch_conv1d(const ConvLaunch &, hipStream_t) { ++g_launches; return
 hipError_t launch_conv_step(const ConvStepLaunch &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_lti_kernel(const LtiKernelLaunch &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_lti_conv(const LtiConvLaunch &, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_lti_chunk_states(const LtiChunkLaunch &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_ssd(const SsdLaunch &, hipStream_t) { ++g_launches; return hipSuccess; }
 
 int lti_fft_log2(int64_t L) {

@@ -185,7 +185,7 @@ def test_lti_validation():
     assert fwd(delta=None) == 1
     assert fwd(N=0) == 2
     assert fwd(N=65) == 3
-    assert fwd(Ln=9000) == 3
+    assert fwd(Ln=9000) == 4                                        # chunked form: valid; scratch needs a device
     assert fwd(y=P(0x200000)) == 5                                   # y overlaps delta
 
 

@@ -132,6 +132,61 @@ def test_lti_matches_selective_scan_with_fixed_parameters():
     _assert_close(a, s, 2 * TAU["f32"], "LTI conv vs recurrent scan")
 
 
+def _oracle_recurrent(inp, rows):
+    """Oracle y [len(rows), L] by the recurrent face of the same system: the prefill scan with Δ, B and C of the
+    row's channel repeated over every step (page "Mambaとは？Transformer以外の系列モデル", section 固定SSMには
+    「再帰」と「畳み込み」の二つの顔がある: both faces give the same output). O(L·N) per row, for long L."""
+    dt = inp["dtype"]
+    x = I.widen(inp["x"], dt)
+    z = None if inp["z"] is None else I.widen(inp["z"], dt)
+    L = x.shape[2]
+    out = np.empty((len(rows), L))
+    for i, (ib, c) in enumerate(rows):
+        rep = lambda v: np.repeat(v[c][None, None, :], L, axis=1)
+        y, _ = oracle.scan_fwd(x[ib:ib + 1, c:c + 1], np.full((1, 1, L), inp["delta"][c]), inp["A"][c:c + 1],
+                               rep(inp["B"]), rep(inp["C"]), None if inp["D"] is None else inp["D"][c:c + 1],
+                               None if z is None else z[ib:ib + 1, c:c + 1])
+        out[i] = y[0, 0]
+    return out
+
+
+# Longer than one transform (8192 steps): chunks of 4096 steps, each convolved on its own with K̄[0, 4096),
+# joined by the state between chunks (each chunk's end state from zero, chained by Ā^4096) whose response
+# Σ_n C_n·Ā_n^{τ+1}·h_n every later chunk adds.
+LONG = [
+    # b, d, L, N, dtype, gate, fraction of A set to 0
+    (3, 8, 8193, 16, "f32", True, 0.0),     # one step past one transform: 3 chunks, the last of 1 step
+    (2, 24, 20000, 16, "f32", True, 0.1),   # 5 chunks, the last partial; A = 0 states (Ā = 1, B̄ = Δ·B)
+    (1, 17, 12289, 7, "bf16", True, 0.0),   # an odd batch: the last transform carries one row
+    (2, 6, 40000, 16, "bf16", False, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", LONG, ids=lambda c: f"b{c[0]}_d{c[1]}_L{c[2]}_N{c[3]}_{c[4]}_g{int(c[5])}")
+def test_lti_fwd_long_sequences_chunked(case):
+    b, d, L, N, dt, gate, a0 = case
+    inp = I.random_lti(b, d, L, N, dtype=dt, gate=gate, seed=L + N, a_zero_frac=a0)
+    t = _upload(inp)
+    y = api.ssm_lti_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"])
+    torch.cuda.synchronize()
+    rows = [(ib, c) for ib in range(b) for c in range(d)]
+    yr = _oracle_recurrent(inp, rows)
+    yg = from_torch(y)
+    _assert_close(np.stack([yg[ib, c] for ib, c in rows]), yr, TAU[dt], f"long L{L} {dt}")
+
+
+def test_lti_fwd_long_against_direct_convolution():
+    """The chunked form against the oracle's direct causal convolution with the full-length K̄ (two rows)."""
+    inp = I.random_lti(2, 4, 12000, 16, dtype="f32", seed=77)
+    t = _upload(inp)
+    y = api.ssm_lti_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"])
+    torch.cuda.synchronize()
+    rows = [(0, 1), (1, 3)]
+    yr, _ = _oracle(inp, rows)
+    yg = from_torch(y)
+    _assert_close(np.stack([yg[ib, c] for ib, c in rows]), yr, TAU["f32"], "long L12000 vs direct convolution")
+
+
 @pytest.mark.parametrize("shape", [(4, 1536, 2048, 16, "f32"), (8, 4096, 4096, 16, "bf16")],
                          ids=["mamba130m_shape_f32", "mamba1p4b_shape_bf16"])
 def test_lti_full_size_sampled(shape):
