@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ssm_scan.h"
+
 namespace ssm {
 
 // Everything the prefill launchers need; validated by the ABI layer beforehand.
