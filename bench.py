@@ -669,7 +669,7 @@ def main():
             for sn in SSD_SHAPES:
                 extra.append(bench_ssd(sn, 20, 3))
         elif n == "lti":
-            for cw in SIDE_WORKLOADS + ["longctx_bf16_b1_d2048_L131072_N16"]:
+            for cw in tuple(SIDE_WORKLOADS) + ("longctx_bf16_b1_d2048_L131072_N16",):
                 extra.append(bench_lti(cw, 20, 3))
         elif n == "conv":
             for cw in SIDE_WORKLOADS:
