@@ -300,7 +300,9 @@ struct LtiConvArgs {
     int64_t N;
 };
 
-template <typename T, int LOGM>
+// RESP: the chunked form, whose chunks after the first add the response of the state entering them (a
+// separate instantiation: the response's loop in the epilogue costs the single-transform form registers).
+template <typename T, int LOGM, bool RESP>
 // At most 128 VGPRs (four wavefronts per SIMD), so that four workgroups of 256 threads or two of 512 share
 // a CU; measured: without the bound, 2^13 points ran at 178 VGPRs, one workgroup per CU, and 1.7× slower.
 __global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiConvArgs a) {
@@ -325,8 +327,8 @@ __global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiCo
     const int L = (int)((a.L - t0) < klen ? (a.L - t0) : klen);
     // chunks after the first add the response of the state entering them: the log2 decays u_n and, per
     // batch row of the pair, w_n = C_n·h_n
-    __shared__ float s_u[SSM_MAX_N], s_w[2][SSM_MAX_N];
-    const bool resp = a.h_in != nullptr && j > 0;
+    __shared__ float s_u[RESP ? SSM_MAX_N : 1], s_w[2][RESP ? SSM_MAX_N : 1];
+    const bool resp = RESP && j > 0;
     if (resp && threadIdx.x < a.N) {
         const int64_t n = threadIdx.x;
         s_u[n] = a.delta[id] * (a.A[id * a.N + n] * kLog2e);
@@ -386,13 +388,15 @@ __global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiCo
             const int e = f.wide_pos(s);
             if (e < L) {
                 float y1 = v[s].x * inv_m, y2 = v[s].y * inv_m;
-                if (resp) {  // + Σ_n w_n·Ā_n^{e+1} (s_w was written before the transforms' barriers)
+                if (RESP && resp) {  // + Σ_n w_n·Ā_n^{e+1} (s_w was written before the transforms' barriers)
                     const float k1 = (float)(e + 1);  // <= 2^13: exact
+#pragma unroll 1
                     for (int n = 0; n < (int)a.N; ++n) {
                         const float pw = exp2_fast(k1 * s_u[n]);
                         y1 = __builtin_fmaf(s_w[0][n], pw, y1);
                         y2 = __builtin_fmaf(s_w[1][n], pw, y2);
                     }
+                    asm volatile("" : "+v"(y1), "+v"(y2));  // one slot at a time: the loop holds few registers
                 }
                 if (zg) {
                     y1 *= silu(widen(z1[e]));
@@ -407,8 +411,15 @@ __global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiCo
 
 template <typename T, int LOGM>
 hipError_t launch_conv_m(const LtiConvArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((lti_fft_conv_kernel<T, LOGM>), dim3((unsigned)(a.d * a.n_chunks)), dim3((1 << LOGM) / 16), 0,
-                       stream, a);
+    const dim3 grid((unsigned)(a.d * a.n_chunks)), block((1 << LOGM) / 16);
+    if (a.h_in) {
+        if constexpr ((int64_t(1) << LOGM) == 2 * kLtiChunk) {
+            hipLaunchKernelGGL((lti_fft_conv_kernel<T, LOGM, true>), grid, block, 0, stream, a);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;  // the chunked form uses one transform size
+    }
+    hipLaunchKernelGGL((lti_fft_conv_kernel<T, LOGM, false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
