@@ -174,9 +174,11 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
     // ---- tile staging (reverse order: tile it + 1 is processed before tile it) ----
     uint4 px[kXC], pd[kXC], pz[kXC], pg[kXC], pb[kBC], pc[kBC];
     auto load_tile = [&](int64_t t0) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));  // form the addresses here rather than keep them across the walk
 #pragma unroll
         for (int i = 0; i < kXC; ++i) {
-            const int k = lane + i * kWave;
+            const int k = ln + i * kWave;
             const int r = k / kRowChunks;
             const int64_t tt = t0 + (k % kRowChunks) * E;
             const bool rok = k < CW * kRowChunks && d0 + r < a.d;
@@ -190,16 +192,18 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
         const int64_t nel = rows * a.N;
 #pragma unroll
         for (int i = 0; i < kBC; ++i) {
-            const int64_t e0 = (int64_t)(lane + i * kWave) * E;
+            const int64_t e0 = (int64_t)(ln + i * kWave) * E;
             const bool ok = e0 < (int64_t)kBT * N;
             if constexpr (!REV) pb[i] = get_chunk<T>(Bg + t0 * a.N, e0, nel, ok, a.vec_bc);
             pc[i] = get_chunk<T>(Cg + t0 * a.N, e0, nel, ok, a.vec_bc);
         }
     };
     auto store_tile = [&]() {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));  // as in load_tile
 #pragma unroll
         for (int i = 0; i < kXC; ++i) {
-            const int k = lane + i * kWave;
+            const int k = ln + i * kWave;
             if (k >= CW * kRowChunks) break;
             const int r = k / kRowChunks;
             const int col = (k % kRowChunks) * E;
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(kWave, 2) void scan_bwd_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < kBC; ++i) {
-            const int e0 = (lane + i * kWave) * E;
+            const int e0 = (ln + i * kWave) * E;
             if (e0 >= kBT * N) break;
             if (N == NPAD) {
                 if constexpr (!REV) put_chunk<T>(Bs + e0, pb[i]);
