@@ -277,9 +277,13 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
     // ---- tile prefetch into registers, and from there into LDS ----
     uint4 px[kXC], pd[kXC], pz[kXC], pb[kBC], pc[kBC];
     auto load_tile = [&](int64_t t0) {
+        // The fused kernels form the staging addresses at each tile (the empty asm hides that they do not
+        // change): kept across the scan, they spilled there (and only there; elsewhere keeping them is faster)
+        int ln = lane;
+        if constexpr (FE) asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int i = 0; i < kXC; ++i) {
-            const int k = lane + i * kWave;
+            const int k = ln + i * kWave;
             const int r = k / kRowChunks;
             const int64_t tt = t0 + (k % kRowChunks) * E;
             const bool rok = k < CW * kRowChunks && d0 + r < a.d;
@@ -294,7 +298,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
         const int64_t nel = rows * a.N;
 #pragma unroll
         for (int i = 0; i < kBC; ++i) {
-            const int64_t e0 = (int64_t)(lane + i * kWave) * E;
+            const int64_t e0 = (int64_t)(ln + i * kWave) * E;
             const bool ok = e0 < (int64_t)kTile * N;
             pb[i] = get_chunk<T>(Bg + t0 * a.N, e0, nel, ok, a.vec_bc);
             if constexpr (RO) pc[i] = get_chunk<T>(Cg + t0 * a.N, e0, nel, ok, a.vec_bc);
@@ -302,6 +306,8 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
     };
     // Stages the tile starting at step t0 (first: the unit's first tile, whose halo came from memory).
     auto store_tile = [&](int64_t t0, bool first) {
+        int ln = lane;
+        if constexpr (FE) asm volatile("" : "+v"(ln));  // as in load_tile
         if constexpr (FE) {
             if (!first) {  // the previous tile's last inputs become this tile's halo
                 const float tail = xraw[fr * kRawPitch + kTile + fq];
@@ -312,7 +318,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
         }
 #pragma unroll
         for (int i = 0; i < kXC; ++i) {
-            const int k = lane + i * kWave;
+            const int k = ln + i * kWave;
             if (k >= CW * kRowChunks) break;
             const int r = k / kRowChunks;
             const int col = (k % kRowChunks) * E;
@@ -372,7 +378,7 @@ __device__ __forceinline__ void scan_unit(const FwdArgs &a, int64_t blk) {
         }
 #pragma unroll
         for (int i = 0; i < kBC; ++i) {
-            const int e0 = (lane + i * kWave) * E;
+            const int e0 = (ln + i * kWave) * E;
             if (e0 >= kTile * N) break;
             if (N == NPAD) {  // the run maps onto the [kTile][NPAD] plane one to one
                 put_chunk<T>(Bs + e0, pb[i]);
