@@ -500,7 +500,7 @@ hipError_t launch_ssd(const SsdLaunch &p, hipStream_t stream) {
     a.S = p.scratch;
     const int64_t es = p.bf16 ? 2 : 4;
     auto aligned = [&](const void *q) { return (reinterpret_cast<uintptr_t>(q) & (uintptr_t)(4 * es - 1)) == 0; };
-    a.vec = (p.L % 4) == 0 && aligned(p.x);
+    a.vec = (p.L % 4) == 0 && aligned(p.x) && aligned(p.y) && (!p.z || aligned(p.z));
     a.vec_bc = aligned(p.B) && aligned(p.C);  // N is a multiple of 32
     a.vec8 = p.bf16 && (p.L % 8) == 0 && (reinterpret_cast<uintptr_t>(p.x) & 15) == 0;
     a.decay = p.scratch ? p.scratch + a.b * a.H * a.nc * (kP * p.N) : nullptr;

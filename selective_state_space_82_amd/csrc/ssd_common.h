@@ -26,7 +26,7 @@ struct SsdArgs {
     float *S;      // [b][H][nc][P][N] chunk states, then entering states
     float *decay;  // [b][H][nc]
     int64_t b, H, L, nc;
-    bool vec;      // x rows allow 16-byte (fp32) / 8-byte (bf16) loads at 4-element steps
+    bool vec;      // x, z and y rows allow 16-byte (fp32) / 8-byte (bf16) accesses at 4-element steps
     bool vec_bc;   // so do the rows of B and C
     bool vec8;     // x rows allow 16-byte loads at 8-element steps (bf16)
     bool fused;    // chunk states and their pass in one kernel (ssd_scan_kernel)

@@ -202,67 +202,76 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(SsdArgs a) {
 
 // ---- the whole chunked form in one ordered walk (bf16 storage) ---------------------------------------
 //
-// Workgroup (b, h) keeps the head's whole [P][N] state in MFMA accumulators (tile τ = w + 4j of the
-// 2·N/32 tiles of 32×32: rows 32(τ % 2) .., columns 32(τ / 2) ..) and, chunk by chunk in order, computes
-// the outputs from the entering state and then advances the state, so neither chunk states nor entering
-// states touch HBM: it reads x, z, Δ, B, C once and writes y once. Per chunk (Q = 64 steps):
-//   G = C Bᵀ on the three 32×32 tiles at or below the diagonal (bf16 products, exact inputs), then
-//     M[t][s] = G e^{a(c_t − c_s)} β_s for s <= t;
-//   Y = M Xᵀ + diag(e^{a c_t}) C H_inᵀ (M and H_in enter the bf16 products as hi + lo);
-//   y = Y + D x, times silu(z);  H ← e^{a c_end} H + X_w Bᵀ with X_w = x e^{a(c_end − c_s)} β_s.
-// The next chunk's Δ, B, C, x and this chunk's z arrive in registers while the current chunk is
-// multiplied. It needs about 2 workgroups per CU (b·H of them, 114 KB of LDS each, one per CU at a time).
-template <int N>
-__global__ __launch_bounds__(kThreads, 1) void ssd_fused_kernel(SsdArgs a) {
+// Workgroup (b, h) walks the chunks of one head in order and keeps its state in MFMA accumulators, so
+// neither chunk states nor entering states touch HBM: it reads x, z, Δ, B, C once and writes y once.
+// Per chunk (Q = 64 steps), with M[t][s] = (C_t·B_s) e^{a(c_t − c_s)} β_s for s <= t:
+//   y_t = e^{a c_t} C_t·h_in + Σ_s M[t][s] x_s + D x_t, times silu(z);
+//   h ← e^{a c_end} h + Σ_s e^{a(c_end − c_s)} β_s x_s B_sᵀ.
+// Wavefront w owns the output tile of steps 32·T .. and channels 32·Pt .. (T = w & 1, Pt = w >> 1) and
+// holds the state columns of its 32 channels over all N states, Hᵀ[n][p], as N/32 accumulator tiles (the
+// two wavefronts of a channel block keep identical copies and update them alike).
+//
+// The accumulator layout does the transposes. Lane l of a 32×32 accumulator holds column l % 32 and,
+// in registers 8κ .. 8κ+7, rows 16κ + {0..3, 8..11} + 4·(l / 32). Read as an MFMA operand those registers
+// are the lane's eight k values of the K block 16κ .. 16κ+15 in that order, so a tile of Hᵀ[n][p] is
+// directly the k = n operand of C·Hᵀ, and a tile of Mᵀ[s][t] (formed as B·Cᵀ) is the k = s operand of
+// M·x. The other operand of each of those products (C, x, Bᵀ rows in LDS) is read in the same k order:
+// two 8-byte LDS reads per lane and K block. Only the decayed product tiles cross wavefronts, as bf16
+// hi and lo planes in LDS in lane order.
+//
+// LDS holds the chunk's C, B, Bᵀ and x (bf16), the decayed product tiles and the chunk's scalars, about
+// 75 KB at N = 128, so two workgroups share a compute unit and each one's barriers and exponentials
+// overlap the other's products. Two barriers per chunk: the second lets the next chunk's staging
+// overwrite the operands while this chunk's outputs are formed from registers and the product tiles.
+// VEC: every row piece is whole and aligned (L a multiple of 8; x, y, z, B, C aligned), so loads and
+// stores go by 16 (8) bytes with one guard per piece; otherwise element by element.
+template <int N, bool VEC>
+__global__ __launch_bounds__(kThreads, VEC ? 2 : 1) void ssd_fused_kernel(SsdArgs a) {
     static_assert(N == 64 || N == 128, "state widths");
     constexpr int NH = N + 8;       // bf16 row stride of N-wide LDS rows
-    constexpr int NF = N + 4;       // fp32 row stride of N-wide LDS rows
     constexpr int HN = N / 2;
-    constexpr int TPW = N / 64;     // state tiles per wavefront
+    constexpr int NT = N / 32;      // state tiles per wavefront
     constexpr int CK = N / 32;      // 16-byte pieces of C (and of B) per thread per chunk
-    __shared__ __align__(16) float s_cum[kQ], s_beta[kQ], s_w[kQ];
+    __shared__ __align__(16) float s_cum[kQ], s_beta[kQ], s_w[kQ], s_et[kQ];
     __shared__ __align__(16) uint16_t s_c[kQ * NH];    // C [t][n]
     __shared__ __align__(16) uint16_t s_b[kQ * NH];    // B [s][n]
     __shared__ __align__(16) uint16_t s_bt[N * kMH];   // Bᵀ [n][s]
     __shared__ __align__(16) uint16_t s_x[kP * kMH];   // x [p][s]
-    __shared__ __align__(16) float s_h[kP * NF];       // entering state [p][n]
-    __shared__ __align__(16) float s_m[kQ * kMS];      // M [t][s]
-    __shared__ __align__(16) float s_o[kP * kMS];      // the outputs [p][t]
+    __shared__ __align__(16) uint4 s_m[3 * 4 * kWave]; // decayed product tiles: [tile][K block, hi / lo][lane]
     const int64_t bh = blockIdx.x, ib = bh / a.H, h = bh % a.H;
     const float ah = a.A[h];
-    const int l = lane(), w = wave(), hi = l / 32, tid = threadIdx.x;
+    const int l = lane(), w = wave(), hi = l / 32, lc = l % 32, tid = threadIdx.x;
+    const int T = w & 1, Pt = w >> 1;
+    const int p = 32 * Pt + lc;              // this lane's channel in the output and state tiles
+    // the decayed product tiles Mᵀ[s][t] with s <= t: (S, T) = (0, 0), (0, 1), (1, 1), slot S + T,
+    // formed by wavefronts 0, 1 and 3
+    const bool gw = w != 2;
+    const int gS = w == 3 ? 1 : 0;
 
-    // the state tiles of this wavefront
-    auto tq_p = [&](int j) { return (w + 4 * j) % 2; };
-    auto tq_n = [&](int j) { return (w + 4 * j) / 2; };
-    auto st_off = [&](int j, int r) {
-        return (int64_t)(32 * tq_p(j) + d_row(r, l)) * N + 32 * tq_n(j) + l % 32;
-    };
-    f16v acc[TPW];
+    f16v acc[NT];  // acc[nt][r] = h[p][32 nt + d_row(r, l)]
 #pragma unroll
-    for (int j = 0; j < TPW; ++j)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[j][r] = a.h0 ? a.h0[bh * (kP * N) + st_off(j, r)] : 0.0f;
+        for (int r = 0; r < 16; ++r)
+            acc[nt][r] = a.h0 ? a.h0[bh * (kP * N) + (int64_t)p * N + 32 * nt + d_row(r, l)] : 0.0f;
 
     const uint16_t *dg = static_cast<const uint16_t *>(a.delta) + bh * a.L;
     const uint16_t *cg = static_cast<const uint16_t *>(a.C) + ib * a.L * N;
     const uint16_t *bg = static_cast<const uint16_t *>(a.B) + ib * a.L * N;
     const uint16_t *xg = static_cast<const uint16_t *>(a.x) + ((ib * a.H + h) * kP) * a.L;
-    const uint16_t *zg = static_cast<const uint16_t *>(a.z);
-    uint16_t *yg = static_cast<uint16_t *>(a.y);
-    // per-thread pieces: C row c_r(k) columns c_c(k) .. +7 (16 lanes per row); B row l, columns
+    const uint16_t *zg = a.z ? static_cast<const uint16_t *>(a.z) + ((ib * a.H + h) * kP + p) * a.L : nullptr;
+    uint16_t *yg = static_cast<uint16_t *>(a.y) + ((ib * a.H + h) * kP + p) * a.L;
+    // staging pieces: C row c_r(k) columns c_c(k) .. +7 (16 lanes per row); B row l, columns
     // 8(w + 4k) .. +7 (one row per lane, so that the transposed stores spread over the banks); x row
-    // x_r(k), steps x_c(k) .. +7; the epilogue's 4-step groups e_p(k), e_t(k) .. +3
-    auto c_r = [&](int k) { return (tid + k * kThreads) / (N / 8); };
-    auto c_c = [&](int k) { return ((tid + k * kThreads) % (N / 8)) * 8; };
+    // x_r(k), steps x_c(k) .. +7
+    auto c_r = [&](int k, int t = threadIdx.x) { return (t + k * kThreads) / (N / 8); };
+    auto c_c = [&](int k, int t = threadIdx.x) { return ((t + k * kThreads) % (N / 8)) * 8; };
     auto b_c = [&](int k) { return 8 * (w + 4 * k); };
-    auto x_r = [&](int k) { return (tid + k * kThreads) / 8; };
-    auto x_c = [&](int k) { return ((tid + k * kThreads) % 8) * 8; };
-    auto e_p = [&](int k) { return (tid + k * kThreads) / 16; };
-    auto e_t = [&](int k) { return ((tid + k * kThreads) % 16) * 4; };
-    // 8 consecutive bf16 of a row as raw bits, zeros at and past `limit` (16-byte load when allowed)
-    auto raw8 = [](const uint16_t *row, int64_t i, int64_t limit, bool vec) {
-        if (vec && i + 8 <= limit) return *reinterpret_cast<const uint4 *>(row + i);
+    auto x_r = [&](int k, int t = threadIdx.x) { return (t + k * kThreads) / 8; };
+    auto x_c = [&](int k, int t = threadIdx.x) { return ((t + k * kThreads) % 8) * 8; };
+    // 8 consecutive bf16 of a row as raw bits, zeros at and past `limit`
+    auto raw8 = [](const uint16_t *row, int64_t i, int64_t limit) {
+        if (VEC) return i + 8 <= limit ? *reinterpret_cast<const uint4 *>(row + i) : make_uint4(0u, 0u, 0u, 0u);
         uint16_t e[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) e[k] = i + k < limit ? row[i + k] : (uint16_t)0;
@@ -270,54 +279,56 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_fused_kernel(SsdArgs a) {
         __builtin_memcpy(&r, e, sizeof(r));
         return r;
     };
-    float dsk[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) dsk[k] = a.D ? a.D[h * kP + e_p(k)] : 0.0f;
+    const float dsk = a.D ? a.D[h * kP + p] : 0.0f;
 
-    float dtr = 0.0f;
+    float dtr = 0.0f, dec = 0.0f;
     uint4 cq[CK], bq[CK], xq[2];
     uint2 zq[4];
+    // The loads take the thread index behind an empty asm, so that their per-lane addresses are formed at
+    // each chunk rather than kept (and spilled) across the walk.
     auto load_chunk = [&](int64_t c) {
+        int th = tid;
+        asm volatile("" : "+v"(th));
+        const int ln = th % kWave;
         const int64_t t0 = c * kQ;
-        dtr = t0 + l < a.L ? widen(dg[t0 + l]) : 0.0f;
+        dtr = t0 + ln < a.L ? widen(dg[t0 + ln]) : 0.0f;
 #pragma unroll
         for (int k = 0; k < CK; ++k) {
-            const int cr = c_r(k);
-            cq[k] = raw8(cg + (t0 + cr) * N, c_c(k), t0 + cr < a.L ? N : 0, a.vec_bc16);
-            bq[k] = raw8(bg + (t0 + l) * N, b_c(k), t0 + l < a.L ? N : 0, a.vec_bc16);
+            const int cr = c_r(k, th);
+            cq[k] = raw8(cg + (t0 + cr) * N, c_c(k, th), t0 + cr < a.L ? N : 0);
+            bq[k] = raw8(bg + (t0 + ln) * N, b_c(k), t0 + ln < a.L ? N : 0);
         }
 #pragma unroll
-        for (int k = 0; k < 2; ++k) xq[k] = raw8(xg + x_r(k) * a.L + t0, x_c(k), a.L - t0, a.vec8);
+        for (int k = 0; k < 2; ++k) xq[k] = raw8(xg + x_r(k, th) * a.L + t0, x_c(k, th), a.L - t0);
     };
+    // z at this lane's output positions: channel p, steps 32 T + 8q + 4 hi .. +3
     auto load_z = [&](int64_t c) {
+        int ln = l;
+        asm volatile("" : "+v"(ln));
         const int64_t t0 = c * kQ;
+        const uint16_t *zr = zg ? static_cast<const uint16_t *>(a.z) + ((ib * a.H + h) * kP + 32 * Pt + ln % 32) * a.L + t0
+                                : nullptr;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            zq[k] = zg ? raw4<uint16_t>(zg + ((ib * a.H + h) * kP + e_p(k)) * a.L + t0, e_t(k), a.L - t0, a.vec)
-                       : make_uint2(0u, 0u);
-    };
-    load_chunk(0);
-    load_z(0);
-    for (int64_t c = 0; c < a.nc; ++c) {
-        const int64_t t0 = c * kQ;
-        const int64_t lim = a.L - t0;
-        // running sums of Δ·a·log2 e, β, the state-update weights and the chunk decay (every wavefront
-        // computes them; wavefront 0 publishes them)
-        float dec;
-        {
-            const float u = dtr * (ah * kLog2e);
-            const float abar = exp2_fast(u);
-            const float beta = zoh_input_coef_log2(dtr, u, abar, 1.0f / ah);
-            const float cu = wave_prefix_sum(u);
-            const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cu), 63));
-            dec = exp2_fast(cend);
-            if (w == 0) {
-                s_cum[l] = cu;
-                s_beta[l] = beta;
-                s_w[l] = exp2_fast(cend - cu) * beta;
-            }
+        for (int q = 0; q < 4; ++q) {
+            const int t4 = 32 * T + 8 * q + 4 * (ln / 32);
+            if (VEC) zq[q] = zr && t4 + 4 <= a.L - t0 ? *reinterpret_cast<const uint2 *>(zr + t4) : make_uint2(0u, 0u);
+            else zq[q] = zr ? raw4<uint16_t>(zr, t4, a.L - t0, false) : make_uint2(0u, 0u);
         }
-        // stage C, B, Bᵀ and x; write out the entering state
+    };
+    // the chunk's scalars (every wavefront forms them from Δ; wavefront 0 publishes them) and its operands
+    auto stage = [&]() {
+        const float u = dtr * (ah * kLog2e);
+        const float abar = exp2_fast(u);
+        const float beta = zoh_input_coef_log2(dtr, u, abar, 1.0f / ah);
+        const float cu = wave_prefix_sum(u);
+        const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cu), 63));
+        dec = exp2_fast(cend);
+        if (w == 0) {
+            s_cum[l] = cu;
+            s_beta[l] = beta;
+            s_w[l] = exp2_fast(cend - cu) * beta;
+            s_et[l] = exp2_fast(cu);
+        }
 #pragma unroll
         for (int k = 0; k < CK; ++k) {
             *reinterpret_cast<uint4 *>(s_c + c_r(k) * NH + c_c(k)) = cq[k];
@@ -329,112 +340,171 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_fused_kernel(SsdArgs a) {
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k) *reinterpret_cast<uint4 *>(s_x + x_r(k) * kMH + x_c(k)) = xq[k];
-#pragma unroll
-        for (int j = 0; j < TPW; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                s_h[(32 * tq_p(j) + d_row(r, l)) * NF + 32 * tq_n(j) + l % 32] = acc[j][r];
-        if (c + 1 < a.nc) load_chunk(c + 1);
-        lds_barrier();
+    };
+    // eight bf16 of an LDS row in accumulator row order: row[0 .. 3] and row[8 .. 11]
+    auto pair8 = [](const uint16_t *row) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(row), v = *reinterpret_cast<const uint2 *>(row + 8);
+        return make_uint4(u.x, u.y, v.x, v.y);
+    };
+    auto bf8 = [](const uint4 &v) { return __builtin_bit_cast(bf8v, v); };
 
-        // G = C Bᵀ (wavefronts 0..2) and the state update (all)
+    load_chunk(0);
+    load_z(0);
+    stage();
+    if (a.nc > 1) load_chunk(1);
+    for (int64_t c = 0; c < a.nc; ++c) {
+        const int64_t t0 = c * kQ;
+        const int64_t lim = a.L - t0;
+        lds_barrier();  // the chunk's operands and scalars; the previous chunk's product tiles are consumed
+
+        // G = B Cᵀ for this wavefront's product tile (rows s = 32 gS .., columns t = 32 T ..)
         f16v g = {};
-        const int qt = w == 0 ? 0 : 1, qs = w == 2 ? 1 : 0;
-        if (w < 3) mfma_tile_bf16<HN>(g, s_c + (32 * qt + l % 32) * NH + hi * HN, s_b + (32 * qs + l % 32) * NH + hi * HN);
+        if (gw) {
+            const uint16_t *arow = s_b + (32 * gS + lc) * NH + hi * HN, *brow = s_c + (32 * T + lc) * NH + hi * HN;
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) {
+            for (int j = 0; j < HN / 8; ++j)
+                g = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf8v *>(arow + 8 * j),
+                                                            *reinterpret_cast<const bf8v *>(brow + 8 * j), g, 0, 0, 0);
+        }
+        // the entering state's part: e^{a c_t} C_t·h_in (C rows in accumulator order, Hᵀ as hi + lo)
+        f16v y = {};
+        {
+            const uint16_t *crow = s_c + (32 * T + lc) * NH + 4 * hi;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[j][r] *= dec;
-            const uint16_t *xr = s_x + (32 * tq_p(j) + l % 32) * kMH + 32 * hi;
-            const float *wr = s_w + 32 * hi;
-            const uint16_t *br = s_bt + (32 * tq_n(j) + l % 32) * kMH + 32 * hi;
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const uint4 xv = *reinterpret_cast<const uint4 *>(xr + 8 * jj);
-                const float4 w0 = *reinterpret_cast<const float4 *>(wr + 8 * jj), w1 = *reinterpret_cast<const float4 *>(wr + 8 * jj + 4);
-                const float4 u0 = make_float4(bf16_lo(xv.x) * w0.x, bf16_hi(xv.x) * w0.y, bf16_lo(xv.y) * w0.z, bf16_hi(xv.y) * w0.w);
-                const float4 u1 = make_float4(bf16_lo(xv.z) * w1.x, bf16_hi(xv.z) * w1.y, bf16_lo(xv.w) * w1.z, bf16_hi(xv.w) * w1.w);
+                for (int kk = 0; kk < 2; ++kk) {
+                    bf8v h8, l8;
+                    split8(make_float4(acc[nt][8 * kk], acc[nt][8 * kk + 1], acc[nt][8 * kk + 2], acc[nt][8 * kk + 3]),
+                           make_float4(acc[nt][8 * kk + 4], acc[nt][8 * kk + 5], acc[nt][8 * kk + 6], acc[nt][8 * kk + 7]),
+                           h8, l8);
+                    const bf8v c8 = bf8(pair8(crow + 32 * nt + 16 * kk));
+                    y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c8, h8, y, 0, 0, 0);
+                    y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c8, l8, y, 0, 0, 0);
+                }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 e4 = *reinterpret_cast<const float4 *>(s_et + 32 * T + 8 * q + 4 * hi);
+                y[4 * q] *= e4.x; y[4 * q + 1] *= e4.y; y[4 * q + 2] *= e4.z; y[4 * q + 3] *= e4.w;
+            }
+        }
+        // the decayed product tile, split into bf16 hi and lo for the wavefronts that multiply it
+        if (gw) {
+            const float ct = s_cum[32 * T + lc];
+            float m[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int s0 = 32 * gS + 8 * q + 4 * hi;
+                const float4 cs = *reinterpret_cast<const float4 *>(s_cum + s0);
+                const float4 bs = *reinterpret_cast<const float4 *>(s_beta + s0);
+                const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, bsv[4] = {bs.x, bs.y, bs.z, bs.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    m[4 * q + i] = s0 + i <= 32 * T + lc ? g[4 * q + i] * exp2_fast(ct - csv[i]) * bsv[i] : 0.0f;
+            }
+            uint4 *mo = s_m + (gS + T) * 4 * kWave + l;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
                 bf8v h8, l8;
-                split8(u0, u1, h8, l8);
-                const bf8v b8 = *reinterpret_cast<const bf8v *>(br + 8 * jj);
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h8, b8, acc[j], 0, 0, 0);
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l8, b8, acc[j], 0, 0, 0);
+                split8(make_float4(m[8 * kk], m[8 * kk + 1], m[8 * kk + 2], m[8 * kk + 3]),
+                       make_float4(m[8 * kk + 4], m[8 * kk + 5], m[8 * kk + 6], m[8 * kk + 7]), h8, l8);
+                mo[(2 * kk) * kWave] = __builtin_bit_cast(uint4, h8);
+                mo[(2 * kk + 1) * kWave] = __builtin_bit_cast(uint4, l8);
             }
         }
-        if (w < 3) {
-            const int s = 32 * qs + l % 32;
-            const float cs = s_cum[s], bs = s_beta[s];
+        // x of channel p over the chunk in accumulator row order: xr[S][kk] holds steps 32 S + 16 kk + ..
+        uint4 xr[2][2];
+        {
+            const uint16_t *xrow = s_x + p * kMH + 4 * hi;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int t = 32 * qt + d_row(r, l);
-                s_m[t * kMS + s] = s <= t ? g[r] * exp2_fast(s_cum[t] - cs) * bs : 0.0f;
-            }
-        } else {
+            for (int S = 0; S < 2; ++S)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s_m[d_row(r, l) * kMS + 32 + l % 32] = 0.0f;
+                for (int kk = 0; kk < 2; ++kk) xr[S][kk] = pair8(xrow + 32 * S + 16 * kk);
         }
-        lds_barrier();
+        // the state update: Hᵀ ← e^{a c_end} Hᵀ + Bᵀ X_w, X_w[s][p] = x[p][s] e^{a(c_end − c_s)} β_s (hi + lo)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[nt][r] *= dec;
+        {
+            const uint16_t *btrow = s_bt + lc * kMH + 4 * hi;
+#pragma unroll
+            for (int S = 0; S < 2; ++S)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int s0 = 32 * S + 16 * kk + 4 * hi;
+                    const float4 w0 = *reinterpret_cast<const float4 *>(s_w + s0);
+                    const float4 w1 = *reinterpret_cast<const float4 *>(s_w + s0 + 8);
+                    const uint4 xv = xr[S][kk];
+                    bf8v h8, l8;
+                    split8(make_float4(bf16_lo(xv.x) * w0.x, bf16_hi(xv.x) * w0.y, bf16_lo(xv.y) * w0.z, bf16_hi(xv.y) * w0.w),
+                           make_float4(bf16_lo(xv.z) * w1.x, bf16_hi(xv.z) * w1.y, bf16_lo(xv.w) * w1.z, bf16_hi(xv.w) * w1.w),
+                           h8, l8);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const bf8v b8 = bf8(pair8(btrow + 32 * nt * kMH + 32 * S + 16 * kk));
+                        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8, h8, acc[nt], 0, 0, 0);
+                        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8, l8, acc[nt], 0, 0, 0);
+                    }
+                }
+        }
+        lds_barrier();  // the product tiles are written; every read of the chunk's operands is done
 
-        // this wavefront's output tile: steps 32·ot .., channels 32·op ..
-        const int ot = w / 2, op = w % 2;
-        f16v yv = {}, inter = {};
-        mfma_tile_split<32, true>(yv, s_m + (32 * ot + l % 32) * kMS + 32 * hi, s_x + (32 * op + l % 32) * kMH + 32 * hi);
-        {
-            const uint16_t *cr = s_c + (32 * ot + l % 32) * NH + hi * HN;
-            const float *hr = s_h + (32 * op + l % 32) * NF + hi * HN;
+        // the next chunk's scalars and operands into LDS, then the loads of the one after
+        if (c + 1 < a.nc) {
+            stage();
+            if (c + 2 < a.nc) load_chunk(c + 2);
+        }
+        // the chunk's own part: Σ_s M[t][s] x_s over the product tiles (S, T), S <= T (M as hi + lo)
 #pragma unroll
-            for (int j = 0; j < HN / 8; ++j) {
-                bf8v h8, l8;
-                split8(*reinterpret_cast<const float4 *>(hr + 8 * j), *reinterpret_cast<const float4 *>(hr + 8 * j + 4), h8, l8);
-                const bf8v c8 = *reinterpret_cast<const bf8v *>(cr + 8 * j);
-                inter = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c8, h8, inter, 0, 0, 0);
-                inter = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c8, l8, inter, 0, 0, 0);
+        for (int S = 0; S < 2; ++S) {
+            if (S > T) break;
+            const uint4 *mi = s_m + (S + T) * 4 * kWave + l;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf8v x8 = bf8(xr[S][kk]);
+                y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf8(mi[(2 * kk) * kWave]), x8, y, 0, 0, 0);
+                y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf8(mi[(2 * kk + 1) * kWave]), x8, y, 0, 0, 0);
             }
         }
-        {
-            const int p = 32 * op + l % 32;
+        // y = outputs + D x, times silu(z): channel p, steps 32 T + 8q + 4 hi .. +3 (registers 4q .. 4q+3)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int t = 32 * ot + d_row(r, l);
-                s_o[p * kMS + t] = yv[r] + exp2_fast(s_cum[t]) * inter[r];
-            }
-        }
-        lds_barrier();
-        // y = outputs + D x, times silu(z), in 4-step pieces
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int p = e_p(k), t4 = e_t(k);
+        for (int q = 0; q < 4; ++q) {
+            const int t4 = 32 * T + 8 * q + 4 * hi;
             if (t4 >= lim) continue;
-            const int64_t off = ((ib * a.H + h) * kP + p) * a.L + t0 + t4;
-            const float4 o = *reinterpret_cast<const float4 *>(s_o + p * kMS + t4);
-            const uint16_t *xs = s_x + p * kMH + t4;
-            float v[4] = {o.x + dsk[k] * widen(xs[0]), o.y + dsk[k] * widen(xs[1]), o.z + dsk[k] * widen(xs[2]),
-                          o.w + dsk[k] * widen(xs[3])};
+            const uint4 xv = T == 0 ? xr[0][q / 2] : xr[1][q / 2];
+            const uint32_t x0 = (q & 1) ? xv.z : xv.x, x1 = (q & 1) ? xv.w : xv.y;
+            float v[4] = {y[4 * q] + dsk * bf16_lo(x0), y[4 * q + 1] + dsk * bf16_hi(x0),
+                          y[4 * q + 2] + dsk * bf16_lo(x1), y[4 * q + 3] + dsk * bf16_hi(x1)};
             if (zg) {
                 float zv[4];
-                raw_elems(zq[k], zv);
+                raw_elems(zq[q], zv);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] *= silu(zv[e]);
             }
-            if (a.vec && t4 + 4 <= lim) {
+            if (VEC) {  // t4 < lim and lim a multiple of 8: the whole piece
                 uint2 pk;
                 pk.x = (uint32_t)narrow<uint16_t>(v[0]) | ((uint32_t)narrow<uint16_t>(v[1]) << 16);
                 pk.y = (uint32_t)narrow<uint16_t>(v[2]) | ((uint32_t)narrow<uint16_t>(v[3]) << 16);
-                *reinterpret_cast<uint2 *>(yg + off) = pk;
+                *reinterpret_cast<uint2 *>(yg + t0 + t4) = pk;
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (t4 + e < lim) yg[off + e] = narrow<uint16_t>(v[e]);
+                    if (t4 + e < lim) yg[t0 + t4 + e] = narrow<uint16_t>(v[e]);
             }
         }
         if (c + 1 < a.nc) load_z(c + 1);
-        lds_barrier();  // the next chunk's staging overwrites every LDS operand
     }
     if (a.hT) {
+        // the lane index behind an empty asm, so that these addresses are formed here and not kept
+        // across the walk
+        int ln = l;
+        asm volatile("" : "+v"(ln));
+        float *ht = a.hT + bh * (kP * N) + (int64_t)(32 * Pt + ln % 32) * N;
 #pragma unroll
-        for (int j = 0; j < TPW; ++j)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) a.hT[bh * (kP * N) + st_off(j, r)] = acc[j][r];
+            for (int r = 0; r < 16; ++r) ht[32 * nt + d_row(r, ln)] = acc[nt][r];
     }
 }
 
@@ -447,8 +517,12 @@ hipError_t launch_walk(const SsdArgs &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fused(const SsdArgs &a, int64_t N, hipStream_t stream) {
-    if (N == 64) hipLaunchKernelGGL((ssd_fused_kernel<64>), dim3((unsigned)(a.b * a.H)), dim3(kThreads), 0, stream, a);
-    else if (N == 128) hipLaunchKernelGGL((ssd_fused_kernel<128>), dim3((unsigned)(a.b * a.H)), dim3(kThreads), 0, stream, a);
+    const dim3 grid((unsigned)(a.b * a.H));
+    const bool vec = a.vec && a.vec8 && a.vec_bc16;
+    if (N == 64 && vec) hipLaunchKernelGGL((ssd_fused_kernel<64, true>), grid, dim3(kThreads), 0, stream, a);
+    else if (N == 64) hipLaunchKernelGGL((ssd_fused_kernel<64, false>), grid, dim3(kThreads), 0, stream, a);
+    else if (N == 128 && vec) hipLaunchKernelGGL((ssd_fused_kernel<128, true>), grid, dim3(kThreads), 0, stream, a);
+    else if (N == 128) hipLaunchKernelGGL((ssd_fused_kernel<128, false>), grid, dim3(kThreads), 0, stream, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
