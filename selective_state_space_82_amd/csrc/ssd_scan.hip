@@ -208,21 +208,24 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(SsdArgs a) {
 //   y_t = e^{a c_t} C_t·h_in + Σ_s M[t][s] x_s + D x_t, times silu(z);
 //   h ← e^{a c_end} h + Σ_s e^{a(c_end − c_s)} β_s x_s B_sᵀ.
 // Wavefront w owns the output tile of steps 32·T .. and channels 32·Pt .. (T = w & 1, Pt = w >> 1) and
-// holds the state columns of its 32 channels over all N states, Hᵀ[n][p], as N/32 accumulator tiles (the
-// two wavefronts of a channel block keep identical copies and update them alike).
+// holds half of the state columns of its 32 channels, Hᵀ[n][p] for n in N/2 · T .. N/2 · T + N/2 − 1, as
+// N/64 accumulator tiles; its partner w ^ 1 holds the other half. Each forms C·Hᵀ over its half for both
+// step tiles and hands the partner the partial sum of the partner's tile through LDS.
 //
 // The accumulator layout does the transposes. Lane l of a 32×32 accumulator holds column l % 32 and,
 // in registers 8κ .. 8κ+7, rows 16κ + {0..3, 8..11} + 4·(l / 32). Read as an MFMA operand those registers
 // are the lane's eight k values of the K block 16κ .. 16κ+15 in that order, so a tile of Hᵀ[n][p] is
 // directly the k = n operand of C·Hᵀ, and a tile of Mᵀ[s][t] (formed as B·Cᵀ) is the k = s operand of
-// M·x. The other operand of each of those products (C, x, Bᵀ rows in LDS) is read in the same k order:
-// two 8-byte LDS reads per lane and K block. Only the decayed product tiles cross wavefronts, as bf16
-// hi and lo planes in LDS in lane order.
+// M·x. The other operand of each of those products (C and x rows in LDS) is read in the same k order:
+// two 8-byte LDS reads per lane and K block; the state update's Bᵀ operand is read down the columns of
+// B's rows, 2 bytes at a time. The decayed product tiles cross wavefronts as bf16 hi and lo planes in LDS
+// in lane order, the partial sums of C·Hᵀ as fp32 in lane order.
 //
-// LDS holds the chunk's C, B, Bᵀ and x (bf16), the decayed product tiles and the chunk's scalars, about
-// 75 KB at N = 128, so two workgroups share a compute unit and each one's barriers and exponentials
-// overlap the other's products. Two barriers per chunk: the second lets the next chunk's staging
-// overwrite the operands while this chunk's outputs are formed from registers and the product tiles.
+// LDS holds the chunk's C, B and x (bf16), the decayed product tiles, the partial sums and the chunk's
+// scalars, about 73 KB at N = 128, so two workgroups share a compute unit and each one's barriers and
+// exponentials overlap the other's products. Two barriers per chunk: the second lets the next chunk's
+// staging overwrite the operands while this chunk's outputs are formed from registers, the product
+// tiles and the partial sums.
 // VEC: every row piece is whole and aligned (L a multiple of 8; x, y, z, B, C aligned), so loads and
 // stores go by 16 (8) bytes with one guard per piece; otherwise element by element.
 template <int N, bool VEC>
@@ -230,30 +233,31 @@ __global__ __launch_bounds__(kThreads, VEC ? 2 : 1) void ssd_fused_kernel(SsdArg
     static_assert(N == 64 || N == 128, "state widths");
     constexpr int NH = N + 8;       // bf16 row stride of N-wide LDS rows
     constexpr int HN = N / 2;
-    constexpr int NT = N / 32;      // state tiles per wavefront
+    constexpr int NS = N / 64;      // state tiles per wavefront
     constexpr int CK = N / 32;      // 16-byte pieces of C (and of B) per thread per chunk
     __shared__ __align__(16) float s_cum[kQ], s_beta[kQ], s_w[kQ], s_et[kQ];
     __shared__ __align__(16) uint16_t s_c[kQ * NH];    // C [t][n]
     __shared__ __align__(16) uint16_t s_b[kQ * NH];    // B [s][n]
-    __shared__ __align__(16) uint16_t s_bt[N * kMH];   // Bᵀ [n][s]
     __shared__ __align__(16) uint16_t s_x[kP * kMH];   // x [p][s]
     __shared__ __align__(16) uint4 s_m[3 * 4 * kWave]; // decayed product tiles: [tile][K block, hi / lo][lane]
+    __shared__ __align__(16) float4 s_i[4 * 4 * kWave]; // partial C·Hᵀ for the partner: [wavefront][4 registers][lane]
     const int64_t bh = blockIdx.x, ib = bh / a.H, h = bh % a.H;
     const float ah = a.A[h];
     const int l = lane(), w = wave(), hi = l / 32, lc = l % 32, tid = threadIdx.x;
     const int T = w & 1, Pt = w >> 1;
     const int p = 32 * Pt + lc;              // this lane's channel in the output and state tiles
+    const int n0 = (N / 2) * T;              // the first state row this wavefront holds
     // the decayed product tiles Mᵀ[s][t] with s <= t: (S, T) = (0, 0), (0, 1), (1, 1), slot S + T,
     // formed by wavefronts 0, 1 and 3
     const bool gw = w != 2;
     const int gS = w == 3 ? 1 : 0;
 
-    f16v acc[NT];  // acc[nt][r] = h[p][32 nt + d_row(r, l)]
+    f16v acc[NS];  // acc[j][r] = h[p][n0 + 32 j + d_row(r, l)]
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int j = 0; j < NS; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            acc[nt][r] = a.h0 ? a.h0[bh * (kP * N) + (int64_t)p * N + 32 * nt + d_row(r, l)] : 0.0f;
+            acc[j][r] = a.h0 ? a.h0[bh * (kP * N) + (int64_t)p * N + n0 + 32 * j + d_row(r, l)] : 0.0f;
 
     const uint16_t *dg = static_cast<const uint16_t *>(a.delta) + bh * a.L;
     const uint16_t *cg = static_cast<const uint16_t *>(a.C) + ib * a.L * N;
@@ -262,8 +266,7 @@ __global__ __launch_bounds__(kThreads, VEC ? 2 : 1) void ssd_fused_kernel(SsdArg
     const uint16_t *zg = a.z ? static_cast<const uint16_t *>(a.z) + ((ib * a.H + h) * kP + p) * a.L : nullptr;
     uint16_t *yg = static_cast<uint16_t *>(a.y) + ((ib * a.H + h) * kP + p) * a.L;
     // staging pieces: C row c_r(k) columns c_c(k) .. +7 (16 lanes per row); B row l, columns
-    // 8(w + 4k) .. +7 (one row per lane, so that the transposed stores spread over the banks); x row
-    // x_r(k), steps x_c(k) .. +7
+    // 8(w + 4k) .. +7 (one row per lane); x row x_r(k), steps x_c(k) .. +7
     auto c_r = [&](int k, int t = threadIdx.x) { return (t + k * kThreads) / (N / 8); };
     auto c_c = [&](int k, int t = threadIdx.x) { return ((t + k * kThreads) % (N / 8)) * 8; };
     auto b_c = [&](int k) { return 8 * (w + 4 * k); };
@@ -333,10 +336,6 @@ __global__ __launch_bounds__(kThreads, VEC ? 2 : 1) void ssd_fused_kernel(SsdArg
         for (int k = 0; k < CK; ++k) {
             *reinterpret_cast<uint4 *>(s_c + c_r(k) * NH + c_c(k)) = cq[k];
             *reinterpret_cast<uint4 *>(s_b + l * NH + b_c(k)) = bq[k];
-            const uint32_t wv[4] = {bq[k].x, bq[k].y, bq[k].z, bq[k].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                s_bt[(b_c(k) + e) * kMH + l] = (uint16_t)((e & 1) ? (wv[e / 2] >> 16) : (wv[e / 2] & 0xffffu));
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k) *reinterpret_cast<uint4 *>(s_x + x_r(k) * kMH + x_c(k)) = xq[k];
@@ -366,26 +365,35 @@ __global__ __launch_bounds__(kThreads, VEC ? 2 : 1) void ssd_fused_kernel(SsdArg
                 g = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf8v *>(arow + 8 * j),
                                                             *reinterpret_cast<const bf8v *>(brow + 8 * j), g, 0, 0, 0);
         }
-        // the entering state's part: e^{a c_t} C_t·h_in (C rows in accumulator order, Hᵀ as hi + lo)
-        f16v y = {};
+        // the entering state's part C_t·h_in over this wavefront's half of the states, for both step tiles
+        // (C rows in accumulator order, Hᵀ as hi + lo); the partner's tile goes to it through LDS
+        f16v y = {}, yo = {};
         {
-            const uint16_t *crow = s_c + (32 * T + lc) * NH + 4 * hi;
+            const uint16_t *crow = s_c + (32 * T + lc) * NH + n0 + 4 * hi;
+            const uint16_t *corow = s_c + (32 * (1 - T) + lc) * NH + n0 + 4 * hi;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
+            for (int j = 0; j < NS; ++j)
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     bf8v h8, l8;
-                    split8(make_float4(acc[nt][8 * kk], acc[nt][8 * kk + 1], acc[nt][8 * kk + 2], acc[nt][8 * kk + 3]),
-                           make_float4(acc[nt][8 * kk + 4], acc[nt][8 * kk + 5], acc[nt][8 * kk + 6], acc[nt][8 * kk + 7]),
+                    split8(make_float4(acc[j][8 * kk], acc[j][8 * kk + 1], acc[j][8 * kk + 2], acc[j][8 * kk + 3]),
+                           make_float4(acc[j][8 * kk + 4], acc[j][8 * kk + 5], acc[j][8 * kk + 6], acc[j][8 * kk + 7]),
                            h8, l8);
-                    const bf8v c8 = bf8(pair8(crow + 32 * nt + 16 * kk));
+                    const bf8v co8 = bf8(pair8(corow + 32 * j + 16 * kk));
+                    yo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(co8, h8, yo, 0, 0, 0);
+                    yo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(co8, l8, yo, 0, 0, 0);
+                    const bf8v c8 = bf8(pair8(crow + 32 * j + 16 * kk));
                     y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c8, h8, y, 0, 0, 0);
                     y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c8, l8, y, 0, 0, 0);
                 }
+            // e^{a c_t} on both partial sums here: the chunk's scalars are overwritten after the next barrier
+            float4 *io = s_i + w * 4 * kWave + l;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float4 e4 = *reinterpret_cast<const float4 *>(s_et + 32 * T + 8 * q + 4 * hi);
                 y[4 * q] *= e4.x; y[4 * q + 1] *= e4.y; y[4 * q + 2] *= e4.z; y[4 * q + 3] *= e4.w;
+                const float4 eo = *reinterpret_cast<const float4 *>(s_et + 32 * (1 - T) + 8 * q + 4 * hi);
+                io[q * kWave] = make_float4(yo[4 * q] * eo.x, yo[4 * q + 1] * eo.y, yo[4 * q + 2] * eo.z, yo[4 * q + 3] * eo.w);
             }
         }
         // the decayed product tile, split into bf16 hi and lo for the wavefronts that multiply it
@@ -421,13 +429,23 @@ __global__ __launch_bounds__(kThreads, VEC ? 2 : 1) void ssd_fused_kernel(SsdArg
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) xr[S][kk] = pair8(xrow + 32 * S + 16 * kk);
         }
-        // the state update: Hᵀ ← e^{a c_end} Hᵀ + Bᵀ X_w, X_w[s][p] = x[p][s] e^{a(c_end − c_s)} β_s (hi + lo)
+        // the state update: Hᵀ ← e^{a c_end} Hᵀ + Bᵀ X_w, X_w[s][p] = x[p][s] e^{a(c_end − c_s)} β_s (hi + lo);
+        // the Bᵀ operand (row n, k = s) is read down column n of B's rows
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int j = 0; j < NS; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[nt][r] *= dec;
+            for (int r = 0; r < 16; ++r) acc[j][r] *= dec;
         {
-            const uint16_t *btrow = s_bt + lc * kMH + 4 * hi;
+            const uint16_t *bcol = s_b + (4 * hi) * NH + n0 + lc;
+            auto col8 = [&](const uint16_t *c) {  // rows 0 .. 3 and 8 .. 11 of a column, packed in pairs
+                uint32_t v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r0 = 2 * e + (e >= 2 ? 4 : 0);
+                    v[e] = (uint32_t)c[r0 * NH] | ((uint32_t)c[(r0 + 1) * NH] << 16);
+                }
+                return make_uint4(v[0], v[1], v[2], v[3]);
+            };
 #pragma unroll
             for (int S = 0; S < 2; ++S)
 #pragma unroll
@@ -441,19 +459,28 @@ __global__ __launch_bounds__(kThreads, VEC ? 2 : 1) void ssd_fused_kernel(SsdArg
                            make_float4(bf16_lo(xv.z) * w1.x, bf16_hi(xv.z) * w1.y, bf16_lo(xv.w) * w1.z, bf16_hi(xv.w) * w1.w),
                            h8, l8);
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        const bf8v b8 = bf8(pair8(btrow + 32 * nt * kMH + 32 * S + 16 * kk));
-                        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8, h8, acc[nt], 0, 0, 0);
-                        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8, l8, acc[nt], 0, 0, 0);
+                    for (int j = 0; j < NS; ++j) {
+                        const bf8v b8 = bf8(col8(bcol + (32 * S + 16 * kk) * NH + 32 * j));
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8, h8, acc[j], 0, 0, 0);
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b8, l8, acc[j], 0, 0, 0);
                     }
                 }
         }
-        lds_barrier();  // the product tiles are written; every read of the chunk's operands is done
+        lds_barrier();  // the product tiles and partial sums are written; every read of the operands is done
 
         // the next chunk's scalars and operands into LDS, then the loads of the one after
         if (c + 1 < a.nc) {
             stage();
             if (c + 2 < a.nc) load_chunk(c + 2);
+        }
+        // the partner's half of e^{a c_t} C_t·h_in
+        {
+            const float4 *ii = s_i + (w ^ 1) * 4 * kWave + l;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 o4 = ii[q * kWave];
+                y[4 * q] += o4.x; y[4 * q + 1] += o4.y; y[4 * q + 2] += o4.z; y[4 * q + 3] += o4.w;
+            }
         }
         // the chunk's own part: Σ_s M[t][s] x_s over the product tiles (S, T), S <= T (M as hi + lo)
 #pragma unroll
@@ -500,11 +527,11 @@ __global__ __launch_bounds__(kThreads, VEC ? 2 : 1) void ssd_fused_kernel(SsdArg
         // across the walk
         int ln = l;
         asm volatile("" : "+v"(ln));
-        float *ht = a.hT + bh * (kP * N) + (int64_t)(32 * Pt + ln % 32) * N;
+        float *ht = a.hT + bh * (kP * N) + (int64_t)(32 * Pt + ln % 32) * N + n0;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int j = 0; j < NS; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) ht[32 * nt + d_row(r, ln)] = acc[nt][r];
+            for (int r = 0; r < 16; ++r) ht[32 * j + d_row(r, ln)] = acc[j][r];
     }
 }
 
