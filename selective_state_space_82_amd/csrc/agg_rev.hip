@@ -10,12 +10,12 @@
 // every step (R ← R·Ā_t after using it), so E accumulates R_t·B̄_t x_t. In the scaled form s = A·h used by
 // the output pass, A·B̄ = Ā − 1, so the walk adds R·(Ā − 1)·B x and scales by 1/A once at the end.
 //
-// Truncation. Once R ≤ 2^-30 for every state a wavefront holds, the steps not yet walked contribute exactly
-// R·h_t, where h_t is the state at the step reached (from zero at the segment start): at most 2^-30·|h_t|.
-// A forward scan rounds its state by about 2^-24·|h_t| at that same step, and that error reaches the
-// segment end decayed by the same R, so the dropped part stays below the rounding of a single step of the
-// scan the output pass itself runs. The walk stops there (a state with A ≥ 0 never decays and is walked to
-// the segment start). The decay rate |A_n|·Δ differs by an order of magnitude across n (A_n ≈ −(n + 1)
+// Truncation. Once R ≤ 2^-24 for every state a wavefront holds, the steps not yet walked contribute exactly
+// R·h_t, where h_t is the state at the step reached (from zero at the segment start): at most 2^-24·|h_t|,
+// fp32's unit roundoff times |h_t|. Holding h_t in fp32 at that step already errs by that much, and that
+// error reaches the segment end decayed by the same R, so dropping the rest costs no more than one
+// rounding of the state the output pass itself carries. The walk stops there (a state with A ≥ 0 never
+// decays and is walked to the segment start). The decay rate |A_n|·Δ differs by an order of magnitude across n (A_n ≈ −(n + 1)
 // under Mamba's initialisation), so a wavefront holds one group of four states of 64 channels (a lane per
 // channel, its four states in registers): the groups of fast states stop after a few dozen steps.
 //
@@ -31,10 +31,11 @@
 // P needs ΣΔ over the whole segment: the wavefront of state group 0 sums Δ over the steps it did not walk
 // (those tiles of Δ alone) and writes P for all N states of its channels; P is exact whatever the sign of Δ.
 //
-// Per (t, n) the common path issues one exp and six fp32 operations (u, Ā − 1, R·(Ā − 1), B·x, the
-// accumulation and R's update). Tiles are classified per wavefront as in the output pass: where some
-// channel's Δ-sum over the tile is small against 1/|A|, Ā − 1 comes from the cubic series of 2^u − 1 near
-// 0, and a wavefront holding a state at the A = 0 limit (|A| < 2^-64) takes B̄ = Δ·B with R = 1 there.
+// Per (t, n) the common path issues one exp and five fp32 operations: u, R·Ā (which is also R's update),
+// B·x, the difference R·Ā − R = R·(Ā − 1), and the accumulation. Tiles are classified per wavefront as in
+// the output pass: where some channel's Δ-sum over the tile is small against 1/|A|, Ā − 1 comes from the
+// cubic series of 2^u − 1 near 0, and a wavefront holding a state at the A = 0 limit (|A| < 2^-64) takes
+// B̄ = Δ·B with R = 1 there.
 //
 // The prefill launcher takes this pass for segments of 1024 steps or more; below that a segment rarely
 // outlasts the slow states' decay, and the forward aggregate pass, whose wavefronts are equally long,
@@ -46,7 +47,7 @@
 namespace ssm {
 namespace {
 
-constexpr float kStopRel = 9.313225746e-10f;   // 2^-30
+constexpr float kStopRel = 5.960464478e-8f;    // 2^-24
 constexpr float kZeroAbs = 5.421010862e-20f;   // 2^-64: |A| below this takes the A = 0 limit
 // 2^u − 1 = u·(c1 + u·(c2 + u·c3)) + O(u^4) with c_k = ln(2)^k / k!: relative error below 4e-6 for |u| < 1/16
 constexpr float kPow2C1 = 0.693147180559945f;
@@ -217,6 +218,10 @@ __global__ __launch_bounds__(kWave, 3) void agg_rev_kernel(AggArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float uu = dt * a2[j];
+                if constexpr (MODE == 0) {  // Ā alone (the accumulation forms R·Ā − R)
+                    ci[j] = cd[j] = exp2_fast(uu);
+                    continue;
+                }
                 float em1 = exp2_fast(uu) - 1.0f;
                 if constexpr (MODE >= 1) {
                     const float p = __builtin_fmaf(__builtin_fmaf(uu, kPow2C3, kPow2C2), uu, kPow2C1);
@@ -240,8 +245,15 @@ __global__ __launch_bounds__(kWave, 3) void agg_rev_kernel(AggArgs a) {
             const float bj[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                Eacc[j] = __builtin_fmaf(R[j] * cin[j], bj[j] * xt, Eacc[j]);
-                R[j] = __builtin_fmaf(R[j], cdec[j], R[j]);
+                if constexpr (MODE == 0) {
+                    // cdec holds Ā itself here: R·(Ā − 1)·B x as (R·Ā − R)·B x, one instruction fewer
+                    const float rn = R[j] * cdec[j];
+                    Eacc[j] = __builtin_fmaf(rn - R[j], bj[j] * xt, Eacc[j]);
+                    R[j] = rn;
+                } else {
+                    Eacc[j] = __builtin_fmaf(R[j] * cin[j], bj[j] * xt, Eacc[j]);
+                    R[j] = __builtin_fmaf(R[j], cdec[j], R[j]);
+                }
             }
             if (k > 0) {
 #pragma unroll

@@ -63,7 +63,7 @@ hipError_t launch_scan_bwd(const BwdLaunch &p, hipStream_t stream);
 
 // Aggregate pass of a time split (agg_rev.hip): for segments 0 .. n_seg − 2, P = Π Ā = exp(A·ΣΔ) and E, the
 // end state from zero, both [n_seg − 1][b][d][N] fp32, by a backward walk that stops once the decay back
-// to the step reached is at most 2^-30 for every state of a wavefront. N <= 64.
+// to the step reached is at most 2^-24 for every state of a wavefront. N <= 64.
 struct AggLaunch {
     const void *x, *delta;
     const float *A;

@@ -267,7 +267,7 @@ def test_initial_state_with_time_segments(dt, seg_len):
 
 # ------------------------------------------------------------------------------------------
 # Segments of 1024 steps or more take the aggregate pass that walks each segment backward and stops once the
-# decay back to the step reached is at most 2^-30 for every state of its wavefront (one group of four states
+# decay back to the step reached is at most 2^-24 for every state of its wavefront (one group of four states
 # of 64 channels); P = exp(A·ΣΔ) still covers the whole segment. These cases make the walks stop at
 # different points, or never.
 # ------------------------------------------------------------------------------------------

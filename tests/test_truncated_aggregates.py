@@ -5,9 +5,10 @@ state there (page "Mambaとは？Transformer以外の系列モデル", section S
 per-step affine maps compose associatively):
     E[0, T) = E[t_s, T) + R·h(t_s),   R = Π_{u >= t_s} Ā_u = exp(A·Σ_{u >= t_s} Δ_u),
 where h(t_s) is the state from zero just before t_s. The aggregate pass stops its backward walk at the first
-tile boundary t_s where R <= 2^-30 for every state of a wavefront, so the part it drops is R·h(t_s), at most
-2^-30·|h(t_s)|. These tests check the identity and that bound on Mamba-shaped inputs (including Δ < 0 steps
-and the long-context decay rates), and that the walk's stopping rule on ΣΔ gives R <= 2^-30.
+tile boundary t_s where R <= 2^-24 (fp32's unit roundoff) for every state of a wavefront, so the part it
+drops is R·h(t_s), at most 2^-24·|h(t_s)|: no more than the error of holding h(t_s) in fp32. These tests
+check the identity and that bound on Mamba-shaped inputs (including Δ < 0 steps and the long-context decay
+rates), and that the walk's stopping rule on ΣΔ gives R <= 2^-24.
 """
 import numpy as np
 import pytest
@@ -45,20 +46,20 @@ def test_split_identity_and_stop_bound(case):
         ts = 0
         for t in range(T - 32, 0, -32):
             R = np.exp(a * tail[:, t][:, None])               # Π_{u >= t} Ā_u per (channel, state)
-            if np.all(R <= 2.0 ** -30):
+            if np.all(R <= 2.0 ** -24):
                 ts = t
                 break
         if ts == 0:
             continue
         stopped += 1
         R = np.exp(a * tail[:, ts][:, None])
-        assert np.all(R <= 2.0 ** -30)
+        assert np.all(R <= 2.0 ** -24)
         trunc = _end_state(x[:, ts:], dl[:, ts:], A, B[ts:])[:, 4 * g:4 * g + 4]
         h_ts = _end_state(x[:, :ts], dl[:, :ts], A, B[:ts])[:, 4 * g:4 * g + 4]
         # the identity, to fp64 rounding
         np.testing.assert_allclose(full[:, 4 * g:4 * g + 4], trunc + R * h_ts, rtol=1e-12, atol=1e-12)
         # the dropped part against the state at the stop
-        assert np.all(np.abs(full[:, 4 * g:4 * g + 4] - trunc) <= 2.0 ** -30 * np.abs(h_ts) + 1e-12)
+        assert np.all(np.abs(full[:, 4 * g:4 * g + 4] - trunc) <= 2.0 ** -24 * np.abs(h_ts) + 1e-12)
     assert stopped >= 1, "no state group stops early on these inputs: the case tests nothing"
 
 
