@@ -126,6 +126,18 @@ ssm_status_t make_plan(int64_t b, int64_t d, int64_t L, int64_t N, const ssm_fwd
         if (S > 64) S = 64;
         if (S < 1) S = 1;
         seg_len = ((Lr / S + ssm::kSegQuantum - 1) / ssm::kSegQuantum) * ssm::kSegQuantum;
+        // Segments of kAggWalkMinSeg steps or more take the truncated backward aggregate walk, which costs
+        // about one walk over the slow states' decay horizon per segment rather than (S-1)/S of the
+        // sequence, so fewer, longer segments pay there: aim at about 5.6 wavefronts per SIMD (45/8). On
+        // b 1, d 2048, L 131072 (S = 45) a sweep put the output pass at its fastest there, and the
+        // aggregate pass no longer shrank below about 47 segments.
+        if (S > 1 && seg_len >= ssm::kAggWalkMinSeg) {
+            int64_t Sw = (simds * 45 + 8 * ncb - 1) / (8 * ncb);
+            if (Sw > S) Sw = S;
+            if (Sw < 2) Sw = 2;
+            const int64_t sl = (((Lr + Sw - 1) / Sw + ssm::kSegQuantum - 1) / ssm::kSegQuantum) * ssm::kSegQuantum;
+            if (sl >= ssm::kAggWalkMinSeg) seg_len = sl;
+        }
     }
     if (seg_len > Lr || seg_len == 0) seg_len = Lr > 0 ? Lr : ssm::kSegQuantum;
     int64_t n_seg = L > 0 ? (L + seg_len - 1) / seg_len : 1;

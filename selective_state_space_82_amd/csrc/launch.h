@@ -180,6 +180,7 @@ constexpr int64_t kNoAllocScratchBytes = INT64_C(32) << 20;
 hipError_t noalloc_scratch(float **out);
 
 constexpr int kSegQuantum = 32; // time segments are multiples of this many steps
+constexpr int64_t kAggWalkMinSeg = 1024;  // segments this long take the truncated backward aggregate walk
 constexpr int kFoldMaxSeg = 16; // up to this many segments the output pass chains the carry itself
 
 // Scratch floats of a time-split prefill: aggregates P and E, plus the carries when a separate

@@ -51,7 +51,6 @@ namespace ssm {
 namespace {
 
 constexpr float kZeroAbsA = 5.421010862e-20f;  // 2^-64: |A| below this takes the A = 0 limit
-constexpr int64_t kAggWalkMinSeg = 1024;       // segments this long take the truncated backward aggregate walk
 constexpr float kPolyU = 1.0f / 16.0f;         // |u| below this: 2^u − 1 from its series (accurate tiles)
 // 2^u − 1 = u·(c1 + u·(c2 + u·c3)) + O(u^4): c_k = ln(2)^k / k!; relative error below 4e-6 at |u| = 1/16
 constexpr float kPolyC1 = 0.693147180559945f;
