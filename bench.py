@@ -318,7 +318,11 @@ def bench_ssd(name, steps, warmup, quiet=False):
     es = 4 if dt == "f32" else 2
     d = H * P
     nbytes = b * d * L * es * 3 + b * H * L * es + 2 * b * L * N * es + b * d * N * 4 + d * 4 + H * 4
-    scratch_traffic = 4 * b * H * (-(-L // 64)) * P * N * 4
+    # chunk states through HBM (written, read and rewritten by the pass, read): none for the single walk
+    # (bf16 storage, N of 64 or 128, b·H at least twice the compute units)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    single_walk = dt == "bf16" and N in (64, 128) and b * H >= 2 * cus
+    scratch_traffic = 0 if single_walk else 4 * b * H * (-(-L // 64)) * P * N * 4
     flops = ssd_mfma_flops(b, H, L, N)
     rotate = int(min(8, max(1, -(-2 * MALL_BYTES // nbytes))))
     sets = []
@@ -347,7 +351,7 @@ def bench_ssd(name, steps, warmup, quiet=False):
     ms = timed(ssd)
     res = {"pass": "ssd_chunked_mfma", "workload": name, "us_per_call": ms * 1e3, "elements_per_s": b * d * L / (ms * 1e-3),
            "algorithmic_bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9, "scratch_bytes_moved": scratch_traffic,
-           "mfma_flops": flops, "mfma_TFLOPs": flops / (ms * 1e-3) / 1e12,
+           "single_walk": single_walk, "mfma_flops": flops, "mfma_TFLOPs": flops / (ms * 1e-3) / 1e12,
            "mfma_instruction": "f32_32x32x2" if dt == "f32" else "bf16_32x32x16 (fp32 operands as hi + lo)",
            "mfma_frac": flops / (ms * 1e-3) / 1e12 / (MFMA_F32_PEAK_TFLOPS if dt == "f32" else MFMA_BF16_PEAK_TFLOPS)}
     if N <= 64:

@@ -226,10 +226,13 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_kernel(SsdArgs a) {
 // exponentials overlap the other's products. Two barriers per chunk: the second lets the next chunk's
 // staging overwrite the operands while this chunk's outputs are formed from registers, the product
 // tiles and the partial sums.
-// VEC: every row piece is whole and aligned (L a multiple of 8; x, y, z, B, C aligned), so loads and
-// stores go by 16 (8) bytes with one guard per piece; otherwise element by element.
-template <int N, bool VEC>
-__global__ __launch_bounds__(kThreads, VEC ? 2 : 1) void ssd_fused_kernel(SsdArgs a) {
+// AM (access mode): 0 element by element with a bound per element; 1 every row piece whole and aligned
+// (L a multiple of 8; x, y, z, B, C aligned), loads and stores by 16 (8) bytes with one guard per piece;
+// 2 as 1 with every chunk whole (L a multiple of 64, 64·L < 2^31): no guards, and each access is a base
+// that is uniform over the workgroup plus a per-lane 32-bit offset kept across the walk.
+template <int N, int AM>
+__global__ __launch_bounds__(kThreads, AM > 0 ? 2 : 1) void ssd_fused_kernel(SsdArgs a) {
+    constexpr bool VEC = AM > 0;
     static_assert(N == 64 || N == 128, "state widths");
     constexpr int NH = N + 8;       // bf16 row stride of N-wide LDS rows
     constexpr int HN = N / 2;
@@ -283,29 +286,69 @@ __global__ __launch_bounds__(kThreads, VEC ? 2 : 1) void ssd_fused_kernel(SsdArg
         return r;
     };
     const float dsk = a.D ? a.D[h * kP + p] : 0.0f;
+    // AM 2: the per-lane offsets of the first piece of each access, in elements from the chunk's uniform
+    // bases; piece k lies a fixed stride further (kThreads threads cover whole rows: C by kThreads/(N/8)
+    // rows, B by 32 columns, x by 32 rows)
+    const uint32_t coff = (uint32_t)(c_r(0) * N + c_c(0));
+    const uint32_t boff = (uint32_t)(l * N + b_c(0));
+    const uint32_t xoff = (uint32_t)(x_r(0) * a.L + x_c(0));
+    const uint32_t poff = (uint32_t)(p * a.L + 32 * T + 4 * hi);  // z and y: channel p, steps 32 T + 4 hi ..
+    const uint16_t *zh = a.z ? static_cast<const uint16_t *>(a.z) + (ib * a.H + h) * kP * a.L : nullptr;
+    uint16_t *yh = static_cast<uint16_t *>(a.y) + (ib * a.H + h) * kP * a.L;
 
-    float dtr = 0.0f, dec = 0.0f;
-    uint4 cq[CK], bq[CK], xq[2];
+    uint16_t dtr = 0;  // Δ of step l of the chunk being loaded, raw (widened where it is used)
+    float dec = 0.0f;
+    // the chunk's operands in flight: vector values rather than arrays, so they always stay in registers
+    // (an array can be left in scratch memory when registers run short)
+    typedef uint32_t rawv __attribute__((ext_vector_type(4 * CK)));
+    typedef uint32_t rawx __attribute__((ext_vector_type(8)));
+    rawv cq, bq;
+    rawx xq;
+    auto put4 = [](auto &v, int k, const uint4 &q) {
+        v[4 * k] = q.x; v[4 * k + 1] = q.y; v[4 * k + 2] = q.z; v[4 * k + 3] = q.w;
+    };
+    auto get4 = [](const auto &v, int k) { return make_uint4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]); };
     uint2 zq[4];
     // The loads take the thread index behind an empty asm, so that their per-lane addresses are formed at
     // each chunk rather than kept (and spilled) across the walk.
     auto load_chunk = [&](int64_t c) {
+        if constexpr (AM == 2) {
+            const int64_t t0 = c * kQ;
+            const uint16_t *cb = cg + t0 * N, *bb = bg + t0 * N, *xb = xg + t0;
+            dtr = dg[t0 + l];
+#pragma unroll
+            for (int k = 0; k < CK; ++k) {
+                put4(cq, k, *reinterpret_cast<const uint4 *>(cb + k * (kThreads / (N / 8)) * N + coff));
+                put4(bq, k, *reinterpret_cast<const uint4 *>(bb + 32 * k + boff));
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) put4(xq, k, *reinterpret_cast<const uint4 *>(xb + k * (kThreads / 8) * a.L + xoff));
+            return;
+        }
         int th = tid;
         asm volatile("" : "+v"(th));
         const int ln = th % kWave;
         const int64_t t0 = c * kQ;
-        dtr = t0 + ln < a.L ? widen(dg[t0 + ln]) : 0.0f;
+        dtr = t0 + ln < a.L ? dg[t0 + ln] : (uint16_t)0;
 #pragma unroll
         for (int k = 0; k < CK; ++k) {
             const int cr = c_r(k, th);
-            cq[k] = raw8(cg + (t0 + cr) * N, c_c(k, th), t0 + cr < a.L ? N : 0);
-            bq[k] = raw8(bg + (t0 + ln) * N, b_c(k), t0 + ln < a.L ? N : 0);
+            put4(cq, k, raw8(cg + (t0 + cr) * N, c_c(k, th), t0 + cr < a.L ? N : 0));
+            put4(bq, k, raw8(bg + (t0 + ln) * N, b_c(k), t0 + ln < a.L ? N : 0));
         }
 #pragma unroll
-        for (int k = 0; k < 2; ++k) xq[k] = raw8(xg + x_r(k, th) * a.L + t0, x_c(k, th), a.L - t0);
+        for (int k = 0; k < 2; ++k) put4(xq, k, raw8(xg + x_r(k, th) * a.L + t0, x_c(k, th), a.L - t0));
     };
     // z at this lane's output positions: channel p, steps 32 T + 8q + 4 hi .. +3
     auto load_z = [&](int64_t c) {
+        if constexpr (AM == 2) {
+            if (zh) {
+                const uint16_t *zb = zh + c * kQ;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) zq[q] = *reinterpret_cast<const uint2 *>(zb + poff + 8 * q);
+            }
+            return;
+        }
         int ln = l;
         asm volatile("" : "+v"(ln));
         const int64_t t0 = c * kQ;
@@ -320,9 +363,10 @@ __global__ __launch_bounds__(kThreads, VEC ? 2 : 1) void ssd_fused_kernel(SsdArg
     };
     // the chunk's scalars (every wavefront forms them from Δ; wavefront 0 publishes them) and its operands
     auto stage = [&]() {
-        const float u = dtr * (ah * kLog2e);
+        const float dt = widen(dtr);
+        const float u = dt * (ah * kLog2e);
         const float abar = exp2_fast(u);
-        const float beta = zoh_input_coef_log2(dtr, u, abar, 1.0f / ah);
+        const float beta = zoh_input_coef_log2(dt, u, abar, 1.0f / ah);
         const float cu = wave_prefix_sum(u);
         const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cu), 63));
         dec = exp2_fast(cend);
@@ -334,11 +378,11 @@ __global__ __launch_bounds__(kThreads, VEC ? 2 : 1) void ssd_fused_kernel(SsdArg
         }
 #pragma unroll
         for (int k = 0; k < CK; ++k) {
-            *reinterpret_cast<uint4 *>(s_c + c_r(k) * NH + c_c(k)) = cq[k];
-            *reinterpret_cast<uint4 *>(s_b + l * NH + b_c(k)) = bq[k];
+            *reinterpret_cast<uint4 *>(s_c + c_r(k) * NH + c_c(k)) = get4(cq, k);
+            *reinterpret_cast<uint4 *>(s_b + l * NH + b_c(k)) = get4(bq, k);
         }
 #pragma unroll
-        for (int k = 0; k < 2; ++k) *reinterpret_cast<uint4 *>(s_x + x_r(k) * kMH + x_c(k)) = xq[k];
+        for (int k = 0; k < 2; ++k) *reinterpret_cast<uint4 *>(s_x + x_r(k) * kMH + x_c(k)) = get4(xq, k);
     };
     // eight bf16 of an LDS row in accumulator row order: row[0 .. 3] and row[8 .. 11]
     auto pair8 = [](const uint16_t *row) {
@@ -350,15 +394,16 @@ __global__ __launch_bounds__(kThreads, VEC ? 2 : 1) void ssd_fused_kernel(SsdArg
     load_chunk(0);
     load_z(0);
     stage();
-    if (a.nc > 1) load_chunk(1);
+    load_chunk(a.nc > 1 ? 1 : 0);
     for (int64_t c = 0; c < a.nc; ++c) {
         const int64_t t0 = c * kQ;
         const int64_t lim = a.L - t0;
         lds_barrier();  // the chunk's operands and scalars; the previous chunk's product tiles are consumed
 
         // G = B Cᵀ for this wavefront's product tile (rows s = 32 gS .., columns t = 32 T ..)
-        f16v g = {};
+        f16v g;  // formed by the wavefronts that own a product tile and read only by them
         if (gw) {
+            g = f16v{};  // inside the branch: the other wavefront keeps no zeroed copy
             const uint16_t *arow = s_b + (32 * gS + lc) * NH + hi * HN, *brow = s_c + (32 * T + lc) * NH + hi * HN;
 #pragma unroll
             for (int j = 0; j < HN / 8; ++j)
@@ -468,11 +513,15 @@ __global__ __launch_bounds__(kThreads, VEC ? 2 : 1) void ssd_fused_kernel(SsdArg
         }
         lds_barrier();  // the product tiles and partial sums are written; every read of the operands is done
 
-        // the next chunk's scalars and operands into LDS, then the loads of the one after
-        if (c + 1 < a.nc) {
-            stage();
-            if (c + 2 < a.nc) load_chunk(c + 2);
-        }
+        // the next chunk's scalars and operands into LDS, then the loads of the one after. Done
+        // unconditionally, with chunk indices clamped to the last chunk, so no branch joins the loads
+        // in flight (a join made the compiler copy, and so wait for, the loaded registers); after the
+        // last chunk these stage a chunk into LDS that nothing reads.
+        stage();
+        // the staging's LDS writes take the previous loads' registers before the next loads are issued
+        // (otherwise both sets are live at once, and the prefetch arrays no longer fit in registers)
+        asm volatile("" ::: "memory");
+        load_chunk(c + 2 < a.nc ? c + 2 : a.nc - 1);
         // the partner's half of e^{a c_t} C_t·h_in
         {
             const float4 *ii = s_i + (w ^ 1) * 4 * kWave + l;
@@ -509,7 +558,12 @@ __global__ __launch_bounds__(kThreads, VEC ? 2 : 1) void ssd_fused_kernel(SsdArg
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] *= silu(zv[e]);
             }
-            if (VEC) {  // t4 < lim and lim a multiple of 8: the whole piece
+            if (AM == 2) {
+                uint2 pk;
+                pk.x = (uint32_t)narrow<uint16_t>(v[0]) | ((uint32_t)narrow<uint16_t>(v[1]) << 16);
+                pk.y = (uint32_t)narrow<uint16_t>(v[2]) | ((uint32_t)narrow<uint16_t>(v[3]) << 16);
+                *reinterpret_cast<uint2 *>(yh + t0 + poff + 8 * q) = pk;
+            } else if (VEC) {  // t4 < lim and lim a multiple of 8: the whole piece
                 uint2 pk;
                 pk.x = (uint32_t)narrow<uint16_t>(v[0]) | ((uint32_t)narrow<uint16_t>(v[1]) << 16);
                 pk.y = (uint32_t)narrow<uint16_t>(v[2]) | ((uint32_t)narrow<uint16_t>(v[3]) << 16);
@@ -520,7 +574,7 @@ __global__ __launch_bounds__(kThreads, VEC ? 2 : 1) void ssd_fused_kernel(SsdArg
                     if (t4 + e < lim) yg[t0 + t4 + e] = narrow<uint16_t>(v[e]);
             }
         }
-        if (c + 1 < a.nc) load_z(c + 1);
+        load_z(c + 1 < a.nc ? c + 1 : a.nc - 1);
     }
     if (a.hT) {
         // the lane index behind an empty asm, so that these addresses are formed here and not kept
@@ -546,10 +600,13 @@ hipError_t launch_walk(const SsdArgs &a, hipStream_t stream) {
 hipError_t launch_fused(const SsdArgs &a, int64_t N, hipStream_t stream) {
     const dim3 grid((unsigned)(a.b * a.H));
     const bool vec = a.vec && a.vec8 && a.vec_bc16;
-    if (N == 64 && vec) hipLaunchKernelGGL((ssd_fused_kernel<64, true>), grid, dim3(kThreads), 0, stream, a);
-    else if (N == 64) hipLaunchKernelGGL((ssd_fused_kernel<64, false>), grid, dim3(kThreads), 0, stream, a);
-    else if (N == 128 && vec) hipLaunchKernelGGL((ssd_fused_kernel<128, true>), grid, dim3(kThreads), 0, stream, a);
-    else if (N == 128) hipLaunchKernelGGL((ssd_fused_kernel<128, false>), grid, dim3(kThreads), 0, stream, a);
+    const bool whole = vec && a.L % kQ == 0 && kP * a.L < (INT64_C(1) << 31);
+    if (N == 64 && whole) hipLaunchKernelGGL((ssd_fused_kernel<64, 2>), grid, dim3(kThreads), 0, stream, a);
+    else if (N == 64 && vec) hipLaunchKernelGGL((ssd_fused_kernel<64, 1>), grid, dim3(kThreads), 0, stream, a);
+    else if (N == 64) hipLaunchKernelGGL((ssd_fused_kernel<64, 0>), grid, dim3(kThreads), 0, stream, a);
+    else if (N == 128 && whole) hipLaunchKernelGGL((ssd_fused_kernel<128, 2>), grid, dim3(kThreads), 0, stream, a);
+    else if (N == 128 && vec) hipLaunchKernelGGL((ssd_fused_kernel<128, 1>), grid, dim3(kThreads), 0, stream, a);
+    else if (N == 128) hipLaunchKernelGGL((ssd_fused_kernel<128, 0>), grid, dim3(kThreads), 0, stream, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -122,12 +122,16 @@ def test_ssd_matches_recurrent_scan_kernel():
 
 # On a 256-CU device: bf16 shapes with b·H >= 512 take the single-walk form (ssd_fused_kernel); other
 # shapes with b·H·N/64 >= 512 take the fused state walk (ssd_scan_kernel) with the output kernel; the
-# cases above take the three-kernel form. Ragged last chunks, initial states, both storage types.
+# cases above take the three-kernel form. Ragged last chunks, initial states, both storage types. The
+# single walk has three access modes: whole chunks (L a multiple of 64), whole 8-step pieces (L a
+# multiple of 8) and element by element.
 FUSED = [
     # b, H, L, N, dtype, initial state
     (8, 64, 130, 64, "f32", True),      # state walk
-    (4, 128, 200, 128, "bf16", True),   # single walk
-    (8, 64, 64, 64, "bf16", False),     # single walk, one whole chunk
+    (4, 128, 200, 128, "bf16", True),   # single walk, whole pieces, ragged last chunk
+    (4, 128, 256, 128, "bf16", True),   # single walk, whole chunks, initial state
+    (2, 256, 192, 64, "bf16", True),    # single walk, whole chunks, N = 64
+    (8, 64, 64, 64, "bf16", False),     # single walk, one whole chunk (whole-chunk mode)
     (4, 64, 333, 128, "f32", False),    # state walk
     (4, 64, 150, 128, "bf16", True),    # state walk (b·H = 256)
     (2, 256, 104, 64, "bf16", False),   # single walk, N = 64, ragged last chunk
