@@ -31,6 +31,11 @@
 // P needs ΣΔ over the whole segment: the wavefront of state group 0 sums Δ over the steps it did not walk
 // (those tiles of Δ alone) and writes P for all N states of its channels; P is exact whatever the sign of Δ.
 //
+// Split walk. When the caller gives E2 (a carry pass follows), group 0's walk, the longest, is split
+// between two wavefronts per unit by the same composition: the later part walks the segment's last tiles
+// into E; the earlier part sums Δ over those tiles, starts with R = exp(A·ΣΔ) (the decay from the segment
+// end back to there) and walks on below them into E2, and forms P. E + E2 is the whole walk's sum.
+//
 // Per (t, n) the common path issues one exp and five fp32 operations: u, R·Ā (which is also R's update),
 // B·x, the difference R·Ā − R = R·(Ā − 1), and the accumulation. Tiles are classified per wavefront as in
 // the output pass: where some channel's Δ-sum over the tile is small against 1/|A|, Ā − 1 comes from the
@@ -67,6 +72,8 @@ struct AggArgs {
     const float *A;
     const void *B;
     float *P, *E;          // [n_seg − 1][b][d][N]
+    float *E2;             // the split walk's earlier sums (states 0..3), or null: no split
+    int split_tiles;       // tiles at the segment end walked by the later part of group 0 (split walk)
     int64_t b, d, L, N;
     int64_t seg_len;
     int64_t n_cb;          // blocks of 64 channels per batch row
@@ -103,9 +110,14 @@ __global__ __launch_bounds__(kWave, 3) void agg_rev_kernel(AggArgs a) {
     // all land on u's XCD
     const uint32_t blk = blockIdx.x;
     const uint32_t nu8 = (uint32_t)((a.n_units + kXcds - 1) / kXcds * kXcds);
-    const int grp = (int)(blk / nu8);
-    const int64_t u = blk - (uint32_t)grp * nu8;
+    const int slot = (int)(blk / nu8);
+    const int64_t u = blk - (uint32_t)slot * nu8;
     if (u >= a.n_units) return;  // padding of the unit count (wave-uniform)
+    // With the split walk, slot 0 is group 0's earlier part and slot 1 its later part (the longest walks
+    // first); the other groups follow. part: 0 whole walk, 1 earlier part, 2 later part.
+    const bool split = a.E2 != nullptr;
+    const int grp = split ? (slot < 2 ? 0 : slot - 1) : slot;
+    const int part = split && slot < 2 ? (slot == 0 ? 1 : 2) : 0;
     const uint32_t ncb = (uint32_t)(a.b * a.n_cb);
     const int64_t seg = u / ncb;
     const uint32_t cb = (uint32_t)(u - seg * ncb);
@@ -267,45 +279,81 @@ __global__ __launch_bounds__(kWave, 3) void agg_rev_kernel(AggArgs a) {
     };
 
     float dsum = 0.0f;
+    // tiles [it_lo, ntiles) belong to the later part of a split walk, [0, it_lo) to the earlier part
+    const int it_lo = ntiles > a.split_tiles ? ntiles - a.split_tiles : 0;
     int it = ntiles - 1;
-    const int64_t t_last = t_begin + (int64_t)it * kT;
-    for (int i = lane; i < kT * kNP; i += kWave) Bs[i] = 0.0f;
-    load_tile(t_last, true);
-    wave_sync();
-    store_tile(true);
-    if (it > 0) load_tile(t_last - kT, true);
-    wave_sync();
+    if (part == 1) {
+        // the earlier part: ΣΔ over the later part's tiles (Δ alone), so that R starts as the decay from the
+        // segment end back to it, exp(A·ΣΔ); then the walk continues below it as a whole walk would
+        load_tile(t_begin + (int64_t)(ntiles - 1) * kT, false);
 #pragma unroll 1
-    for (; it >= 0; --it) {
-        const float ts = row_dsum();
-        dsum += ts;
-        if (wave_zero) {
-            walk_tile(std::integral_constant<int, 2>{});
-        } else if (__any(ts < thr_sum)) {
-            walk_tile(std::integral_constant<int, 1>{});
-        } else {
-            walk_tile(std::integral_constant<int, 0>{});
+        for (int k = ntiles - 1; k >= it_lo; --k) {  // one tile ahead
+            wave_sync();
+            store_tile(false);
+            wave_sync();
+            if (k > it_lo) load_tile(t_begin + (int64_t)(k - 1) * kT, false);
+            dsum += row_dsum();
         }
-        if (it == 0) break;
-        // stop once every live state's decay back to here is negligible (a NaN never passes)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) R[j] = zero[j] ? 1.0f : exp2_fast(a2[j] * dsum);
+        it = it_lo - 1;
+    }
+    // the walk over tiles [lo, it]: everything for a whole walk, the later part's tiles, or from below them
+    const int lo = part == 2 ? it_lo : 0;
+    bool walk = it >= lo;
+    if (walk && part == 1) {
         bool done = true;
 #pragma unroll
         for (int j = 0; j < 4; ++j) done = done && (!live[j] || R[j] <= kStopRel);
-        if (__all(done)) break;
-        const int64_t t0 = t_begin + (int64_t)it * kT;
-        wave_sync();  // the walk's reads of the tile come before it is overwritten
-        store_tile(true);
-        wave_sync();
-        if (it > 1) load_tile(t0 - 2 * kT, true);
+        walk = !__all(done);
     }
+    if (walk) {
+        const int64_t t_last = t_begin + (int64_t)it * kT;
+        for (int i = lane; i < kT * kNP; i += kWave) Bs[i] = 0.0f;
+        load_tile(t_last, true);
+        wave_sync();
+        store_tile(true);
+        if (it > lo) load_tile(t_last - kT, true);
+        wave_sync();
+#pragma unroll 1
+        for (; it >= lo; --it) {
+            const float ts = row_dsum();
+            dsum += ts;
+            if (wave_zero) {
+                walk_tile(std::integral_constant<int, 2>{});
+            } else if (__any(ts < thr_sum)) {
+                walk_tile(std::integral_constant<int, 1>{});
+            } else {
+                walk_tile(std::integral_constant<int, 0>{});
+            }
+            if (it == lo) {
+                --it;
+                break;
+            }
+            // stop once every live state's decay back to here is negligible (a NaN never passes)
+            bool done = true;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) done = done && (!live[j] || R[j] <= kStopRel);
+            if (__all(done)) {
+                --it;
+                break;
+            }
+            const int64_t t0 = t_begin + (int64_t)it * kT;
+            wave_sync();  // the walk's reads of the tile come before it is overwritten
+            store_tile(true);
+            wave_sync();
+            if (it > lo + 1) load_tile(t0 - 2 * kT, true);
+        }
+    }
+    // `it` is now the highest tile not walked (−1 when the walk reached the segment start)
 
     const int64_t base = (seg * a.b * a.d + bi * a.d + ch) * a.N;
-    if (grp == 0) {
-        // ΣΔ over the tiles not walked (0 .. it − 1), Δ only, one tile ahead
-        if (it > 0) {
-            load_tile(t_begin + (int64_t)(it - 1) * kT, false);
+    if (grp == 0 && part != 2) {
+        // ΣΔ over the tiles not walked (0 .. it), Δ only, one tile ahead
+        if (it >= 0) {
+            load_tile(t_begin + (int64_t)it * kT, false);
 #pragma unroll 1
-            for (int k = it - 1; k >= 0; --k) {
+            for (int k = it; k >= 0; --k) {
                 wave_sync();
                 store_tile(false);
                 wave_sync();
@@ -320,9 +368,10 @@ __global__ __launch_bounds__(kWave, 3) void agg_rev_kernel(AggArgs a) {
             }
         }
     }
+    float *Eo = part == 1 ? a.E2 : a.E;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        if (live[j]) a.E[base + n0 + j] = Eacc[j] * isc[j];
+        if (live[j]) Eo[base + n0 + j] = Eacc[j] * isc[j];
 }
 
 }  // namespace
@@ -331,7 +380,7 @@ hipError_t launch_agg_rev(const AggLaunch &p, hipStream_t stream) {
     if (p.n_seg <= 1) return hipSuccess;
     if (p.N < 1 || p.N > 64) return hipErrorInvalidValue;
     AggArgs a{};
-    a.x = p.x; a.delta = p.delta; a.A = p.A; a.B = p.B; a.P = p.P; a.E = p.E;
+    a.x = p.x; a.delta = p.delta; a.A = p.A; a.B = p.B; a.P = p.P; a.E = p.E; a.E2 = p.E2;
     a.b = p.b; a.d = p.d; a.L = p.L; a.N = p.N; a.seg_len = p.seg_len;
     a.n_cb = (p.d + kWave - 1) / kWave;
     a.n_units = (int64_t)(p.n_seg - 1) * p.b * a.n_cb;
@@ -340,7 +389,11 @@ hipError_t launch_agg_rev(const AggLaunch &p, hipStream_t stream) {
     auto aligned16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
     a.vec_rows = ((p.L * esize) % 16 == 0) && aligned16(p.x) && aligned16(p.delta);
     a.vec_bc = ((p.L * p.N * esize) % 16 == 0) && aligned16(p.B);
-    const int64_t grid = (a.n_units + kXcds - 1) / kXcds * kXcds * a.n_grp;
+    // the split walk: group 0's later part takes the last fifth of each segment (on the long-context
+    // recipe, about half of that group's walk), so the two parts take similar times
+    const int kt = p.bf16 ? 32 : 16;
+    a.split_tiles = a.E2 ? (int)((p.seg_len / kt + 4) / 5) : 0;
+    const int64_t grid = (a.n_units + kXcds - 1) / kXcds * kXcds * (a.n_grp + (a.E2 ? 1 : 0));
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const dim3 g((unsigned)grid), w(kWave);
     if (p.bf16) {

@@ -69,6 +69,10 @@ struct AggLaunch {
     const float *A;
     const void *B;
     float *P, *E;
+    // E2 (may be null): when given, the walk of state group 0 (states 0..3) is split between two wavefronts
+    // per unit, and the earlier part's sum goes to E2 [n_seg-1][b][d][N] (states 0..3 only), to be added
+    // to E by the carry pass; E then holds the later part's
+    float *E2;
     int64_t b, d, L, N, seg_len;
     int n_seg;
     bool bf16;

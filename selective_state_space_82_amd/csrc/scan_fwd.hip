@@ -680,11 +680,15 @@ __global__ __launch_bounds__(kWave, (G == 4 && NPL == 4) ? 3 : 1) void scan_ckpt
 
 // Chunk carry for many segments: h_in[k] = P[k]·h_in[k−1] + E[k] per (b, d, n), from the
 // initial state.
+// States n < e2_states (the slowest group, whose backward walk was split in two) have the earlier part of
+// their end state parked in Hin by the aggregate pass: it is read and added to E before the carry
+// overwrites it (same thread, same element).
 __global__ __launch_bounds__(256) void carry_kernel(const float *__restrict__ P, const float *__restrict__ Eend,
                                                     float *__restrict__ Hin, const float *__restrict__ init,
-                                                    int64_t bdn, int n_seg) {
+                                                    int64_t bdn, int n_seg, int N, int e2_states) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= bdn) return;
+    const bool e2 = (int)(i % N) < e2_states;
     float h = init ? init[i] : 0.0f;
     // eight segments' aggregates in flight at a time: one memory round trip per eight steps of the chain
     int k = 0;
@@ -693,7 +697,7 @@ __global__ __launch_bounds__(256) void carry_kernel(const float *__restrict__ P,
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             p[q] = P[(k + q) * bdn + i];
-            e[q] = Eend[(k + q) * bdn + i];
+            e[q] = Eend[(k + q) * bdn + i] + (e2 ? Hin[(k + q) * bdn + i] : 0.0f);
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -702,7 +706,8 @@ __global__ __launch_bounds__(256) void carry_kernel(const float *__restrict__ P,
         }
     }
     for (; k + 1 < n_seg; ++k) {
-        h = __builtin_fmaf(P[k * bdn + i], h, Eend[k * bdn + i]);
+        const float ek = Eend[k * bdn + i] + (e2 ? Hin[k * bdn + i] : 0.0f);
+        h = __builtin_fmaf(P[k * bdn + i], h, ek);
         Hin[k * bdn + i] = h;
     }
 }
@@ -727,14 +732,18 @@ hipError_t launch_typed(const FwdArgs &args, int n_seg, int64_t ncb, const FwdLa
         } else {
             AggLaunch g{};
             g.x = p.x; g.delta = p.delta; g.A = p.A; g.B = p.B; g.P = args.agg_P; g.E = args.agg_E;
+            // with a carry pass to come, its output array holds the split walk's second sums until then
+            g.E2 = args.h_in ? const_cast<float *>(args.h_in) : nullptr;
             g.b = p.b; g.d = p.d; g.L = p.L; g.N = p.N; g.seg_len = p.seg_len; g.n_seg = n_seg; g.bf16 = p.bf16;
             e = launch_agg_rev(g, stream);
         }
         if (e != hipSuccess) return e;
         if (args.h_in) {
             const int64_t bdn = p.b * p.d * p.N;
+            const int e2_states = (FE || p.seg_len < kAggWalkMinSeg) ? 0 : 4;
             hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((bdn + 255) / 256)), dim3(256), 0, stream, args.agg_P,
-                               args.agg_E, const_cast<float *>(args.h_in), p.init_state, bdn, n_seg);
+                               args.agg_E, const_cast<float *>(args.h_in), p.init_state, bdn, n_seg, (int)p.N,
+                               e2_states);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

@@ -278,6 +278,12 @@ TRUNC = {
     "spread": dict(L=4096, delta_mu=-2.0, seg_len=1024),
     # slow decay (|Δ·A| ~ 1e-4 per step): no walk stops
     "slow": dict(L=3072, a_value=-0.01, delta_value=0.01, seg_len=1024),
+    # more than 16 segments (the carry pass): state group 0's walk is split between two wavefronts, the
+    # earlier part starting from the decay over the later part's steps; long-context decay rates
+    "split": dict(L=17 * 1024 + 300, delta_mu=-4.0, a_kind="neg_index_u", seg_len=1024),
+    # the same with fast decay (the later part stops within its own steps) and with slow decay (no stop)
+    "split_fast": dict(L=18 * 1024, delta_mu=0.5, seg_len=1024),
+    "split_slow": dict(L=17 * 1024 + 64, a_value=-0.01, delta_value=0.01, seg_len=1024),
 }
 
 
