@@ -298,6 +298,9 @@ struct LtiConvArgs {
     int64_t chunk, n_chunks;
     const float *h_in, *delta, *A, *C;
     int64_t N;
+    // items (batch row, chunk) of a channel, b·n_chunks of them in that order, handled by one workgroup:
+    // its K̄ spectrum is formed once and serves all of them (two per transform)
+    int64_t items_per_wg;
 };
 
 // RESP: the chunked form, whose chunks after the first add the response of the state entering them (a
@@ -319,22 +322,28 @@ __global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiCo
         sincospif(2.0f * (float)i / (float)M, &s, &c);  // 2i/M is exact
         (j < M / 64 ? s_hi[j] : s_lo[j - M / 64]) = make_float2(c, -s);
     }
-    // workgroup -> (chunk j, channel id); one chunk spans the whole sequence when the form is not chunked
+    // workgroup -> (channel id, group g of its items); an item is (batch row, chunk), and one chunk spans
+    // the whole sequence when the form is not chunked
     const int64_t id = blockIdx.x % a.d;
-    const int64_t j = blockIdx.x / a.d;
+    const int64_t g = blockIdx.x / a.d;
     const int64_t klen = a.chunk > 0 ? a.chunk : a.L;  // taps of K per channel
-    const int64_t t0 = j * klen;                         // the chunk's first step
-    const int L = (int)((a.L - t0) < klen ? (a.L - t0) : klen);
+    const int64_t nch = RESP ? a.n_chunks : 1;  // the single-transform form has one chunk per row
+    const int64_t i_begin = g * a.items_per_wg;
+    const int64_t i_end = (a.b * nch - i_begin) < a.items_per_wg ? a.b * nch : i_begin + a.items_per_wg;
     // chunks after the first add the response of the state entering them: the log2 decays u_n and, per
-    // batch row of the pair, w_n = C_n·h_n
+    // item of the pair, w_n = C_n·h_n (0 for a first chunk)
     __shared__ float s_u[RESP ? SSM_MAX_N : 1], s_w[2][RESP ? SSM_MAX_N : 1];
-    const bool resp = RESP && j > 0;
-    if (resp && threadIdx.x < a.N) {
+    if (RESP && threadIdx.x < a.N) {
         const int64_t n = threadIdx.x;
         s_u[n] = a.delta[id] * (a.A[id * a.N + n] * kLog2e);
     }
     __syncthreads();
 
+    // taps of K̄ (and, in the single-transform form, steps). t00 is 0 there (one workgroup per channel); the
+    // expressions keep the shape under which that form's kernels fit 128 registers without spilling (a
+    // plainer min(L, klen) cost the 2^13-point bf16 kernel two spilled registers and 3.5 %)
+    const int64_t t00 = RESP ? 0 : (blockIdx.x / a.d) * klen;
+    const int kl = (int)((a.L - t00) < klen ? (a.L - t00) : klen);
     // spectrum of K' (K̄ with D added to its first tap), kept in registers
     float2 kf[16];
     {
@@ -345,7 +354,7 @@ __global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiCo
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
             const int e = f.wide_pos(s);
-            if (e < L) kf[s].x = Kd[e];
+            if (e < kl) kf[s].x = Kd[e];
         }
         if (threadIdx.x == 0) kf[0].x += dsk;  // wide_pos(0) of thread 0 is position 0
         f.forward(kf);
@@ -355,55 +364,110 @@ __global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiCo
     const T *zg = static_cast<const T *>(a.z);
     T *yg = static_cast<T *>(a.y);
     constexpr float inv_m = 1.0f / (float)M;
-    for (int64_t b1 = 0; b1 < a.b; b1 += 2) {
-        const bool two = b1 + 1 < a.b;
-        // the pair's rows (workgroup-uniform pointers; per-lane offsets stay 32-bit)
-        const T *x1 = xg + (b1 * a.d + id) * a.L + t0;
-        const T *x2 = two ? x1 + a.d * a.L : x1;
-        float2 v[16];
-#pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            const int e = f.wide_pos(s);
-            const bool in = e < L;
-            v[s] = make_float2(in ? widen(x1[e]) : 0.0f, in && two ? widen(x2[e]) : 0.0f);
-        }
-        __syncthreads();  // the previous pair's last reads of s_buf (and s_w) are done
-        if (resp && threadIdx.x < a.N) {
-            const int64_t n = threadIdx.x;
-            const float cn = a.C[id * a.N + n];
-            const int64_t hrow = (b1 * a.d + id) * (a.n_chunks - 1) + (j - 1);
-            s_w[0][n] = cn * a.h_in[hrow * a.N + n];
-            s_w[1][n] = two ? cn * a.h_in[(hrow + a.d * (a.n_chunks - 1)) * a.N + n] : 0.0f;
-        }
-        f.forward(v);
-#pragma unroll
-        for (int s = 0; s < 16; ++s) v[s] = cmul(v[s], kf[s]);
-        f.inverse(v);
-        const int64_t o1 = (b1 * a.d + id) * a.L + t0;
-        const int64_t o2 = two ? o1 + a.d * a.L : o1;
-        T *y1p = yg + o1, *y2p = yg + o2;
-        const T *z1 = zg ? zg + o1 : nullptr, *z2 = zg ? zg + o2 : nullptr;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            const int e = f.wide_pos(s);
-            if (e < L) {
-                float y1 = v[s].x * inv_m, y2 = v[s].y * inv_m;
-                if (RESP && resp) {  // + Σ_n w_n·Ā_n^{e+1} (s_w was written before the transforms' barriers)
-                    const float k1 = (float)(e + 1);  // <= 2^13: exact
-#pragma unroll 1
-                    for (int n = 0; n < (int)a.N; ++n) {
-                        const float pw = exp2_fast(k1 * s_u[n]);
-                        y1 = __builtin_fmaf(s_w[0][n], pw, y1);
-                        y2 = __builtin_fmaf(s_w[1][n], pw, y2);
+    if constexpr (!RESP) {  // one transform per row pair: the batch rows of the pair share the chunk
+        for (int64_t b1 = 0; b1 < a.b; b1 += 2) {
+            const bool two = b1 + 1 < a.b;
+            // the pair's rows (workgroup-uniform pointers; per-lane offsets stay 32-bit)
+            const T *x1 = xg + (b1 * a.d + id) * a.L + t00;
+            const T *x2 = two ? x1 + a.d * a.L : x1;
+            float2 v[16];
+    #pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const int e = f.wide_pos(s);
+                const bool in = e < kl;
+                v[s] = make_float2(in ? widen(x1[e]) : 0.0f, in && two ? widen(x2[e]) : 0.0f);
+            }
+            __syncthreads();  // the previous pair's last reads of s_buf (and s_w) are done
+            f.forward(v);
+    #pragma unroll
+            for (int s = 0; s < 16; ++s) v[s] = cmul(v[s], kf[s]);
+            f.inverse(v);
+            const int64_t o1 = (b1 * a.d + id) * a.L + t00;
+            const int64_t o2 = two ? o1 + a.d * a.L : o1;
+            T *y1p = yg + o1, *y2p = yg + o2;
+            const T *z1 = zg ? zg + o1 : nullptr, *z2 = zg ? zg + o2 : nullptr;
+    #pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const int e = f.wide_pos(s);
+                if (e < kl) {
+                    float y1 = v[s].x * inv_m, y2 = v[s].y * inv_m;
+                    if (zg) {
+                        y1 *= silu(widen(z1[e]));
+                        if (two) y2 *= silu(widen(z2[e]));
                     }
-                    asm volatile("" : "+v"(y1), "+v"(y2));  // one slot at a time: the loop holds few registers
+                    y1p[e] = narrow<T>(y1);
+                    if (two) y2p[e] = narrow<T>(y2);
                 }
-                if (zg) {
-                    y1 *= silu(widen(z1[e]));
-                    if (two) y2 *= silu(widen(z2[e]));
+            }
+        }
+    } else {  // the chunked form: the workgroup's items (batch row, chunk), two per transform
+        for (int64_t i1 = i_begin; i1 < i_end; i1 += 2) {
+            const bool two = i1 + 1 < i_end;
+            // the pair's items: (batch row, chunk), their first steps and lengths
+            const int64_t b1 = i1 / nch, j1 = i1 - b1 * nch;
+            const int64_t b2 = two ? (i1 + 1) / nch : b1, j2 = two ? (i1 + 1) - b2 * nch : j1;
+            const int64_t t01 = j1 * klen, t02 = j2 * klen;
+            const int L1 = (int)((a.L - t01) < klen ? (a.L - t01) : klen);
+            const int L2 = two ? (int)((a.L - t02) < klen ? (a.L - t02) : klen) : 0;
+            // the pair's rows (workgroup-uniform pointers; per-lane offsets stay 32-bit)
+            const T *x1 = xg + (b1 * a.d + id) * a.L + t01;
+            const T *x2 = xg + (b2 * a.d + id) * a.L + t02;
+            float2 v[16];
+    #pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const int e = f.wide_pos(s);
+                v[s] = make_float2(e < L1 ? widen(x1[e]) : 0.0f, e < L2 ? widen(x2[e]) : 0.0f);
+            }
+            __syncthreads();  // the previous pair's last reads of s_buf (and s_w) are done
+            if (RESP && threadIdx.x < a.N) {
+                const int64_t n = threadIdx.x;
+                const float cn = a.C[id * a.N + n];
+                s_w[0][n] = j1 > 0 ? cn * a.h_in[((b1 * a.d + id) * (nch - 1) + (j1 - 1)) * a.N + n] : 0.0f;
+                s_w[1][n] = j2 > 0 && two ? cn * a.h_in[((b2 * a.d + id) * (nch - 1) + (j2 - 1)) * a.N + n] : 0.0f;
+            }
+            f.forward(v);
+    #pragma unroll
+            for (int s = 0; s < 16; ++s) v[s] = cmul(v[s], kf[s]);
+            f.inverse(v);
+            if (RESP) {
+                // + M·Σ_n w_n·Ā_n^{e+1} on the unscaled outputs (M is a power of 2, so the later 1/M is exact).
+                // This thread's positions are e = tid + NT·k (k = 0 .. 15, slot (k % G0)·R0 + k / G0), so the
+                // powers form a geometric sequence in k: Ā^{tid+1} and the ratio Ā^{NT}, one exp each per state,
+                // then a product per position (at most 15 products: about 16 ulp). s_w was written before the
+                // transforms' barriers.
+                const float e0 = (float)(threadIdx.x + 1);
+    #pragma unroll 1
+                for (int n = 0; n < (int)a.N; ++n) {
+                    const float un = s_u[n];
+                    const float w1 = s_w[0][n] * (float)M, w2 = s_w[1][n] * (float)M;
+                    float pw = exp2_fast(e0 * un);
+                    const float q = exp2_fast((float)F::NT * un);
+    #pragma unroll
+                    for (int k = 0; k < 16; ++k) {
+                        const int sl = (k % F::G0) * F::R0 + k / F::G0;
+                        v[sl].x = __builtin_fmaf(w1, pw, v[sl].x);
+                        v[sl].y = __builtin_fmaf(w2, pw, v[sl].y);
+                        pw *= q;
+                    }
                 }
-                y1p[e] = narrow<T>(y1);
-                if (two) y2p[e] = narrow<T>(y2);
+            }
+            const int64_t o1 = (b1 * a.d + id) * a.L + t01;
+            const int64_t o2 = (b2 * a.d + id) * a.L + t02;
+            T *y1p = yg + o1, *y2p = yg + o2;
+            const T *z1 = zg ? zg + o1 : nullptr, *z2 = zg ? zg + o2 : nullptr;
+    #pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const int e = f.wide_pos(s);
+                if (e < L1) {
+                    float y1 = v[s].x * inv_m;
+                    if (zg) y1 *= silu(widen(z1[e]));
+                    y1p[e] = narrow<T>(y1);
+                }
+                if (e < L2) {
+                    float y2 = v[s].y * inv_m;
+                    if (zg) y2 *= silu(widen(z2[e]));
+                    y2p[e] = narrow<T>(y2);
+                }
             }
         }
     }
@@ -411,7 +475,8 @@ __global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiCo
 
 template <typename T, int LOGM>
 hipError_t launch_conv_m(const LtiConvArgs &a, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.d * a.n_chunks)), block((1 << LOGM) / 16);
+    const int64_t groups = (a.b * a.n_chunks + a.items_per_wg - 1) / a.items_per_wg;
+    const dim3 grid((unsigned)(a.d * groups)), block((1 << LOGM) / 16);
     if (a.h_in) {
         if constexpr ((int64_t(1) << LOGM) == 2 * kLtiChunk) {
             hipLaunchKernelGGL((lti_fft_conv_kernel<T, LOGM, true>), grid, block, 0, stream, a);
@@ -512,10 +577,15 @@ hipError_t launch_lti_conv(const LtiConvLaunch &p, hipStream_t stream) {
     if (p.b == 0 || p.d == 0 || p.L == 0) return hipSuccess;
     const int64_t klen = p.chunk > 0 ? p.chunk : p.L;
     const int64_t n_chunks = (p.L + klen - 1) / klen;
+    // the chunked form: up to 32 items (batch row, chunk) per workgroup, an even number so that they pair
+    // up, the channel's K̄ spectrum transformed once for all of them; the single-transform form: all batch
+    // rows of a channel in one workgroup
+    const int64_t items = p.b * n_chunks;
+    const int64_t per_wg = n_chunks == 1 ? p.b : (items < 32 ? items + (items & 1) : 32);
     const LtiConvArgs a{p.x, p.z, p.K, p.D, p.y, p.b, p.d, p.L, p.chunk, n_chunks,
-                        n_chunks > 1 ? p.h_in : nullptr, p.delta, p.A, p.C, p.N};
+                        n_chunks > 1 ? p.h_in : nullptr, p.delta, p.A, p.C, p.N, per_wg};
     if (n_chunks > 1 && (!p.h_in || !p.delta || !p.A || !p.C || p.N < 1 || p.N > SSM_MAX_N)) return hipErrorInvalidValue;
-    if (p.d * n_chunks > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (p.d * ((items + per_wg - 1) / per_wg) > 0x7fffffffLL) return hipErrorInvalidValue;
     const int logm = lti_fft_log2(klen);
     if (logm > kLtiMaxLog2) return hipErrorInvalidValue;
     if (p.bf16) return launch_conv_typed<uint16_t>(a, logm, stream);
