@@ -32,7 +32,7 @@ PROFILE_SOURCES = {
                  "tile_common.h"),
     "conv1d": ("abi.cpp", "device_common.h", "launch.h", "conv1d.hip", "tile_common.h"),
     "frontend": ("abi.cpp", "conv1d.hip", "device_common.h", "launch.h", "scan_fwd.hip", "tile_common.h"),
-    "lti": ("abi.cpp", "device_common.h", "launch.h", "lti.hip"),
+    "lti": ("abi.cpp", "device_common.h", "launch.h", "lti.hip", "tile_common.h"),
     "ssd": ("abi.cpp", "device_common.h", "launch.h", "ssd.hip", "ssd_common.h", "ssd_scan.hip"),
 }
 

@@ -27,6 +27,7 @@
 #include "device_common.h"
 #include "launch.h"
 #include "ssm_scan.h"
+#include "tile_common.h"
 
 namespace ssm {
 namespace {
@@ -489,43 +490,73 @@ hipError_t launch_conv_m(const LtiConvArgs &a, hipStream_t stream) {
 }
 
 // End state of chunk j of row (b, d) from zero, for chunks 0 .. n_chunks − 2 (all of full length):
-// E_n = B̄_n·Σ_s Ā_n^{chunk−1−s}·x_s. A workgroup per (row, chunk); thread i takes 16 consecutive steps by
-// Horner's rule (acc ← acc·Ā + x, so no power is formed) and scales its sum by Ā^{chunk−16−16i} (one exp);
-// the 256 partial sums of each state are added in LDS.
+// E_n = B̄_n·Σ_s Ā_n^{chunk−1−s}·x_s. One wavefront per (row, chunk): lane l takes the 64 consecutive steps
+// 64 l .. 64 l + 63 (16-byte loads) by Horner's rule (acc ← acc·Ā + x, so no power is formed), for 16 states
+// at a time, and scales its sum by Ā^{chunk−64(l+1)} (one exp per state). The 64 lanes' sums of the 16
+// states are then added by a transposing butterfly: at each of the first four exchanges a lane keeps half of
+// the states it still holds and hands the other half to its partner, so 8 + 4 + 2 + 1 + 2 = 17 exchanges
+// leave lane l with the whole sum of one state (15 of them per state at one exchange per state and step).
 template <typename T>
-__global__ __launch_bounds__(256) void lti_chunk_agg_kernel(LtiChunkLaunch p, int64_t n_chunks) {
-    constexpr int kPer = 16;
-    __shared__ float s_part[256];
-    __shared__ float s_res[SSM_MAX_N];
+__global__ __launch_bounds__(kWave) void lti_chunk_agg_kernel(LtiChunkLaunch p, int64_t n_chunks, int vec) {
+    constexpr int kPer = 64;                        // steps per lane
+    constexpr int E = Chunk<T>::kElems;
+    constexpr int kG = 16;                          // states per group
     const int64_t nc1 = n_chunks - 1;
     const int64_t row = blockIdx.x / nc1;           // b·d + d
     const int64_t j = blockIdx.x - row * nc1;
     const int64_t id = row % p.d;
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x;
     const T *xr = static_cast<const T *>(p.x) + row * p.L + j * p.chunk;
-    const int64_t s0 = (int64_t)tid * kPer;
-    float xv[kPer];
+    const int64_t s0 = (int64_t)lane * kPer;
+    uint4 xv[kPer / E];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) xv[k] = s0 + k < p.chunk ? widen(xr[s0 + k]) : 0.0f;
+    for (int q = 0; q < kPer / E; ++q) xv[q] = get_chunk<T>(xr, s0 + q * E, p.chunk, s0 < p.chunk, vec != 0);
     const float dt = p.delta[id];
-    for (int n = 0; n < (int)p.N; ++n) {
-        const float an = p.A[id * p.N + n];
-        const float u = dt * (an * kLog2e);
-        const float abar = exp2_fast(u);
-        float acc = 0.0f;
+    const bool in = s0 < p.chunk;                     // chunk is a multiple of kPer: a lane is wholly in or out
+    const float rest = in ? (float)(p.chunk - kPer - s0) : 0.0f;  // steps after this lane's last one
+    for (int n0 = 0; n0 < (int)p.N; n0 += kG) {
+        float u[kG], ab[kG], acc[kG];
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) acc = __builtin_fmaf(acc, abar, xv[k]);
-        const int64_t rest = p.chunk - kPer - s0;  // steps after this thread's last one
-        s_part[tid] = rest >= 0 ? acc * exp2_fast((float)rest * u) : 0.0f;
-        __syncthreads();
-        for (int w = 128; w > 0; w >>= 1) {
-            if (tid < w) s_part[tid] += s_part[tid + w];
-            __syncthreads();
+        for (int i = 0; i < kG; ++i) {
+            const int n = n0 + i;
+            u[i] = n < (int)p.N ? dt * (p.A[id * p.N + n] * kLog2e) : 0.0f;
+            ab[i] = exp2_fast(u[i]);
+            acc[i] = 0.0f;
         }
-        if (tid == 0) s_res[n] = s_part[0] * (zoh_input_coef_log2(dt, u, abar, 1.0f / an) * p.B[id * p.N + n]);
-        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kPer / E; ++q) {
+            float xs[E];
+            chunk_to_regs<T>(xs, xv[q]);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+#pragma unroll
+                for (int i = 0; i < kG; ++i) acc[i] = __builtin_fmaf(acc[i], ab[i], xs[e]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kG; ++i) acc[i] = in ? acc[i] * exp2_fast(rest * u[i]) : 0.0f;
+        // transposing butterfly over the lanes: exchange across lane bit m keeps the lower half of the
+        // states held when that bit is 0, the upper half when it is 1
+#pragma unroll
+        for (int h = kG / 2, m = 32; h >= 1; h /= 2, m /= 2) {
+            const bool up = (lane & m) != 0;
+#pragma unroll
+            for (int i = 0; i < h; ++i) {
+                const float keep = up ? acc[h + i] : acc[i];
+                const float give = up ? acc[i] : acc[h + i];
+                acc[i] = keep + __shfl_xor(give, m);
+            }
+        }
+        acc[0] += __shfl_xor(acc[0], 2);
+        acc[0] += __shfl_xor(acc[0], 1);
+        // lane l now holds state n0 + 8·bit5 + 4·bit4 + 2·bit3 + bit2 of l
+        const int n = n0 + ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
+        if ((lane & 3) == 0 && n < (int)p.N) {
+            const float an = p.A[id * p.N + n];
+            const float un = dt * (an * kLog2e);
+            p.H[(row * nc1 + j) * p.N + n] = acc[0] * (zoh_input_coef_log2(dt, un, exp2_fast(un), 1.0f / an) * p.B[id * p.N + n]);
+        }
     }
-    if (tid < p.N) p.H[(row * nc1 + j) * p.N + tid] = s_res[tid];
 }
 
 // The states between chunks, in place: H_j ← Ā^chunk·H_{j−1} + H_j per (row, n), walking the chunks in order.
@@ -595,13 +626,16 @@ hipError_t launch_lti_conv(const LtiConvLaunch &p, hipStream_t stream) {
 hipError_t launch_lti_chunk_states(const LtiChunkLaunch &p, hipStream_t stream) {
     const int64_t n_chunks = (p.L + p.chunk - 1) / p.chunk;
     if (n_chunks <= 1 || p.b == 0 || p.d == 0) return hipSuccess;
-    if (p.chunk > 256 * 16 || p.N < 1 || p.N > SSM_MAX_N) return hipErrorInvalidValue;
+    if (p.chunk > 64 * kWave || p.chunk % 64 != 0 || p.N < 1 || p.N > SSM_MAX_N) return hipErrorInvalidValue;
     const int64_t blocks = p.b * p.d * (n_chunks - 1);
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    // 16-byte loads when every chunk of every row starts on a 16-byte boundary
+    const int64_t esize = p.bf16 ? 2 : 4;
+    const int vec = (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0 && (p.L * esize) % 16 == 0 && (p.chunk * esize) % 16 == 0;
     if (p.bf16)
-        hipLaunchKernelGGL(lti_chunk_agg_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream, p, n_chunks);
+        hipLaunchKernelGGL(lti_chunk_agg_kernel<uint16_t>, dim3((unsigned)blocks), dim3(kWave), 0, stream, p, n_chunks, vec);
     else
-        hipLaunchKernelGGL(lti_chunk_agg_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, p, n_chunks);
+        hipLaunchKernelGGL(lti_chunk_agg_kernel<float>, dim3((unsigned)blocks), dim3(kWave), 0, stream, p, n_chunks, vec);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t rows = p.b * p.d * p.N;

@@ -159,6 +159,7 @@ LONG = [
     (2, 24, 20000, 16, "f32", True, 0.1),   # 5 chunks, the last partial; A = 0 states (Ā = 1, B̄ = Δ·B)
     (1, 17, 12289, 7, "bf16", True, 0.0),   # an odd batch: the last transform carries one row
     (2, 6, 40000, 16, "bf16", False, 0.0),
+    (1, 5, 9000, 40, "f32", True, 0.05),    # N = 40: the chunk states in three groups of 16, the last partial
 ]
 
 
@@ -202,3 +203,18 @@ def test_lti_full_size_sampled(shape):
     yg = from_torch(y)
     got = np.stack([yg[ib, idd] for ib, idd in rows])
     _assert_close(got, yr, TAU[dt], f"full size {shape}")
+
+
+def test_lti_longctx_full_size_sampled():
+    """The long-context layer (b 1, d 2048, L 131072, N 16, bf16) in the chunked form the benchmark times:
+    32 chunks of 4096 steps joined through the state, checked on sampled rows against the recurrent oracle."""
+    b, d, L, N, dt = 1, 2048, 131072, 16, "bf16"
+    inp = I.random_lti(b, d, L, N, dtype=dt, seed=2)
+    t = _upload(inp)
+    y = api.ssm_lti_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = [(0, 0), (0, d - 1)] + [(0, int(c)) for c in rng.integers(1, d - 1, size=4)]
+    yr = _oracle_recurrent(inp, rows)
+    yg = from_torch(y)
+    _assert_close(np.stack([yg[ib, c] for ib, c in rows]), yr, TAU[dt], "long-context full size")
