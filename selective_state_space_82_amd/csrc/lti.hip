@@ -402,11 +402,14 @@ __global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiCo
             }
         }
     } else {  // the chunked form: the workgroup's items (batch row, chunk), two per transform
+        // the pair's items (batch row, chunk), stepped along without divisions (a 64-bit division per pair
+        // held enough registers to make this instantiation spill in its transform loop)
+        int64_t b1 = i_begin / nch, j1 = i_begin - b1 * nch;
         for (int64_t i1 = i_begin; i1 < i_end; i1 += 2) {
             const bool two = i1 + 1 < i_end;
-            // the pair's items: (batch row, chunk), their first steps and lengths
-            const int64_t b1 = i1 / nch, j1 = i1 - b1 * nch;
-            const int64_t b2 = two ? (i1 + 1) / nch : b1, j2 = two ? (i1 + 1) - b2 * nch : j1;
+            int64_t bn = b1, jn = j1 + 1;  // item i1 + 1
+            if (jn == nch) { jn = 0; ++bn; }
+            const int64_t b2 = two ? bn : b1, j2 = two ? jn : j1;
             const int64_t t01 = j1 * klen, t02 = j2 * klen;
             const int L1 = (int)((a.L - t01) < klen ? (a.L - t01) : klen);
             const int L2 = two ? (int)((a.L - t02) < klen ? (a.L - t02) : klen) : 0;
@@ -470,6 +473,9 @@ __global__ __launch_bounds__((1 << LOGM) / 16, 4) void lti_fft_conv_kernel(LtiCo
                     y2p[e] = narrow<T>(y2);
                 }
             }
+            b1 = bn;  // item i1 + 2
+            j1 = jn + 1;
+            if (j1 == nch) { j1 = 0; ++b1; }
         }
     }
 }
