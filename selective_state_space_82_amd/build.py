@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssmscan.so")
-SOURCES = ["scan_fwd.hip", "agg_rev.hip", "scan_bwd.hip", "scan_step.hip", "conv1d.hip", "lti.hip", "ssd.hip",
+SOURCES = ["scan_fwd.hip", "scan_small.hip", "agg_rev.hip", "scan_bwd.hip", "scan_step.hip", "conv1d.hip", "lti.hip", "ssd.hip",
            "ssd_scan.hip", "noalloc.hip", "abi.cpp"]
 ARCH = "gfx950"
 
@@ -23,7 +23,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=
 
 
 # The sources that decide the prefill kernels and their launch shapes.
-FWD_KERNEL_SOURCES = ("abi.cpp", "agg_rev.hip", "device_common.h", "launch.h", "scan_fwd.hip", "tile_common.h")
+FWD_KERNEL_SOURCES = ("abi.cpp", "agg_rev.hip", "device_common.h", "launch.h", "scan_fwd.hip", "scan_small.hip",
+                      "tile_common.h")
 # The sources behind each group of kernels a profile under profiles/ covers.
 PROFILE_SOURCES = {
     "scan_fwd": FWD_KERNEL_SOURCES,

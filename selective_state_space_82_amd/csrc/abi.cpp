@@ -161,6 +161,24 @@ ssm_status_t make_plan(int64_t b, int64_t d, int64_t L, int64_t N, const ssm_fwd
     return SSM_OK;
 }
 
+// A short sequence on few channel blocks (ssm::small_problem) runs the small-problem kernel, unless an option
+// asked for a plan of the main kernel. Its plan: segments of 8 or 16 steps, a workgroup per block of 16 channels
+// with a wavefront per segment, no aggregate pass and no scratch.
+bool plan_small(int64_t b, int64_t d, int64_t L, int64_t N, const ssm_fwd_opts_t *o, Plan *pl) {
+    if (o && (o->seg_len != 0 || o->lanes_per_channel != 0)) return false;
+    if (!ssm::small_problem(b, d, L, N)) return false;
+    const int64_t ncb = b * ((d + ssm::kSmallCh - 1) / ssm::kSmallCh);
+    pl->lanes = 4;
+    pl->npl = 4;
+    pl->seg_len = ssm::small_seg(L);
+    pl->n_seg = (int)((L + pl->seg_len - 1) / pl->seg_len);
+    pl->waves_per_seg = ncb;
+    pl->groups_out = ncb;
+    pl->groups_agg = 0;
+    pl->scratch_bytes = 0;
+    return true;
+}
+
 ssm_status_t check_fwd_sizes(int64_t b, int64_t d, int64_t L, int64_t N, ssm_dtype_t dtype) {
     if (!valid_dtype(dtype)) return SSM_ERR_UNSUPPORTED;
     if (b < 1 || d < 1 || N < 1 || L < 0) return SSM_ERR_SHAPE;
@@ -244,6 +262,7 @@ ssm_status_t fwd_impl(const void *x, const void *delta, const float *A, const vo
     st = make_plan(b, d, L, N, o, cu_count(), &pl);
     if (st != SSM_OK) return st;
     FwdLaunch p{};
+    p.small = !fe && plan_small(b, d, L, N, o, &pl);
     p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.y = y;
     p.final_state = final_state;
     p.init_state = o ? o->initial_state : nullptr;
@@ -476,6 +495,7 @@ ssm_status_t ssm_scan_fwd_plan(int64_t b, int64_t d, int64_t L, int64_t N, ssm_d
     Plan pl{};
     st = make_plan(b, d, L, N, opts, 256, &pl);
     if (st != SSM_OK) return st;
+    plan_small(b, d, L, N, opts, &pl);
     plan->seg_len = (int32_t)pl.seg_len;
     plan->lanes_per_channel = pl.lanes;
     plan->states_per_lane = pl.npl;

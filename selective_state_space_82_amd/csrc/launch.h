@@ -34,7 +34,25 @@ struct FwdLaunch {
     float *conv_state_out;
     void *x_out;
     int conv_W, delta_softplus;
+    // the small-problem kernel (small_problem() holds and no option forced a plan): no scratch, no segments
+    bool small;
 };
+
+// Small problems: at most kSmallMaxBlocks blocks of 16 channels over 2·kSmallSeg < L <= kSmallSeg·kSmallMaxWaves
+// steps with N <= 16 run as one workgroup per block, one wavefront per kSmallSeg steps (scan_small.hip).
+constexpr int kSmallSeg = 16;
+constexpr int kSmallMaxWaves = 16;
+constexpr int kSmallCh = 16;  // channels per workgroup
+constexpr int64_t kSmallMaxBlocks = 256;
+inline bool small_problem(int64_t b, int64_t d, int64_t L, int64_t N) {
+    return N <= 16 && L > 2 * kSmallSeg && L <= (int64_t)kSmallSeg * kSmallMaxWaves &&
+           b * ((d + kSmallCh - 1) / kSmallCh) <= kSmallMaxBlocks;
+}
+// Steps per wavefront: half of kSmallSeg where kSmallMaxWaves such segments cover the sequence.
+inline int small_seg(int64_t L) {
+    return L <= (int64_t)(kSmallSeg / 2) * kSmallMaxWaves ? kSmallSeg / 2 : kSmallSeg;
+}
+hipError_t launch_scan_small(const FwdLaunch &p, hipStream_t stream);
 
 // Everything the gradient launcher needs (validated by the ABI layer).
 struct BwdLaunch {

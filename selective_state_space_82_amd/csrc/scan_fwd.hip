@@ -783,6 +783,7 @@ hipError_t dispatch_shape(const FwdArgs &args, int n_seg, int64_t ncb, const Fwd
 }  // namespace
 
 hipError_t launch_scan_fwd(const FwdLaunch &p, hipStream_t stream) {
+    if (p.small) return launch_scan_small(p, stream);
     FwdArgs a{};
     a.x = p.x; a.delta = p.delta; a.A = p.A; a.B = p.B; a.C = p.C; a.D = p.D; a.z = p.z; a.y = p.y;
     a.final_state = p.final_state;

@@ -10,6 +10,7 @@ int g_launches = 0;
 
 hipError_t launch_scan_fwd(const FwdLaunch &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_fill_zero(float *, int64_t, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_scan_small(const FwdLaunch &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_scan_step(const StepLaunch &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_scan_bwd(const BwdLaunch &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_conv1d(const ConvLaunch &, hipStream_t) { ++g_launches; return hipSuccess; }

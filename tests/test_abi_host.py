@@ -91,9 +91,18 @@ def test_step_validation():
 
 
 def test_plan_shapes():
+    # a short sequence on few channel blocks: the small-problem kernel, one workgroup per block of 16 channels
+    # with a wavefront per 8 steps (16 steps beyond 128), no aggregate pass and no scratch
     p = api.ssm_scan_fwd_plan(1, 8, 128, 4)
-    assert p["n_segments"] == 1 and p["lanes_per_channel"] == 4 and p["states_per_lane"] == 4
-    assert p["scratch_bytes"] == 0 and p["waves_per_segment"] == 1
+    assert p["n_segments"] == 16 and p["seg_len"] == 8 and p["lanes_per_channel"] == 4 and p["states_per_lane"] == 4
+    assert p["scratch_bytes"] == 0 and p["waves_per_segment"] == 1 and p["groups_aggregate_pass"] == 0
+    p = api.ssm_scan_fwd_plan(2, 40, 200, 16)
+    assert p["n_segments"] == 13 and p["seg_len"] == 16 and p["groups_output_pass"] == 2 * 3
+    # an option asking for a plan of the main kernel, a sequence too long for it, or N > 16: the main kernel
+    p = api.ssm_scan_fwd_plan(1, 8, 128, 4, lanes_per_channel=4)
+    assert p["n_segments"] == 1 and p["seg_len"] == 128
+    assert api.ssm_scan_fwd_plan(1, 8, 257, 4)["n_segments"] == 1
+    assert api.ssm_scan_fwd_plan(1, 8, 128, 17)["n_segments"] == 1
     p = api.ssm_scan_fwd_plan(1, 2048, 131072, 16)
     assert p["n_segments"] > 1 and p["seg_len"] % 32 == 0
     assert p["seg_len"] * p["n_segments"] >= 131072

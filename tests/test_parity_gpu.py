@@ -134,6 +134,57 @@ def test_small_shapes(case):
     check_rows(inp, y, h, all_rows(b, d), f"small b{b} d{d} L{L} N{N} {dt} {opts}")
 
 
+# ------------------------------------------------------------------------------------------
+# Short sequences on few channel blocks (N <= 16, 32 < L <= 256, at most 256 blocks of 16 channels) run the
+# small-problem kernel: a workgroup per block of 16 channels, a wavefront per 8 steps (16 beyond L = 128),
+# each segment's map formed in LDS and chained before the segment is walked again with the readout.
+# ------------------------------------------------------------------------------------------
+SMALL_KERNEL = [
+    # b, d, L, N, dtype, gate, D, fraction of A set to 0
+    (1, 8, 128, 4, "f32", False, True, 0.0),     # the tiny workload's shape
+    (1, 1, 33, 1, "f32", True, True, 0.0),       # five segments, the last of one step; one channel, one state
+    (2, 17, 47, 5, "f32", True, False, 0.2),     # ragged channels, states and steps; A = 0 entries
+    (3, 70, 100, 16, "bf16", True, True, 0.0),
+    (1, 33, 255, 12, "bf16", False, True, 0.1),  # sixteen segments, the last of 15 steps
+    (2, 16, 256, 16, "f32", True, True, 0.0),    # sixteen whole segments
+]
+
+
+@pytest.mark.parametrize("case", SMALL_KERNEL, ids=lambda c: f"b{c[0]}_d{c[1]}_L{c[2]}_N{c[3]}_{c[4]}_g{int(c[5])}")
+def test_small_problem_kernel(case):
+    b, d, L, N, dt, gate, with_D, a0 = case
+    plan = api.ssm_scan_fwd_plan(b, d, L, N, torch.float32 if dt == "f32" else torch.bfloat16)
+    assert plan["seg_len"] == (8 if L <= 128 else 16) and plan["groups_aggregate_pass"] == 0, plan
+    inp = I.random_prefill(b, d, L, N, dtype=dt, gate=gate, with_D=with_D, seed=3 * L + N, a_zero_frac=a0)
+    y, h = run_fwd(inp)
+    check_rows(inp, y, h, all_rows(b, d), f"small-problem kernel b{b} d{d} L{L} N{N} {dt}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_small_problem_kernel_slow_channels(dt):
+    """The slow regime (A ~ -U(2^-10, 0.05), Δ = softplus(N(-5, 1))) through the small-problem kernel."""
+    inp = I.random_prefill(2, 24, 160, 16, dtype=dt, seed=13, a_kind="small", delta_mu=-5.0)
+    assert api.ssm_scan_fwd_plan(2, 24, 160, 16)["seg_len"] == 16
+    y, h = run_fwd(inp)
+    check_rows(inp, y, h, all_rows(2, 24), f"small-problem kernel slow channels {dt}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_small_problem_kernel_initial_state_and_main_kernel(dt):
+    """An initial state through the small-problem kernel, and the same call forced onto the main kernel
+    (an option that asks for its plan): both within the bar of the oracle."""
+    b, d, L, N = 2, 40, 200, 16
+    inp = I.random_prefill(b, d, L, N, dtype=dt, seed=41)
+    h0 = (np.random.default_rng(4).standard_normal((b, d, N)) * 0.5).astype(np.float32)
+    t = upload(inp)
+    for kw in ({}, {"lanes_per_channel": 4}):
+        y, h = api.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                                initial_state=torch.from_numpy(h0).cuda(), **kw)
+        torch.cuda.synchronize()
+        check_rows(inp, from_torch(y), from_torch(h), all_rows(b, d), f"h0 {dt} {kw or 'small-problem kernel'}",
+                   h0=h0.astype(np.float64))
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_zero_and_tiny_A_take_the_limit(dt):
     """A = 0 entries (ZOH limit Δ·B) and tiny |A| entries mixed with ordinary ones."""
