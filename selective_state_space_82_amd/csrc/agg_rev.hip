@@ -28,8 +28,11 @@
 // of step t − 1 are formed in the same stretch of code as the accumulation of step t, which carries only R
 // and E from step to step, so a wavefront has eight independent chains in flight.
 //
-// P needs ΣΔ over the whole segment: the wavefront of state group 0 sums Δ over the steps it did not walk
-// (those tiles of Δ alone) and writes P for all N states of its channels; P is exact whatever the sign of Δ.
+// P = exp(A·ΣΔ): each wavefront writes it for its own states, exact when its walk reached the segment start,
+// and 0 when the walk stopped early (every state it holds had decayed below 2^-24 by then, and P is no larger
+// than that decay times the carried-in state's own decay over the steps not walked; the term P·h_in is then
+// within one fp32 rounding of a state there, as the truncated part of E is). So no step beyond a walk's
+// stop is read.
 //
 // Split walk. When the caller gives E2 (a carry pass follows), group 0's walk, the longest, is split
 // between two wavefronts per unit by the same composition: the later part walks the segment's last tiles
@@ -348,25 +351,16 @@ __global__ __launch_bounds__(kWave, 3) void agg_rev_kernel(AggArgs a) {
     // `it` is now the highest tile not walked (−1 when the walk reached the segment start)
 
     const int64_t base = (seg * a.b * a.d + bi * a.d + ch) * a.N;
-    if (grp == 0 && part != 2) {
-        // ΣΔ over the tiles not walked (0 .. it), Δ only, one tile ahead
-        if (it >= 0) {
-            load_tile(t_begin + (int64_t)it * kT, false);
-#pragma unroll 1
-            for (int k = it; k >= 0; --k) {
-                wave_sync();
-                store_tile(false);
-                wave_sync();
-                if (k > 0) load_tile(t_begin + (int64_t)(k - 1) * kT, false);
-                dsum += row_dsum();
-            }
-        }
-        if (ch_ok) {
-            for (int m = 0; m < N; ++m) {
-                const float am = a.A[ch * a.N + m];
-                a.P[base + m] = __builtin_fabsf(am) < kZeroAbs ? 1.0f : exp2_fast(am * kLog2e * dsum);
-            }
-        }
+    if (part != 2) {
+        // P of this wavefront's states. A walk that reached the segment start has summed Δ over all of it, so
+        // P = exp(A·ΣΔ) is exact. A walk that stopped at step t_s did so with R ≤ 2^-24 for every live state, and
+        // the carried-in state h_in reaches the segment end as P·h_in = R·g(t_s), g(t_s) being h_in carried to
+        // t_s without inputs: at most 2^-24·|g(t_s)|, no more than one fp32 rounding of a state at t_s, so P is
+        // taken as 0 there and the tiles not walked are never read.
+        const bool whole = it < 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (live[j]) a.P[base + n0 + j] = zero[j] ? 1.0f : (whole ? exp2_fast(a2[j] * dsum) : 0.0f);
     }
     float *Eo = part == 1 ? a.E2 : a.E;
 #pragma unroll

@@ -84,3 +84,48 @@ def test_split_identity_with_negative_delta():
     h1 = _end_state(x, dl, A, B, h0=np.ones((d, N)))
     P = np.exp(A * dl.sum(axis=1)[:, None])
     np.testing.assert_allclose(h1, P * 1.0 + full, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", [
+    dict(delta_mu=-4.0, a_kind="neg_index_u", T=2944, neg=False),  # the long-context recipe, its segment length
+    dict(delta_mu=-2.0, a_kind="neg_index", T=1024, neg=False),
+    dict(delta_mu=0.0, a_kind="random", T=600, neg=True),          # Δ < 0 steps before the stop
+])
+def test_early_stop_drops_the_carried_term_within_a_rounding(case):
+    """A walk that stops early (R <= 2^-24 for every state of its group at a tile boundary t_s) leaves P = 0.
+    The term it drops from the segment's map, P·h_in, equals R·g(t_s), g(t_s) being the carried-in state h_in
+    taken to t_s without inputs (the state from h_in minus the state from zero there): it is at most 2^-24 times
+    those states, one fp32 rounding of a state at t_s. Where Δ >= 0 and A <= 0, P <= R <= 2^-24 as well."""
+    d, N, T = 16, 16, case["T"]
+    inp = I.random_prefill(1, d, T, N, dtype="f32", seed=T + 7, delta_mu=case["delta_mu"], a_kind=case["a_kind"])
+    x = I.widen(inp["x"], "f32")[0].astype(np.float64)
+    dl = I.widen(inp["delta"], "f32")[0].astype(np.float64)
+    if case["neg"]:
+        dl[:, 40:46] = -0.08
+    B = I.widen(inp["B"], "f32")[0].astype(np.float64)
+    A = inp["A"].astype(np.float64)
+    h_in = np.random.default_rng(T).standard_normal((d, N)) * 3.0
+    tail = np.cumsum(dl[:, ::-1], axis=1)[:, ::-1]
+    P = np.exp(A * dl.sum(axis=1)[:, None])
+    full_from_h = _end_state(x, dl, A, B, h0=h_in)
+    full_from_0 = _end_state(x, dl, A, B)
+    np.testing.assert_allclose(full_from_h, P * h_in + full_from_0, rtol=1e-10, atol=1e-12)
+    stopped = 0
+    for g in range(N // 4):
+        a = A[:, 4 * g:4 * g + 4]
+        ts = 0
+        for t in range(T - 32, 0, -32):
+            if np.all(np.exp(a * tail[:, t][:, None]) <= 2.0 ** -24):
+                ts = t
+                break
+        if ts == 0:
+            continue
+        stopped += 1
+        sl = slice(4 * g, 4 * g + 4)
+        h_t = _end_state(x[:, :ts], dl[:, :ts], A, B[:ts], h0=h_in)[:, sl]   # the state at t_s from h_in
+        h0_t = _end_state(x[:, :ts], dl[:, :ts], A, B[:ts])[:, sl]           # and from zero
+        dropped = (P * h_in)[:, sl]
+        assert np.all(np.abs(dropped) <= 2.0 ** -24 * (np.abs(h_t) + np.abs(h0_t)) + 1e-12)
+        if not case["neg"]:
+            assert np.all(P[:, sl] <= 2.0 ** -24)
+    assert stopped >= 1, "no state group stops early on these inputs: the case tests nothing"
