@@ -160,6 +160,18 @@ def test_small_problem_kernel(case):
     check_rows(inp, y, h, all_rows(b, d), f"small-problem kernel b{b} d{d} L{L} N{N} {dt}")
 
 
+def test_small_problem_kernel_without_state_gate_or_skip():
+    """The small-problem kernel with no final state asked for, no z and no D: y alone, against the oracle."""
+    b, d, L, N = 1, 20, 90, 6
+    inp = I.random_prefill(b, d, L, N, dtype="f32", gate=False, with_D=False, seed=77)
+    t = upload(inp)
+    y, h = api.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], None, None, return_final_state=False)
+    torch.cuda.synchronize()
+    assert h is None
+    yr, _ = oracle_prefill_rows(inp, all_rows(b, d))
+    assert_close(from_torch(y)[tuple(np.array(all_rows(b, d)).T)], yr, TAU["f32"], "small-problem kernel, y alone")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_small_problem_kernel_slow_channels(dt):
     """The slow regime (A ~ -U(2^-10, 0.05), Δ = softplus(N(-5, 1))) through the small-problem kernel."""

@@ -45,6 +45,14 @@ def check(inp, what, **kw):
     assert np.array_equal(y, y_ref) and np.array_equal(h, h_ref), f"{what}: results differ from ssm_scan_fwd"
 
 
+def test_small_problem_needs_no_scratch():
+    """A short sequence on few channel blocks (the small-problem kernel) through the no-allocation entry point:
+    no scratch at all, and the same bits as ssm_scan_fwd."""
+    plan = api.ssm_scan_fwd_plan(2, 40, 200, 16)
+    assert plan["scratch_bytes"] == 0 and plan["groups_aggregate_pass"] == 0
+    check(I.random_prefill(2, 40, 200, 16, dtype="bf16", seed=8), "small-problem kernel")
+
+
 def test_two_calls_in_a_row_second_smaller():
     """32 segments (a carry kernel chains the aggregates: carries in scratch too), then 11 segments on a
     smaller input (each output wavefront chains them)."""
