@@ -383,10 +383,10 @@ hipError_t launch_agg_rev(const AggLaunch &p, hipStream_t stream) {
     auto aligned16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
     a.vec_rows = ((p.L * esize) % 16 == 0) && aligned16(p.x) && aligned16(p.delta);
     a.vec_bc = ((p.L * p.N * esize) % 16 == 0) && aligned16(p.B);
-    // the split walk: group 0's later part takes the last fifth of each segment (on the long-context
-    // recipe, about half of that group's walk), so the two parts take similar times
+    // the split walk: group 0's later part takes the last eighth of each segment (the fastest fraction
+    // measured on the long-context recipe, among 1/3 .. 1/24)
     const int kt = p.bf16 ? 32 : 16;
-    a.split_tiles = a.E2 ? (int)((p.seg_len / kt + 4) / 5) : 0;
+    a.split_tiles = a.E2 ? (int)((p.seg_len / kt + 7) / 8) : 0;
     const int64_t grid = (a.n_units + kXcds - 1) / kXcds * kXcds * (a.n_grp + (a.E2 ? 1 : 0));
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const dim3 g((unsigned)grid), w(kWave);
