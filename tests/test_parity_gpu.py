@@ -347,6 +347,8 @@ TRUNC = {
     # the same with fast decay (the later part stops within its own steps) and with slow decay (no stop)
     "split_fast": dict(L=18 * 1024, delta_mu=0.5, seg_len=1024),
     "split_slow": dict(L=17 * 1024 + 64, a_value=-0.01, delta_value=0.01, seg_len=1024),
+    # a segment whose tile count (38 bf16 tiles, 76 fp32 tiles) is no multiple of the later part's share
+    "split_ragged_share": dict(L=17 * 1216 + 40, delta_mu=-4.0, a_kind="neg_index_u", seg_len=1216),
 }
 
 
